@@ -1,0 +1,164 @@
+"""Batch scheduler over the naive tree (oracle).
+
+The request path follows the SGLang explainer, section 04 ("from request
+arrival to cache reclamation" figure): waiting queue, tree match, admit
+within memory while protecting the matched path, evict reclaimable leaves
+when memory is short, run, then insert the new path.  The admission test
+follows the v0.2 handbook chapter ("new_token_ratio and retract" section):
+available = free slots + evictable tokens - sum over running requests of
+their remaining new tokens times a ratio; the ratio is fixed at 1.0 here
+because every request's output length is known in advance.
+
+Readings where the pages are silent: first come first served by arrival
+and request id, stop at the first request that does not fit; at most 256
+running requests and 16384 extend tokens per iteration (the first admitted
+request is exempt from the token cap); a request extended in iteration k
+decodes from iteration k+1; a request is inserted into the tree only when
+it finishes (prompt plus the tokens it fed), duplicate slots that the tree
+already holds are freed, then the admission lock is released.
+
+Attention outputs come from ``recompute_rows`` (full recompute, float64).
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .attention import recompute_rows
+from .radix_tree import NaivePool, NaiveRadixTree
+
+
+@dataclass
+class _Running:
+    req: object
+    prefix_len: int
+    node: int
+    slots: list
+    admit_iter: int
+    generated: int = 0
+
+
+@dataclass
+class OracleTrace:
+    iterations: list = field(default_factory=list)
+    cached_tokens: int = 0
+    prefill_tokens: int = 0
+    request_slots: dict = field(default_factory=dict)
+    dumps: list = field(default_factory=list)
+    outputs: dict = field(default_factory=dict)
+    free_list: list = field(default_factory=list)
+
+
+def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
+                 attention=True, want=None, keep_dumps=False, max_iterations=100000):
+    """Drive workload ``wl`` through the naive tree.  ``want(kind, rid, step)``
+    (kind 'ext' or 'dec') selects which attention outputs are recomputed;
+    by default all of them when ``attention`` is true."""
+    pool = NaivePool(num_slots if num_slots is not None else wl.num_slots)
+    tree = NaiveRadixTree(pool)
+    tr = OracleTrace()
+    pending = list(wl.requests)
+    finished = set()
+    waiting, running = [], []
+
+    def arrive():
+        nonlocal pending
+        still = []
+        for r in pending:
+            if all(a in finished for a in r.after):
+                waiting.append(r)
+            else:
+                still.append(r)
+        pending = still
+
+    def finish(run, it_rec):
+        full = list(run.req.prompt) + list(run.req.gen)
+        present = tree.insert(full, run.slots[:len(full)])
+        dups = run.slots[run.prefix_len:present] if present > run.prefix_len else []
+        pool.release(dups)
+        tree.unlock(run.node)
+        tr.request_slots[run.req.rid] = list(run.slots[:len(full)])
+        it_rec["finished"].append((run.req.rid, present, list(dups)))
+        finished.add(run.req.rid)
+
+    def selected(kind, rid, step):
+        if not attention:
+            return False
+        return True if want is None else want(kind, rid, step)
+
+    arrive()
+    it = 0
+    while waiting or running or pending:
+        if it >= max_iterations:
+            raise RuntimeError("workload did not drain")
+        rec = {"admitted": [], "extend_loc": [], "extend_freed": [], "decode": [],
+               "decode_freed": [], "finished": []}
+        # 1. admission, first come first served
+        reserved = sum(len(r.req.gen) - r.generated for r in running)
+        budget = max_extend_tokens
+        admitted = []
+        while waiting and len(running) + len(admitted) < max_running:
+            req = waiting[0]
+            slots, node = tree.match_prefix(req.prompt)
+            tree.lock(node)
+            p = len(slots)
+            e = len(req.prompt) - p
+            need = e + len(req.gen)
+            avail = pool.available() + tree.evictable_size() - reserved
+            if need > avail or (admitted and e > budget):
+                tree.unlock(node)
+                break
+            waiting.pop(0)
+            admitted.append(_Running(req, p, node, list(slots), it))
+            reserved += need
+            budget -= e
+        # 2. extend the admitted batch
+        if admitted:
+            total = sum(len(r.req.prompt) - r.prefix_len for r in admitted)
+            loc, freed = tree.alloc_with_evict(total) if total > 0 else ([], [])
+            rec["extend_loc"], rec["extend_freed"] = list(loc), list(freed)
+            off = 0
+            for r in admitted:
+                e = len(r.req.prompt) - r.prefix_len
+                r.slots += loc[off:off + e]
+                off += e
+                rec["admitted"].append((r.req.rid, r.prefix_len, e))
+                tr.cached_tokens += r.prefix_len
+                tr.prefill_tokens += len(r.req.prompt)
+                if e > 0 and not wl.skip_extend_attention and selected("ext", r.req.rid, 0):
+                    pos = np.arange(r.prefix_len, len(r.req.prompt))
+                    tr.outputs[("ext", r.req.rid, 0)] = recompute_rows(
+                        r.req.prompt, pos, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                        wl.seed, wl.sm_scale)
+            for r in admitted:
+                if len(r.req.gen) == 0:
+                    finish(r, rec)
+                else:
+                    running.append(r)
+        # 3. one decode step for requests admitted in earlier iterations
+        dec = [r for r in running if r.admit_iter < it]
+        if dec:
+            loc, freed = tree.alloc_with_evict(len(dec))
+            rec["decode_freed"] = list(freed)
+            for r, s in zip(dec, loc):
+                pos = len(r.req.prompt) + r.generated
+                r.slots.append(s)
+                rec["decode"].append((r.req.rid, pos, s))
+                if selected("dec", r.req.rid, r.generated):
+                    seq = list(r.req.prompt) + list(r.req.gen[:r.generated + 1])
+                    tr.outputs[("dec", r.req.rid, r.generated)] = recompute_rows(
+                        seq, [pos], wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                        wl.seed, wl.sm_scale)
+                r.generated += 1
+            done = [r for r in dec if r.generated == len(r.req.gen)]
+            for r in done:
+                running.remove(r)
+                finish(r, rec)
+        tr.iterations.append(rec)
+        if keep_dumps:
+            tr.dumps.append(tree.dump())
+        arrive()
+        it += 1
+    tr.free_list = list(pool.free)
+    tr.final_dump = tree.dump()
+    return tr

@@ -1,0 +1,75 @@
+"""The oracle scheduler on the small workloads: hit-rate integers against
+Theorem 3.1, conservation of slots, and the eviction script of the tiny
+workload with a 160-slot pool."""
+
+import numpy as np
+
+from oracle.hit_rate import optimal_hit_rate
+from oracle.runner import run_workload
+from synth import workloads
+
+
+def _slots_conserved(tr, num_slots):
+    tree_slots = []
+    for line in tr.final_dump.splitlines():
+        v = line.split(" v=")[1]
+        tree_slots += [int(s) for s in v.split(",")] if v else []
+    assert sorted(tree_slots + tr.free_list) == list(range(1, num_slots + 1))
+
+
+def test_tiny_512_reaches_theorem_optimum():
+    wl = workloads.tiny(512)
+    tr = run_workload(wl, attention=False)
+    assert (tr.cached_tokens, tr.prefill_tokens) == (96, 192)
+    assert tr.cached_tokens * 1 == int(optimal_hit_rate([r.prompt for r in wl.requests]) * 192)
+    _slots_conserved(tr, 512)
+    # nothing was evicted
+    assert all(not r["extend_freed"] and not r["decode_freed"] for r in tr.iterations)
+
+
+def test_tiny_160_eviction_script():
+    """Wave 2 needs 4 x (16 + 8) slots with 32 free: the extend allocation
+    of 64 evicts r0's tail then r1's leaf (48 tokens); the 4th decode step
+    evicts r2's leaf; the shared prefix and r3's leaf survive."""
+    wl = workloads.tiny(160)
+    tr = run_workload(wl, attention=False)
+    assert (tr.cached_tokens, tr.prefill_tokens) == (96 + 128, 192 + 192)
+    rs = tr.request_slots
+    wave2 = next(i for i, r in enumerate(tr.iterations) if any(a[0] == 4 for a in r["admitted"]))
+    rec = tr.iterations[wave2]
+    assert [a[1:] for a in rec["admitted"]] == [(32, 16)] * 4
+    assert rec["extend_freed"] == rs[0][32:] + rs[1][32:]
+    evict_steps = [i for i, r in enumerate(tr.iterations) if r["decode_freed"]]
+    assert len(evict_steps) == 1 and evict_steps[0] == wave2 + 5  # wave-2 decode step 4
+    assert tr.iterations[evict_steps[0]]["decode_freed"] == rs[2][32:]
+    _slots_conserved(tr, 160)
+    survivors = tr.final_dump
+    assert ",".join(map(str, rs[3][32:])) in survivors
+    for r in (0, 1, 2):
+        assert ",".join(map(str, rs[r][32:])) not in survivors
+
+
+def test_few_shot_and_chat_drain_and_conserve():
+    wl = workloads.few_shot(batch=6, prefix_len=64, suffix_len=16, decode_steps=2, num_slots=1000)
+    tr = run_workload(wl, attention=False)
+    assert tr.cached_tokens == 6 * 64 and tr.prefill_tokens == 64 + 6 * 80
+    _slots_conserved(tr, 1000)
+    wl = workloads.chat(sessions=6, turns=3, system_len=40, user_lo=8, user_hi=20, gen_len=6)
+    tr = run_workload(wl, attention=False)
+    _slots_conserved(tr, wl.num_slots)
+    assert tr.prefill_tokens == sum(len(r.prompt) for r in wl.requests)
+    # a 60% pool forces eviction and re-extension
+    assert any(r["extend_freed"] or r["decode_freed"] for r in tr.iterations)
+
+
+def test_outputs_are_recomputed_rows():
+    wl = workloads.tiny(512)
+    tr = run_workload(wl, attention=True)
+    assert tr.outputs[("ext", 0, 0)].shape == (48, 4, 64)
+    assert tr.outputs[("ext", 1, 0)].shape == (16, 4, 64)
+    assert tr.outputs[("dec", 2, 7)].shape == (1, 4, 64)
+    # r1's extend rows equal the corresponding rows of a full prefill of r1
+    from oracle.attention import recompute_rows
+    r1 = wl.requests[1]
+    full = recompute_rows(r1.prompt, np.arange(48), 4, 4, 64, wl.seed, wl.sm_scale)
+    assert np.max(np.abs(full[32:] - tr.outputs[("ext", 1, 0)])) < 1e-13
