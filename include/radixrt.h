@@ -1,0 +1,263 @@
+/*
+ * radixrt -- the RadixAttention hot path for AMD Instinct MI355X (gfx950).
+ *
+ * A host-side radix tree over a token-granular KV pool finds each request's
+ * cached prefix; HIP kernels scatter new K/V rows into the pool and run
+ * attention over pool rows gathered through a per-request slot table
+ * (req_to_token).  Sources (the four pages the project is built from):
+ *
+ *  [P1] SGLang paper summary (paperlayer.ai, arXiv 2312.07104v2), section 3
+ *       "Efficient KV Cache Reuse with RadixAttention": the tree maps token
+ *       sequences to KV tensors, LRU eviction of leaves, reference counters
+ *       protect nodes of running requests, cache and running requests share
+ *       one dynamically allocated pool.
+ *  [P2] SGLang explainer (yaopepe.com/papers/sglang), section 04
+ *       "RadixAttention": longest-prefix match from the root, edge split on a
+ *       partial match, the walkthrough figure (insert S+A, split on S+B,
+ *       evict leaf A while S and B are protected, C reuses S), the
+ *       token-weighted hit-rate formula, and the source excerpts on prefix
+ *       match (stamp access time, split, accumulate slots) and eviction (heap
+ *       of evictable leaves, free the leaf's slots, re-push a parent that
+ *       became an unlocked leaf).
+ *  [P4] SGLang v0.2 handbook chapter (anrans.github.io), sections "CUDA
+ *       Graph" and "new_token_ratio and retract": runtime metadata
+ *       req_pool_indices / seq_lens / out_cache_loc, padded entries writing
+ *       slot 0, and the admission estimate free + evictable - reservations.
+ *
+ * Conventions for every call:
+ *  - Status: RT_OK (0) or a negative RT_ERR_*; no exception crosses the ABI.
+ *    rt_last_error() returns a message for the calling thread's last error.
+ *  - Slots: the pool has usable slots 1..num_slots; slot 0 is reserved as the
+ *    harmless target of padded writes [P4] and is never handed out.
+ *  - Host pointers are marked (host); device pointers (device).  The caller
+ *    owns every buffer; the library never keeps a caller pointer after a call
+ *    returns.  Device calls allocate nothing, launch asynchronously on
+ *    `stream` (a hipStream_t; NULL is the default stream) and do not
+ *    synchronise.  A device call must follow, on the same stream, the
+ *    kv_store that wrote the slots it reads.
+ *  - The tree and pool are single-threaded objects: calls on one tree (or
+ *    its pool) must not overlap.
+ */
+#ifndef RADIXRT_H
+#define RADIXRT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum rt_status {
+  RT_OK = 0,
+  RT_ERR_INVALID = -1, /* bad argument, shape, length or handle */
+  RT_ERR_OOM = -2,     /* not enough free + evictable slots; nothing allocated */
+  RT_ERR_LOCKED = -3,  /* reserved: operation refused on a locked node */
+  RT_ERR_HIP = -4      /* a HIP launch or runtime call failed */
+};
+
+enum rt_dtype { RT_F32 = 0, RT_BF16 = 1 };
+
+typedef struct rt_pool rt_pool;
+typedef struct rt_tree rt_tree;
+/* Node handle: the node's creation id.  Valid until that node is evicted;
+ * a split keeps the handle on the lower part of the edge.  0 is the root. */
+typedef int64_t rt_node;
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* rt_last_error(void);
+/* ABI version of this header (incremented on incompatible changes). */
+int rt_abi_version(void);
+
+/* ---------------------------------------------------------------- pool --
+ * Token-slot allocator [P1 "one shared pool"; P2 freeing a leaf's slots].
+ * Free slots form a FIFO list that starts as 1..num_slots ascending;
+ * allocation takes from the head, frees append at the tail in the order
+ * given. */
+
+/* num_slots >= 1.  *out receives the pool (free with rt_pool_destroy). */
+int rt_pool_create(int32_t num_slots, rt_pool** out);
+void rt_pool_destroy(rt_pool* pool);
+/* Take n slots (host out_slots[n]); RT_ERR_OOM if fewer are free (nothing
+ * taken).  Never evicts: see rt_alloc_with_evict. */
+int rt_pool_alloc(rt_pool* pool, int32_t n, int32_t* out_slots);
+/* Return n slots (host).  Each must be in 1..num_slots; RT_ERR_INVALID if a
+ * slot is out of range or the free list would exceed num_slots (nothing is
+ * freed then). */
+int rt_pool_free(rt_pool* pool, const int32_t* slots, int32_t n);
+int32_t rt_pool_available(const rt_pool* pool);
+int32_t rt_pool_capacity(const rt_pool* pool);
+/* Copy the free list, head first, into host out[cap]; *out_len = its length
+ * (RT_ERR_INVALID, nothing copied, if cap < length). */
+int rt_pool_free_list(const rt_pool* pool, int32_t* out, int32_t cap, int32_t* out_len);
+
+/* ---------------------------------------------------------------- tree --
+ * Radix tree of cached prefixes bound to a pool [P1, P2].  A node holds a
+ * run of tokens and the KV slot of each; children are keyed by their first
+ * token.  An LRU clock advances by one per rt_match_prefix / rt_insert
+ * call; every node such a call walks through or creates is stamped with it.
+ * Eviction order is (last access, node id) ascending. */
+
+int rt_tree_create(rt_pool* pool, rt_tree** out);
+/* Destroys the tree; its slots are NOT returned to the pool. */
+void rt_tree_destroy(rt_tree* tree);
+
+/* Longest cached prefix of tokens[n] (host) [P2 prefix-match excerpt].
+ * Writes its slots to host out_slots (out_cap >= n required), its length to
+ * *out_len and the handle of its last node to *out_last (0 = root when
+ * nothing matches).  If the match ends inside an edge, the edge is split so
+ * that the matched part becomes its own node, which is returned; the new
+ * upper node copies the lower node's lock count. */
+int rt_match_prefix(rt_tree* tree, const int32_t* tokens, int32_t n, int32_t* out_slots,
+                    int32_t out_cap, int32_t* out_len, rt_node* out_last);
+
+/* Insert tokens[n] with their slots[n] (host) [P2 walkthrough step 2].
+ * Diverging edges are split; the unmatched rest becomes a new leaf.  Where
+ * the tree already holds a token its slot is kept; *out_present_len (may be
+ * NULL) receives how many leading tokens were already present, and the
+ * caller owns (and must free) its own slots in that range that it
+ * allocated. */
+int rt_insert(rt_tree* tree, const int32_t* tokens, const int32_t* slots, int32_t n,
+              int32_t* out_present_len);
+
+/* Reference counts on every non-root node from `node` up to the root
+ * [P1 "reference counters"; P2 lifetime figure].  Locked nodes are never
+ * evicted.  rt_unlock on a path with a zero count fails with
+ * RT_ERR_INVALID and changes nothing.  Locking the root is a no-op. */
+int rt_lock(rt_tree* tree, rt_node node);
+int rt_unlock(rt_tree* tree, rt_node node);
+
+/* Evict whole unlocked leaves, least recently used first, until at least
+ * num_tokens tokens are freed or no candidate is left [P2 eviction
+ * excerpt]; a parent that becomes an unlocked leaf joins the candidates.
+ * Freed slots go to the pool's tail in node order.  *out_evicted (may be
+ * NULL) receives the number of tokens freed; the first min(that, freed_cap)
+ * freed slots are copied to host out_freed_slots (may be NULL). */
+int rt_evict_lru_leaves(rt_tree* tree, int32_t num_tokens, int32_t* out_evicted,
+                        int32_t* out_freed_slots, int32_t freed_cap);
+
+/* Allocate n slots, first evicting the deficit (n - free) if the pool is
+ * short.  RT_ERR_OOM if still short: nothing is allocated, but evictions
+ * already made stand.  *out_evicted (may be NULL) = tokens evicted. */
+int rt_alloc_with_evict(rt_tree* tree, int32_t n, int32_t* out_slots, int32_t* out_evicted);
+
+/* Tokens held by unlocked nodes / by locked nodes (root excluded). */
+int64_t rt_evictable_size(const rt_tree* tree);
+int64_t rt_protected_size(const rt_tree* tree);
+int64_t rt_tree_num_nodes(const rt_tree* tree);
+
+/* Canonical text dump into host buf[cap]: pre-order from the root, children
+ * by first token ascending, one line per node
+ *   "<id> <parent id> <lock count> <last access> k=<t,t,...> v=<s,s,...>\n"
+ * with the root as "0 -1 0 0 k= v=".  *out_len = bytes needed (without a
+ * terminating NUL, which is written when it fits); RT_ERR_INVALID if cap is
+ * too small (then only *out_len is set). */
+int rt_tree_dump(const rt_tree* tree, char* buf, int64_t cap, int64_t* out_len);
+
+/* ------------------------------------------------------ batch helpers --
+ * Compositions of the calls above for a whole batch, so that a batch costs
+ * one crossing of the ABI.  Request i's tokens are
+ * tokens[token_offsets[i] .. token_offsets[i+1]) (host).  Row r of the slot
+ * table is req_to_token[r * stride .. r * stride + stride) (host). */
+
+/* For i in order: rt_match_prefix, rt_lock; then one rt_alloc_with_evict of
+ * sum_i (len_i - prefix_len_i) slots, split among the requests in order.
+ * Row rows[i] of req_to_token receives the matched slots followed by the
+ * new ones.  Outputs (host, n entries): prefix_lens, extend_lens, nodes;
+ * out_cache_loc receives the new slots (cap out_cache_cap), *out_num_new
+ * their count.  On RT_ERR_OOM every lock taken here is released (the
+ * matches' splits and stamps remain).  RT_ERR_INVALID if a request is
+ * longer than stride. */
+int rt_admit_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_offsets,
+                   int32_t n, int32_t* req_to_token, int64_t stride, const int32_t* rows,
+                   int32_t* prefix_lens, int32_t* extend_lens, rt_node* nodes,
+                   int32_t* out_cache_loc, int64_t out_cache_cap, int64_t* out_num_new);
+
+/* One decode step's slots: rt_alloc_with_evict(n), then
+ * req_to_token[rows[i] * stride + positions[i]] = slot i (host).
+ * out_cache_loc (host, n) receives the slots. */
+int rt_decode_slots_batch(rt_tree* tree, int32_t n, const int32_t* rows, const int32_t* positions,
+                          int32_t* req_to_token, int64_t stride, int32_t* out_cache_loc);
+
+/* Finish requests: for i in order, rt_insert(tokens_i, row rows[i] of
+ * req_to_token), free the row's slots in [prefix_lens[i], present_len)
+ * (the duplicates the tree already held), then rt_unlock(nodes[i]).
+ * *out_freed (may be NULL) = total duplicate slots freed. */
+int rt_finish_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_offsets,
+                    int32_t n, const int32_t* req_to_token, int64_t stride, const int32_t* rows,
+                    const int32_t* prefix_lens, const rt_node* nodes, int64_t* out_freed);
+
+/* -------------------------------------------------------------- device --
+ * Pools k_pool / v_pool: (device) [num_slots + 1, num_kv_heads, head_dim],
+ * contiguous, element type `dtype` (RT_F32 or RT_BF16), the same as q / o.
+ * head_dim is 64 or 128; num_q_heads is a positive multiple of num_kv_heads;
+ * query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * req_to_token: (device) int32 [rows, req_to_token_stride]; request b uses
+ * row req_pool_indices[b] (or row b when req_pool_indices is NULL), whose
+ * first prefix_lens[b] + extend_lens[b] entries are pool slots.  Slot
+ * contents are not range-checked on the device; the host checks shapes and
+ * host-side scalars and returns RT_ERR_INVALID before launching anything. */
+
+/* Scatter new rows into the pool [P4 out_cache_loc]:
+ * k_pool[out_cache_loc[t]] = k_new[t], v_pool[...] = v_new[t] for
+ * t < n_tokens; k_new / v_new (device) [n_tokens, num_kv_heads, head_dim].
+ * Bit-exact copy.  Repeated slots (e.g. padding to slot 0) leave one of the
+ * written rows there. */
+int kv_store(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+             const int32_t* out_cache_loc, int32_t n_tokens, int32_t num_kv_heads,
+             int32_t head_dim, int dtype, void* stream);
+
+/* Per-step update of the device slot table [P4 req_to_token written from
+ * out_cache_loc]: req_to_token[rows[i] * stride + positions[i]] = slots[i]
+ * for i < n.  rows, positions, slots: (device) int32 [n].  Positions must
+ * be < stride and rows inside the table (not checked on the device). */
+int req_to_token_scatter(int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* rows,
+                         const int32_t* positions, const int32_t* slots, int32_t n, void* stream);
+
+/* Extend (prefill of the uncached suffix) attention [P2 "match the longest
+ * prefix, reference the shared KV, prefill only the missed suffix"].
+ * For request b, extend row j < extend_lens[b] and query head h:
+ *   o[qo_indptr[b] + j][h] = sum_i softmax_i(sm_scale * q.k_i) v_i over keys
+ *   i = 0 .. prefix_lens[b] + j, k_i / v_i = pool rows at slot
+ *   req_to_token[row_b][i] of KV head h / (Hq / Hkv).
+ * q, o: (device) [total extend rows, num_q_heads, head_dim], rows packed in
+ * batch order with qo_indptr (device, int32 [batch + 1]) the exclusive
+ * prefix sum of extend_lens.  prefix_lens, extend_lens (device, int32
+ * [batch]).  max_extend_len (host) bounds every extend_lens[b] and sizes the
+ * grid.  extend_lens[b] = 0 is allowed (no rows).  fp32 accumulation; o has
+ * the input dtype. */
+int radix_extend_attention(const void* q, void* o, const void* k_pool, const void* v_pool,
+                           const int32_t* req_to_token, int32_t req_to_token_stride,
+                           const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                           const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
+                           int32_t max_extend_len, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, float sm_scale, int dtype, void* stream);
+
+/* Bytes of device workspace radix_decode_attention needs for these sizes
+ * (split-K partial maxima, sums and accumulators, fp32).  Negative on bad
+ * arguments. */
+int64_t radix_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                     int32_t max_kv_len);
+
+/* Batched decode attention: one query row per request, at sequence position
+ * prefix_lens[b] (its K/V already stored at req_to_token[row_b][prefix_lens[b]]):
+ *   o[b][h] = softmax-weighted sum over keys 0 .. prefix_lens[b] of KV head
+ *   h / (Hq / Hkv), gathered through req_to_token.
+ * q, o: (device) [batch, num_q_heads, head_dim].  extend_lens (device) may
+ * be NULL; if given every entry must be 1 (not checked on the device).
+ * max_kv_len (host) >= every prefix_lens[b] + 1.  The context is split into
+ * chunks processed in parallel and merged exactly by their (max, sum)
+ * statistics.  workspace (device) of workspace_bytes >=
+ * radix_decode_workspace_bytes(batch, num_q_heads, head_dim, max_kv_len). */
+int radix_decode_attention(const void* q, void* o, const void* k_pool, const void* v_pool,
+                           const int32_t* req_to_token, int32_t req_to_token_stride,
+                           const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                           const int32_t* extend_lens, int32_t batch, int32_t max_kv_len,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           float sm_scale, int dtype, void* workspace, int64_t workspace_bytes,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RADIXRT_H */

@@ -1,0 +1,333 @@
+"""ctypes binding of libradixrt.so.  Argument marshalling only: every call
+goes straight to the C entry point of the same name in include/radixrt.h.
+
+Host arrays are numpy int32/int64 arrays; device buffers are torch tensors
+(passed as raw pointers together with the current HIP stream).
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libradixrt.so")
+
+RT_OK, RT_ERR_INVALID, RT_ERR_OOM, RT_ERR_LOCKED, RT_ERR_HIP = 0, -1, -2, -3, -4
+RT_F32, RT_BF16 = 0, 1
+
+EXPORTS = [
+    "rt_last_error", "rt_abi_version",
+    "rt_pool_create", "rt_pool_destroy", "rt_pool_alloc", "rt_pool_free", "rt_pool_available",
+    "rt_pool_capacity", "rt_pool_free_list",
+    "rt_tree_create", "rt_tree_destroy", "rt_match_prefix", "rt_insert", "rt_lock", "rt_unlock",
+    "rt_evict_lru_leaves", "rt_alloc_with_evict", "rt_evictable_size", "rt_protected_size",
+    "rt_tree_num_nodes", "rt_tree_dump", "rt_admit_batch", "rt_decode_slots_batch", "rt_finish_batch",
+    "kv_store", "req_to_token_scatter", "radix_extend_attention", "radix_decode_workspace_bytes", "radix_decode_attention",
+]
+
+
+class RadixRTError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"radixrt error {code}: {msg}")
+        self.code = code
+
+
+class OOMError(RadixRTError):
+    pass
+
+
+_lib = None
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+
+
+def lib():
+    """The loaded library.  Fails loudly if it has not been built: there is
+    no fallback implementation."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m prefix_shared_kv_rt_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "rt_last_error": (ctypes.c_char_p, []),
+            "rt_abi_version": (ctypes.c_int, []),
+            "rt_pool_create": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(_vp)]),
+            "rt_pool_destroy": (None, [_vp]),
+            "rt_pool_alloc": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p]),
+            "rt_pool_free": (ctypes.c_int, [_vp, _i32p, ctypes.c_int32]),
+            "rt_pool_available": (ctypes.c_int32, [_vp]),
+            "rt_pool_capacity": (ctypes.c_int32, [_vp]),
+            "rt_pool_free_list": (ctypes.c_int, [_vp, _i32p, ctypes.c_int32, _i32p]),
+            "rt_tree_create": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
+            "rt_tree_destroy": (None, [_vp]),
+            "rt_match_prefix": (ctypes.c_int, [_vp, _i32p, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p, _i64p]),
+            "rt_insert": (ctypes.c_int, [_vp, _i32p, _i32p, ctypes.c_int32, _i32p]),
+            "rt_lock": (ctypes.c_int, [_vp, ctypes.c_int64]),
+            "rt_unlock": (ctypes.c_int, [_vp, ctypes.c_int64]),
+            "rt_evict_lru_leaves": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p, _i32p, ctypes.c_int32]),
+            "rt_alloc_with_evict": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p, _i32p]),
+            "rt_evictable_size": (ctypes.c_int64, [_vp]),
+            "rt_protected_size": (ctypes.c_int64, [_vp]),
+            "rt_tree_num_nodes": (ctypes.c_int64, [_vp]),
+            "rt_tree_dump": (ctypes.c_int, [_vp, ctypes.c_char_p, ctypes.c_int64, _i64p]),
+            "rt_admit_batch": (ctypes.c_int, [_vp, _i32p, _i64p, ctypes.c_int32, _i32p, ctypes.c_int64, _i32p,
+                                              _i32p, _i32p, _i64p, _i32p, ctypes.c_int64, _i64p]),
+            "rt_decode_slots_batch": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p, _i32p, _i32p, ctypes.c_int64,
+                                                     _i32p]),
+            "rt_finish_batch": (ctypes.c_int, [_vp, _i32p, _i64p, ctypes.c_int32, _i32p, ctypes.c_int64, _i32p,
+                                               _i32p, _i64p, _i64p]),
+            "kv_store": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int, _vp]),
+            "req_to_token_scatter": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int32, _vp]),
+            "radix_extend_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
+                                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
+                                                      _vp]),
+            "radix_decode_workspace_bytes": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                              ctypes.c_int32]),
+            "radix_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
+                                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
+                                                      _vp, ctypes.c_int64, _vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != RT_OK:
+        msg = lib().rt_last_error().decode()
+        if rc == RT_ERR_OOM:
+            raise OOMError(rc, msg)
+        raise RadixRTError(rc, msg)
+    return rc
+
+
+def _p32(a):
+    return a.ctypes.data_as(_i32p) if a is not None else None
+
+
+def _p64(a):
+    return a.ctypes.data_as(_i64p) if a is not None else None
+
+
+def _i32(x):
+    return np.ascontiguousarray(x, dtype=np.int32)
+
+
+# ------------------------------------------------------------------ host --
+def rt_pool_create(num_slots):
+    h = _vp()
+    _check(lib().rt_pool_create(int(num_slots), ctypes.byref(h)))
+    return h
+
+
+def rt_pool_destroy(pool):
+    lib().rt_pool_destroy(pool)
+
+
+def rt_pool_alloc(pool, n):
+    out = np.empty(max(int(n), 0), dtype=np.int32)
+    _check(lib().rt_pool_alloc(pool, int(n), _p32(out)))
+    return out
+
+
+def rt_pool_free(pool, slots):
+    s = _i32(slots)
+    _check(lib().rt_pool_free(pool, _p32(s), int(s.size)))
+
+
+def rt_pool_available(pool):
+    return int(lib().rt_pool_available(pool))
+
+
+def rt_pool_capacity(pool):
+    return int(lib().rt_pool_capacity(pool))
+
+
+def rt_pool_free_list(pool):
+    n = rt_pool_available(pool)
+    out = np.empty(n, dtype=np.int32)
+    got = ctypes.c_int32()
+    _check(lib().rt_pool_free_list(pool, _p32(out), n, ctypes.byref(got)))
+    return out[:got.value]
+
+
+def rt_tree_create(pool):
+    h = _vp()
+    _check(lib().rt_tree_create(pool, ctypes.byref(h)))
+    return h
+
+
+def rt_tree_destroy(tree):
+    lib().rt_tree_destroy(tree)
+
+
+def rt_match_prefix(tree, tokens):
+    t = _i32(tokens)
+    out = np.empty(max(t.size, 1), dtype=np.int32)
+    n = ctypes.c_int32()
+    node = ctypes.c_int64()
+    _check(lib().rt_match_prefix(tree, _p32(t), int(t.size), _p32(out), int(out.size), ctypes.byref(n),
+                                 ctypes.byref(node)))
+    return out[:n.value].copy(), int(node.value)
+
+
+def rt_insert(tree, tokens, slots):
+    t, s = _i32(tokens), _i32(slots)
+    if t.size != s.size:
+        raise ValueError("tokens and slots differ in length")
+    present = ctypes.c_int32()
+    _check(lib().rt_insert(tree, _p32(t), _p32(s), int(t.size), ctypes.byref(present)))
+    return int(present.value)
+
+
+def rt_lock(tree, node):
+    _check(lib().rt_lock(tree, int(node)))
+
+
+def rt_unlock(tree, node):
+    _check(lib().rt_unlock(tree, int(node)))
+
+
+def rt_evict_lru_leaves(tree, num_tokens, freed_cap=None):
+    """Returns (tokens evicted, freed slots in order)."""
+    cap = int(freed_cap) if freed_cap is not None else int(rt_evictable_size(tree))
+    out = np.empty(max(cap, 1), dtype=np.int32)
+    ev = ctypes.c_int32()
+    _check(lib().rt_evict_lru_leaves(tree, int(num_tokens), ctypes.byref(ev), _p32(out), cap))
+    return int(ev.value), out[:min(ev.value, cap)].copy()
+
+
+def rt_alloc_with_evict(tree, n):
+    """Returns (slots, tokens evicted)."""
+    out = np.empty(max(int(n), 1), dtype=np.int32)
+    ev = ctypes.c_int32()
+    _check(lib().rt_alloc_with_evict(tree, int(n), _p32(out), ctypes.byref(ev)))
+    return out[:int(n)].copy(), int(ev.value)
+
+
+def rt_evictable_size(tree):
+    return int(lib().rt_evictable_size(tree))
+
+
+def rt_protected_size(tree):
+    return int(lib().rt_protected_size(tree))
+
+
+def rt_tree_num_nodes(tree):
+    return int(lib().rt_tree_num_nodes(tree))
+
+
+def rt_tree_dump(tree):
+    need = ctypes.c_int64()
+    lib().rt_tree_dump(tree, None, 0, ctypes.byref(need))
+    buf = ctypes.create_string_buffer(need.value + 1)
+    _check(lib().rt_tree_dump(tree, buf, need.value + 1, ctypes.byref(need)))
+    return buf.raw[:need.value].decode()
+
+
+def rt_admit_batch(tree, tokens, token_offsets, req_to_token, rows):
+    """tokens: int32 concat; token_offsets: int64 [n+1]; req_to_token: int32
+    [R, stride] host array (written in place).  Returns (prefix_lens,
+    extend_lens, nodes, out_cache_loc)."""
+    t = _i32(tokens)
+    off = np.ascontiguousarray(token_offsets, dtype=np.int64)
+    rows = _i32(rows)
+    n = rows.size
+    assert req_to_token.dtype == np.int32 and req_to_token.flags.c_contiguous
+    stride = req_to_token.shape[1]
+    pl = np.empty(n, dtype=np.int32)
+    el = np.empty(n, dtype=np.int32)
+    nodes = np.empty(n, dtype=np.int64)
+    cap = int(off[-1] - off[0]) if n else 0
+    loc = np.empty(max(cap, 1), dtype=np.int32)
+    nnew = ctypes.c_int64()
+    _check(lib().rt_admit_batch(tree, _p32(t), _p64(off), n, _p32(req_to_token), stride, _p32(rows), _p32(pl),
+                                _p32(el), _p64(nodes), _p32(loc), cap, ctypes.byref(nnew)))
+    return pl, el, nodes, loc[:nnew.value].copy()
+
+
+def rt_decode_slots_batch(tree, rows, positions, req_to_token):
+    rows, pos = _i32(rows), _i32(positions)
+    out = np.empty(max(rows.size, 1), dtype=np.int32)
+    _check(lib().rt_decode_slots_batch(tree, rows.size, _p32(rows), _p32(pos), _p32(req_to_token),
+                                       req_to_token.shape[1], _p32(out)))
+    return out[:rows.size].copy()
+
+
+def rt_finish_batch(tree, tokens, token_offsets, req_to_token, rows, prefix_lens, nodes):
+    t = _i32(tokens)
+    off = np.ascontiguousarray(token_offsets, dtype=np.int64)
+    rows, pl = _i32(rows), _i32(prefix_lens)
+    nodes = np.ascontiguousarray(nodes, dtype=np.int64)
+    freed = ctypes.c_int64()
+    _check(lib().rt_finish_batch(tree, _p32(t), _p64(off), rows.size, _p32(req_to_token), req_to_token.shape[1],
+                                 _p32(rows), _p32(pl), _p64(nodes), ctypes.byref(freed)))
+    return int(freed.value)
+
+
+# ---------------------------------------------------------------- device --
+def _dptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return RT_BF16
+    if t.dtype == torch.float32:
+        return RT_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def kv_store(k_pool, v_pool, k_new, v_new, out_cache_loc, stream=None):
+    n, hkv, d = k_new.shape
+    _check(lib().kv_store(_dptr(k_pool), _dptr(v_pool), _dptr(k_new), _dptr(v_new), _dptr(out_cache_loc), n, hkv,
+                          d, _dtype_code(k_new), _stream(stream)))
+
+
+def req_to_token_scatter(req_to_token, rows, positions, slots, stream=None):
+    _check(lib().req_to_token_scatter(_dptr(req_to_token), req_to_token.shape[1], _dptr(rows), _dptr(positions),
+                                      _dptr(slots), rows.shape[0], _stream(stream)))
+
+
+def radix_extend_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens, extend_lens,
+                           qo_indptr, max_extend_len, sm_scale, stream=None):
+    _, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    batch = prefix_lens.shape[0]
+    _check(lib().radix_extend_attention(_dptr(q), _dptr(o), _dptr(k_pool), _dptr(v_pool), _dptr(req_to_token),
+                                        req_to_token.shape[1], _dptr(req_pool_indices), _dptr(prefix_lens),
+                                        _dptr(extend_lens), _dptr(qo_indptr), batch, int(max_extend_len), hq, hkv, d,
+                                        float(sm_scale), _dtype_code(q), _stream(stream)))
+
+
+def radix_decode_workspace_bytes(batch, num_q_heads, head_dim, max_kv_len):
+    return int(lib().radix_decode_workspace_bytes(int(batch), int(num_q_heads), int(head_dim), int(max_kv_len)))
+
+
+def radix_decode_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens, max_kv_len, sm_scale,
+                           workspace, extend_lens=None, stream=None):
+    batch, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    _check(lib().radix_decode_attention(_dptr(q), _dptr(o), _dptr(k_pool), _dptr(v_pool), _dptr(req_to_token),
+                                        req_to_token.shape[1], _dptr(req_pool_indices), _dptr(prefix_lens),
+                                        _dptr(extend_lens), batch, int(max_kv_len), hq, hkv, d, float(sm_scale),
+                                        _dtype_code(q), _dptr(workspace), workspace.numel() * workspace.element_size(),
+                                        _stream(stream)))

@@ -1,0 +1,375 @@
+// radix_extend_attention: attention for the uncached suffix of each request.
+//
+// The radix tree hands each request a cached prefix of P tokens whose K/V
+// already sit in the pool; only the E suffix tokens are new (SGLang
+// explainer, section 04: match the longest prefix, reference the shared
+// KV, prefill only the missed suffix).  Extend row j of request b attends
+// keys 0..P+j, all gathered through req_to_token -- the prefix in place,
+// the suffix just written by the scatter kernel.
+//
+// bf16 path (the hot one).  Work item = (KV head, request, tile of 128
+// query rows).  The query rows of a tile are (extend row, group head) pairs
+// with the G = Hq / Hkv heads of one KV head innermost, so every K/V tile
+// staged in LDS serves all G heads at once.  Four wavefronts own 32 rows
+// each.  Per 64-key tile:
+//   * 256 threads gather the 64 K rows and 64 V rows of this KV head
+//     (D*2 bytes each, 16-byte pieces, slots from req_to_token) into
+//     registers, then LDS; the next tile's gather is issued before the
+//     current tile's math so its HBM latency hides behind the MFMAs.
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B =
+//     the wave's Q rows held in registers for the whole kernel).  With keys
+//     as MFMA rows, each lane owns one query row, so the softmax max/sum
+//     need only one cross-lane exchange (lane ^ 32).
+//   * Online softmax in the log2 domain; the accumulator rescale is skipped
+//     when no row's running max moved (usual after the first tiles).
+//   * O^T += V^T P^T with the same MFMA.  P^T comes straight from the score
+//     registers (the key order of the contraction is chosen to match the
+//     score layout); V^T operands are read from LDS as 4-dim runs per lane
+//     and regrouped per dim with byte permutes.
+//   * Causal masking is applied only on tiles that cross the wave's
+//     diagonal; tiles beyond a wave's last row are skipped.
+// Work items are laid out so that each XCD (blockIdx % 8 on MI355X) runs a
+// contiguous slice of (KV head, request) items: requests that share a
+// prefix read the same K/V rows and find them in that XCD's L2.
+//
+// fp32 path: one wavefront per (extend row, query head), lanes over dims,
+// keys in order with wave-wide dot products.  For full-precision checks.
+
+#include <math.h>
+
+#include "dev_common.h"
+#include "radixrt.h"
+#include "rt_internal.h"
+
+namespace {
+
+using namespace rtk;
+
+constexpr int kBM = 128;  // query rows per work item (4 waves x 32)
+constexpr int kBN = 64;   // keys per LDS tile
+
+template <int D>
+struct ExtendCfg {
+  static constexpr int kRowBytes = D * 2;                 // one K or V row of one head
+  static constexpr int kPitch = kRowBytes + 16;           // LDS row pitch (bank spread)
+  static constexpr int kPieces = kBN * kRowBytes / 16;    // 16-byte pieces per tile
+  static constexpr int kPerThread = kPieces / 256;        // per thread, K and V each
+  static constexpr int kKS = D / 16;                      // 16-dim steps of Q K^T
+  static constexpr int kR = D / 32;                       // dims per lane in P V (tiles of O^T)
+};
+
+__device__ __forceinline__ int xcd_slice(int bid, int nblk) {
+  const int xcd = bid & 7, local = bid >> 3;
+  const int q = nblk >> 3, r = nblk & 7;
+  return xcd * q + min(xcd, r) + local;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) extend_bf16(
+    const char* __restrict__ q, char* __restrict__ o, const char* __restrict__ k_pool,
+    const char* __restrict__ v_pool, const int32_t* __restrict__ req_to_token, int64_t stride,
+    const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
+    const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ qo_indptr, int B, int Hq, int Hkv,
+    int G, int n_qt, float scale_log2) {
+  using C = ExtendCfg<D>;
+  __shared__ __attribute__((aligned(16))) char s_k[kBN * C::kPitch];
+  __shared__ __attribute__((aligned(16))) char s_v[kBN * C::kPitch];
+
+  const int work = xcd_slice(blockIdx.x, gridDim.x);
+  const int qt = work % n_qt;
+  const int b = (work / n_qt) % B;
+  const int kvh = work / (n_qt * B);
+
+  const int E = extend_lens[b];
+  const int row0 = qt * kBM;                  // first query row of this item
+  const int j_first = row0 / G;
+  if (j_first >= E) return;
+  const int P = prefix_lens[b];
+  const int j_last = min(E - 1, (row0 + kBM - 1) / G);
+  const int kv_end = P + j_last + 1;
+  const int n_tiles = (kv_end + kBN - 1) / kBN;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int r32 = lane & 31;   // this lane's query row within the wave / MFMA column
+  const int hi = lane >> 5;    // MFMA k-half
+
+  // This lane's query row.
+  const int qrow = row0 + wave * 32 + r32;
+  const int j = qrow / G;
+  const int g = qrow - j * G;
+  const bool row_ok = j < E;
+  const int limit = P + min(j, E - 1);        // last visible key (invalid rows mimic the last row)
+  const int wj_first = min((row0 + wave * 32) / G, E - 1);
+  const int wj_last = min((row0 + wave * 32 + 31) / G, E - 1);
+  const int w_min_limit = P + wj_first;       // keys <= this are visible to every row of the wave
+  const int w_end = P + wj_last + 1;          // keys >= this are invisible to every row of the wave
+
+  const int32_t* idx_row = req_to_token + int64_t(rpi ? rpi[b] : b) * stride;
+  const int64_t pool_row = int64_t(Hkv) * C::kRowBytes;
+  const char* kbase = k_pool + int64_t(kvh) * C::kRowBytes;
+  const char* vbase = v_pool + int64_t(kvh) * C::kRowBytes;
+
+  // Q^T operand (B of S^T = K Q^T): column r32 = query row, k = dims 16*ks + 8*hi + t.
+  bf16x8 qop[C::kKS];
+  {
+    const int64_t tok = int64_t(qo_indptr[b]) + j;
+    const char* qp = q + (tok * Hq + int64_t(kvh) * G + g) * C::kRowBytes + hi * 16;
+#pragma unroll
+    for (int ks = 0; ks < C::kKS; ++ks)
+      qop[ks] = as_bf16x8(row_ok ? ld16(qp + ks * 32) : u32x4{0, 0, 0, 0});
+  }
+
+  floatx16 oacc[C::kR];
+#pragma unroll
+  for (int r = 0; r < C::kR; ++r)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[r][i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  // Gather staging: piece p = tid + 256*it of the tile; key p / (D/8), 16-byte chunk p % (D/8).
+  u32x4 kst[C::kPerThread], vst[C::kPerThread];
+  auto gather = [&](int tile) {
+#pragma unroll
+    for (int it = 0; it < C::kPerThread; ++it) {
+      const int p = tid + 256 * it;
+      const int key = tile * kBN + p / (D / 8);
+      const int off = (p % (D / 8)) * 16;
+      if (key < kv_end) {
+        const int64_t slot = idx_row[key];
+        kst[it] = ld16(kbase + slot * pool_row + off);
+        vst[it] = ld16(vbase + slot * pool_row + off);
+      } else {
+        kst[it] = u32x4{0, 0, 0, 0};
+        vst[it] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  gather(0);
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < C::kPerThread; ++it) {
+      const int p = tid + 256 * it;
+      const int lds = (p / (D / 8)) * C::kPitch + (p % (D / 8)) * 16;
+      *reinterpret_cast<u32x4*>(s_k + lds) = kst[it];
+      *reinterpret_cast<u32x4*>(s_v + lds) = vst[it];
+    }
+    __syncthreads();
+    if (tile + 1 < n_tiles) gather(tile + 1);
+
+    const int base = tile * kBN;
+    if (base >= w_end) continue;              // wave-uniform: every row of this wave is done
+    const int nblk = (w_end - base) > 32 ? 2 : 1;
+
+    // ---- scores S^T[key][row] for up to two 32-key blocks
+    floatx16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+      if (kb < nblk) {
+        const char* kr = s_k + (kb * 32 + r32) * C::kPitch + hi * 16;
+#pragma unroll
+        for (int ks = 0; ks < C::kKS; ++ks)
+          sacc[kb] = mfma_32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(kr + ks * 32)), qop[ks], sacc[kb]);
+      }
+    }
+    // Lane holds keys base + 32*kb + 8*(v/4) + 4*hi + (v%4) of query row r32.
+    const bool need_mask = base + 2 * 32 - 1 > w_min_limit;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = base + 32 * kb + 8 * (v >> 2) + 4 * hi + (v & 3);
+        float s = sacc[kb][v];
+        if (kb >= nblk || (need_mask && key > limit)) s = -INFINITY;
+        sacc[kb][v] = s;
+        mx = fmaxf(mx, s);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m, mx * scale_log2);
+    if (__any(m_new > m)) {
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int r = 0; r < C::kR; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[r][i] *= alpha;
+      m = m_new;
+    }
+    const float neg_m = -m;
+
+    // ---- O^T += V^T P^T, 16 keys per MFMA
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb >= nblk) continue;
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        float p[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          p[t] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * sh + t], scale_log2, neg_m));
+          l += p[t];
+        }
+        const bf16x8 pop = as_bf16x8(u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
+        // logical k = 8*hi + t  <->  key 32*kb + 16*sh + 8*(t/4) + 4*hi + (t%4)
+        const char* vr = s_v + (32 * kb + 16 * sh + 4 * hi) * C::kPitch + r32 * (C::kR * 2);
+        if constexpr (D == 128) {
+          u32x2 L[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            L[t] = *reinterpret_cast<const u32x2*>(vr + (8 * (t >> 2) + (t & 3)) * C::kPitch);
+          u32x4 a0, a1, a2, a3;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            a0[w] = pack_lo16(L[2 * w].x, L[2 * w + 1].x);
+            a1[w] = pack_hi16(L[2 * w].x, L[2 * w + 1].x);
+            a2[w] = pack_lo16(L[2 * w].y, L[2 * w + 1].y);
+            a3[w] = pack_hi16(L[2 * w].y, L[2 * w + 1].y);
+          }
+          oacc[0] = mfma_32x32x16(as_bf16x8(a0), pop, oacc[0]);
+          oacc[1] = mfma_32x32x16(as_bf16x8(a1), pop, oacc[1]);
+          oacc[2] = mfma_32x32x16(as_bf16x8(a2), pop, oacc[2]);
+          oacc[3] = mfma_32x32x16(as_bf16x8(a3), pop, oacc[3]);
+        } else {
+          uint32_t L[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            L[t] = *reinterpret_cast<const uint32_t*>(vr + (8 * (t >> 2) + (t & 3)) * C::kPitch);
+          u32x4 a0, a1;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            a0[w] = pack_lo16(L[2 * w], L[2 * w + 1]);
+            a1[w] = pack_hi16(L[2 * w], L[2 * w + 1]);
+          }
+          oacc[0] = mfma_32x32x16(as_bf16x8(a0), pop, oacc[0]);
+          oacc[1] = mfma_32x32x16(as_bf16x8(a1), pop, oacc[1]);
+        }
+      }
+    }
+  }
+
+  // ---- normalise and store: tile r, register v holds dim kR*i + r, i = 8*(v/4) + 4*hi + (v%4)
+  l += __shfl_xor(l, 32, 64);
+  if (!row_ok) return;
+  const float inv = 1.f / l;
+  const int64_t tok = int64_t(qo_indptr[b]) + j;
+  char* op = o + (tok * Hq + int64_t(kvh) * G + g) * C::kRowBytes;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int i = 8 * (v >> 2) + 4 * hi + (v & 3);
+    if constexpr (D == 128) {
+      u32x2 w = {pack_bf16x2(oacc[0][v] * inv, oacc[1][v] * inv), pack_bf16x2(oacc[2][v] * inv, oacc[3][v] * inv)};
+      *reinterpret_cast<u32x2*>(op + (4 * i) * 2) = w;
+    } else {
+      *reinterpret_cast<uint32_t*>(op + (2 * i) * 2) = pack_bf16x2(oacc[0][v] * inv, oacc[1][v] * inv);
+    }
+  }
+}
+
+// ----------------------------------------------------------------- fp32 --
+template <int D>
+__global__ void __launch_bounds__(64) extend_f32(const float* __restrict__ q, float* __restrict__ o,
+                                                 const float* __restrict__ k_pool, const float* __restrict__ v_pool,
+                                                 const int32_t* __restrict__ req_to_token, int64_t stride,
+                                                 const int32_t* __restrict__ rpi,
+                                                 const int32_t* __restrict__ prefix_lens,
+                                                 const int32_t* __restrict__ extend_lens,
+                                                 const int32_t* __restrict__ qo_indptr, int Hq, int Hkv, int G,
+                                                 float scale_log2) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x;
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (j >= extend_lens[b]) return;
+  const int kvh = h / G;
+  const int n_keys = prefix_lens[b] + j + 1;
+  const int32_t* idx_row = req_to_token + int64_t(rpi ? rpi[b] : b) * stride;
+  const int64_t pool_row = int64_t(Hkv) * D;
+  const int64_t qo = (int64_t(qo_indptr[b]) + j) * Hq + h;
+  float qd[PER], acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    qd[i] = q[qo * D + lane + 64 * i];
+    acc[i] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int key = 0; key < n_keys; ++key) {
+    const int64_t slot = idx_row[key];
+    const float* kr = k_pool + slot * pool_row + int64_t(kvh) * D;
+    const float* vr = v_pool + slot * pool_row + int64_t(kvh) * D;
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) part = fmaf(qd[i], kr[lane + 64 * i], part);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+    const float sc = part * scale_log2;
+    const float m_new = fmaxf(m, sc);
+    const float alpha = exp2f(m - m_new);
+    const float p = exp2f(sc - m_new);
+    l = l * alpha + p;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = fmaf(p, vr[lane + 64 * i], acc[i] * alpha);
+    m = m_new;
+  }
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o[qo * D + lane + 64 * i] = acc[i] * inv;
+}
+
+}  // namespace
+
+extern "C" int radix_extend_attention(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                      const int32_t* req_to_token, int32_t req_to_token_stride,
+                                      const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                      const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
+                                      int32_t max_extend_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, float sm_scale, int dtype, void* stream) {
+  if (batch < 0 || max_extend_len < 0 || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_q_heads % num_kv_heads != 0 || (head_dim != 64 && head_dim != 128) ||
+      (dtype != RT_F32 && dtype != RT_BF16) || req_to_token_stride < 1 || !(sm_scale > 0.f))
+    return rt::fail(RT_ERR_INVALID, "radix_extend_attention: bad shape, dtype, stride or scale");
+  if (batch == 0 || max_extend_len == 0) return RT_OK;
+  if (!q || !o || !k_pool || !v_pool || !req_to_token || !prefix_lens || !extend_lens || !qo_indptr)
+    return rt::fail(RT_ERR_INVALID, "radix_extend_attention: null pointer");
+  const int G = num_q_heads / num_kv_heads;
+  const float scale_log2 = sm_scale * kLog2e;
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == RT_BF16) {
+    const int64_t n_qt = (int64_t(max_extend_len) * G + kBM - 1) / kBM;
+    const int64_t grid = n_qt * batch * num_kv_heads;
+    if (grid > INT32_MAX) return rt::fail(RT_ERR_INVALID, "radix_extend_attention: grid too large");
+    if (head_dim == 128)
+      hipLaunchKernelGGL(extend_bf16<128>, dim3(uint32_t(grid)), dim3(256), 0, st, (const char*)q, (char*)o,
+                         (const char*)k_pool, (const char*)v_pool, req_to_token, int64_t(req_to_token_stride),
+                         req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch, num_q_heads, num_kv_heads,
+                         G, int(n_qt), scale_log2);
+    else
+      hipLaunchKernelGGL(extend_bf16<64>, dim3(uint32_t(grid)), dim3(256), 0, st, (const char*)q, (char*)o,
+                         (const char*)k_pool, (const char*)v_pool, req_to_token, int64_t(req_to_token_stride),
+                         req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch, num_q_heads, num_kv_heads,
+                         G, int(n_qt), scale_log2);
+  } else {
+    if (max_extend_len > 65535 * 16 || num_q_heads > 65535 || batch > 65535)
+      return rt::fail(RT_ERR_INVALID, "radix_extend_attention: fp32 grid too large");
+    const dim3 grid{uint32_t(max_extend_len), uint32_t(num_q_heads), uint32_t(batch)};
+    if (head_dim == 128)
+      hipLaunchKernelGGL(extend_f32<128>, grid, dim3(64), 0, st, (const float*)q, (float*)o,
+                         (const float*)k_pool, (const float*)v_pool, req_to_token, int64_t(req_to_token_stride),
+                         req_pool_indices, prefix_lens, extend_lens, qo_indptr, num_q_heads, num_kv_heads, G,
+                         scale_log2);
+    else
+      hipLaunchKernelGGL(extend_f32<64>, grid, dim3(64), 0, st, (const float*)q, (float*)o,
+                         (const float*)k_pool, (const float*)v_pool, req_to_token, int64_t(req_to_token_stride),
+                         req_pool_indices, prefix_lens, extend_lens, qo_indptr, num_q_heads, num_kv_heads, G,
+                         scale_log2);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return rt::fail(RT_ERR_HIP, std::string("radix_extend_attention launch: ") + hipGetErrorString(e));
+  return RT_OK;
+}

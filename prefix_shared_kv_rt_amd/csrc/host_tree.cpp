@@ -1,0 +1,542 @@
+// Host-side radix tree and token-slot pool behind the C ABI.
+//
+// Behaviour follows the SGLang explainer, section 04 (RadixAttention): the
+// walkthrough figure (insert, split on a shared prefix, evict an idle LRU
+// leaf while running paths stay protected), and the two source excerpts
+// (prefix match that stamps each visited child and splits a partially
+// matched edge; eviction from a heap of unlocked leaves that re-pushes a
+// parent once it is an unlocked leaf).  Locks and the shared pool follow the
+// SGLang paper summary, section 3 ("Cache management").
+//
+// Data layout: nodes own their key and slot runs in std::vector; children
+// sit in a hash map keyed by first token; a side set tracks the unlocked
+// leaves so that eviction heapifies only the candidates; evictable and
+// protected token counts are kept incrementally.
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <memory>
+#include <queue>
+#include <string>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "radixrt.h"
+#include "rt_internal.h"
+
+namespace rt {
+
+// ------------------------------------------------------------------ pool --
+struct Pool {
+  int32_t capacity = 0;
+  std::vector<int32_t> ring;  // FIFO free list of capacity slots
+  int64_t head = 0;           // index of the first free slot in ring
+  int32_t count = 0;          // number of free slots
+
+  explicit Pool(int32_t n) : capacity(n), ring(n) {
+    for (int32_t i = 0; i < n; ++i) ring[i] = i + 1;
+    count = n;
+  }
+  int32_t take_one() {
+    int32_t s = ring[head];
+    head = (head + 1) % capacity;
+    --count;
+    return s;
+  }
+  void put_one(int32_t s) {
+    ring[(head + count) % capacity] = s;
+    ++count;
+  }
+  int alloc(int32_t n, int32_t* out) {
+    if (n < 0) return fail(RT_ERR_INVALID, "negative allocation");
+    if (n > count) return fail(RT_ERR_OOM, "pool: need " + std::to_string(n) + ", free " +
+                                               std::to_string(count));
+    for (int32_t i = 0; i < n; ++i) out[i] = take_one();
+    return RT_OK;
+  }
+  int release(const int32_t* slots, int64_t n) {
+    if (n < 0) return fail(RT_ERR_INVALID, "negative free");
+    if (int64_t(count) + n > capacity) return fail(RT_ERR_INVALID, "pool: free list overflow (double free?)");
+    for (int64_t i = 0; i < n; ++i)
+      if (slots[i] < 1 || slots[i] > capacity)
+        return fail(RT_ERR_INVALID, "pool: slot " + std::to_string(slots[i]) + " out of range");
+    for (int64_t i = 0; i < n; ++i) put_one(slots[i]);
+    return RT_OK;
+  }
+};
+
+// ------------------------------------------------------------------ tree --
+struct Node {
+  int64_t id;
+  std::vector<int32_t> key;
+  std::vector<int32_t> value;
+  std::unordered_map<int32_t, Node*> children;
+  Node* parent = nullptr;
+  int32_t lock_ref = 0;
+  uint64_t last_access = 0;
+};
+
+struct Tree {
+  Pool* pool;
+  uint64_t clock = 0;
+  int64_t next_id = 1;
+  std::unique_ptr<Node> root_owner;
+  Node* root;
+  std::unordered_map<int64_t, std::unique_ptr<Node>> nodes;  // non-root nodes by id
+  std::unordered_set<Node*> evictable_leaves;                // unlocked, childless, non-root
+  int64_t evictable = 0;
+  int64_t protected_ = 0;
+
+  explicit Tree(Pool* p) : pool(p), root_owner(new Node()) {
+    root = root_owner.get();
+    root->id = 0;
+  }
+
+  bool is_candidate(const Node* n) const {
+    return n != root && n->children.empty() && n->lock_ref == 0;
+  }
+  void refresh(Node* n) {
+    if (n == root) return;
+    if (is_candidate(n))
+      evictable_leaves.insert(n);
+    else
+      evictable_leaves.erase(n);
+  }
+
+  Node* make_node(Node* parent, const int32_t* key, const int32_t* val, int64_t len, uint64_t stamp) {
+    auto owned = std::make_unique<Node>();
+    Node* n = owned.get();
+    n->id = next_id++;
+    n->key.assign(key, key + len);
+    n->value.assign(val, val + len);
+    n->parent = parent;
+    n->last_access = stamp;
+    nodes.emplace(n->id, std::move(owned));
+    return n;
+  }
+
+  Node* find(int64_t id) {
+    if (id == 0) return root;
+    auto it = nodes.find(id);
+    return it == nodes.end() ? nullptr : it->second.get();
+  }
+
+  // Cut child's edge after k tokens (0 < k < len); the upper part becomes a
+  // new node with a fresh id, the child's stamp and lock count.
+  Node* split(Node* child, int64_t k) {
+    Node* parent = child->parent;
+    Node* upper = make_node(parent, child->key.data(), child->value.data(), k, child->last_access);
+    upper->lock_ref = child->lock_ref;
+    parent->children[child->key[0]] = upper;
+    child->key.erase(child->key.begin(), child->key.begin() + k);
+    child->value.erase(child->value.begin(), child->value.begin() + k);
+    child->parent = upper;
+    upper->children.emplace(child->key[0], child);
+    // token counts are unchanged (same lock count on both parts)
+    refresh(upper);
+    return upper;
+  }
+
+  static int64_t common_len(const std::vector<int32_t>& a, const int32_t* b, int64_t nb) {
+    int64_t m = std::min<int64_t>(int64_t(a.size()), nb);
+    int64_t k = 0;
+    while (k < m && a[k] == b[k]) ++k;
+    return k;
+  }
+
+  // Returns the last matched node; appends matched slots to out (if given).
+  Node* match(const int32_t* tokens, int64_t n, int32_t* out, int64_t* out_len) {
+    uint64_t stamp = ++clock;
+    Node* node = root;
+    int64_t pos = 0, len = 0;
+    while (pos < n) {
+      auto it = node->children.find(tokens[pos]);
+      if (it == node->children.end()) break;
+      Node* child = it->second;
+      child->last_access = stamp;
+      int64_t k = common_len(child->key, tokens + pos, n - pos);
+      if (k < int64_t(child->key.size())) {
+        Node* upper = split(child, k);
+        if (out) std::memcpy(out + len, upper->value.data(), sizeof(int32_t) * k);
+        len += k;
+        node = upper;
+        break;
+      }
+      if (out) std::memcpy(out + len, child->value.data(), sizeof(int32_t) * k);
+      len += k;
+      pos += k;
+      node = child;
+    }
+    *out_len = len;
+    return node;
+  }
+
+  int64_t insert(const int32_t* tokens, const int32_t* slots, int64_t n) {
+    uint64_t stamp = ++clock;
+    Node* node = root;
+    int64_t pos = 0;
+    while (pos < n) {
+      auto it = node->children.find(tokens[pos]);
+      if (it == node->children.end()) break;
+      Node* child = it->second;
+      child->last_access = stamp;
+      int64_t k = common_len(child->key, tokens + pos, n - pos);
+      if (k < int64_t(child->key.size())) child = split(child, k);
+      pos += k;
+      node = child;
+    }
+    if (pos < n) {
+      Node* leaf = make_node(node, tokens + pos, slots + pos, n - pos, stamp);
+      node->children.emplace(tokens[pos], leaf);
+      evictable += n - pos;
+      refresh(node);
+      refresh(leaf);
+    }
+    return pos;
+  }
+
+  void lock(Node* n) {
+    for (; n != root; n = n->parent) {
+      if (n->lock_ref++ == 0) {
+        evictable -= int64_t(n->key.size());
+        protected_ += int64_t(n->key.size());
+        refresh(n);
+      }
+    }
+  }
+
+  bool unlock(Node* n) {
+    for (Node* p = n; p != root; p = p->parent)
+      if (p->lock_ref == 0) return false;
+    for (; n != root; n = n->parent) {
+      if (--n->lock_ref == 0) {
+        protected_ -= int64_t(n->key.size());
+        evictable += int64_t(n->key.size());
+        refresh(n);
+      }
+    }
+    return true;
+  }
+
+  // Evicts leaves; appends freed slots to `freed` (if given).
+  int64_t evict(int64_t num_tokens, std::vector<int32_t>* freed) {
+    using Key = std::pair<std::pair<uint64_t, int64_t>, Node*>;
+    auto cmp = [](const Key& a, const Key& b) { return a.first > b.first; };  // min-heap
+    std::vector<Key> init;
+    init.reserve(evictable_leaves.size());
+    for (Node* n : evictable_leaves) init.push_back({{n->last_access, n->id}, n});
+    std::priority_queue<Key, std::vector<Key>, decltype(cmp)> heap(cmp, std::move(init));
+    int64_t evicted = 0;
+    while (evicted < num_tokens && !heap.empty()) {
+      Node* x = heap.top().second;
+      heap.pop();
+      int64_t len = int64_t(x->value.size());
+      pool->release(x->value.data(), len);  // cannot fail: the slots came from this pool
+      if (freed) freed->insert(freed->end(), x->value.begin(), x->value.end());
+      evicted += len;
+      evictable -= len;
+      Node* parent = x->parent;
+      parent->children.erase(x->key[0]);
+      evictable_leaves.erase(x);
+      nodes.erase(x->id);
+      if (is_candidate(parent)) {
+        evictable_leaves.insert(parent);
+        heap.push({{parent->last_access, parent->id}, parent});
+      }
+    }
+    return evicted;
+  }
+
+  int alloc_with_evict(int32_t n, int32_t* out, int32_t* out_evicted) {
+    if (n < 0) return fail(RT_ERR_INVALID, "negative allocation");
+    int64_t ev = 0;
+    if (n > pool->count) ev = evict(int64_t(n) - pool->count, nullptr);
+    if (out_evicted) *out_evicted = int32_t(ev);
+    if (n > pool->count)
+      return fail(RT_ERR_OOM, "need " + std::to_string(n) + " slots, " + std::to_string(pool->count) +
+                                  " free after evicting " + std::to_string(ev));
+    return pool->alloc(n, out);
+  }
+
+  void dump_node(const Node* n, int64_t parent_id, std::string& s) const {
+    s += std::to_string(n->id);
+    s += ' ';
+    s += std::to_string(parent_id);
+    s += ' ';
+    s += std::to_string(n->lock_ref);
+    s += ' ';
+    s += std::to_string(n->last_access);
+    s += " k=";
+    for (size_t i = 0; i < n->key.size(); ++i) {
+      if (i) s += ',';
+      s += std::to_string(n->key[i]);
+    }
+    s += " v=";
+    for (size_t i = 0; i < n->value.size(); ++i) {
+      if (i) s += ',';
+      s += std::to_string(n->value[i]);
+    }
+    s += '\n';
+    std::vector<std::pair<int32_t, const Node*>> kids(n->children.begin(), n->children.end());
+    std::sort(kids.begin(), kids.end(),
+              [](const auto& a, const auto& b) { return a.first < b.first; });
+    for (auto& kv : kids) dump_node(kv.second, n->id, s);
+  }
+};
+
+}  // namespace rt
+
+// ===================================================================== ABI ==
+using rt::fail;
+
+struct rt_pool {
+  rt::Pool impl;
+  explicit rt_pool(int32_t n) : impl(n) {}
+};
+struct rt_tree {
+  rt::Tree impl;
+  explicit rt_tree(rt_pool* p) : impl(&p->impl) {}
+};
+
+#define RT_GUARD_BEGIN try {
+#define RT_GUARD_END                                        \
+  }                                                         \
+  catch (const std::bad_alloc&) {                           \
+    return fail(RT_ERR_OOM, "host allocation failed");      \
+  }                                                         \
+  catch (const std::exception& e) {                         \
+    return fail(RT_ERR_INVALID, e.what());                  \
+  }
+
+extern "C" {
+
+int rt_pool_create(int32_t num_slots, rt_pool** out) {
+  if (!out || num_slots < 1) return fail(RT_ERR_INVALID, "rt_pool_create: num_slots >= 1 and out required");
+  RT_GUARD_BEGIN
+  *out = new rt_pool(num_slots);
+  return RT_OK;
+  RT_GUARD_END
+}
+
+void rt_pool_destroy(rt_pool* pool) { delete pool; }
+
+int rt_pool_alloc(rt_pool* pool, int32_t n, int32_t* out_slots) {
+  if (!pool || (n > 0 && !out_slots)) return fail(RT_ERR_INVALID, "rt_pool_alloc: null argument");
+  return pool->impl.alloc(n, out_slots);
+}
+
+int rt_pool_free(rt_pool* pool, const int32_t* slots, int32_t n) {
+  if (!pool || (n > 0 && !slots)) return fail(RT_ERR_INVALID, "rt_pool_free: null argument");
+  return pool->impl.release(slots, n);
+}
+
+int32_t rt_pool_available(const rt_pool* pool) { return pool ? pool->impl.count : 0; }
+int32_t rt_pool_capacity(const rt_pool* pool) { return pool ? pool->impl.capacity : 0; }
+
+int rt_pool_free_list(const rt_pool* pool, int32_t* out, int32_t cap, int32_t* out_len) {
+  if (!pool || !out_len) return fail(RT_ERR_INVALID, "rt_pool_free_list: null argument");
+  const rt::Pool& p = pool->impl;
+  *out_len = p.count;
+  if (cap < p.count || (p.count > 0 && !out)) return fail(RT_ERR_INVALID, "rt_pool_free_list: buffer too small");
+  for (int32_t i = 0; i < p.count; ++i) out[i] = p.ring[(p.head + i) % p.capacity];
+  return RT_OK;
+}
+
+int rt_tree_create(rt_pool* pool, rt_tree** out) {
+  if (!pool || !out) return fail(RT_ERR_INVALID, "rt_tree_create: null argument");
+  RT_GUARD_BEGIN
+  *out = new rt_tree(pool);
+  return RT_OK;
+  RT_GUARD_END
+}
+
+void rt_tree_destroy(rt_tree* tree) { delete tree; }
+
+int rt_match_prefix(rt_tree* tree, const int32_t* tokens, int32_t n, int32_t* out_slots,
+                    int32_t out_cap, int32_t* out_len, rt_node* out_last) {
+  if (!tree || n < 0 || (n > 0 && (!tokens || !out_slots)) || !out_len || !out_last)
+    return fail(RT_ERR_INVALID, "rt_match_prefix: bad argument");
+  if (out_cap < n) return fail(RT_ERR_INVALID, "rt_match_prefix: out_cap < n");
+  RT_GUARD_BEGIN
+  int64_t len = 0;
+  rt::Node* last = tree->impl.match(tokens, n, out_slots, &len);
+  *out_len = int32_t(len);
+  *out_last = last->id;
+  return RT_OK;
+  RT_GUARD_END
+}
+
+int rt_insert(rt_tree* tree, const int32_t* tokens, const int32_t* slots, int32_t n,
+              int32_t* out_present_len) {
+  if (!tree || n < 0 || (n > 0 && (!tokens || !slots))) return fail(RT_ERR_INVALID, "rt_insert: bad argument");
+  RT_GUARD_BEGIN
+  int64_t present = tree->impl.insert(tokens, slots, n);
+  if (out_present_len) *out_present_len = int32_t(present);
+  return RT_OK;
+  RT_GUARD_END
+}
+
+int rt_lock(rt_tree* tree, rt_node node) {
+  if (!tree) return fail(RT_ERR_INVALID, "rt_lock: null tree");
+  rt::Node* n = tree->impl.find(node);
+  if (!n) return fail(RT_ERR_INVALID, "rt_lock: unknown node " + std::to_string(node));
+  tree->impl.lock(n);
+  return RT_OK;
+}
+
+int rt_unlock(rt_tree* tree, rt_node node) {
+  if (!tree) return fail(RT_ERR_INVALID, "rt_unlock: null tree");
+  rt::Node* n = tree->impl.find(node);
+  if (!n) return fail(RT_ERR_INVALID, "rt_unlock: unknown node " + std::to_string(node));
+  if (!tree->impl.unlock(n)) return fail(RT_ERR_INVALID, "rt_unlock: lock count would go below zero");
+  return RT_OK;
+}
+
+int rt_evict_lru_leaves(rt_tree* tree, int32_t num_tokens, int32_t* out_evicted,
+                        int32_t* out_freed_slots, int32_t freed_cap) {
+  if (!tree || num_tokens < 0) return fail(RT_ERR_INVALID, "rt_evict_lru_leaves: bad argument");
+  RT_GUARD_BEGIN
+  std::vector<int32_t> freed;
+  int64_t ev = tree->impl.evict(num_tokens, out_freed_slots ? &freed : nullptr);
+  if (out_evicted) *out_evicted = int32_t(ev);
+  if (out_freed_slots) {
+    int64_t m = std::min<int64_t>(int64_t(freed.size()), std::max(freed_cap, 0));
+    std::memcpy(out_freed_slots, freed.data(), sizeof(int32_t) * m);
+  }
+  return RT_OK;
+  RT_GUARD_END
+}
+
+int rt_alloc_with_evict(rt_tree* tree, int32_t n, int32_t* out_slots, int32_t* out_evicted) {
+  if (!tree || (n > 0 && !out_slots)) return fail(RT_ERR_INVALID, "rt_alloc_with_evict: bad argument");
+  RT_GUARD_BEGIN
+  return tree->impl.alloc_with_evict(n, out_slots, out_evicted);
+  RT_GUARD_END
+}
+
+int64_t rt_evictable_size(const rt_tree* tree) { return tree ? tree->impl.evictable : 0; }
+int64_t rt_protected_size(const rt_tree* tree) { return tree ? tree->impl.protected_ : 0; }
+int64_t rt_tree_num_nodes(const rt_tree* tree) { return tree ? int64_t(tree->impl.nodes.size()) + 1 : 0; }
+
+int rt_tree_dump(const rt_tree* tree, char* buf, int64_t cap, int64_t* out_len) {
+  if (!tree || !out_len) return fail(RT_ERR_INVALID, "rt_tree_dump: null argument");
+  RT_GUARD_BEGIN
+  std::string s;
+  tree->impl.dump_node(tree->impl.root, -1, s);
+  *out_len = int64_t(s.size());
+  if (!buf || cap < int64_t(s.size())) return fail(RT_ERR_INVALID, "rt_tree_dump: buffer too small");
+  std::memcpy(buf, s.data(), s.size());
+  if (cap > int64_t(s.size())) buf[s.size()] = '\0';
+  return RT_OK;
+  RT_GUARD_END
+}
+
+int rt_admit_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_offsets, int32_t n,
+                   int32_t* req_to_token, int64_t stride, const int32_t* rows, int32_t* prefix_lens,
+                   int32_t* extend_lens, rt_node* nodes, int32_t* out_cache_loc,
+                   int64_t out_cache_cap, int64_t* out_num_new) {
+  if (!tree || n < 0 || !token_offsets || (n > 0 && (!tokens || !req_to_token || !rows || !prefix_lens ||
+                                                      !extend_lens || !nodes)) ||
+      stride < 1 || !out_num_new)
+    return fail(RT_ERR_INVALID, "rt_admit_batch: bad argument");
+  RT_GUARD_BEGIN
+  rt::Tree& t = tree->impl;
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int64_t len = token_offsets[i + 1] - token_offsets[i];
+    if (len < 0 || len > stride) return fail(RT_ERR_INVALID, "rt_admit_batch: request longer than stride");
+    if (rows[i] < 0) return fail(RT_ERR_INVALID, "rt_admit_batch: negative row");
+    total += len;
+  }
+  int64_t new_total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t* tk = tokens + token_offsets[i];
+    int64_t len = token_offsets[i + 1] - token_offsets[i];
+    int32_t* row = req_to_token + int64_t(rows[i]) * stride;
+    int64_t plen = 0;
+    rt::Node* last = t.match(tk, len, row, &plen);
+    t.lock(last);
+    nodes[i] = last->id;
+    prefix_lens[i] = int32_t(plen);
+    extend_lens[i] = int32_t(len - plen);
+    new_total += len - plen;
+  }
+  *out_num_new = new_total;
+  auto unlock_all = [&]() {
+    for (int32_t i = n - 1; i >= 0; --i) t.unlock(t.find(nodes[i]));
+  };
+  if (new_total > out_cache_cap || (new_total > 0 && !out_cache_loc)) {
+    unlock_all();
+    return fail(RT_ERR_INVALID, "rt_admit_batch: out_cache_loc too small");
+  }
+  if (new_total > INT32_MAX) {
+    unlock_all();
+    return fail(RT_ERR_INVALID, "rt_admit_batch: too many new tokens");
+  }
+  int rc = t.alloc_with_evict(int32_t(new_total), out_cache_loc, nullptr);
+  if (rc != RT_OK) {
+    unlock_all();
+    return rc;
+  }
+  int64_t off = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t* row = req_to_token + int64_t(rows[i]) * stride;
+    std::memcpy(row + prefix_lens[i], out_cache_loc + off, sizeof(int32_t) * extend_lens[i]);
+    off += extend_lens[i];
+  }
+  (void)total;
+  return RT_OK;
+  RT_GUARD_END
+}
+
+int rt_decode_slots_batch(rt_tree* tree, int32_t n, const int32_t* rows, const int32_t* positions,
+                          int32_t* req_to_token, int64_t stride, int32_t* out_cache_loc) {
+  if (!tree || n < 0 || (n > 0 && (!rows || !positions || !req_to_token || !out_cache_loc)) || stride < 1)
+    return fail(RT_ERR_INVALID, "rt_decode_slots_batch: bad argument");
+  for (int32_t i = 0; i < n; ++i)
+    if (rows[i] < 0 || positions[i] < 0 || positions[i] >= stride)
+      return fail(RT_ERR_INVALID, "rt_decode_slots_batch: row or position out of range");
+  RT_GUARD_BEGIN
+  int rc = tree->impl.alloc_with_evict(n, out_cache_loc, nullptr);
+  if (rc != RT_OK) return rc;
+  for (int32_t i = 0; i < n; ++i) req_to_token[int64_t(rows[i]) * stride + positions[i]] = out_cache_loc[i];
+  return RT_OK;
+  RT_GUARD_END
+}
+
+int rt_finish_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_offsets, int32_t n,
+                    const int32_t* req_to_token, int64_t stride, const int32_t* rows,
+                    const int32_t* prefix_lens, const rt_node* nodes, int64_t* out_freed) {
+  if (!tree || n < 0 || !token_offsets ||
+      (n > 0 && (!tokens || !req_to_token || !rows || !prefix_lens || !nodes)) || stride < 1)
+    return fail(RT_ERR_INVALID, "rt_finish_batch: bad argument");
+  RT_GUARD_BEGIN
+  rt::Tree& t = tree->impl;
+  for (int32_t i = 0; i < n; ++i) {
+    int64_t len = token_offsets[i + 1] - token_offsets[i];
+    if (len < 0 || len > stride || rows[i] < 0 || prefix_lens[i] < 0 || prefix_lens[i] > len)
+      return fail(RT_ERR_INVALID, "rt_finish_batch: bad request " + std::to_string(i));
+    if (!t.find(nodes[i])) return fail(RT_ERR_INVALID, "rt_finish_batch: unknown node");
+  }
+  int64_t freed = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t* tk = tokens + token_offsets[i];
+    int64_t len = token_offsets[i + 1] - token_offsets[i];
+    const int32_t* row = req_to_token + int64_t(rows[i]) * stride;
+    int64_t present = t.insert(tk, row, len);
+    if (present > prefix_lens[i]) {
+      int rc = t.pool->release(row + prefix_lens[i], present - prefix_lens[i]);
+      if (rc != RT_OK) return rc;
+      freed += present - prefix_lens[i];
+    }
+    rt::Node* node = t.find(nodes[i]);
+    if (!node || !t.unlock(node)) return fail(RT_ERR_INVALID, "rt_finish_batch: unlock failed");
+  }
+  if (out_freed) *out_freed = freed;
+  return RT_OK;
+  RT_GUARD_END
+}
+
+}  // extern "C"

@@ -1,0 +1,276 @@
+"""Host driver of the RadixAttention hot path.
+
+``RadixRuntime`` owns one tree + pool (C++, through the C ABI), the device
+K/V pools, the request-to-slot table and the decode workspace, and runs the
+device steps (scatter, extend attention, decode attention) on one stream.
+
+``Scheduler`` drives a list of requests through it, batch by batch.  The
+request path follows the SGLang explainer, section 04 (figure "from request
+arrival to cache reclamation"): waiting queue, tree match, admission within
+memory while the matched path is protected, eviction when memory is short,
+execution, then insertion of the finished sequence.  Admission uses the v0.2
+handbook's estimate (section "new_token_ratio and retract"): free slots +
+evictable tokens - remaining new tokens of running requests, with the ratio
+fixed at 1 since output lengths are known in advance.  Where the pages are
+silent the policy is: first come first served, stop at the first request
+that does not fit, at most ``max_running`` requests and
+``max_extend_tokens`` extend tokens per iteration (the first admitted
+request is exempt from the token cap), a request extended in iteration k
+decodes from iteration k+1, and a request enters the tree only when it
+finishes (its duplicate slots are freed, then its admission lock released).
+
+Q/K/V of new tokens come from a caller-supplied ``qkv_source(rid, tokens,
+positions)`` returning device tensors; the runtime itself computes no
+attention values on the host.
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+class RadixRuntime:
+    def __init__(self, num_slots, num_q_heads, num_kv_heads, head_dim, dtype, max_reqs, max_ctx,
+                 device="cuda", stream=None):
+        self.num_slots = int(num_slots)
+        self.hq, self.hkv, self.d = int(num_q_heads), int(num_kv_heads), int(head_dim)
+        self.dtype = dtype
+        self.max_reqs, self.max_ctx = int(max_reqs), int(max_ctx)
+        self.device = torch.device(device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        self.pool = B.rt_pool_create(self.num_slots)
+        self.tree = B.rt_tree_create(self.pool)
+        # Slot 0 stays zero: padded writes land there and it is never read as data.
+        self.k_pool = torch.zeros((self.num_slots + 1, self.hkv, self.d), dtype=dtype, device=self.device)
+        self.v_pool = torch.zeros_like(self.k_pool)
+        self.r2t_host_t = torch.zeros((self.max_reqs, self.max_ctx), dtype=torch.int32, pin_memory=True)
+        self.r2t_host = self.r2t_host_t.numpy()
+        self.r2t_dev = torch.zeros((self.max_reqs, self.max_ctx), dtype=torch.int32, device=self.device)
+        self.free_rows = list(range(self.max_reqs))
+        self.sm_scale = 1.0 / float(np.sqrt(self.d))
+        self._ws = torch.empty(0, dtype=torch.uint8, device=self.device)
+
+    def close(self):
+        if self.tree is not None:
+            B.rt_tree_destroy(self.tree)
+            B.rt_pool_destroy(self.pool)
+            self.tree = self.pool = None
+
+    # ----------------------------------------------------------- helpers --
+    def _to_dev(self, arr, dtype=torch.int32):
+        t = torch.from_numpy(np.ascontiguousarray(arr)).to(dtype)
+        return t.pin_memory().to(self.device, non_blocking=True)
+
+    def workspace(self, batch, max_kv_len):
+        need = B.radix_decode_workspace_bytes(batch, self.hq, self.d, max_kv_len)
+        if self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def upload_rows(self, rows, lens):
+        """Copy the first lens[i] entries of host rows rows[i] to the device table."""
+        with torch.cuda.stream(self.stream):
+            for r, n in zip(rows, lens):
+                if n > 0:
+                    self.r2t_dev[r, :n].copy_(self.r2t_host_t[r, :n], non_blocking=True)
+
+    # ------------------------------------------------------ device steps --
+    def run_extend(self, rows, prefix_lens, extend_lens, q, k_new, v_new, out_cache_loc, attention=True):
+        """kv_store of the new rows, then extend attention.  Returns o (or None)."""
+        n = len(rows)
+        with torch.cuda.stream(self.stream):
+            loc = self._to_dev(out_cache_loc)
+            if loc.numel() > 0:
+                B.kv_store(self.k_pool, self.v_pool, k_new, v_new, loc, stream=self.stream)
+            if not attention or loc.numel() == 0:
+                return None
+            qo = np.zeros(n + 1, dtype=np.int32)
+            qo[1:] = np.cumsum(extend_lens)
+            o = torch.empty_like(q)
+            B.radix_extend_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, self._to_dev(rows),
+                                     self._to_dev(prefix_lens), self._to_dev(extend_lens), self._to_dev(qo),
+                                     int(max(extend_lens)), self.sm_scale, stream=self.stream)
+            return o
+
+    def run_decode(self, rows, positions, slots, q, k_new, v_new):
+        """Write the new slots into the table, store the new rows, decode."""
+        n = len(rows)
+        with torch.cuda.stream(self.stream):
+            rows_d, pos_d, slots_d = self._to_dev(rows), self._to_dev(positions), self._to_dev(slots)
+            B.req_to_token_scatter(self.r2t_dev, rows_d, pos_d, slots_d, stream=self.stream)
+            B.kv_store(self.k_pool, self.v_pool, k_new, v_new, slots_d, stream=self.stream)
+            o = torch.empty_like(q)
+            max_kv = int(max(positions)) + 1
+            ws = self.workspace(n, max_kv)
+            B.radix_decode_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, max_kv,
+                                     self.sm_scale, ws, stream=self.stream)
+            return o
+
+
+@dataclass
+class _Run:
+    req: object
+    row: int
+    prefix_len: int
+    node: int
+    admit_iter: int
+    generated: int = 0
+
+
+class Scheduler:
+    """Drives requests (objects with rid, prompt, gen, after) through a
+    RadixRuntime.  ``record(kind, rid, step, o)`` receives every attention
+    output (kind 'ext' or 'dec'); ``trace`` collects the host decisions."""
+
+    def __init__(self, rt, requests, qkv_source, max_running=256, max_extend_tokens=16384,
+                 skip_extend_attention=False, record=None, keep_dumps=False):
+        if rt.max_reqs < max_running:
+            raise ValueError("the slot table needs a row per running request")
+        self.rt = rt
+        self.pending = list(requests)
+        self.qkv = qkv_source
+        self.max_running = max_running
+        self.max_extend_tokens = max_extend_tokens
+        self.skip_extend_attention = skip_extend_attention
+        self.record = record
+        self.keep_dumps = keep_dumps
+        self.finished = set()
+        self.waiting, self.running = [], []
+        self.cached_tokens = self.prefill_tokens = 0
+        self.iterations, self.dumps = [], []
+        self.request_slots = {}
+
+    def _arrive(self):
+        still = []
+        for r in self.pending:
+            if all(a in self.finished for a in r.after):
+                self.waiting.append(r)
+            else:
+                still.append(r)
+        self.pending = still
+
+    def _finish(self, run, rec):
+        rt = self.rt
+        full = list(run.req.prompt) + list(run.req.gen)
+        row = rt.r2t_host[run.row, :len(full)].copy()
+        present = B.rt_insert(rt.tree, full, row)
+        dups = row[run.prefix_len:present] if present > run.prefix_len else row[:0]
+        if dups.size:
+            B.rt_pool_free(rt.pool, dups)
+        B.rt_unlock(rt.tree, run.node)
+        self.request_slots[run.req.rid] = [int(x) for x in row]
+        rec["finished"].append((run.req.rid, present, [int(x) for x in dups]))
+        self.finished.add(run.req.rid)
+        rt.free_rows.append(run.row)
+
+    def step(self, it):
+        rt = self.rt
+        rec = {"admitted": [], "extend_loc": [], "extend_freed": [], "decode": [], "decode_freed": [],
+               "finished": []}
+        reserved = sum(len(r.req.gen) - r.generated for r in self.running)
+        budget = self.max_extend_tokens
+        admitted = []
+        while self.waiting and len(self.running) + len(admitted) < self.max_running:
+            req = self.waiting[0]
+            slots, node = B.rt_match_prefix(rt.tree, req.prompt)
+            B.rt_lock(rt.tree, node)
+            p = len(slots)
+            e = len(req.prompt) - p
+            need = e + len(req.gen)
+            avail = B.rt_pool_available(rt.pool) + B.rt_evictable_size(rt.tree) - reserved
+            if need > avail or (admitted and e > budget):
+                B.rt_unlock(rt.tree, node)
+                break
+            self.waiting.pop(0)
+            row = rt.free_rows.pop(0)
+            rt.r2t_host[row, :p] = slots
+            admitted.append(_Run(req, row, p, node, it))
+            reserved += need
+            budget -= e
+
+        if admitted:
+            ext = [len(r.req.prompt) - r.prefix_len for r in admitted]
+            total = sum(ext)
+            if total > 0:
+                loc, evicted = B.rt_alloc_with_evict(rt.tree, total)
+                rec["extend_loc"] = [int(x) for x in loc]
+                rec["extend_freed_tokens"] = evicted
+            else:
+                loc = np.zeros(0, dtype=np.int32)
+            off = 0
+            for r, e in zip(admitted, ext):
+                rt.r2t_host[r.row, r.prefix_len:r.prefix_len + e] = loc[off:off + e]
+                off += e
+                rec["admitted"].append((r.req.rid, r.prefix_len, e))
+                self.cached_tokens += r.prefix_len
+                self.prefill_tokens += len(r.req.prompt)
+            rt.upload_rows([r.row for r in admitted], [len(r.req.prompt) for r in admitted])
+            if total > 0:
+                qs, ks, vs = [], [], []
+                for r, e in zip(admitted, ext):
+                    if e == 0:
+                        continue
+                    q, k, v = self.qkv(r.req.rid, r.req.prompt, np.arange(r.prefix_len, len(r.req.prompt)))
+                    qs.append(q)
+                    ks.append(k)
+                    vs.append(v)
+                q, k, v = torch.cat(qs), torch.cat(ks), torch.cat(vs)
+                o = rt.run_extend([r.row for r in admitted], [r.prefix_len for r in admitted], ext, q, k, v, loc,
+                                  attention=not self.skip_extend_attention)
+                if o is not None and self.record is not None:
+                    off = 0
+                    for r, e in zip(admitted, ext):
+                        if e:
+                            self.record("ext", r.req.rid, 0, o[off:off + e])
+                        off += e
+            for r in admitted:
+                if len(r.req.gen) == 0:
+                    self._finish(r, rec)
+                else:
+                    self.running.append(r)
+
+        dec = [r for r in self.running if r.admit_iter < it]
+        if dec:
+            slots, evicted = B.rt_alloc_with_evict(rt.tree, len(dec))
+            rec["decode_freed_tokens"] = evicted
+            positions = np.array([len(r.req.prompt) + r.generated for r in dec], dtype=np.int32)
+            rows = np.array([r.row for r in dec], dtype=np.int32)
+            for r, s, pos in zip(dec, slots, positions):
+                rt.r2t_host[r.row, pos] = s
+                rec["decode"].append((r.req.rid, int(pos), int(s)))
+            qs, ks, vs = [], [], []
+            for r, pos in zip(dec, positions):
+                seq = list(r.req.prompt) + list(r.req.gen[:r.generated + 1])
+                q, k, v = self.qkv(r.req.rid, seq, np.array([pos]))
+                qs.append(q)
+                ks.append(k)
+                vs.append(v)
+            o = rt.run_decode(rows, positions, slots, torch.cat(qs), torch.cat(ks), torch.cat(vs))
+            if self.record is not None:
+                for i, r in enumerate(dec):
+                    self.record("dec", r.req.rid, r.generated, o[i:i + 1])
+            for r in dec:
+                r.generated += 1
+            done = [r for r in dec if r.generated == len(r.req.gen)]
+            for r in done:
+                self.running.remove(r)
+                self._finish(r, rec)
+        # Host rows and pinned staging are reused by later iterations.
+        rt.stream.synchronize()
+        self.iterations.append(rec)
+        if self.keep_dumps:
+            self.dumps.append(B.rt_tree_dump(rt.tree))
+
+    def run(self, max_iterations=100000):
+        self._arrive()
+        it = 0
+        while self.waiting or self.running or self.pending:
+            if it >= max_iterations:
+                raise RuntimeError("workload did not drain")
+            self.step(it)
+            self._arrive()
+            it += 1
+        return self

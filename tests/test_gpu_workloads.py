@@ -1,0 +1,98 @@
+"""Workload parity on the GPU: the runtime (C++ tree + HIP kernels) and the
+oracle (naive tree + float64 full recompute) run the same seeded workload;
+host decisions must be bit-identical and attention within tolerance."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.runner import run_workload
+from prefix_shared_kv_rt_amd.runtime import RadixRuntime, Scheduler
+from synth import workloads
+from synth.sources import QKVSource
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def run_both(wl, want=None, max_running=256, max_extend_tokens=16384, max_reqs=None):
+    ora = run_workload(wl, want=want, max_running=max_running, max_extend_tokens=max_extend_tokens)
+    outs = {}
+
+    def record(kind, rid, step, o):
+        if want is None or want(kind, rid, step):
+            outs[(kind, rid, step)] = o.float().cpu().numpy()
+
+    rt = RadixRuntime(wl.num_slots, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, TORCH_DT[wl.dtype],
+                      max_reqs or max(max_running, 8), wl.max_ctx)
+    src = QKVSource(wl.seed, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, TORCH_DT[wl.dtype])
+    sch = Scheduler(rt, wl.requests, src, max_running=max_running, max_extend_tokens=max_extend_tokens,
+                    skip_extend_attention=wl.skip_extend_attention, record=record).run()
+    from prefix_shared_kv_rt_amd import binding as B
+    final_dump = B.rt_tree_dump(rt.tree)
+    free_list = list(B.rt_pool_free_list(rt.pool))
+    rt.close()
+    return ora, sch, outs, final_dump, free_list
+
+
+def check_host_identical(ora, sch, final_dump, free_list):
+    assert (sch.cached_tokens, sch.prefill_tokens) == (ora.cached_tokens, ora.prefill_tokens)
+    assert len(sch.iterations) == len(ora.iterations)
+    for a, b in zip(sch.iterations, ora.iterations):
+        assert a["admitted"] == b["admitted"]
+        assert a["extend_loc"] == b["extend_loc"]
+        assert a.get("extend_freed_tokens", 0) == len(b["extend_freed"])
+        assert a["decode"] == b["decode"]
+        assert a.get("decode_freed_tokens", 0) == len(b["decode_freed"])
+        assert a["finished"] == b["finished"]
+    assert sch.request_slots == ora.request_slots
+    assert final_dump == ora.final_dump
+    assert free_list == ora.free_list
+
+
+def check_outputs(ora, outs, tol):
+    assert set(outs) == set(ora.outputs)
+    worst = 0.0
+    for key, want in ora.outputs.items():
+        worst = max(worst, float(np.max(np.abs(outs[key].astype(np.float64) - want))))
+    print(f"  {len(outs)} outputs, max abs err {worst:.3e}", flush=True)
+    assert worst <= tol
+
+
+@pytest.mark.parametrize("pool", [512, 160])
+def test_tiny_workload(pool):
+    print(f"tiny workload pool={pool}", flush=True)
+    wl = workloads.tiny(pool)
+    ora, sch, outs, dump, free = run_both(wl)
+    check_host_identical(ora, sch, dump, free)
+    check_outputs(ora, outs, TOL["f32"])
+    assert (sch.cached_tokens, sch.prefill_tokens) == ((96, 192) if pool == 512 else (224, 384))
+
+
+def test_tiny_workload_in_bf16():
+    print("tiny workload bf16", flush=True)
+    wl = workloads.tiny(160)
+    wl.dtype = "bf16"
+    ora, sch, outs, dump, free = run_both(wl)
+    check_host_identical(ora, sch, dump, free)
+    check_outputs(ora, outs, TOL["bf16"])
+
+
+def test_small_few_shot_bf16():
+    print("few-shot (8 x [256 + 64], 2 decode steps)", flush=True)
+    wl = workloads.few_shot(batch=8, prefix_len=256, suffix_len=64, decode_steps=2, num_slots=4096)
+    ora, sch, outs, dump, free = run_both(wl)
+    check_host_identical(ora, sch, dump, free)
+    check_outputs(ora, outs, TOL["bf16"])
+
+
+def test_small_chat_with_eviction_bf16():
+    print("chat (6 sessions x 3 turns, pool 60%)", flush=True)
+    wl = workloads.chat(sessions=6, turns=3, system_len=64, user_lo=16, user_hi=48, gen_len=6)
+    sel = lambda kind, rid, step: kind == "ext" or step in (0, 5)
+    ora, sch, outs, dump, free = run_both(wl, want=sel, max_running=4, max_extend_tokens=128)
+    check_host_identical(ora, sch, dump, free)
+    check_outputs(ora, outs, TOL["bf16"])
+    assert any(len(it["extend_freed"]) or len(it["decode_freed"]) for it in ora.iterations)
