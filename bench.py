@@ -1,0 +1,352 @@
+"""Benchmark of the RadixAttention hot path on one MI355X.
+
+Default workload (few-shot shared prefix at the Llama-3-8B attention shape:
+32 query heads, 8 KV heads, head dim 128, bf16): a warm-up request puts a
+1024-token prefix into the radix tree; then every step serves one batch of
+64 fresh requests = that prefix + 128 distinct suffix tokens, through the
+whole path:
+
+  host   rt_admit_batch     match each request, lock its path, allocate the
+                            suffix slots (evicting LRU leaves on a deficit),
+                            fill its req_to_token row
+  device kv_store           scatter the suffix K/V into the pool
+  device extend attention   suffix rows against prefix + suffix K/V
+  host   rt_decode_slots    one slot per request for its first generated token
+  device req_to_token_scatter, kv_store, decode attention (split-K)
+  host   rt_finish_batch    insert prompt + token, free duplicates, unlock
+
+Q/K/V of every step are generated into HBM before the timed region.  A
+suffix that starts like an earlier finished request's suffix matches more
+than 1024 tokens; its already-cached rows are padded to slot 0 in the
+scatter and skipped by extend (they are not counted as work).
+
+Output: one JSON line (metric, value = extend + decode tokens per second of
+whole steps, roofline of the extend kernel from HIP events on its stream,
+CPU oracle baseline on a bounded sample).  ``--workload long_context`` or
+``fork`` time decode steps instead (extra lines, not the headline).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "extend+decode attention tokens/s at Llama-3-8B shape; % HBM/MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="few_shot", choices=["few_shot", "long_context", "fork"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=192, help="requests in the oracle's timed sample")
+    ap.add_argument("--check", action="store_true", help="check sampled outputs of the last step against the oracle")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------- few-shot --
+class FewShotBench:
+    B, PREFIX, SUFFIX = 64, 1024, 128
+    HQ, HKV, D = 32, 8, 128
+    SLOTS = 262144
+    SEED = 1
+
+    def __init__(self, n_batches, torch, B_mod, gen_t):
+        self.torch = torch
+        self.Bm = B_mod
+        self.gen_t = gen_t
+        self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.Stream(self.dev)
+        rng = np.random.Generator(np.random.PCG64(self.SEED))
+        self.prefix = rng.integers(0, 1000, size=self.PREFIX).astype(np.int32)
+        # every batch: 64 suffixes of 128 tokens + 1 generated token each
+        self.suffix = [rng.integers(0, 1000, size=(self.B, self.SUFFIX + 1)).astype(np.int32) for _ in range(n_batches)]
+        self.stride = self.PREFIX + self.SUFFIX + 1
+        bf16 = torch.bfloat16
+        self.pool = B_mod.rt_pool_create(self.SLOTS)
+        self.tree = B_mod.rt_tree_create(self.pool)
+        self.k_pool = torch.zeros((self.SLOTS + 1, self.HKV, self.D), dtype=bf16, device=self.dev)
+        self.v_pool = torch.zeros_like(self.k_pool)
+        # two row sets of 64 so that host writes for step i+1 never touch rows still being copied for step i
+        self.r2t_host_t = torch.zeros((2 * self.B, self.stride), dtype=torch.int32, pin_memory=True)
+        self.r2t_host = self.r2t_host_t.numpy()
+        self.r2t_dev = torch.zeros((2 * self.B, self.stride), dtype=torch.int32, device=self.dev)
+        # pinned metadata staging per row set: prefix, extend, qo_indptr(65), rows, dec_pos, dec_slots, loc(8192)
+        self.meta_n = 5 * self.B + 1 + self.B * self.SUFFIX
+        self.meta_host_t = torch.zeros((2, self.meta_n), dtype=torch.int32, pin_memory=True)
+        self.meta_host = self.meta_host_t.numpy()
+        self.meta_dev = torch.zeros((2, self.meta_n), dtype=torch.int32, device=self.dev)
+        self.copy_done = [None, None]
+        self.ws = torch.empty(B_mod.radix_decode_workspace_bytes(self.B, self.HQ, self.D, self.stride),
+                              dtype=torch.uint8, device=self.dev)
+        self.o_ext = torch.empty((self.B * self.SUFFIX, self.HQ, self.D), dtype=bf16, device=self.dev)
+        self.o_dec = torch.empty((self.B, self.HQ, self.D), dtype=bf16, device=self.dev)
+        self.sm_scale = 1.0 / np.sqrt(self.D)
+        self.ext_events = []
+        self.dec_events = []
+        self.flops = []
+        self.ext_tokens = []
+        self.dec_bytes = []
+
+    def gen_inputs(self, n_batches):
+        """Q/K/V of every suffix position and of the generated token, in HBM."""
+        torch, T = self.torch, self.gen_t
+        bf16 = torch.bfloat16
+        pre = torch.from_numpy(self.prefix.astype(np.int64)).to(self.dev).unsqueeze(0)
+        ph = T.prefix_hashes_t(pre, seed=self.SEED)
+        start = int(ph[0, -1].item()) & ((1 << 64) - 1)
+        self.inputs = []
+        for i in range(n_batches):
+            suf = torch.from_numpy(self.suffix[i].astype(np.int64)).to(self.dev)
+            h = T.prefix_hashes_t(suf, start_hash=start)            # [64, 129]
+            hs, hd = h[:, :self.SUFFIX].reshape(-1), h[:, self.SUFFIX].contiguous()
+            q = T.qkv_values_t(hs, 1, range(self.HQ), self.D, self.SEED, bf16)
+            k = T.qkv_values_t(hs, 2, range(self.HKV), self.D, self.SEED, bf16)
+            v = T.qkv_values_t(hs, 3, range(self.HKV), self.D, self.SEED, bf16)
+            qd = T.qkv_values_t(hd, 1, range(self.HQ), self.D, self.SEED, bf16)
+            kd = T.qkv_values_t(hd, 2, range(self.HKV), self.D, self.SEED, bf16)
+            vd = T.qkv_values_t(hd, 3, range(self.HKV), self.D, self.SEED, bf16)
+            self.inputs.append((q, k, v, qd, kd, vd))
+        torch.cuda.synchronize()
+
+    def warm_prefix(self):
+        """The warm-up request: extend the 1024-token prefix and insert it."""
+        torch, Bm, T = self.torch, self.Bm, self.gen_t
+        bf16 = torch.bfloat16
+        pre = torch.from_numpy(self.prefix.astype(np.int64)).to(self.dev).unsqueeze(0)
+        h = T.prefix_hashes_t(pre, seed=self.SEED).reshape(-1)
+        q = T.qkv_values_t(h, 1, range(self.HQ), self.D, self.SEED, bf16)
+        k = T.qkv_values_t(h, 2, range(self.HKV), self.D, self.SEED, bf16)
+        v = T.qkv_values_t(h, 3, range(self.HKV), self.D, self.SEED, bf16)
+        toks = self.prefix
+        off = np.array([0, self.PREFIX], dtype=np.int64)
+        rows = np.array([0], dtype=np.int32)
+        pl, el, nodes, loc = Bm.rt_admit_batch(self.tree, toks, off, self.r2t_host, rows)
+        with torch.cuda.stream(self.stream):
+            self.r2t_dev[0, :self.PREFIX].copy_(self.r2t_host_t[0, :self.PREFIX])
+            dloc = torch.from_numpy(loc).to(self.dev)
+            Bm.kv_store(self.k_pool, self.v_pool, k, v, dloc, stream=self.stream)
+            o = torch.empty_like(q)
+            meta = torch.tensor([0, self.PREFIX, 0, self.PREFIX, 0], dtype=torch.int32, device=self.dev)
+            Bm.radix_extend_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, meta[4:5], meta[0:1], meta[1:2],
+                                      meta[2:4], self.PREFIX, self.sm_scale, stream=self.stream)
+        self.stream.synchronize()
+        Bm.rt_finish_batch(self.tree, toks, off, self.r2t_host, rows, pl, nodes)
+
+    def step(self, i, timed):
+        torch, Bm = self.torch, self.Bm
+        B, S, P0 = self.B, self.SUFFIX, self.PREFIX
+        q, k, v, qd, kd, vd = self.inputs[i]
+        rs = i % 2
+        if self.copy_done[rs] is not None:
+            self.copy_done[rs].synchronize()       # host staging of this row set is free again
+        rows = np.arange(rs * B, rs * B + B, dtype=np.int32)
+        prompts = np.concatenate([np.broadcast_to(self.prefix, (B, P0)), self.suffix[i][:, :S]], axis=1)
+        toks = prompts.reshape(-1)
+        off = np.arange(0, B * (P0 + S) + 1, P0 + S, dtype=np.int64)
+        pl, el, nodes, loc = Bm.rt_admit_batch(self.tree, toks, off, self.r2t_host, rows)
+        if int(pl.min()) < P0:
+            raise RuntimeError("the shared prefix left the cache; the pool is too small for this run")
+        # scatter targets: already-cached suffix rows go to the dummy slot 0
+        meta = self.meta_host[rs]
+        meta[0:B] = pl
+        meta[B:2 * B] = el
+        qo = np.arange(B, dtype=np.int32) * S + (pl - P0)
+        meta[2 * B:3 * B] = qo
+        meta[3 * B] = B * S
+        meta[3 * B + 1:4 * B + 1] = rows
+        base = 5 * B + 1
+        pad = np.zeros(B * S, dtype=np.int32)
+        o = 0
+        for b in range(B):
+            e = int(el[b])
+            pad[b * S + S - e:(b + 1) * S] = loc[o:o + e]
+            o += e
+        meta[base:base + B * S] = pad
+        # one decode slot per request, at position P0 + S
+        pos = np.full(B, P0 + S, dtype=np.int32)
+        dslots = Bm.rt_decode_slots_batch(self.tree, rows, pos, self.r2t_host)
+        meta[4 * B + 1:5 * B + 1] = dslots
+        md = self.meta_dev[rs]
+        with torch.cuda.stream(self.stream):
+            self.r2t_dev[rs * B:(rs + 1) * B].copy_(self.r2t_host_t[rs * B:(rs + 1) * B], non_blocking=True)
+            md.copy_(self.meta_host_t[rs], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(self.stream)
+            self.copy_done[rs] = ev
+            d_pl, d_el, d_qo, d_rows = md[0:B], md[B:2 * B], md[2 * B:3 * B + 1], md[3 * B + 1:4 * B + 1]
+            d_dslots, d_loc = md[4 * B + 1:5 * B + 1], md[base:base + B * S]
+            Bm.kv_store(self.k_pool, self.v_pool, k, v, d_loc, stream=self.stream)
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(self.stream)
+            Bm.radix_extend_attention(q, self.o_ext, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pl, d_el, d_qo,
+                                      int(el.max()), self.sm_scale, stream=self.stream)
+            if timed:
+                e1.record(self.stream)
+                self.ext_events.append((e0, e1))
+            d_pos = self.pos_dev
+            Bm.req_to_token_scatter(self.r2t_dev, d_rows, d_pos, d_dslots, stream=self.stream)
+            Bm.kv_store(self.k_pool, self.v_pool, kd, vd, d_dslots, stream=self.stream)
+            if timed:
+                e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e2.record(self.stream)
+            Bm.radix_decode_attention(qd, self.o_dec, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pos,
+                                      P0 + S + 1, self.sm_scale, self.ws, stream=self.stream)
+            if timed:
+                e3.record(self.stream)
+                self.dec_events.append((e2, e3))
+        # finish: prompt + generated token into the tree
+        full = np.concatenate([prompts, self.suffix[i][:, S:S + 1]], axis=1)
+        foff = np.arange(0, B * (P0 + S + 1) + 1, P0 + S + 1, dtype=np.int64)
+        Bm.rt_finish_batch(self.tree, full.reshape(-1), foff, self.r2t_host, rows, pl, nodes)
+        self.last_prefix_lens = pl.copy()
+        if timed:
+            rows_keys = sum(int(p) * int(e) + int(e) * (int(e) + 1) // 2 for p, e in zip(pl, el))
+            self.flops.append(4.0 * self.D * self.HQ * rows_keys)
+            self.ext_tokens.append(int(el.sum()) + B)
+            kv_len = P0 + S + 1
+            self.dec_bytes.append(B * kv_len * (self.HKV * self.D * 2 * 2 + 4) + 2 * B * self.HQ * self.D * 2)
+        return int(el.sum()) + B
+
+
+def run_few_shot(args, torch):
+    from prefix_shared_kv_rt_amd import binding as Bm
+    from synth import torch_gen
+    n = args.warmup + args.steps
+    fb = FewShotBench(n, torch, Bm, torch_gen)
+    fb.pos_dev = torch.full((fb.B,), fb.PREFIX + fb.SUFFIX, dtype=torch.int32, device=fb.dev)
+    fb.gen_inputs(n)
+    fb.warm_prefix()
+    for i in range(args.warmup):
+        fb.step(i, timed=False)
+    fb.stream.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tokens = 0
+    for i in range(args.warmup, n):
+        tokens += fb.step(i, timed=True)
+    fb.stream.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ext_ms = [a.elapsed_time(b) for a, b in fb.ext_events]
+    dec_ms = [a.elapsed_time(b) for a, b in fb.dec_events]
+    ext_avg_s = float(np.mean(ext_ms)) / 1e3
+    dec_avg_s = float(np.mean(dec_ms)) / 1e3
+    flops_avg = float(np.mean(fb.flops))
+    achieved_tflops = flops_avg / ext_avg_s / 1e12
+    result = {
+        "metric": METRIC,
+        "value": tokens / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "few-shot shared prefix, Llama-3-8B attention shape: 64 requests x (1024 shared + 128 "
+                        "distinct tokens) per step, one extend pass + one decode step, tree match/insert on host",
+            "batch": fb.B, "prefix_len": fb.PREFIX, "suffix_len": fb.SUFFIX, "num_q_heads": fb.HQ,
+            "num_kv_heads": fb.HKV, "head_dim": fb.D, "pool_slots": fb.SLOTS,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "radix_extend_attention (extend_bf16<128>)",
+            "achieved": achieved_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved_tflops / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "flops_per_launch": flops_avg,
+            "avg_launch_us": ext_avg_s * 1e6,
+        },
+        "kernels": {
+            "extend_us": ext_avg_s * 1e6,
+            "extend_tokens_per_s": (fb.B * fb.SUFFIX) / ext_avg_s,
+            "decode_us": dec_avg_s * 1e6,
+            "decode_hbm_gbs": float(np.mean(fb.dec_bytes)) / dec_avg_s / 1e9,
+        },
+    }
+    if args.check:
+        result["check"] = check_few_shot(fb, n - 1)
+    return result, fb
+
+
+def check_few_shot(fb, i):
+    """Sampled outputs of batch i against the oracle's full recompute."""
+    from oracle.attention import recompute_rows
+    o_ext = fb.o_ext.float().cpu().numpy()
+    o_dec = fb.o_dec.float().cpu().numpy()
+    worst = 0.0
+    for b in (0, 31, 63):
+        toks = list(fb.prefix) + list(fb.suffix[i][b])
+        p = int(fb.last_prefix_lens[b])  # rows below p were cached, not recomputed
+        rows = sorted({p, (p + fb.PREFIX + fb.SUFFIX) // 2, fb.PREFIX + fb.SUFFIX - 1})
+        want = recompute_rows(toks, rows, fb.HQ, fb.HKV, fb.D, fb.SEED, fb.sm_scale)
+        got = o_ext[[b * fb.SUFFIX + (r - fb.PREFIX) for r in rows]]
+        worst = max(worst, float(np.abs(got - want).max()))
+        want_d = recompute_rows(toks, [fb.PREFIX + fb.SUFFIX], fb.HQ, fb.HKV, fb.D, fb.SEED, fb.sm_scale)
+        worst = max(worst, float(np.abs(o_dec[b:b + 1] - want_d).max()))
+    return {"max_abs_err": worst, "tol": 2e-2, "ok": worst <= 2e-2}
+
+
+def run_decode_bench(args, torch):
+    raise NotImplementedError(args.workload)
+
+
+def cpu_baseline(args):
+    """The oracle, unchanged, on a bounded sample of the same workload: a
+    batch of --cpu-sample requests (1024 shared + 128 distinct tokens, one
+    decode step) through the naive tree and float64 full recompute."""
+    from oracle.runner import run_workload
+    from synth import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    wl = workloads.few_shot(batch=args.cpu_sample, decode_steps=1)
+    t0 = time.perf_counter()
+    run_workload(wl, want=lambda kind, rid, step: rid != 0)
+    dt = time.perf_counter() - t0
+    tokens = args.cpu_sample * (128 + 1)
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{args.cpu_sample} few-shot requests (1024 shared + 128 distinct tokens + 1 decode step) "
+                      f"after the warm-up prefix, naive tree + float64 full recompute; {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    if args.workload == "few_shot":
+        result, _ = run_few_shot(args, torch)
+    else:
+        result = run_decode_bench(args, torch)
+    if not args.no_cpu_baseline and args.workload == "few_shot":
+        result["cpu_baseline"] = cpu_baseline(args)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

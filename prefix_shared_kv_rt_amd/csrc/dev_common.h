@@ -27,8 +27,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
 }
+// Two floats -> packed bfloat16 pair (lo in bits 0..15), round to nearest
+// even; one v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2_t{lo, hi}, bf16x2_t));
 }
 
 // Byte-select of two dwords (v_perm_b32): result byte i = selector byte i

@@ -128,37 +128,47 @@ __global__ void __launch_bounds__(256, 2) extend_bf16(
     for (int i = 0; i < 16; ++i) oacc[r][i] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  // Gather staging: piece p = tid + 256*it of the tile; key p / (D/8), 16-byte chunk p % (D/8).
+  // Gather staging: piece p = tid + 256*it of a tile is key p / (D/8), 16-byte chunk
+  // p % (D/8).  Keys past kv_end are clamped to the last valid key: they are
+  // masked out of the softmax, and a real pool row keeps the staged values finite.
+  // Slot indices run one tile ahead of the K/V gather so the index -> row
+  // dependency never stalls the gather.
   u32x4 kst[C::kPerThread], vst[C::kPerThread];
-  auto gather = [&](int tile) {
+  uint32_t slot_next[C::kPerThread];
+  const int piece_key = tid / (D / 8);
+  const int piece_off = (tid % (D / 8)) * 16;
+  auto load_idx = [&](int tile, uint32_t* out) {
 #pragma unroll
     for (int it = 0; it < C::kPerThread; ++it) {
-      const int p = tid + 256 * it;
-      const int key = tile * kBN + p / (D / 8);
-      const int off = (p % (D / 8)) * 16;
-      if (key < kv_end) {
-        const int64_t slot = idx_row[key];
-        kst[it] = ld16(kbase + slot * pool_row + off);
-        vst[it] = ld16(vbase + slot * pool_row + off);
-      } else {
-        kst[it] = u32x4{0, 0, 0, 0};
-        vst[it] = u32x4{0, 0, 0, 0};
-      }
+      const int key = min(tile * kBN + piece_key + it * (256 / (D / 8)), kv_end - 1);
+      out[it] = uint32_t(idx_row[key]);
+    }
+  };
+  auto gather = [&](const uint32_t* slots) {
+#pragma unroll
+    for (int it = 0; it < C::kPerThread; ++it) {
+      const uint64_t off = uint64_t(slots[it]) * uint32_t(pool_row) + uint32_t(piece_off);
+      kst[it] = ld16(kbase + off);
+      vst[it] = ld16(vbase + off);
     }
   };
 
-  gather(0);
+  load_idx(0, slot_next);
+  gather(slot_next);
+  if (n_tiles > 1) load_idx(1, slot_next);
   for (int tile = 0; tile < n_tiles; ++tile) {
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < C::kPerThread; ++it) {
-      const int p = tid + 256 * it;
-      const int lds = (p / (D / 8)) * C::kPitch + (p % (D / 8)) * 16;
+      const int lds = (piece_key + it * (256 / (D / 8))) * C::kPitch + piece_off;
       *reinterpret_cast<u32x4*>(s_k + lds) = kst[it];
       *reinterpret_cast<u32x4*>(s_v + lds) = vst[it];
     }
     __syncthreads();
-    if (tile + 1 < n_tiles) gather(tile + 1);
+    if (tile + 1 < n_tiles) {
+      gather(slot_next);
+      if (tile + 2 < n_tiles) load_idx(tile + 2, slot_next);
+    }
 
     const int base = tile * kBN;
     if (base >= w_end) continue;              // wave-uniform: every row of this wave is done
@@ -178,18 +188,20 @@ __global__ void __launch_bounds__(256, 2) extend_bf16(
       }
     }
     // Lane holds keys base + 32*kb + 8*(v/4) + 4*hi + (v%4) of query row r32.
-    const bool need_mask = base + 2 * 32 - 1 > w_min_limit;
+    // Only tiles that cross this wave's diagonal (or its last key) need a mask.
+    if (base + 2 * 32 - 1 > w_min_limit) {
+      const int rel = base + 4 * hi - limit;  // key - limit = rel + const(kb, v)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (rel + 32 * kb + 8 * (v >> 2) + (v & 3) > 0) sacc[kb][v] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = base + 32 * kb + 8 * (v >> 2) + 4 * hi + (v & 3);
-        float s = sacc[kb][v];
-        if (kb >= nblk || (need_mask && key > limit)) s = -INFINITY;
-        sacc[kb][v] = s;
-        mx = fmaxf(mx, s);
-      }
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m, mx * scale_log2);
     if (__any(m_new > m)) {
