@@ -66,7 +66,17 @@ __device__ __forceinline__ floatx16 mfma_32x32x16(bf16x8 a, bf16x8 b, floatx16 c
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Global loads that bypass nothing special; 16 / 8 byte vectors.
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j receives component j%4 of the four 16-bit values addressed by each
+// of the lanes 4t + j/4 (t = 0..3), in t order.
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 ds_read_tr16(const void* lds_ptr) {
+  typedef __attribute__((address_space(3))) shortx4_t lds_shortx4;
+  const shortx4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(lds_ptr));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Global loads; 16 / 8 byte vectors.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 

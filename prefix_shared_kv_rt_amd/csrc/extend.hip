@@ -24,8 +24,9 @@
 //     when no row's running max moved (usual after the first tiles).
 //   * O^T += V^T P^T with the same MFMA.  P^T comes straight from the score
 //     registers (the key order of the contraction is chosen to match the
-//     score layout); V^T operands are read from LDS as 4-dim runs per lane
-//     and regrouped per dim with byte permutes.
+//     score layout); V^T operands come from LDS through gfx950's transpose
+//     read (ds_read_b64_tr_b16), which hands each lane 4 consecutive keys of
+//     one dim -- no register shuffles.
 //   * Causal masking is applied only on tiles that cross the wave's
 //     diagonal; tiles beyond a wave's last row are skipped.
 // Work items are laid out so that each XCD (blockIdx % 8 on MI355X) runs a
@@ -47,21 +48,37 @@ using namespace rtk;
 
 constexpr int kBM = 128;  // query rows per work item (4 waves x 32)
 constexpr int kBN = 64;   // keys per LDS tile
+constexpr float kSlack = 8.f;  // log2 headroom of the lazy softmax rescale
 
 template <int D>
 struct ExtendCfg {
   static constexpr int kRowBytes = D * 2;                 // one K or V row of one head
-  static constexpr int kPitch = kRowBytes + 16;           // LDS row pitch (bank spread)
-  static constexpr int kPieces = kBN * kRowBytes / 16;    // 16-byte pieces per tile
-  static constexpr int kPerThread = kPieces / 256;        // per thread, K and V each
+  static constexpr int kCPR = kRowBytes / 16;             // 16-byte chunks per row
+  static constexpr int kKPI = 64 / kCPR;                  // rows per 64-lane LDS load (1 KiB)
+  static constexpr int kLoadsPerWave = kBN / kKPI / 4;    // per wave per tile, K and V each
+  static constexpr int kTile = kBN * kRowBytes;           // bytes of one K (or V) tile
   static constexpr int kKS = D / 16;                      // 16-dim steps of Q K^T
-  static constexpr int kR = D / 32;                       // dims per lane in P V (tiles of O^T)
+  static constexpr int kR = D / 32;                       // 32-dim tiles of O^T
 };
 
 __device__ __forceinline__ int xcd_slice(int bid, int nblk) {
   const int xcd = bid & 7, local = bid >> 3;
   const int q = nblk >> 3, r = nblk & 7;
   return xcd * q + min(xcd, r) + local;
+}
+
+// LDS tile layout: rows (keys) of D*2 bytes, unpadded; the 16-byte chunks of
+// row k are permuted by chunk ^ f(k).  f is a bijection on the low 4 bits of
+// k chosen so that both access patterns are free of bank conflicts whether
+// the LDS serves 128 or 256 bytes per cycle: 8 or 16 consecutive keys read at
+// one chunk index (the K operand) land on distinct bank groups, and so do 4
+// consecutive keys read at 2 or 4 consecutive chunks (the transpose reads).
+__device__ __forceinline__ int swz_f(int k) {
+  return ((0xCA60 >> (4 * (k & 3))) & 0xF) ^ ((k >> 2) & 1) ^ (((k >> 3) & 1) << 1);
+}
+template <int D>
+__device__ __forceinline__ int swz(int key, int chunk) {
+  return key * ExtendCfg<D>::kRowBytes + ((chunk ^ (swz_f(key) & (ExtendCfg<D>::kCPR - 1))) << 4);
 }
 
 template <int D>
@@ -72,8 +89,13 @@ __global__ void __launch_bounds__(256, 2) extend_bf16(
     const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ qo_indptr, int B, int Hq, int Hkv,
     int G, int n_qt, float scale_log2) {
   using C = ExtendCfg<D>;
-  __shared__ __attribute__((aligned(16))) char s_k[kBN * C::kPitch];
-  __shared__ __attribute__((aligned(16))) char s_v[kBN * C::kPitch];
+  // Two stages of K and V tiles: the next tile streams into one stage while the
+  // other is used.  Separate arrays let the compiler see that LDS reads of one
+  // stage never wait on the loads still landing in the other.
+  __shared__ __attribute__((aligned(1024))) char sk0[C::kTile];
+  __shared__ __attribute__((aligned(1024))) char sv0[C::kTile];
+  __shared__ __attribute__((aligned(1024))) char sk1[C::kTile];
+  __shared__ __attribute__((aligned(1024))) char sv1[C::kTile];
 
   const int work = xcd_slice(blockIdx.x, gridDim.x);
   const int qt = work % n_qt;
@@ -107,7 +129,7 @@ __global__ void __launch_bounds__(256, 2) extend_bf16(
   const int w_end = P + wj_last + 1;          // keys >= this are invisible to every row of the wave
 
   const int32_t* idx_row = req_to_token + int64_t(rpi ? rpi[b] : b) * stride;
-  const int64_t pool_row = int64_t(Hkv) * C::kRowBytes;
+  const uint32_t pool_row = uint32_t(Hkv) * C::kRowBytes;
   const char* kbase = k_pool + int64_t(kvh) * C::kRowBytes;
   const char* vbase = v_pool + int64_t(kvh) * C::kRowBytes;
 
@@ -128,64 +150,63 @@ __global__ void __launch_bounds__(256, 2) extend_bf16(
     for (int i = 0; i < 16; ++i) oacc[r][i] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  // Gather staging: piece p = tid + 256*it of a tile is key p / (D/8), 16-byte chunk
-  // p % (D/8).  Keys past kv_end are clamped to the last valid key: they are
-  // masked out of the softmax, and a real pool row keeps the staged values finite.
-  // Slot indices run one tile ahead of the K/V gather so the index -> row
-  // dependency never stalls the gather.
-  u32x4 kst[C::kPerThread], vst[C::kPerThread];
-  uint32_t slot_next[C::kPerThread];
-  const int piece_key = tid / (D / 8);
-  const int piece_off = (tid % (D / 8)) * 16;
-  auto load_idx = [&](int tile, uint32_t* out) {
+  // Tile loads go straight from HBM to LDS (global_load_lds_dwordx4): one
+  // 64-lane load fills kKPI consecutive rows (1 KiB).  Wave w issues loads
+  // n = w + 4*it; lane i takes row kKPI*n + i/kCPR and the logical chunk that
+  // the swizzle stores at physical chunk i%kCPR.  Keys past kv_end are clamped
+  // to the last valid key (masked later; a real row keeps the tile finite).
+  // Slot indices run one tile ahead of the loads that use them.
+  const int ld_row = lane / C::kCPR;
+  const int ld_pchunk = lane % C::kCPR;
+  uint32_t slot_next[C::kLoadsPerWave];
+  auto load_idx = [&](int tile) {
 #pragma unroll
-    for (int it = 0; it < C::kPerThread; ++it) {
-      const int key = min(tile * kBN + piece_key + it * (256 / (D / 8)), kv_end - 1);
-      out[it] = uint32_t(idx_row[key]);
+    for (int it = 0; it < C::kLoadsPerWave; ++it) {
+      const int key = min(tile * kBN + C::kKPI * (wave + 4 * it) + ld_row, kv_end - 1);
+      slot_next[it] = uint32_t(idx_row[key]);
     }
   };
-  auto gather = [&](const uint32_t* slots) {
+  auto issue = [&](char* sk, char* sv) {
 #pragma unroll
-    for (int it = 0; it < C::kPerThread; ++it) {
-      const uint64_t off = uint64_t(slots[it]) * uint32_t(pool_row) + uint32_t(piece_off);
-      kst[it] = ld16(kbase + off);
-      vst[it] = ld16(vbase + off);
+    for (int it = 0; it < C::kLoadsPerWave; ++it) {
+      const int krow = C::kKPI * (wave + 4 * it) + ld_row;
+      const int lchunk = ld_pchunk ^ (swz_f(krow) & (C::kCPR - 1));
+      const uint64_t off = uint64_t(slot_next[it]) * pool_row + uint32_t(lchunk << 4);
+      const int dst = C::kKPI * (wave + 4 * it) * C::kRowBytes;
+      __builtin_amdgcn_global_load_lds(kbase + off, (__attribute__((address_space(3))) void*)(sk + dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + off, (__attribute__((address_space(3))) void*)(sv + dst), 16, 0, 0);
     }
   };
 
-  load_idx(0, slot_next);
-  gather(slot_next);
-  if (n_tiles > 1) load_idx(1, slot_next);
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < C::kPerThread; ++it) {
-      const int lds = (piece_key + it * (256 / (D / 8))) * C::kPitch + piece_off;
-      *reinterpret_cast<u32x4*>(s_k + lds) = kst[it];
-      *reinterpret_cast<u32x4*>(s_v + lds) = vst[it];
-    }
-    __syncthreads();
+  // V transpose-read source of this lane: lane s = lane%16 of group gr = lane/16
+  // addresses key 4*(gr/2) + s/4 and the 4-dim run at dims 16*(gr%2) + 4*(s%4)
+  // (+32 per O^T tile): chunk 2*(gr%2) + (s%4)/2 (+4 per tile), half s%2.
+  const int tr_key = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_half = (lane & 1) * 8;
+
+  // One tile: wait for its loads (barrier), start the next tile's loads into
+  // the other stage, then compute from this stage.
+  auto step = [&](int tile, const char* sk, const char* sv, char* sk_next, char* sv_next) {
+    __syncthreads();  // this tile's loads landed everywhere; the other stage is free
     if (tile + 1 < n_tiles) {
-      gather(slot_next);
-      if (tile + 2 < n_tiles) load_idx(tile + 2, slot_next);
+      issue(sk_next, sv_next);
+      if (tile + 2 < n_tiles) load_idx(tile + 2);
     }
-
     const int base = tile * kBN;
-    if (base >= w_end) continue;              // wave-uniform: every row of this wave is done
-    const int nblk = (w_end - base) > 32 ? 2 : 1;
-
-    // ---- scores S^T[key][row] for up to two 32-key blocks
+    if (base >= w_end) return;                // wave-uniform: every row of this wave is done
+    // ---- scores S^T[key][row] for two 32-key blocks
     floatx16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      u32x4 ka[C::kKS];
+#pragma unroll
+      for (int ks = 0; ks < C::kKS; ++ks)
+        ka[ks] = *reinterpret_cast<const u32x4*>(sk + swz<D>(kb * 32 + r32, 2 * ks + hi));
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-      if (kb < nblk) {
-        const char* kr = s_k + (kb * 32 + r32) * C::kPitch + hi * 16;
 #pragma unroll
-        for (int ks = 0; ks < C::kKS; ++ks)
-          sacc[kb] = mfma_32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(kr + ks * 32)), qop[ks], sacc[kb]);
-      }
+      for (int ks = 0; ks < C::kKS; ++ks) sacc[kb] = mfma_32x32x16(as_bf16x8(ka[ks]), qop[ks], sacc[kb]);
     }
     // Lane holds keys base + 32*kb + 8*(v/4) + 4*hi + (v%4) of query row r32.
     // Only tiles that cross this wave's diagonal (or its last key) need a mask.
@@ -203,8 +224,12 @@ __global__ void __launch_bounds__(256, 2) extend_bf16(
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m, mx * scale_log2);
-    if (__any(m_new > m)) {
+    // Lazy rescale: the reference max m only moves when some row's max
+    // exceeds it by more than 2^kSlack, so probabilities stay <= 2^kSlack
+    // (harmless in fp32 and bf16) and the accumulator rescale is rare.
+    const float m_tile = mx * scale_log2;
+    if (__any(m_tile > m + kSlack)) {
+      const float m_new = fmaxf(m, m_tile);
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);
       l *= alpha;
 #pragma unroll
@@ -218,7 +243,6 @@ __global__ void __launch_bounds__(256, 2) extend_bf16(
     // ---- O^T += V^T P^T, 16 keys per MFMA
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      if (kb >= nblk) continue;
 #pragma unroll
       for (int sh = 0; sh < 2; ++sh) {
         float p[8];
@@ -229,59 +253,47 @@ __global__ void __launch_bounds__(256, 2) extend_bf16(
         }
         const bf16x8 pop = as_bf16x8(u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
-        // logical k = 8*hi + t  <->  key 32*kb + 16*sh + 8*(t/4) + 4*hi + (t%4)
-        const char* vr = s_v + (32 * kb + 16 * sh + 4 * hi) * C::kPitch + r32 * (C::kR * 2);
-        if constexpr (D == 128) {
-          u32x2 L[8];
+        // logical k = 8*hi + t  <->  key 32*kb + 16*sh + 8*(t/4) + 4*hi + (t%4).
+        // The V^T operand (32 dims x these 8 keys) comes from two LDS
+        // transpose reads of 4 keys each.
+        const int k0 = 32 * kb + 16 * sh + tr_key;
+        u32x2 vt[C::kR][2];
 #pragma unroll
-          for (int t = 0; t < 8; ++t)
-            L[t] = *reinterpret_cast<const u32x2*>(vr + (8 * (t >> 2) + (t & 3)) * C::kPitch);
-          u32x4 a0, a1, a2, a3;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            a0[w] = pack_lo16(L[2 * w].x, L[2 * w + 1].x);
-            a1[w] = pack_hi16(L[2 * w].x, L[2 * w + 1].x);
-            a2[w] = pack_lo16(L[2 * w].y, L[2 * w + 1].y);
-            a3[w] = pack_hi16(L[2 * w].y, L[2 * w + 1].y);
-          }
-          oacc[0] = mfma_32x32x16(as_bf16x8(a0), pop, oacc[0]);
-          oacc[1] = mfma_32x32x16(as_bf16x8(a1), pop, oacc[1]);
-          oacc[2] = mfma_32x32x16(as_bf16x8(a2), pop, oacc[2]);
-          oacc[3] = mfma_32x32x16(as_bf16x8(a3), pop, oacc[3]);
-        } else {
-          uint32_t L[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t)
-            L[t] = *reinterpret_cast<const uint32_t*>(vr + (8 * (t >> 2) + (t & 3)) * C::kPitch);
-          u32x4 a0, a1;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            a0[w] = pack_lo16(L[2 * w], L[2 * w + 1]);
-            a1[w] = pack_hi16(L[2 * w], L[2 * w + 1]);
-          }
-          oacc[0] = mfma_32x32x16(as_bf16x8(a0), pop, oacc[0]);
-          oacc[1] = mfma_32x32x16(as_bf16x8(a1), pop, oacc[1]);
+        for (int dt = 0; dt < C::kR; ++dt) {
+          vt[dt][0] = ds_read_tr16(sv + swz<D>(k0, tr_chunk + 4 * dt) + tr_half);
+          vt[dt][1] = ds_read_tr16(sv + swz<D>(k0 + 8, tr_chunk + 4 * dt) + tr_half);
         }
+#pragma unroll
+        for (int dt = 0; dt < C::kR; ++dt)
+          oacc[dt] = mfma_32x32x16(as_bf16x8(u32x4{vt[dt][0].x, vt[dt][0].y, vt[dt][1].x, vt[dt][1].y}), pop,
+                                   oacc[dt]);
       }
     }
+  };
+
+  load_idx(0);
+  issue(sk0, sv0);
+  if (n_tiles > 1) load_idx(1);
+  for (int tile = 0; tile < n_tiles; tile += 2) {
+    step(tile, sk0, sv0, sk1, sv1);
+    if (tile + 1 < n_tiles) step(tile + 1, sk1, sv1, sk0, sv0);
   }
 
-  // ---- normalise and store: tile r, register v holds dim kR*i + r, i = 8*(v/4) + 4*hi + (v%4)
+  // ---- normalise and store: O^T tile dt row i = dim 32*dt + i; this lane holds
+  // rows i = 8*(v/4) + 4*hi + (v%4) of query row r32.
   l += __shfl_xor(l, 32, 64);
   if (!row_ok) return;
   const float inv = 1.f / l;
   const int64_t tok = int64_t(qo_indptr[b]) + j;
   char* op = o + (tok * Hq + int64_t(kvh) * G + g) * C::kRowBytes;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int i = 8 * (v >> 2) + 4 * hi + (v & 3);
-    if constexpr (D == 128) {
-      u32x2 w = {pack_bf16x2(oacc[0][v] * inv, oacc[1][v] * inv), pack_bf16x2(oacc[2][v] * inv, oacc[3][v] * inv)};
-      *reinterpret_cast<u32x2*>(op + (4 * i) * 2) = w;
-    } else {
-      *reinterpret_cast<uint32_t*>(op + (2 * i) * 2) = pack_bf16x2(oacc[0][v] * inv, oacc[1][v] * inv);
+  for (int dt = 0; dt < C::kR; ++dt)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const u32x2 w = {pack_bf16x2(oacc[dt][4 * v4 + 0] * inv, oacc[dt][4 * v4 + 1] * inv),
+                       pack_bf16x2(oacc[dt][4 * v4 + 2] * inv, oacc[dt][4 * v4 + 3] * inv)};
+      *reinterpret_cast<u32x2*>(op + (32 * dt + 8 * v4 + 4 * hi) * 2) = w;
     }
-  }
 }
 
 // ----------------------------------------------------------------- fp32 --

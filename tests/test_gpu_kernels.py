@@ -193,3 +193,39 @@ def test_bad_arguments_are_rejected_before_launch():
         B.radix_extend_attention(q, q, kp, kp, r2t, None, lens, lens, lens, 4, 0.1)
     with pytest.raises(B.RadixRTError):
         B.radix_decode_attention(q, q, kp, kp, r2t, None, lens, 100, 0.1, torch.empty(16, device="cuda"))
+
+
+@pytest.mark.parametrize("trend", [+1.0, -1.0])
+def test_extend_and_decode_with_steep_score_trends(trend):
+    """Scores that rise (or fall) steeply along the context move each row's
+    running max by far more than the kernels' rescale slack, tile after tile."""
+    _announce(f"steep score trend {trend}")
+    rng = np.random.default_rng(21)
+    hq, hkv, d, dtype = 8, 2, 128, "bf16"
+    P, E = [700, 0, 260], [90, 150, 1]
+    case = make_pool_case(rng, P, E, hq, hkv, d, dtype)
+    qdir = np.zeros(d)
+    qdir[:8] = 1.0
+    for b in range(len(P)):
+        n = P[b] + E[b]
+        ramp = trend * np.linspace(0, 24, n)[:, None, None] * qdir[None, None, :]
+        for arr, pool in ((case["k"][b], case["kpool"]),):
+            arr += ramp
+            arr[:] = torch.from_numpy(arr.astype(np.float32)).to(torch.bfloat16).double().numpy()
+        sl = case["r2t"][case["rows"][b], :n]
+        case["kpool"][sl] = case["k"][b]
+    q_host = host_values(rng, (sum(E), hq, d), dtype)
+    q_host[:, :, :8] = np.abs(q_host[:, :, :8]) + 1.0
+    o = _run_extend(case, q_host, P, E, hq, hkv, d, dtype)
+    off, worst = 0, 0.0
+    for b, (p, e) in enumerate(zip(P, E)):
+        want = oracle_rows(q_host[off:off + e], case["k"][b], case["v"][b], np.arange(p, p + e), 1.0 / np.sqrt(d))
+        worst = max(worst, max_err(o[off:off + e], want))
+        off += e
+    qd = q_host[:len(P)].copy()
+    od = _run_decode(case, qd, [p + e - 1 for p, e in zip(P, E)], hq, hkv, d, dtype)
+    for b, (p, e) in enumerate(zip(P, E)):
+        want = oracle_rows(qd[b:b + 1], case["k"][b], case["v"][b], np.array([p + e - 1]), 1.0 / np.sqrt(d))
+        worst = max(worst, max_err(od[b:b + 1], want))
+    print(f"  max abs err {worst:.3e}")
+    assert worst <= TOL[dtype]
