@@ -87,7 +87,7 @@ class FewShotBench:
         self.meta_host = self.meta_host_t.numpy()
         self.meta_dev = torch.zeros((2, self.meta_n), dtype=torch.int32, device=self.dev)
         self.copy_done = [None, None]
-        self.ws = torch.empty(B_mod.radix_decode_workspace_bytes(self.B, self.HQ, self.D, self.stride),
+        self.ws = torch.empty(B_mod.radix_decode_workspace_bytes(self.B, self.HQ, self.HKV, self.D, self.stride),
                               dtype=torch.uint8, device=self.dev)
         self.o_ext = torch.empty((self.B * self.SUFFIX, self.HQ, self.D), dtype=bf16, device=self.dev)
         self.o_dec = torch.empty((self.B, self.HQ, self.D), dtype=bf16, device=self.dev)
@@ -101,14 +101,13 @@ class FewShotBench:
     def gen_inputs(self, n_batches):
         """Q/K/V of every suffix position and of the generated token, in HBM."""
         torch, T = self.torch, self.gen_t
+        from synth import chain_start, prefix_hashes_rows_np
         bf16 = torch.bfloat16
-        pre = torch.from_numpy(self.prefix.astype(np.int64)).to(self.dev).unsqueeze(0)
-        ph = T.prefix_hashes_t(pre, seed=self.SEED)
-        start = int(ph[0, -1].item()) & ((1 << 64) - 1)
+        ph = prefix_hashes_rows_np(self.prefix[None, :], [chain_start(self.SEED)])
         self.inputs = []
         for i in range(n_batches):
-            suf = torch.from_numpy(self.suffix[i].astype(np.int64)).to(self.dev)
-            h = T.prefix_hashes_t(suf, start_hash=start)            # [64, 129]
+            hn = prefix_hashes_rows_np(self.suffix[i], np.full(self.B, ph[0, -1], dtype=np.uint64))
+            h = torch.from_numpy(hn.view(np.int64)).to(self.dev)    # [64, 129]
             hs, hd = h[:, :self.SUFFIX].reshape(-1), h[:, self.SUFFIX].contiguous()
             q = T.qkv_values_t(hs, 1, range(self.HQ), self.D, self.SEED, bf16)
             k = T.qkv_values_t(hs, 2, range(self.HKV), self.D, self.SEED, bf16)
@@ -122,9 +121,10 @@ class FewShotBench:
     def warm_prefix(self):
         """The warm-up request: extend the 1024-token prefix and insert it."""
         torch, Bm, T = self.torch, self.Bm, self.gen_t
+        from synth import chain_start, prefix_hashes_rows_np
         bf16 = torch.bfloat16
-        pre = torch.from_numpy(self.prefix.astype(np.int64)).to(self.dev).unsqueeze(0)
-        h = T.prefix_hashes_t(pre, seed=self.SEED).reshape(-1)
+        hn = prefix_hashes_rows_np(self.prefix[None, :], [chain_start(self.SEED)])
+        h = torch.from_numpy(hn.view(np.int64).reshape(-1)).to(self.dev)
         q = T.qkv_values_t(h, 1, range(self.HQ), self.D, self.SEED, bf16)
         k = T.qkv_values_t(h, 2, range(self.HKV), self.D, self.SEED, bf16)
         v = T.qkv_values_t(h, 3, range(self.HKV), self.D, self.SEED, bf16)
@@ -305,8 +305,172 @@ def check_few_shot(fb, i):
     return {"max_abs_err": worst, "tol": 2e-2, "ok": worst <= 2e-2}
 
 
+class DecodeBench:
+    """Decode steps of a batch whose prompts are already in the pool.
+
+    long_context: 32 requests, 16384 shared + 16384 private prompt tokens,
+    Hq 64 / Hkv 8 / D 128.  fork: 16 prompts of 2048 tokens, each matched
+    whole by 8 branches (batch 128), Hq 32 / Hkv 8 / D 128.  Prompt K/V are
+    scattered into the pool with kv_store (no extend attention); each timed
+    step allocates one slot per request, scatters its slot and K/V, and runs
+    decode attention over the whole context."""
+
+    def __init__(self, name, torch, Bm, gen_t, n_steps):
+        self.torch, self.Bm, self.T = torch, Bm, gen_t
+        self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.Stream(self.dev)
+        self.name = name
+        if name == "long_context":
+            self.SEED, self.HQ, self.HKV, self.D = 4, 64, 8, 128
+            self.B, self.groups, self.shared, self.private = 32, 1, 16384, 16384
+            self.SLOTS = 1 << 20
+        else:  # fork
+            self.SEED, self.HQ, self.HKV, self.D = 2, 32, 8, 128
+            self.B, self.groups, self.shared, self.private = 128, 16, 2048, 0
+            self.SLOTS = 262144
+        self.n_steps = n_steps
+        rng = np.random.Generator(np.random.PCG64(self.SEED))
+        self.prompt_len = self.shared + self.private
+        # group g's shared part; request b belongs to group b // (B / groups)
+        self.shared_toks = rng.integers(0, 1000, size=(self.groups, self.shared)).astype(np.int32)
+        self.private_toks = rng.integers(0, 1000, size=(self.B, self.private)).astype(np.int32)
+        self.gen_toks = rng.integers(0, 1000, size=(self.B, n_steps)).astype(np.int32)
+        self.stride = self.prompt_len + n_steps
+        self.pool = Bm.rt_pool_create(self.SLOTS)
+        self.tree = Bm.rt_tree_create(self.pool)
+        bf16 = torch.bfloat16
+        self.k_pool = torch.zeros((self.SLOTS + 1, self.HKV, self.D), dtype=bf16, device=self.dev)
+        self.v_pool = torch.zeros_like(self.k_pool)
+        self.r2t_host = np.zeros((self.B + self.groups, self.stride), dtype=np.int32)
+        self.r2t_dev = torch.zeros((self.B + self.groups, self.stride), dtype=torch.int32, device=self.dev)
+        self.sm_scale = 1.0 / np.sqrt(self.D)
+
+    def _values(self, hashes, kind, heads):
+        return self.T.qkv_values_t(hashes, kind, range(heads), self.D, self.SEED, self.torch.bfloat16)
+
+    def _dev_hashes(self, h):
+        return self.torch.from_numpy(np.ascontiguousarray(h).view(np.int64)).to(self.dev)
+
+    def _store(self, hashes, slots):
+        """Scatter generated K/V of positions with these (host) hashes into the pool."""
+        torch = self.torch
+        for lo in range(0, hashes.size, 16384):
+            h = self._dev_hashes(hashes[lo:lo + 16384])
+            loc = torch.from_numpy(np.ascontiguousarray(slots[lo:lo + 16384])).to(self.dev)
+            self.Bm.kv_store(self.k_pool, self.v_pool, self._values(h, 2, self.HKV), self._values(h, 3, self.HKV),
+                             loc, stream=self.torch.cuda.current_stream())
+
+    def setup(self):
+        torch, Bm, T = self.torch, self.Bm, self.T
+        per = self.B // self.groups
+        # shared prompts: admitted, stored and inserted first (prompt-only requests)
+        from synth import chain_start, prefix_hashes_rows_np
+        sh_hash = prefix_hashes_rows_np(self.shared_toks, np.full(self.groups, chain_start(self.SEED), dtype=np.uint64))
+        toks = self.shared_toks.reshape(-1)
+        off = np.arange(0, self.groups * self.shared + 1, self.shared, dtype=np.int64)
+        rows = np.arange(self.B, self.B + self.groups, dtype=np.int32)
+        pl, el, nodes, loc = Bm.rt_admit_batch(self.tree, toks, off, self.r2t_host, rows)
+        self._store(sh_hash.reshape(-1), loc)
+        Bm.rt_finish_batch(self.tree, toks, off, self.r2t_host, rows, pl, nodes)
+        # the decoding requests: match the shared part, store their private part
+        prompts = np.concatenate([np.repeat(self.shared_toks, per, axis=0), self.private_toks], axis=1)
+        toks = prompts.reshape(-1)
+        off = np.arange(0, self.B * self.prompt_len + 1, self.prompt_len, dtype=np.int64)
+        rows = np.arange(self.B, dtype=np.int32)
+        self.pl, el, self.nodes, loc = Bm.rt_admit_batch(self.tree, toks, off, self.r2t_host, rows)
+        assert (self.pl == self.shared).all()
+        start = np.repeat(sh_hash[:, -1], per)                                    # [B]
+        if self.private:
+            ph = prefix_hashes_rows_np(self.private_toks, start)
+            self._store(ph.reshape(-1), loc)
+            start = ph[:, -1]
+        # decode inputs for every step
+        gh = self._dev_hashes(prefix_hashes_rows_np(self.gen_toks, start))         # [B, steps]
+        self.q = [self._values(gh[:, s].contiguous(), 1, self.HQ) for s in range(self.n_steps)]
+        self.k = [self._values(gh[:, s].contiguous(), 2, self.HKV) for s in range(self.n_steps)]
+        self.v = [self._values(gh[:, s].contiguous(), 3, self.HKV) for s in range(self.n_steps)]
+        self.r2t_dev.copy_(torch.from_numpy(self.r2t_host))
+        self.rows_dev = torch.arange(self.B, dtype=torch.int32, device=self.dev)
+        self.o = torch.empty((self.B, self.HQ, self.D), dtype=torch.bfloat16, device=self.dev)
+        self.ws = torch.empty(Bm.radix_decode_workspace_bytes(self.B, self.HQ, self.HKV, self.D, self.stride),
+                              dtype=torch.uint8, device=self.dev)
+        self.events = []
+        torch.cuda.synchronize()
+
+    def step(self, s, timed):
+        torch, Bm = self.torch, self.Bm
+        pos = np.full(self.B, self.prompt_len + s, dtype=np.int32)
+        rows = np.arange(self.B, dtype=np.int32)
+        slots = Bm.rt_decode_slots_batch(self.tree, rows, pos, self.r2t_host)
+        with torch.cuda.stream(self.stream):
+            meta = torch.from_numpy(np.concatenate([pos, slots])).pin_memory().to(self.dev, non_blocking=True)
+            d_pos, d_slots = meta[:self.B], meta[self.B:]
+            Bm.req_to_token_scatter(self.r2t_dev, self.rows_dev, d_pos, d_slots, stream=self.stream)
+            Bm.kv_store(self.k_pool, self.v_pool, self.k[s], self.v[s], d_slots, stream=self.stream)
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(self.stream)
+            Bm.radix_decode_attention(self.q[s], self.o, self.k_pool, self.v_pool, self.r2t_dev, self.rows_dev, d_pos,
+                                      self.prompt_len + s + 1, self.sm_scale, self.ws, stream=self.stream)
+            if timed:
+                e1.record(self.stream)
+                self.events.append((e0, e1, int(pos[0]) + 1))
+        return self.B
+
+    def check(self, s):
+        """Sampled outputs of step s against the oracle's full recompute."""
+        from oracle.attention import recompute_rows
+        o = self.o.float().cpu().numpy()
+        per = self.B // self.groups
+        worst = 0.0
+        for b in (0, self.B - 1):
+            toks = list(self.shared_toks[b // per]) + list(self.private_toks[b]) + list(self.gen_toks[b, :s + 1])
+            want = recompute_rows(toks, [self.prompt_len + s], self.HQ, self.HKV, self.D, self.SEED, self.sm_scale)
+            worst = max(worst, float(np.abs(o[b:b + 1] - want).max()))
+        return {"max_abs_err": worst, "tol": 2e-2, "ok": worst <= 2e-2}
+
+
 def run_decode_bench(args, torch):
-    raise NotImplementedError(args.workload)
+    from prefix_shared_kv_rt_amd import binding as Bm
+    from synth import torch_gen
+    n = args.warmup + args.steps
+    db = DecodeBench(args.workload, torch, Bm, torch_gen, n)
+    db.setup()
+    for s in range(args.warmup):
+        db.step(s, timed=False)
+    db.stream.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tokens = 0
+    for s in range(args.warmup, n):
+        tokens += db.step(s, timed=True)
+    db.stream.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b, _ in db.events]
+    avg_s = float(np.mean(ms)) / 1e3
+    kv = np.mean([k for _, _, k in db.events])
+    row = db.HKV * db.D * 2
+    alg_bytes = db.B * kv * (2 * row + 4) + 2 * db.B * db.HQ * db.D * 2
+    distinct = db.groups * db.shared * 2 * row + db.B * (kv - db.shared) * (2 * row + 4)
+    achieved = alg_bytes / avg_s / 1e9
+    label = ("long-context decode: 32 requests x (16384 shared + 16384 private) context, Hq 64 / Hkv 8 / D 128"
+             if db.name == "long_context" else
+             "fork decode: 16 prompts x 2048 tokens, 8 branches each (batch 128), Hq 32 / Hkv 8 / D 128")
+    result = {
+        "metric": METRIC + " (decode)", "value": tokens / wall, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": label, "batch": db.B, "num_q_heads": db.HQ, "num_kv_heads": db.HKV,
+                   "head_dim": db.D, "pool_slots": db.SLOTS},
+        "roofline": {"bound": "hbm", "kernel": "radix_decode_attention (decode_split_bf16<128> + decode_combine)",
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": None, "bytes_per_launch": alg_bytes, "distinct_bytes_per_launch": distinct,
+                     "avg_launch_us": avg_s * 1e6},
+    }
+    if args.check:
+        result["check"] = db.check(n - 1)
+    return result
 
 
 def cpu_baseline(args):

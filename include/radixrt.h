@@ -235,8 +235,8 @@ int radix_extend_attention(const void* q, void* o, const void* k_pool, const voi
 /* Bytes of device workspace radix_decode_attention needs for these sizes
  * (split-K partial maxima, sums and accumulators, fp32).  Negative on bad
  * arguments. */
-int64_t radix_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
-                                     int32_t max_kv_len);
+int64_t radix_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t max_kv_len);
 
 /* Batched decode attention: one query row per request, at sequence position
  * prefix_lens[b] (its K/V already stored at req_to_token[row_b][prefix_lens[b]]):
@@ -247,7 +247,8 @@ int64_t radix_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t
  * max_kv_len (host) >= every prefix_lens[b] + 1.  The context is split into
  * chunks processed in parallel and merged exactly by their (max, sum)
  * statistics.  workspace (device) of workspace_bytes >=
- * radix_decode_workspace_bytes(batch, num_q_heads, head_dim, max_kv_len). */
+ * radix_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+ * max_kv_len). */
 int radix_decode_attention(const void* q, void* o, const void* k_pool, const void* v_pool,
                            const int32_t* req_to_token, int32_t req_to_token_stride,
                            const int32_t* req_pool_indices, const int32_t* prefix_lens,

@@ -89,7 +89,7 @@ def lib():
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
                                                       _vp]),
             "radix_decode_workspace_bytes": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                                              ctypes.c_int32]),
+                                                              ctypes.c_int32, ctypes.c_int32]),
             "radix_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
@@ -318,8 +318,9 @@ def radix_extend_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices,
                                         float(sm_scale), _dtype_code(q), _stream(stream)))
 
 
-def radix_decode_workspace_bytes(batch, num_q_heads, head_dim, max_kv_len):
-    return int(lib().radix_decode_workspace_bytes(int(batch), int(num_q_heads), int(head_dim), int(max_kv_len)))
+def radix_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_kv_len):
+    return int(lib().radix_decode_workspace_bytes(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim),
+                                                  int(max_kv_len)))
 
 
 def radix_decode_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens, max_kv_len, sm_scale,

@@ -16,9 +16,10 @@ BUILD_DIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 # Device code: no packed-fp32 instructions (compiler-generated v_pk_* fp32
-# forms are kept out of every kernel).
+# forms are kept out of every kernel); MFMA accumulators stay in VGPRs so the
+# online-softmax rescale never copies them out of AGPRs.
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          ""]
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def sources():

@@ -15,10 +15,9 @@
 //    kernel merges the chunks exactly from their (max, sum, accumulator).
 //  * GQA grouping: the wavefront computes all G = Hq / Hkv query heads of
 //    its KV head at once, so each K/V row is fetched once per group.
-//  * The per-chunk slot indices are staged in LDS in runs of 512, so the
-//    dependent index->row load chain costs one round trip per run, and the
-//    next 16-key block's rows are requested before the current block is
-//    consumed.
+//  * A chunk's slot indices are staged in the wave's LDS once, so the
+//    dependent index->row load chain costs one round trip per chunk, and the
+//    rows of the next 16-key block are in flight while one is consumed.
 //  * bf16: the G x 16-key score tile and the PV update are MFMA
 //    contractions (16x16x32 for Q K^T, 16x16x16 for P V) whose operands are
 //    loaded straight from HBM in the MFMA lane layout: K rows as 64-byte
@@ -30,6 +29,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "dev_common.h"
 #include "radixrt.h"
 #include "rt_internal.h"
@@ -38,163 +39,180 @@ namespace {
 
 using namespace rtk;
 
-constexpr int kIdxRun = 512;  // slot indices staged per LDS run (per wave)
-
 struct DecodePlan {
-  int splits;
-  int chunk;
+  int splits;  // context chunks per (request, KV head)
+  int chunk;   // keys per chunk (multiple of 16, at most kMaxChunk)
 };
 
-// Chunking depends only on (batch, max_kv_len) so the workspace size is
-// known without the head layout: aim for >= 512 (request, chunk) pairs,
-// chunks of at least 64 keys, at most 64 chunks per request.
-DecodePlan plan_decode(int32_t batch, int32_t max_kv_len) {
-  int s = (512 + batch - 1) / batch;
-  if (s > 64) s = 64;
-  if (s < 1) s = 1;
-  int chunk = (max_kv_len + s - 1) / s;
+constexpr int kMaxChunk = 2048;      // slot indices of one chunk staged in LDS (8 KiB)
+constexpr int kTargetItems = 6144;   // about two work items per resident wave on 256 CUs
+constexpr float kSlack = 8.f;        // log2 headroom of the lazy softmax rescale
+
+// Chunk the context so that there are enough (chunk, KV head, request) work
+// items to keep every wave of the chip busy about twice over, chunks hold at
+// least 64 keys and at most kMaxChunk.  Depends only on the call's sizes.
+DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len) {
+  const int64_t units = int64_t(batch) * num_kv_heads;
+  int64_t s = (kTargetItems + units - 1) / units;
+  s = std::max<int64_t>(s, (max_kv_len + kMaxChunk - 1) / kMaxChunk);
+  s = std::min<int64_t>(s, std::max(1, (max_kv_len + 63) / 64));
+  s = std::max<int64_t>(std::min<int64_t>(s, 1024), 1);
+  int chunk = int((max_kv_len + s - 1) / s);
   chunk = (chunk + 15) / 16 * 16;
-  if (chunk < 64) chunk = 64;
-  int splits = (max_kv_len + chunk - 1) / chunk;
-  if (splits < 1) splits = 1;
+  const int splits = (max_kv_len + chunk - 1) / chunk;
   return {splits, chunk};
 }
 
 // ----------------------------------------------------------------- bf16 --
+// Persistent waves: the grid holds as many waves as fit on the chip; work
+// items (chunk s, KV head h, request b) are ordered with b innermost and cut
+// into 8 contiguous slices, one per XCD (the hardware places block i on XCD
+// i % 8).  Requests that share a cached prefix read the same slots for the
+// same (s, h), so their concurrent waves on one XCD meet those rows in L2.
+template <int D>
+struct DecBlock {
+  u32x4 k[D / 32];        // K operand rows: key kb + col, dims 32*ks + 8*grp .. +7
+  u32x2 v[D / 64][4];     // V rows kb + 4*grp + t, dims 64*h + 4*col .. +3
+};
+
 template <int D>
 __global__ void __launch_bounds__(64) decode_split_bf16(
     const char* __restrict__ q, const char* __restrict__ k_pool, const char* __restrict__ v_pool,
     const int32_t* __restrict__ req_to_token, int64_t stride, const int32_t* __restrict__ rpi,
-    const int32_t* __restrict__ prefix_lens, int Hq, int Hkv, int G, int S, int chunk, float scale_log2,
+    const int32_t* __restrict__ prefix_lens, int B, int Hq, int Hkv, int G, int S, int chunk, float scale_log2,
     float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
   constexpr int KS = D / 32;      // 32-dim steps of the score contraction
   constexpr int VH = D / 64;      // 64-dim halves of the PV update
-  __shared__ int32_t s_idx[kIdxRun];
+  __shared__ int32_t s_idx[kMaxChunk];
 
   const int lane = threadIdx.x;
   const int col = lane & 15;      // MFMA column: query head within the group / key within block
   const int grp = lane >> 4;      // MFMA k-group
-  int item = blockIdx.x;
-  const int s = item % S;
-  item /= S;
-  const int kvh = item % Hkv;
-  const int b = item / Hkv;
-
-  const int kv_len = prefix_lens[b] + 1;
-  const int start = s * chunk;
-  const int end = min(kv_len, start + chunk);
   const int64_t row_bytes = int64_t(Hkv) * D * 2;
-  const int32_t* idx_row = req_to_token + int64_t(rpi ? rpi[b] : b) * stride;
-  const char* kbase = k_pool + int64_t(kvh) * D * 2;
-  const char* vbase = v_pool + int64_t(kvh) * D * 2;
 
-  // Q^T operand: column = query head kvh*G + col, k = dims 32*ks + 8*grp + t.
-  bf16x8 qop[KS];
-  if (col < G) {
-    const char* qp = q + (int64_t(b) * Hq + kvh * G + col) * D * 2;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qop[ks] = as_bf16x8(ld16(qp + (32 * ks + 8 * grp) * 2));
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qop[ks] = as_bf16x8(u32x4{0, 0, 0, 0});
-  }
+  // This wave's share of its XCD's slice of the item list.
+  const int n_items = B * Hkv * S;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+  const int q8 = n_items >> 3, r8 = n_items & 7;
+  const int lo = xcd * q8 + min(xcd, r8);
+  const int hi_item = lo + q8 + (xcd < r8 ? 1 : 0);
 
-  floatx4 o[VH * 4];
-#pragma unroll
-  for (int i = 0; i < VH * 4; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  for (int item = lo + local; item < hi_item; item += per_xcd) {
+    const int b = item % B;
+    const int kvh = (item / B) % Hkv;
+    const int s = item / (B * Hkv);
+    const int kv_len = prefix_lens[b] + 1;
+    const int start = s * chunk;
+    const int end = min(kv_len, start + chunk);
+    const int32_t* idx_row = req_to_token + int64_t(rpi ? rpi[b] : b) * stride;
+    const char* kbase = k_pool + int64_t(kvh) * D * 2 + (8 * grp) * 2;
+    const char* vbase = v_pool + int64_t(kvh) * D * 2 + (4 * col) * 2;
 
-  for (int run = start; run < end; run += kIdxRun) {
-    const int run_end = min(end, run + kIdxRun);
-    __syncthreads();
-    for (int i = lane; i < run_end - run; i += 64) s_idx[i] = idx_row[run + i];
+    // Slot indices of the whole chunk into this wave's LDS, once.
+    __syncthreads();  // the previous item's index reads are complete
+    for (int i = lane; i < end - start; i += 64) s_idx[i] = idx_row[start + i];
     __syncthreads();
 
-    // Operand registers of one 16-key block.
-    u32x4 kreg[KS];
-    u32x2 vreg[VH][4];
-    auto load_block = [&](int kb) {
-      const int kk = kb + col;
-      if (kk < run_end) {
-        const char* kp = kbase + int64_t(s_idx[kk - run]) * row_bytes + (8 * grp) * 2;
+    // Q^T operand: column = query head kvh*G + col, k = dims 32*ks + 8*grp + t.
+    bf16x8 qop[KS];
+    if (col < G) {
+      const char* qp = q + (int64_t(b) * Hq + kvh * G + col) * D * 2;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kreg[ks] = ld16(kp + 64 * ks);
-      } else {
+      for (int ks = 0; ks < KS; ++ks) qop[ks] = as_bf16x8(ld16(qp + (32 * ks + 8 * grp) * 2));
+    } else {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kreg[ks] = u32x4{0, 0, 0, 0};
-      }
+      for (int ks = 0; ks < KS; ++ks) qop[ks] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
+
+    floatx4 o[VH * 4];
+#pragma unroll
+    for (int i = 0; i < VH * 4; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+
+    // Keys past `end` are clamped to the chunk's last key (masked below), so
+    // every load is valid and the loop needs no tail branches.
+    auto load = [&](DecBlock<D>& blk, int kb) {
+      const int kk = min(kb + col, end - 1) - start;
+      const char* kp = kbase + int64_t(uint32_t(s_idx[kk])) * row_bytes;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) blk.k[ks] = ld16(kp + 64 * ks);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int kv = kb + 4 * grp + t;
-        if (kv < run_end) {
-          const char* vp = vbase + int64_t(s_idx[kv - run]) * row_bytes + (4 * col) * 2;
+        const int kv = min(kb + 4 * grp + t, end - 1) - start;
+        const char* vp = vbase + int64_t(uint32_t(s_idx[kv])) * row_bytes;
 #pragma unroll
-          for (int h = 0; h < VH; ++h) vreg[h][t] = ld8(vp + 128 * h);
-        } else {
-#pragma unroll
-          for (int h = 0; h < VH; ++h) vreg[h][t] = u32x2{0, 0};
-        }
+        for (int h = 0; h < VH; ++h) blk.v[h][t] = ld8(vp + 128 * h);
       }
     };
 
-    load_block(run);
-    for (int kb = run; kb < run_end; kb += 16) {
-      // Consume the current block's registers into MFMA operands, then
-      // start the next block's loads before the dependent math.
+    auto consume = [&](const DecBlock<D>& cur, int kb) {
       floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sacc = mfma_16x16x32(as_bf16x8(kreg[ks]), qop[ks], sacc);
-      bf16x4 vop[VH][4];
-#pragma unroll
-      for (int h = 0; h < VH; ++h) {
-        vop[h][0] = as_bf16x4(u32x2{pack_lo16(vreg[h][0].x, vreg[h][1].x), pack_lo16(vreg[h][2].x, vreg[h][3].x)});
-        vop[h][1] = as_bf16x4(u32x2{pack_hi16(vreg[h][0].x, vreg[h][1].x), pack_hi16(vreg[h][2].x, vreg[h][3].x)});
-        vop[h][2] = as_bf16x4(u32x2{pack_lo16(vreg[h][0].y, vreg[h][1].y), pack_lo16(vreg[h][2].y, vreg[h][3].y)});
-        vop[h][3] = as_bf16x4(u32x2{pack_hi16(vreg[h][0].y, vreg[h][1].y), pack_hi16(vreg[h][2].y, vreg[h][3].y)});
-      }
-      if (kb + 16 < run_end) load_block(kb + 16);
-
-      // Scores of keys kb + 4*grp + v for head `col` (log2 domain).
+      for (int ks = 0; ks < KS; ++ks) sacc = mfma_16x16x32(as_bf16x8(cur.k[ks]), qop[ks], sacc);
+      // Scores of keys kb + 4*grp + v for head `col` (log2 domain); keys at or
+      // past `end` (a block wholly past it included) contribute nothing.
       float sv[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sv[v] = (kb + 4 * grp + v < run_end) ? sacc[v] * scale_log2 : -INFINITY;
+      for (int v = 0; v < 4; ++v) sv[v] = (kb + 4 * grp + v < end) ? sacc[v] * scale_log2 : -INFINITY;
       float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       mx = fmaxf(mx, shfl_xor(mx, 16));
       mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      // Lazy rescale: m only moves when a score exceeds it by 2^kSlack.
+      if (__any(mx > m + kSlack)) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int i2 = 0; i2 < VH * 4; ++i2) o[i2] *= alpha;
+        m = m_new;
+      }
       float p[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) p[v] = __builtin_amdgcn_exp2f(sv[v] - m_new);
-      l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-      m = m_new;
-#pragma unroll
-      for (int i = 0; i < VH * 4; ++i) o[i] *= alpha;
+      for (int v = 0; v < 4; ++v) p[v] = __builtin_amdgcn_exp2f(sv[v] - m);
+      l += (p[0] + p[1]) + (p[2] + p[3]);
       const bf16x4 pop = as_bf16x4(u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
+#pragma unroll
+      for (int h = 0; h < VH; ++h) {
+        const u32x2* w = cur.v[h];
+        o[h * 4 + 0] = mfma_16x16x16(as_bf16x4(u32x2{pack_lo16(w[0].x, w[1].x), pack_lo16(w[2].x, w[3].x)}), pop, o[h * 4 + 0]);
+        o[h * 4 + 1] = mfma_16x16x16(as_bf16x4(u32x2{pack_hi16(w[0].x, w[1].x), pack_hi16(w[2].x, w[3].x)}), pop, o[h * 4 + 1]);
+        o[h * 4 + 2] = mfma_16x16x16(as_bf16x4(u32x2{pack_lo16(w[0].y, w[1].y), pack_lo16(w[2].y, w[3].y)}), pop, o[h * 4 + 2]);
+        o[h * 4 + 3] = mfma_16x16x16(as_bf16x4(u32x2{pack_hi16(w[0].y, w[1].y), pack_hi16(w[2].y, w[3].y)}), pop, o[h * 4 + 3]);
+      }
+    };
+
+    // Two register buffers: the next 16-key block is always in flight while
+    // one is consumed (past `end` the loads repeat the clamped last row).
+    const int nb = end > start ? (end - start + 15) >> 4 : 0;
+    if (nb > 0) {
+      DecBlock<D> cur, nxt;
+      load(cur, start);
+      for (int i = 0; i < nb; ++i) {
+        const int kb = start + 16 * i;
+        load(nxt, kb + 16);
+        consume(cur, kb);
+        cur = nxt;
+      }
+    }
+
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    if (col < G) {
+      const int64_t part = (int64_t(b) * Hq + kvh * G + col) * S + s;
+      if (grp == 0) {
+        ws_ml[part * 2 + 0] = m;
+        ws_ml[part * 2 + 1] = l;
+      }
+      float* acc = ws_acc + part * D;
+      // Tile (h, r) row i holds dim 64h + 4i + r; this lane holds rows i = 4*grp + v.
 #pragma unroll
       for (int h = 0; h < VH; ++h)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[h * 4 + r] = mfma_16x16x16(vop[h][r], pop, o[h * 4 + r]);
+        for (int v = 0; v < 4; ++v) {
+          floatx4 w = {o[h * 4 + 0][v], o[h * 4 + 1][v], o[h * 4 + 2][v], o[h * 4 + 3][v]};
+          *reinterpret_cast<floatx4*>(acc + 64 * h + 16 * grp + 4 * v) = w;
+        }
     }
-  }
-
-  l += shfl_xor(l, 16);
-  l += shfl_xor(l, 32);
-  if (col < G) {
-    const int64_t part = (int64_t(b) * Hq + kvh * G + col) * S + s;
-    if (grp == 0) {
-      ws_ml[part * 2 + 0] = m;
-      ws_ml[part * 2 + 1] = l;
-    }
-    float* acc = ws_acc + part * D;
-    // Tile (h, r) row i holds dim 64h + 4i + r; this lane holds rows i = 4*grp + v.
-#pragma unroll
-    for (int h = 0; h < VH; ++h)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        floatx4 w = {o[h * 4 + 0][v], o[h * 4 + 1][v], o[h * 4 + 2][v], o[h * 4 + 3][v]};
-        *reinterpret_cast<floatx4*>(acc + 64 * h + 16 * grp + 4 * v) = w;
-      }
   }
 }
 
@@ -285,16 +303,35 @@ __global__ void __launch_bounds__(64) decode_combine(const float* __restrict__ w
   }
 }
 
+// Resident 64-thread blocks of the bf16 split kernel on this device
+// (occupancy x compute units, a multiple of 8), queried once per device.
+template <int D>
+int resident_waves() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 2048;
+  if (cached[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_bf16<D>, 64, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 ||
+        cus < 1)
+      return 2048;
+    cached[dev] = std::max(8, (per_cu * cus) / 8 * 8);
+  }
+  return cached[dev];
+}
+
 template <int D>
 void launch_decode(const void* q, void* o, const void* k_pool, const void* v_pool, const int32_t* r2t,
                    int64_t stride, const int32_t* rpi, const int32_t* plens, int B, int Hq, int Hkv,
                    DecodePlan pl, float scale_log2, int dtype, float* ws_acc, float* ws_ml, hipStream_t st) {
   const int G = Hq / Hkv;
   if (dtype == RT_BF16) {
-    const uint32_t grid = uint32_t(int64_t(B) * Hkv * pl.splits);
-    hipLaunchKernelGGL(decode_split_bf16<D>, dim3(grid), dim3(64), 0, st, (const char*)q, (const char*)k_pool,
-                       (const char*)v_pool, r2t, stride, rpi, plens, Hq, Hkv, G, pl.splits, pl.chunk,
-                       scale_log2, ws_acc, ws_ml);
+    const int64_t items = int64_t(B) * Hkv * pl.splits;
+    const int64_t grid = std::min<int64_t>(resident_waves<D>(), (items + 7) / 8 * 8);
+    hipLaunchKernelGGL(decode_split_bf16<D>, dim3(uint32_t(grid)), dim3(64), 0, st, (const char*)q, (const char*)k_pool,
+                       (const char*)v_pool, r2t, stride, rpi, plens, B, Hq, Hkv, G, pl.splits, pl.chunk, scale_log2,
+                       ws_acc, ws_ml);
     hipLaunchKernelGGL((decode_combine<D, true>), dim3(uint32_t(int64_t(B) * Hq)), dim3(64), 0, st, ws_acc,
                        ws_ml, pl.splits, o);
   } else {
@@ -309,11 +346,13 @@ void launch_decode(const void* q, void* o, const void* k_pool, const void* v_poo
 
 }  // namespace
 
-extern "C" int64_t radix_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
-                                                int32_t max_kv_len) {
-  if (batch < 0 || num_q_heads < 1 || (head_dim != 64 && head_dim != 128) || max_kv_len < 1) return -1;
+extern "C" int64_t radix_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t max_kv_len) {
+  if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
+      (head_dim != 64 && head_dim != 128) || max_kv_len < 1)
+    return -1;
   if (batch == 0) return 0;
-  DecodePlan pl = plan_decode(batch, max_kv_len);
+  DecodePlan pl = plan_decode(batch, num_kv_heads, max_kv_len);
   return int64_t(batch) * num_q_heads * pl.splits * (head_dim + 2) * int64_t(sizeof(float));
 }
 
@@ -329,15 +368,17 @@ extern "C" int radix_decode_attention(const void* q, void* o, const void* k_pool
       (head_dim != 64 && head_dim != 128) || (dtype != RT_F32 && dtype != RT_BF16) || max_kv_len < 1 ||
       req_to_token_stride < max_kv_len || !(sm_scale > 0.f))
     return rt::fail(RT_ERR_INVALID, "radix_decode_attention: bad shape, dtype, stride or scale");
+  if (int64_t(max_kv_len) > int64_t(kMaxChunk) * 1024)
+    return rt::fail(RT_ERR_INVALID, "radix_decode_attention: max_kv_len above 2097152");
   if (dtype == RT_BF16 && num_q_heads / num_kv_heads > 16)
     return rt::fail(RT_ERR_INVALID, "radix_decode_attention: bf16 path supports at most 16 query heads per KV head");
   if (batch == 0) return RT_OK;
   if (!q || !o || !k_pool || !v_pool || !req_to_token || !prefix_lens || !workspace)
     return rt::fail(RT_ERR_INVALID, "radix_decode_attention: null pointer");
-  const int64_t need = radix_decode_workspace_bytes(batch, num_q_heads, head_dim, max_kv_len);
+  const int64_t need = radix_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_kv_len);
   if (workspace_bytes < need)
     return rt::fail(RT_ERR_INVALID, "radix_decode_attention: workspace too small (need " + std::to_string(need) + ")");
-  const DecodePlan pl = plan_decode(batch, max_kv_len);
+  const DecodePlan pl = plan_decode(batch, num_kv_heads, max_kv_len);
   float* ws_acc = static_cast<float*>(workspace);
   float* ws_ml = ws_acc + int64_t(batch) * num_q_heads * pl.splits * head_dim;
   const float scale_log2 = sm_scale * kLog2e;

@@ -65,7 +65,7 @@ class RadixRuntime:
         return t.pin_memory().to(self.device, non_blocking=True)
 
     def workspace(self, batch, max_kv_len):
-        need = B.radix_decode_workspace_bytes(batch, self.hq, self.d, max_kv_len)
+        need = B.radix_decode_workspace_bytes(batch, self.hq, self.hkv, self.d, max_kv_len)
         if self._ws.numel() < need:
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._ws

@@ -25,6 +25,8 @@ from .gen import (
     splitmix64_np,
     prefix_hashes_np,
     prefix_hashes_from_np,
+    prefix_hashes_rows_np,
+    chain_start,
     value_keys_np,
     qkv_values_np,
     KIND_Q,
@@ -37,6 +39,8 @@ __all__ = [
     "splitmix64_np",
     "prefix_hashes_np",
     "prefix_hashes_from_np",
+    "prefix_hashes_rows_np",
+    "chain_start",
     "value_keys_np",
     "qkv_values_np",
     "KIND_Q",

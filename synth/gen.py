@@ -45,6 +45,21 @@ def prefix_hashes_from_np(tokens, start_hash):
     return out
 
 
+def prefix_hashes_rows_np(tokens, start_hashes):
+    """Rolling hashes of several rows at once: tokens int [R, L], start_hashes
+    uint64 [R] (hash before each row's first token).  Returns uint64 [R, L]."""
+    toks = np.asarray(tokens, dtype=np.int64)
+    R, L = toks.shape
+    out = np.empty((R, L), dtype=np.uint64)
+    h = np.asarray(start_hashes, dtype=np.uint64).copy()
+    t1 = (toks + 1).astype(np.uint64)
+    with np.errstate(over="ignore"):
+        for i in range(L):
+            h = splitmix64_np(h ^ t1[:, i])
+            out[:, i] = h
+    return out
+
+
 def prefix_hashes_np(tokens, seed):
     """Rolling hash of tokens[0..i] for every i (uint64 [len(tokens)])."""
     return prefix_hashes_from_np(tokens, _chain_start(seed))

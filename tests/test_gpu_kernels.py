@@ -92,7 +92,7 @@ def _run_decode(case, q_host, prefix_lens, hq, hkv, d, dtype, rows=None, r2t=Non
     o = torch.full_like(q, float("nan"))
     kp, vp = to_dev(case["kpool"], dtype), to_dev(case["vpool"], dtype)
     max_kv = max(prefix_lens) + 1
-    ws = torch.empty(B.radix_decode_workspace_bytes(len(prefix_lens), hq, d, max_kv), dtype=torch.uint8,
+    ws = torch.empty(B.radix_decode_workspace_bytes(len(prefix_lens), hq, hkv, d, max_kv), dtype=torch.uint8,
                      device="cuda")
     B.radix_decode_attention(q, o, kp, vp, i32(case["r2t"] if r2t is None else r2t),
                              i32(case["rows"] if rows is None else rows), i32(prefix_lens), max_kv,

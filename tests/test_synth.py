@@ -52,3 +52,10 @@ def test_workload_shapes():
     assert [len(r.prompt) for r in f.requests] == [1024] + [1152] * 4
     c = workloads.chat(sessions=4)
     assert len(c.requests) == 1 + 16
+
+
+def test_row_hash_chains_equal_single_chains():
+    from synth import chain_start, prefix_hashes_rows_np
+    toks = np.random.default_rng(2).integers(0, 1000, size=(4, 33))
+    rows = prefix_hashes_rows_np(toks, [chain_start(3)] * 4)
+    assert np.array_equal(rows, np.stack([prefix_hashes_np(t, 3) for t in toks]))
