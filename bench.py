@@ -42,6 +42,22 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
+def profiled_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    runs (profiles/traffic.json), or None once the kernel source has changed
+    since those counters were taken."""
+    import hashlib
+    try:
+        data = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+        ent = data[kernel]
+        src = open(os.path.join(ROOT, ent["source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest() != ent["source_sha256"]:
+            return None
+        return (ent["fetch_kib"] * data["fetch_factor"] + ent["write_kib"] * data["write_factor"]) * 1024.0
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,7 +287,7 @@ def run_few_shot(args, torch):
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved_tflops / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": profiled_traffic("extend_bf16"),
             "flops_per_launch": flops_avg,
             "avg_launch_us": ext_avg_s * 1e6,
         },
@@ -465,7 +481,8 @@ def run_decode_bench(args, torch):
                    "head_dim": db.D, "pool_slots": db.SLOTS},
         "roofline": {"bound": "hbm", "kernel": "radix_decode_attention (decode_split_bf16<128> + decode_combine)",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": None, "bytes_per_launch": alg_bytes, "distinct_bytes_per_launch": distinct,
+                     "traffic": profiled_traffic("decode_split_bf16") if db.name == "long_context" else None,
+                     "bytes_per_launch": alg_bytes, "distinct_bytes_per_launch": distinct,
                      "avg_launch_us": avg_s * 1e6},
     }
     if args.check:
