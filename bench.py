@@ -108,6 +108,7 @@ class FewShotBench:
         self.o_ext = torch.empty((self.B * self.SUFFIX, self.HQ, self.D), dtype=bf16, device=self.dev)
         self.o_dec = torch.empty((self.B, self.HQ, self.D), dtype=bf16, device=self.dev)
         self.sm_scale = 1.0 / np.sqrt(self.D)
+        self.pos_dev = torch.full((self.B,), self.PREFIX + self.SUFFIX, dtype=torch.int32, device=self.dev)
         self.ext_events = []
         self.dec_events = []
         self.flops = []
@@ -241,7 +242,6 @@ def run_few_shot(args, torch):
     from synth import torch_gen
     n = args.warmup + args.steps
     fb = FewShotBench(n, torch, Bm, torch_gen)
-    fb.pos_dev = torch.full((fb.B,), fb.PREFIX + fb.SUFFIX, dtype=torch.int32, device=fb.dev)
     fb.gen_inputs(n)
     fb.warm_prefix()
     for i in range(args.warmup):

@@ -33,24 +33,32 @@ from . import binding as B
 
 
 class RadixRuntime:
+    """device=None runs the host half only (tree, pool, slot table): the
+    device steps are skipped and return None.  Used to check host decisions
+    on machines without a GPU."""
+
     def __init__(self, num_slots, num_q_heads, num_kv_heads, head_dim, dtype, max_reqs, max_ctx,
                  device="cuda", stream=None):
         self.num_slots = int(num_slots)
         self.hq, self.hkv, self.d = int(num_q_heads), int(num_kv_heads), int(head_dim)
         self.dtype = dtype
         self.max_reqs, self.max_ctx = int(max_reqs), int(max_ctx)
-        self.device = torch.device(device)
-        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         self.pool = B.rt_pool_create(self.num_slots)
         self.tree = B.rt_tree_create(self.pool)
+        self.free_rows = list(range(self.max_reqs))
+        self.sm_scale = 1.0 / float(np.sqrt(self.d))
+        self.device = None if device is None else torch.device(device)
+        if self.device is None:
+            self.stream = None
+            self.r2t_host = np.zeros((self.max_reqs, self.max_ctx), dtype=np.int32)
+            return
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         # Slot 0 stays zero: padded writes land there and it is never read as data.
         self.k_pool = torch.zeros((self.num_slots + 1, self.hkv, self.d), dtype=dtype, device=self.device)
         self.v_pool = torch.zeros_like(self.k_pool)
         self.r2t_host_t = torch.zeros((self.max_reqs, self.max_ctx), dtype=torch.int32, pin_memory=True)
         self.r2t_host = self.r2t_host_t.numpy()
         self.r2t_dev = torch.zeros((self.max_reqs, self.max_ctx), dtype=torch.int32, device=self.device)
-        self.free_rows = list(range(self.max_reqs))
-        self.sm_scale = 1.0 / float(np.sqrt(self.d))
         self._ws = torch.empty(0, dtype=torch.uint8, device=self.device)
 
     def close(self):
@@ -72,6 +80,8 @@ class RadixRuntime:
 
     def upload_rows(self, rows, lens):
         """Copy the first lens[i] entries of host rows rows[i] to the device table."""
+        if self.device is None:
+            return
         with torch.cuda.stream(self.stream):
             for r, n in zip(rows, lens):
                 if n > 0:
@@ -80,6 +90,8 @@ class RadixRuntime:
     # ------------------------------------------------------ device steps --
     def run_extend(self, rows, prefix_lens, extend_lens, q, k_new, v_new, out_cache_loc, attention=True):
         """kv_store of the new rows, then extend attention.  Returns o (or None)."""
+        if self.device is None:
+            return None
         n = len(rows)
         with torch.cuda.stream(self.stream):
             loc = self._to_dev(out_cache_loc)
@@ -97,6 +109,8 @@ class RadixRuntime:
 
     def run_decode(self, rows, positions, slots, q, k_new, v_new):
         """Write the new slots into the table, store the new rows, decode."""
+        if self.device is None:
+            return None
         n = len(rows)
         with torch.cuda.stream(self.stream):
             rows_d, pos_d, slots_d = self._to_dev(rows), self._to_dev(positions), self._to_dev(slots)
@@ -208,7 +222,7 @@ class Scheduler:
                 self.cached_tokens += r.prefix_len
                 self.prefill_tokens += len(r.req.prompt)
             rt.upload_rows([r.row for r in admitted], [len(r.req.prompt) for r in admitted])
-            if total > 0:
+            if total > 0 and rt.device is not None:
                 qs, ks, vs = [], [], []
                 for r, e in zip(admitted, ext):
                     if e == 0:
@@ -241,15 +255,17 @@ class Scheduler:
             for r, s, pos in zip(dec, slots, positions):
                 rt.r2t_host[r.row, pos] = s
                 rec["decode"].append((r.req.rid, int(pos), int(s)))
-            qs, ks, vs = [], [], []
-            for r, pos in zip(dec, positions):
-                seq = list(r.req.prompt) + list(r.req.gen[:r.generated + 1])
-                q, k, v = self.qkv(r.req.rid, seq, np.array([pos]))
-                qs.append(q)
-                ks.append(k)
-                vs.append(v)
-            o = rt.run_decode(rows, positions, slots, torch.cat(qs), torch.cat(ks), torch.cat(vs))
-            if self.record is not None:
+            o = None
+            if rt.device is not None:
+                qs, ks, vs = [], [], []
+                for r, pos in zip(dec, positions):
+                    seq = list(r.req.prompt) + list(r.req.gen[:r.generated + 1])
+                    q, k, v = self.qkv(r.req.rid, seq, np.array([pos]))
+                    qs.append(q)
+                    ks.append(k)
+                    vs.append(v)
+                o = rt.run_decode(rows, positions, slots, torch.cat(qs), torch.cat(ks), torch.cat(vs))
+            if o is not None and self.record is not None:
                 for i, r in enumerate(dec):
                     self.record("dec", r.req.rid, r.generated, o[i:i + 1])
             for r in dec:
@@ -259,7 +275,8 @@ class Scheduler:
                 self.running.remove(r)
                 self._finish(r, rec)
         # Host rows and pinned staging are reused by later iterations.
-        rt.stream.synchronize()
+        if rt.stream is not None:
+            rt.stream.synchronize()
         self.iterations.append(rec)
         if self.keep_dumps:
             self.dumps.append(B.rt_tree_dump(rt.tree))

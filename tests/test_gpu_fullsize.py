@@ -1,0 +1,60 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py
+times (its own classes drive the same kernels with the same grids): sampled
+outputs against the oracle's float64 full recompute of those rows."""
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+from oracle.attention import recompute_rows
+from prefix_shared_kv_rt_amd import binding as B
+from synth import torch_gen
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def test_few_shot_full_size_bench_path():
+    """64 requests x (1024 shared + 128 distinct) per step, three steps: the
+    extend rows actually computed (position >= matched prefix) and the
+    decode row of sampled requests."""
+    print("few-shot full size", flush=True)
+    fb = bench.FewShotBench(3, torch, B, torch_gen)
+    fb.gen_inputs(3)
+    fb.warm_prefix()
+    worst = 0.0
+    for i in range(3):
+        fb.step(i, timed=False)
+        fb.stream.synchronize()
+        res = bench.check_few_shot(fb, i)
+        print(f"  step {i}: {res}", flush=True)
+        worst = max(worst, res["max_abs_err"])
+    assert worst <= TOL
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,steps,sample_steps", [
+    ("fork", 256, (0, 127, 255)),
+    ("long_context", 128, (0, 64, 127)),
+])
+def test_decode_full_size_bench_path(name, steps, sample_steps):
+    print(f"{name} full size, {steps} decode steps", flush=True)
+    db = bench.DecodeBench(name, torch, B, torch_gen, steps)
+    db.setup()
+    saved = {}
+    for s in range(steps):
+        db.step(s, timed=False)
+        if s in sample_steps:
+            db.stream.synchronize()
+            saved[s] = db.o.float().cpu().numpy()
+    per = db.B // db.groups
+    worst = 0.0
+    for b in (0, db.B - 1):
+        toks = list(db.shared_toks[b // per]) + list(db.private_toks[b]) + list(db.gen_toks[b])
+        pos = [db.prompt_len + s for s in sample_steps]
+        want = recompute_rows(toks, pos, db.HQ, db.HKV, db.D, db.SEED, db.sm_scale)
+        for k, s in enumerate(sample_steps):
+            worst = max(worst, float(np.abs(saved[s][b] - want[k]).max()))
+    print(f"  max abs err {worst:.3e}", flush=True)
+    assert worst <= TOL

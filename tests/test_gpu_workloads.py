@@ -96,3 +96,16 @@ def test_small_chat_with_eviction_bf16():
     check_host_identical(ora, sch, dump, free)
     check_outputs(ora, outs, TOL["bf16"])
     assert any(len(it["extend_freed"]) or len(it["decode_freed"]) for it in ora.iterations)
+
+
+@pytest.mark.timeout(900)
+def test_chat_full_size_sampled():
+    """The full multi-turn chat workload (256 sessions x 4 turns, pool at 60%
+    of the working set, eviction and re-extension): every host decision
+    bit-exact, attention of sampled requests (every 64th) within tolerance."""
+    print("chat full size", flush=True)
+    wl = workloads.chat()
+    sel = lambda kind, rid, step: rid % 64 == 5 and (kind == "ext" or step in (0, 127))
+    ora, sch, outs, dump, free = run_both(wl, want=sel)
+    check_host_identical(ora, sch, dump, free)
+    check_outputs(ora, outs, TOL["bf16"])

@@ -1,0 +1,75 @@
+"""Host decisions of the runtime (C++ tree + pool through the C ABI, batch
+scheduler) against the oracle on the full-size workloads: admitted batches,
+prefix lengths, every allocated slot, evictions, finishes, hit-rate
+integers, the final tree and the final free list must be identical.  No GPU:
+the runtime runs its host half only."""
+
+import time
+
+import pytest
+
+from oracle.runner import run_workload
+from prefix_shared_kv_rt_amd import binding as B
+from prefix_shared_kv_rt_amd.runtime import RadixRuntime, Scheduler
+from synth import workloads
+
+
+def _host_compare(wl, max_running=256, max_extend_tokens=16384):
+    t0 = time.time()
+    ora = run_workload(wl, attention=False, max_running=max_running, max_extend_tokens=max_extend_tokens)
+    t1 = time.time()
+    rt = RadixRuntime(wl.num_slots, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, None,
+                      max(max_running, 8), wl.max_ctx, device=None)
+    sch = Scheduler(rt, wl.requests, None, max_running=max_running, max_extend_tokens=max_extend_tokens).run()
+    t2 = time.time()
+    print(f"{wl.name}: oracle {t1 - t0:.1f}s, runtime {t2 - t1:.1f}s, {len(ora.iterations)} iterations, "
+          f"hit {ora.cached_tokens}/{ora.prefill_tokens}", flush=True)
+    assert (sch.cached_tokens, sch.prefill_tokens) == (ora.cached_tokens, ora.prefill_tokens)
+    assert len(sch.iterations) == len(ora.iterations)
+    for i, (a, b) in enumerate(zip(sch.iterations, ora.iterations)):
+        assert a["admitted"] == b["admitted"], i
+        assert a["extend_loc"] == b["extend_loc"], i
+        assert a.get("extend_freed_tokens", 0) == len(b["extend_freed"]), i
+        assert a["decode"] == b["decode"], i
+        assert a.get("decode_freed_tokens", 0) == len(b["decode_freed"]), i
+        assert a["finished"] == b["finished"], i
+    assert sch.request_slots == ora.request_slots
+    assert B.rt_tree_dump(rt.tree) == ora.final_dump
+    assert list(B.rt_pool_free_list(rt.pool)) == ora.free_list
+    rt.close()
+    return ora
+
+
+@pytest.mark.parametrize("pool", [512, 160])
+def test_tiny(pool):
+    ora = _host_compare(workloads.tiny(pool))
+    assert (ora.cached_tokens, ora.prefill_tokens) == ((96, 192) if pool == 512 else (224, 384))
+
+
+def test_few_shot_full():
+    ora = _host_compare(workloads.few_shot())
+    assert ora.cached_tokens == 64 * 1024 and ora.prefill_tokens == 1024 + 64 * 1152
+
+
+def test_fork_full():
+    ora = _host_compare(workloads.fork())
+    assert ora.cached_tokens == 128 * 2048 and ora.prefill_tokens == 144 * 2048
+
+
+def test_long_context_full():
+    ora = _host_compare(workloads.long_context())
+    assert ora.cached_tokens == 32 * 16384
+
+
+def test_chat_full_with_eviction():
+    wl = workloads.chat()
+    ora = _host_compare(wl)
+    evicted = sum(len(it["extend_freed"]) + len(it["decode_freed"]) for it in ora.iterations)
+    assert evicted > 0
+    # re-extension: some turn matched less than the whole history its previous
+    # turn inserted (part of it was evicted in between)
+    by_rid = {r.rid: r for r in wl.requests}
+    matched = {rid: p for it in ora.iterations for rid, p, _ in it["admitted"]}
+    redo = [r.rid for r in wl.requests if r.after and r.after[0] != 0 and
+            matched[r.rid] < len(by_rid[r.after[0]].prompt) + len(by_rid[r.after[0]].gen)]
+    assert redo
