@@ -12,16 +12,17 @@
 // with the G = Hq / Hkv heads of one KV head innermost, so every K/V tile
 // staged in LDS serves all G heads at once.  Four wavefronts own 32 rows
 // each.  Per 64-key tile:
-//   * 256 threads gather the 64 K rows and 64 V rows of this KV head
-//     (D*2 bytes each, 16-byte pieces, slots from req_to_token) into
-//     registers, then LDS; the next tile's gather is issued before the
-//     current tile's math so its HBM latency hides behind the MFMAs.
+//   * the slot indices of the item's keys are staged in LDS once per 2048
+//     keys; each wave then issues direct HBM-to-LDS loads
+//     (global_load_lds_dwordx4, 1 KiB per instruction) for its share of the
+//     next tile's 64 K rows and 64 V rows while the current tile is used
+//     (two LDS stages);
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B =
 //     the wave's Q rows held in registers for the whole kernel).  With keys
 //     as MFMA rows, each lane owns one query row, so the softmax max/sum
 //     need only one cross-lane exchange (lane ^ 32).
-//   * Online softmax in the log2 domain; the accumulator rescale is skipped
-//     when no row's running max moved (usual after the first tiles).
+//   * Online softmax in the log2 domain with a lazy rescale: the running max
+//     moves only when a tile's max exceeds it by more than 2^8.
 //   * O^T += V^T P^T with the same MFMA.  P^T comes straight from the score
 //     registers (the key order of the contraction is chosen to match the
 //     score layout); V^T operands come from LDS through gfx950's transpose
@@ -46,8 +47,11 @@ namespace {
 
 using namespace rtk;
 
-constexpr int kBM = 128;  // query rows per work item (4 waves x 32)
-constexpr int kBN = 64;   // keys per LDS tile
+constexpr int kBN = 64;        // keys per LDS tile
+// 32-row query blocks per wave.  2 halves the LDS reads per MFMA but needs
+// more than 256 registers (one wave per SIMD); on gfx950 1 measures faster.
+constexpr int kRB = 1;
+constexpr int kSeg = 2048;     // keys whose slot indices are staged in LDS at a time
 constexpr float kSlack = 8.f;  // log2 headroom of the lazy softmax rescale
 
 template <int D>
@@ -56,6 +60,7 @@ struct ExtendCfg {
   static constexpr int kCPR = kRowBytes / 16;             // 16-byte chunks per row
   static constexpr int kKPI = 64 / kCPR;                  // rows per 64-lane LDS load (1 KiB)
   static constexpr int kLoadsPerWave = kBN / kKPI / 4;    // per wave per tile, K and V each
+  static constexpr int kKB = kBN / 32;                    // 32-key blocks per tile
   static constexpr int kTile = kBN * kRowBytes;           // bytes of one K (or V) tile
   static constexpr int kKS = D / 16;                      // 16-dim steps of Q K^T
   static constexpr int kR = D / 32;                       // 32-dim tiles of O^T
@@ -81,21 +86,24 @@ __device__ __forceinline__ int swz(int key, int chunk) {
   return key * ExtendCfg<D>::kRowBytes + ((chunk ^ (swz_f(key) & (ExtendCfg<D>::kCPR - 1))) << 4);
 }
 
-template <int D>
-__global__ void __launch_bounds__(256, 2) extend_bf16(
+template <int D, int RB>
+__global__ void __launch_bounds__(256, RB == 1 ? 2 : 1) extend_bf16(
     const char* __restrict__ q, char* __restrict__ o, const char* __restrict__ k_pool,
     const char* __restrict__ v_pool, const int32_t* __restrict__ req_to_token, int64_t stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
     const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ qo_indptr, int B, int Hq, int Hkv,
     int G, int n_qt, float scale_log2) {
   using C = ExtendCfg<D>;
-  // Two stages of K and V tiles: the next tile streams into one stage while the
-  // other is used.  Separate arrays let the compiler see that LDS reads of one
-  // stage never wait on the loads still landing in the other.
+  constexpr int kWaveRows = 32 * RB;          // query rows per wave (RB blocks of 32)
+  constexpr int kItemRows = 4 * kWaveRows;    // query rows per work item
+  // Two stages of K and V tiles: the next tile streams into one stage while
+  // the other is used.  Separate arrays let the compiler see that LDS reads of
+  // one stage never wait on the loads still landing in the other.
   __shared__ __attribute__((aligned(1024))) char sk0[C::kTile];
   __shared__ __attribute__((aligned(1024))) char sv0[C::kTile];
   __shared__ __attribute__((aligned(1024))) char sk1[C::kTile];
   __shared__ __attribute__((aligned(1024))) char sv1[C::kTile];
+  __shared__ uint32_t s_slot[kSeg];
 
   const int work = xcd_slice(blockIdx.x, gridDim.x);
   const int qt = work % n_qt;
@@ -103,28 +111,32 @@ __global__ void __launch_bounds__(256, 2) extend_bf16(
   const int kvh = work / (n_qt * B);
 
   const int E = extend_lens[b];
-  const int row0 = qt * kBM;                  // first query row of this item
-  const int j_first = row0 / G;
-  if (j_first >= E) return;
+  const int row0 = qt * kItemRows;            // first query row of this item
+  if (row0 / G >= E) return;
   const int P = prefix_lens[b];
-  const int j_last = min(E - 1, (row0 + kBM - 1) / G);
+  const int j_last = min(E - 1, (row0 + kItemRows - 1) / G);
   const int kv_end = P + j_last + 1;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int lane = tid & 63;
-  const int r32 = lane & 31;   // this lane's query row within the wave / MFMA column
+  const int r32 = lane & 31;   // this lane's query row within a 32-row block / MFMA column
   const int hi = lane >> 5;    // MFMA k-half
 
-  // This lane's query row.
-  const int qrow = row0 + wave * 32 + r32;
-  const int j = qrow / G;
-  const int g = qrow - j * G;
-  const bool row_ok = j < E;
-  const int limit = P + min(j, E - 1);        // last visible key (invalid rows mimic the last row)
-  const int wj_first = min((row0 + wave * 32) / G, E - 1);
-  const int wj_last = min((row0 + wave * 32 + 31) / G, E - 1);
+  // This lane's query row in each of the wave's row blocks.
+  int jrow[RB], grow[RB], limit[RB];
+  bool row_ok[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int qrow = row0 + wave * kWaveRows + rb * 32 + r32;
+    jrow[rb] = qrow / G;
+    grow[rb] = qrow - jrow[rb] * G;
+    row_ok[rb] = jrow[rb] < E;
+    limit[rb] = P + min(jrow[rb], E - 1);    // last visible key (invalid rows mimic the last row)
+  }
+  const int wj_first = min((row0 + wave * kWaveRows) / G, E - 1);
+  const int wj_last = min((row0 + wave * kWaveRows + kWaveRows - 1) / G, E - 1);
   const int w_min_limit = P + wj_first;       // keys <= this are visible to every row of the wave
   const int w_end = P + wj_last + 1;          // keys >= this are invisible to every row of the wave
 
@@ -133,45 +145,50 @@ __global__ void __launch_bounds__(256, 2) extend_bf16(
   const char* kbase = k_pool + int64_t(kvh) * C::kRowBytes;
   const char* vbase = v_pool + int64_t(kvh) * C::kRowBytes;
 
-  // Q^T operand (B of S^T = K Q^T): column r32 = query row, k = dims 16*ks + 8*hi + t.
-  bf16x8 qop[C::kKS];
-  {
-    const int64_t tok = int64_t(qo_indptr[b]) + j;
-    const char* qp = q + (tok * Hq + int64_t(kvh) * G + g) * C::kRowBytes + hi * 16;
+  // Q^T operands (B of S^T = K Q^T): column r32 = query row, k = dims 16*ks + 8*hi + t.
+  bf16x8 qop[RB][C::kKS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int64_t tok = int64_t(qo_indptr[b]) + jrow[rb];
+    const char* qp = q + (tok * Hq + int64_t(kvh) * G + grow[rb]) * C::kRowBytes + hi * 16;
 #pragma unroll
     for (int ks = 0; ks < C::kKS; ++ks)
-      qop[ks] = as_bf16x8(row_ok ? ld16(qp + ks * 32) : u32x4{0, 0, 0, 0});
+      qop[rb][ks] = as_bf16x8(row_ok[rb] ? ld16(qp + ks * 32) : u32x4{0, 0, 0, 0});
   }
 
-  floatx16 oacc[C::kR];
+  floatx16 oacc[RB][C::kR];
 #pragma unroll
-  for (int r = 0; r < C::kR; ++r)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[r][i] = 0.f;
-  float m = -INFINITY, l = 0.f;
+    for (int r = 0; r < C::kR; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[rb][r][i] = 0.f;
+  float m[RB], l[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+  }
 
   // Tile loads go straight from HBM to LDS (global_load_lds_dwordx4): one
   // 64-lane load fills kKPI consecutive rows (1 KiB).  Wave w issues loads
   // n = w + 4*it; lane i takes row kKPI*n + i/kCPR and the logical chunk that
   // the swizzle stores at physical chunk i%kCPR.  Keys past kv_end are clamped
   // to the last valid key (masked later; a real row keeps the tile finite).
-  // Slot indices run one tile ahead of the loads that use them.
+  // Slot indices come from s_slot, staged per segment of kSeg keys.
   const int ld_row = lane / C::kCPR;
   const int ld_pchunk = lane % C::kCPR;
-  uint32_t slot_next[C::kLoadsPerWave];
-  auto load_idx = [&](int tile) {
+  int seg0 = 0;  // first key of the segment whose slot indices are in s_slot
+  // Loads of one wave read the slot indices at s_slot[tile_key + krow]; the
+  // staging pads the segment's last tile with the last valid key, so no clamp.
+  const int krow0 = C::kKPI * wave + ld_row;
+  const int lchunk = ld_pchunk ^ (swz_f(krow0) & (C::kCPR - 1));  // same for every it: krow = krow0 + 16*kKPI*it
+  const uint64_t lane_off = uint64_t(lchunk << 4);
+  auto issue = [&](int tile, char* sk, char* sv) {
+    const uint32_t* srow = s_slot + (tile * kBN - seg0) + krow0;
 #pragma unroll
     for (int it = 0; it < C::kLoadsPerWave; ++it) {
-      const int key = min(tile * kBN + C::kKPI * (wave + 4 * it) + ld_row, kv_end - 1);
-      slot_next[it] = uint32_t(idx_row[key]);
-    }
-  };
-  auto issue = [&](char* sk, char* sv) {
-#pragma unroll
-    for (int it = 0; it < C::kLoadsPerWave; ++it) {
-      const int krow = C::kKPI * (wave + 4 * it) + ld_row;
-      const int lchunk = ld_pchunk ^ (swz_f(krow) & (C::kCPR - 1));
-      const uint64_t off = uint64_t(slot_next[it]) * pool_row + uint32_t(lchunk << 4);
+      const uint64_t off = uint64_t(srow[4 * C::kKPI * it]) * pool_row + lane_off;
       const int dst = C::kKPI * (wave + 4 * it) * C::kRowBytes;
       __builtin_amdgcn_global_load_lds(kbase + off, (__attribute__((address_space(3))) void*)(sk + dst), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vbase + off, (__attribute__((address_space(3))) void*)(sv + dst), 16, 0, 0);
@@ -185,74 +202,77 @@ __global__ void __launch_bounds__(256, 2) extend_bf16(
   const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int tr_half = (lane & 1) * 8;
 
-  // One tile: wait for its loads (barrier), start the next tile's loads into
-  // the other stage, then compute from this stage.
+  // One tile: barrier (this tile's loads have landed everywhere and the other
+  // stage is free), start the next tile's loads into the other stage, then
+  // compute from this one.
+  int seg_end = 0;  // tiles below seg_end have their slot indices staged
   auto step = [&](int tile, const char* sk, const char* sv, char* sk_next, char* sv_next) {
-    __syncthreads();  // this tile's loads landed everywhere; the other stage is free
-    if (tile + 1 < n_tiles) {
-      issue(sk_next, sv_next);
-      if (tile + 2 < n_tiles) load_idx(tile + 2);
-    }
+    __syncthreads();
+    if (tile + 1 < seg_end) issue(tile + 1, sk_next, sv_next);
     const int base = tile * kBN;
     if (base >= w_end) return;                // wave-uniform: every row of this wave is done
-    // ---- scores S^T[key][row] for two 32-key blocks
-    floatx16 sacc[2];
+
+    // ---- scores S^T[key][row] for the tile's 32-key blocks; each K operand
+    // read from LDS feeds the wave's RB row blocks
+    floatx16 sacc[RB][C::kKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < C::kKB; ++kb) {
       u32x4 ka[C::kKS];
 #pragma unroll
       for (int ks = 0; ks < C::kKS; ++ks)
         ka[ks] = *reinterpret_cast<const u32x4*>(sk + swz<D>(kb * 32 + r32, 2 * ks + hi));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+      for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int ks = 0; ks < C::kKS; ++ks) sacc[kb] = mfma_32x32x16(as_bf16x8(ka[ks]), qop[ks], sacc[kb]);
+        for (int i = 0; i < 16; ++i) sacc[rb][kb][i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < C::kKS; ++ks)
+          sacc[rb][kb] = mfma_32x32x16(as_bf16x8(ka[ks]), qop[rb][ks], sacc[rb][kb]);
+      }
     }
-    // Lane holds keys base + 32*kb + 8*(v/4) + 4*hi + (v%4) of query row r32.
+    // Lane holds keys base + 32*kb + 8*(v/4) + 4*hi + (v%4) of its query rows.
     // Only tiles that cross this wave's diagonal (or its last key) need a mask.
-    if (base + 2 * 32 - 1 > w_min_limit) {
-      const int rel = base + 4 * hi - limit;  // key - limit = rel + const(kb, v)
+    const bool masked = base + kBN - 1 > w_min_limit;
+    float neg_m[RB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int rb = 0; rb < RB; ++rb) {
+      if (masked) {
+        const int rel = base + 4 * hi - limit[rb];  // key - limit = rel + const(kb, v)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (rel + 32 * kb + 8 * (v >> 2) + (v & 3) > 0) sacc[kb][v] = -INFINITY;
+        for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (rel + 32 * kb + 8 * (v >> 2) + (v & 3) > 0) sacc[rb][kb][v] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[rb][kb][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // Lazy rescale: the reference max m only moves when some row's max
+      // exceeds it by more than 2^kSlack, so probabilities stay <= 2^kSlack
+      // (harmless in fp32 and bf16) and the accumulator rescale is rare.
+      const float m_tile = mx * scale_log2;
+      if (__any(m_tile > m[rb] + kSlack)) {
+        const float m_new = fmaxf(m[rb], m_tile);
+        const float alpha = __builtin_amdgcn_exp2f(m[rb] - m_new);
+        l[rb] *= alpha;
+#pragma unroll
+        for (int r = 0; r < C::kR; ++r)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[rb][r][i] *= alpha;
+        m[rb] = m_new;
+      }
+      neg_m[rb] = -m[rb];
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Lazy rescale: the reference max m only moves when some row's max
-    // exceeds it by more than 2^kSlack, so probabilities stay <= 2^kSlack
-    // (harmless in fp32 and bf16) and the accumulator rescale is rare.
-    const float m_tile = mx * scale_log2;
-    if (__any(m_tile > m + kSlack)) {
-      const float m_new = fmaxf(m, m_tile);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      l *= alpha;
-#pragma unroll
-      for (int r = 0; r < C::kR; ++r)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[r][i] *= alpha;
-      m = m_new;
-    }
-    const float neg_m = -m;
 
-    // ---- O^T += V^T P^T, 16 keys per MFMA
+    // ---- O^T += V^T P^T, 16 keys per MFMA; each V operand read feeds the
+    // wave's RB row blocks
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < C::kKB; ++kb) {
 #pragma unroll
       for (int sh = 0; sh < 2; ++sh) {
-        float p[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          p[t] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * sh + t], scale_log2, neg_m));
-          l += p[t];
-        }
-        const bf16x8 pop = as_bf16x8(u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
         // logical k = 8*hi + t  <->  key 32*kb + 16*sh + 8*(t/4) + 4*hi + (t%4).
         // The V^T operand (32 dims x these 8 keys) comes from two LDS
         // transpose reads of 4 keys each.
@@ -264,36 +284,57 @@ __global__ void __launch_bounds__(256, 2) extend_bf16(
           vt[dt][1] = ds_read_tr16(sv + swz<D>(k0 + 8, tr_chunk + 4 * dt) + tr_half);
         }
 #pragma unroll
-        for (int dt = 0; dt < C::kR; ++dt)
-          oacc[dt] = mfma_32x32x16(as_bf16x8(u32x4{vt[dt][0].x, vt[dt][0].y, vt[dt][1].x, vt[dt][1].y}), pop,
-                                   oacc[dt]);
+        for (int rb = 0; rb < RB; ++rb) {
+          float p[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) p[t] = __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][8 * sh + t], scale_log2, neg_m[rb]));
+          const u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+#pragma unroll
+          for (int t = 0; t < 8; ++t) l[rb] += p[t];
+          const bf16x8 pop = as_bf16x8(pk);
+#pragma unroll
+          for (int dt = 0; dt < C::kR; ++dt)
+            oacc[rb][dt] = mfma_32x32x16(as_bf16x8(u32x4{vt[dt][0].x, vt[dt][0].y, vt[dt][1].x, vt[dt][1].y}),
+                                         pop, oacc[rb][dt]);
+        }
       }
     }
   };
 
-  load_idx(0);
-  issue(sk0, sv0);
-  if (n_tiles > 1) load_idx(1);
-  for (int tile = 0; tile < n_tiles; tile += 2) {
-    step(tile, sk0, sv0, sk1, sv1);
-    if (tile + 1 < n_tiles) step(tile + 1, sk1, sv1, sk0, sv0);
+  // Segments of kSeg keys: stage their slot indices in LDS, start tile 0 of
+  // the segment, then stream its tiles through the two stages.
+  const int tiles_per_seg = kSeg / kBN;
+  for (int seg_tile = 0; seg_tile < n_tiles; seg_tile += tiles_per_seg) {
+    seg0 = seg_tile * kBN;
+    seg_end = min(n_tiles, seg_tile + tiles_per_seg);
+    __syncthreads();  // previous segment fully consumed
+    for (int i = tid; i < (seg_end - seg_tile) * kBN; i += 256) s_slot[i] = uint32_t(idx_row[min(seg0 + i, kv_end - 1)]);
+    __syncthreads();
+    issue(seg_tile, sk0, sv0);
+    for (int tile = seg_tile; tile < seg_end; tile += 2) {
+      step(tile, sk0, sv0, sk1, sv1);
+      if (tile + 1 < seg_end) step(tile + 1, sk1, sv1, sk0, sv0);
+    }
   }
 
   // ---- normalise and store: O^T tile dt row i = dim 32*dt + i; this lane holds
-  // rows i = 8*(v/4) + 4*hi + (v%4) of query row r32.
-  l += __shfl_xor(l, 32, 64);
-  if (!row_ok) return;
-  const float inv = 1.f / l;
-  const int64_t tok = int64_t(qo_indptr[b]) + j;
-  char* op = o + (tok * Hq + int64_t(kvh) * G + g) * C::kRowBytes;
+  // rows i = 8*(v/4) + 4*hi + (v%4) of its query rows.
 #pragma unroll
-  for (int dt = 0; dt < C::kR; ++dt)
+  for (int rb = 0; rb < RB; ++rb) {
+    const float lsum = l[rb] + __shfl_xor(l[rb], 32, 64);
+    if (!row_ok[rb]) continue;
+    const float inv = 1.f / lsum;
+    const int64_t tok = int64_t(qo_indptr[b]) + jrow[rb];
+    char* op = o + (tok * Hq + int64_t(kvh) * G + grow[rb]) * C::kRowBytes;
 #pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4) {
-      const u32x2 w = {pack_bf16x2(oacc[dt][4 * v4 + 0] * inv, oacc[dt][4 * v4 + 1] * inv),
-                       pack_bf16x2(oacc[dt][4 * v4 + 2] * inv, oacc[dt][4 * v4 + 3] * inv)};
-      *reinterpret_cast<u32x2*>(op + (32 * dt + 8 * v4 + 4 * hi) * 2) = w;
-    }
+    for (int dt = 0; dt < C::kR; ++dt)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const u32x2 w = {pack_bf16x2(oacc[rb][dt][4 * v4 + 0] * inv, oacc[rb][dt][4 * v4 + 1] * inv),
+                         pack_bf16x2(oacc[rb][dt][4 * v4 + 2] * inv, oacc[rb][dt][4 * v4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + (32 * dt + 8 * v4 + 4 * hi) * 2) = w;
+      }
+  }
 }
 
 // ----------------------------------------------------------------- fp32 --
@@ -364,16 +405,17 @@ extern "C" int radix_extend_attention(const void* q, void* o, const void* k_pool
   const float scale_log2 = sm_scale * kLog2e;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == RT_BF16) {
-    const int64_t n_qt = (int64_t(max_extend_len) * G + kBM - 1) / kBM;
+    const int64_t item_rows = 4 * 32 * kRB;
+    const int64_t n_qt = (int64_t(max_extend_len) * G + item_rows - 1) / item_rows;
     const int64_t grid = n_qt * batch * num_kv_heads;
     if (grid > INT32_MAX) return rt::fail(RT_ERR_INVALID, "radix_extend_attention: grid too large");
     if (head_dim == 128)
-      hipLaunchKernelGGL(extend_bf16<128>, dim3(uint32_t(grid)), dim3(256), 0, st, (const char*)q, (char*)o,
+      hipLaunchKernelGGL((extend_bf16<128, kRB>), dim3(uint32_t(grid)), dim3(256), 0, st, (const char*)q, (char*)o,
                          (const char*)k_pool, (const char*)v_pool, req_to_token, int64_t(req_to_token_stride),
                          req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch, num_q_heads, num_kv_heads,
                          G, int(n_qt), scale_log2);
     else
-      hipLaunchKernelGGL(extend_bf16<64>, dim3(uint32_t(grid)), dim3(256), 0, st, (const char*)q, (char*)o,
+      hipLaunchKernelGGL((extend_bf16<64, kRB>), dim3(uint32_t(grid)), dim3(256), 0, st, (const char*)q, (char*)o,
                          (const char*)k_pool, (const char*)v_pool, req_to_token, int64_t(req_to_token_stride),
                          req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch, num_q_heads, num_kv_heads,
                          G, int(n_qt), scale_log2);
