@@ -63,7 +63,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="few_shot", choices=["few_shot", "long_context", "fork"])
+    ap.add_argument("--workload", default="few_shot", choices=["few_shot", "long_context", "fork", "chat"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=192, help="requests in the oracle's timed sample")
     ap.add_argument("--check", action="store_true", help="check sampled outputs of the last step against the oracle")
@@ -490,6 +490,65 @@ def run_decode_bench(args, torch):
     return result
 
 
+def run_chat(args, torch):
+    """The multi-turn chat workload through the scheduler once: 256 sessions
+    x 4 turns on a shared 512-token system prompt, U{128..384} user tokens
+    and 128 generated tokens per turn, pool at 60 % of the working set (so
+    eviction and re-extension happen).  Every kernel is timed with HIP
+    events; mixed tokens/s = (extend + decode tokens) / summed kernel time."""
+    from prefix_shared_kv_rt_amd.runtime import RadixRuntime, Scheduler
+    from synth import workloads
+    from synth.sources import QKVSource
+    wl = workloads.chat()
+    rt = RadixRuntime(wl.num_slots, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, torch.bfloat16, 256, wl.max_ctx)
+    src = QKVSource(wl.seed, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, torch.bfloat16)
+    rt.events = []
+    sch = Scheduler(rt, wl.requests, src, max_running=256, max_extend_tokens=16384)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    sch.run()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {}
+    for kind, a, b, info in rt.events:
+        d = per.setdefault(kind, {"launches": 0, "ms": 0.0, "tokens": 0, "flops": 0.0, "bytes": 0.0, "rows": 0})
+        d["launches"] += 1
+        d["ms"] += a.elapsed_time(b)
+        for k in ("tokens", "flops", "bytes", "rows"):
+            d[k] += info.get(k, 0)
+    rt.close()
+    ext, dec = per.get("extend", {}), per.get("decode", {})
+    kernel_s = sum(d["ms"] for d in per.values()) / 1e3
+    tokens = ext.get("tokens", 0) + dec.get("tokens", 0)
+    byrid = {r.rid: r for r in wl.requests}
+    evicted = sum(it.get("extend_freed_tokens", 0) + it.get("decode_freed_tokens", 0) for it in sch.iterations)
+    re_extended = 0
+    for it in sch.iterations:
+        for rid, p, e in it["admitted"]:
+            for a in byrid[rid].after:
+                prev = byrid[a]
+                re_extended += max(0, min(len(byrid[rid].prompt), len(prev.prompt) + len(prev.gen)) - p)
+    ext_tf = ext.get("flops", 0.0) / max(ext.get("ms", 0.0), 1e-9) / 1e9
+    dec_gbs = dec.get("bytes", 0.0) / max(dec.get("ms", 0.0), 1e-9) / 1e6
+    return {
+        "metric": METRIC + " (chat, mixed)", "value": tokens / kernel_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": len(sch.iterations), "warmup": 0, "ms_per_step": wall / len(sch.iterations) * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "multi-turn chat: 512-token system prompt, 256 sessions x 4 turns, "
+                               "U{128..384} user + 128 generated tokens per turn, pool 60% of the working set; "
+                               "one pass of the whole workload, a step = one scheduler iteration",
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                   "pool_slots": wl.num_slots},
+        "wall_tokens_per_s": tokens / wall,
+        "kernels": {k: {"launches": d["launches"], "ms": d["ms"]} for k, d in per.items()},
+        "extend": {"tokens": ext.get("tokens", 0), "tflops": ext_tf, "mfma_frac": ext_tf / PEAK_BF16_TFLOPS},
+        "decode": {"tokens": dec.get("tokens", 0), "gbs": dec_gbs, "hbm_frac": dec_gbs / PEAK_HBM_GBS},
+        "hit_rate": {"cached": sch.cached_tokens, "prefill": sch.prefill_tokens,
+                     "ratio": sch.cached_tokens / max(sch.prefill_tokens, 1)},
+        "evicted_tokens": evicted, "re_extended_tokens": re_extended,
+    }
+
+
 def cpu_baseline(args):
     """The oracle, unchanged, on a bounded sample of the same workload: a
     batch of --cpu-sample requests (1024 shared + 128 distinct tokens, one
@@ -522,6 +581,8 @@ def main():
         sys.exit(2)
     if args.workload == "few_shot":
         result, _ = run_few_shot(args, torch)
+    elif args.workload == "chat":
+        result = run_chat(args, torch)
     else:
         result = run_decode_bench(args, torch)
     if not args.no_cpu_baseline and args.workload == "few_shot":

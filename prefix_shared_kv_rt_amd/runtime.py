@@ -60,6 +60,15 @@ class RadixRuntime:
         self.r2t_host = self.r2t_host_t.numpy()
         self.r2t_dev = torch.zeros((self.max_reqs, self.max_ctx), dtype=torch.int32, device=self.device)
         self._ws = torch.empty(0, dtype=torch.uint8, device=self.device)
+        # When a list, every device step appends (kind, start event, end event,
+        # info) for the kernels it launches; kind is 'kv_store', 'extend' or
+        # 'decode' (the decode entry covers its scatter and store too).
+        self.events = None
+
+    def _event(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
 
     def close(self):
         if self.tree is not None:
@@ -96,15 +105,24 @@ class RadixRuntime:
         with torch.cuda.stream(self.stream):
             loc = self._to_dev(out_cache_loc)
             if loc.numel() > 0:
+                e0 = self._event() if self.events is not None else None
                 B.kv_store(self.k_pool, self.v_pool, k_new, v_new, loc, stream=self.stream)
+                if e0 is not None:
+                    self.events.append(("kv_store", e0, self._event(), {"rows": int(loc.numel())}))
             if not attention or loc.numel() == 0:
                 return None
             qo = np.zeros(n + 1, dtype=np.int32)
             qo[1:] = np.cumsum(extend_lens)
             o = torch.empty_like(q)
-            B.radix_extend_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, self._to_dev(rows),
-                                     self._to_dev(prefix_lens), self._to_dev(extend_lens), self._to_dev(qo),
+            args = (self._to_dev(rows), self._to_dev(prefix_lens), self._to_dev(extend_lens), self._to_dev(qo))
+            e0 = self._event() if self.events is not None else None
+            B.radix_extend_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, *args,
                                      int(max(extend_lens)), self.sm_scale, stream=self.stream)
+            if e0 is not None:
+                pl = np.asarray(prefix_lens, dtype=np.float64)
+                el = np.asarray(extend_lens, dtype=np.float64)
+                flops = 4.0 * self.d * self.hq * float(np.sum(el * pl + el * (el + 1) / 2))
+                self.events.append(("extend", e0, self._event(), {"tokens": int(el.sum()), "flops": flops}))
             return o
 
     def run_decode(self, rows, positions, slots, q, k_new, v_new):
@@ -114,13 +132,19 @@ class RadixRuntime:
         n = len(rows)
         with torch.cuda.stream(self.stream):
             rows_d, pos_d, slots_d = self._to_dev(rows), self._to_dev(positions), self._to_dev(slots)
-            B.req_to_token_scatter(self.r2t_dev, rows_d, pos_d, slots_d, stream=self.stream)
-            B.kv_store(self.k_pool, self.v_pool, k_new, v_new, slots_d, stream=self.stream)
             o = torch.empty_like(q)
             max_kv = int(max(positions)) + 1
             ws = self.workspace(n, max_kv)
+            e0 = self._event() if self.events is not None else None
+            B.req_to_token_scatter(self.r2t_dev, rows_d, pos_d, slots_d, stream=self.stream)
+            B.kv_store(self.k_pool, self.v_pool, k_new, v_new, slots_d, stream=self.stream)
             B.radix_decode_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, max_kv,
                                      self.sm_scale, ws, stream=self.stream)
+            if e0 is not None:
+                kv = np.asarray(positions, dtype=np.float64) + 1
+                eb = q.element_size()
+                nbytes = float(np.sum(kv * (2 * self.hkv * self.d * eb + 4))) + 2.0 * n * self.hq * self.d * eb
+                self.events.append(("decode", e0, self._event(), {"tokens": n, "bytes": nbytes}))
             return o
 
 
