@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="few_shot", choices=["few_shot", "long_context", "fork", "chat"])
+    ap.add_argument("--policy", default="fcfs", choices=["fcfs", "lspf"],
+                    help="admission order of the chat workload's scheduler")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=192, help="requests in the oracle's timed sample")
     ap.add_argument("--check", action="store_true", help="check sampled outputs of the last step against the oracle")
@@ -503,7 +505,7 @@ def run_chat(args, torch):
     rt = RadixRuntime(wl.num_slots, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, torch.bfloat16, 256, wl.max_ctx)
     src = QKVSource(wl.seed, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, torch.bfloat16)
     rt.events = []
-    sch = Scheduler(rt, wl.requests, src, max_running=256, max_extend_tokens=16384)
+    sch = Scheduler(rt, wl.requests, src, max_running=256, max_extend_tokens=16384, policy=args.policy)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     sch.run()
@@ -537,6 +539,7 @@ def run_chat(args, torch):
         "config": {"workload": "multi-turn chat: 512-token system prompt, 256 sessions x 4 turns, "
                                "U{128..384} user + 128 generated tokens per turn, pool 60% of the working set; "
                                "one pass of the whole workload, a step = one scheduler iteration",
+                   "policy": args.policy,
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "pool_slots": wl.num_slots},
         "wall_tokens_per_s": tokens / wall,

@@ -17,6 +17,14 @@ decodes from iteration k+1; a request is inserted into the tree only when
 it finishes (prompt plus the tokens it fed), duplicate slots that the tree
 already holds are freed, then the admission lock is released.
 
+Policy "lspf" (longest shared prefix first; SGLang paper summary, section
+3 "Cache-aware scheduling" and appendix A.3; SGLang explainer, section 04,
+cache-aware scheduling): at each iteration every waiting request is matched
+against the tree in arrival order (each match stamps the LRU clock and may
+split an edge, as any match does), and admission walks the waiting requests
+by matched length, longest first, ties in arrival order, still stopping at
+the first that does not fit.
+
 Attention outputs come from ``recompute_rows`` (full recompute, float64).
 """
 
@@ -50,7 +58,7 @@ class OracleTrace:
 
 
 def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
-                 attention=True, want=None, keep_dumps=False, max_iterations=100000):
+                 attention=True, want=None, keep_dumps=False, max_iterations=100000, policy="fcfs"):
     """Drive workload ``wl`` through the naive tree.  ``want(kind, rid, step)``
     (kind 'ext' or 'dec') selects which attention outputs are recomputed;
     by default all of them when ``attention`` is true."""
@@ -93,12 +101,20 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
             raise RuntimeError("workload did not drain")
         rec = {"admitted": [], "extend_loc": [], "extend_freed": [], "decode": [],
                "decode_freed": [], "finished": []}
-        # 1. admission, first come first served
+        # 1. admission in policy order
+        if policy == "fcfs":
+            order = list(waiting)
+        elif policy == "lspf":
+            matched = [len(tree.match_prefix(r.prompt)[0]) for r in waiting]
+            order = [waiting[i] for i in sorted(range(len(waiting)), key=lambda i: (-matched[i], i))]
+        else:
+            raise ValueError(f"unknown policy {policy!r}")
         reserved = sum(len(r.req.gen) - r.generated for r in running)
         budget = max_extend_tokens
         admitted = []
-        while waiting and len(running) + len(admitted) < max_running:
-            req = waiting[0]
+        for req in order:
+            if len(running) + len(admitted) >= max_running:
+                break
             slots, node = tree.match_prefix(req.prompt)
             tree.lock(node)
             p = len(slots)
@@ -108,7 +124,7 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
             if need > avail or (admitted and e > budget):
                 tree.unlock(node)
                 break
-            waiting.pop(0)
+            waiting.remove(req)
             admitted.append(_Running(req, p, node, list(slots), it))
             reserved += need
             budget -= e

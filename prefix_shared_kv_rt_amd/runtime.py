@@ -19,6 +19,11 @@ request is exempt from the token cap), a request extended in iteration k
 decodes from iteration k+1, and a request enters the tree only when it
 finishes (its duplicate slots are freed, then its admission lock released).
 
+``policy="lspf"`` is the paper's cache-aware order (SGLang paper summary,
+section 3 "Cache-aware scheduling", appendix A.3): each iteration matches
+every waiting request against the tree in arrival order, then admits by
+matched length, longest first, ties in arrival order.
+
 Q/K/V of new tokens come from a caller-supplied ``qkv_source(rid, tokens,
 positions)`` returning device tensors; the runtime itself computes no
 attention values on the host.
@@ -164,9 +169,12 @@ class Scheduler:
     output (kind 'ext' or 'dec'); ``trace`` collects the host decisions."""
 
     def __init__(self, rt, requests, qkv_source, max_running=256, max_extend_tokens=16384,
-                 skip_extend_attention=False, record=None, keep_dumps=False):
+                 skip_extend_attention=False, record=None, keep_dumps=False, policy="fcfs"):
         if rt.max_reqs < max_running:
             raise ValueError("the slot table needs a row per running request")
+        if policy not in ("fcfs", "lspf"):
+            raise ValueError(f"unknown policy {policy!r}")
+        self.policy = policy
         self.rt = rt
         self.pending = list(requests)
         self.qkv = qkv_source
@@ -211,8 +219,13 @@ class Scheduler:
         reserved = sum(len(r.req.gen) - r.generated for r in self.running)
         budget = self.max_extend_tokens
         admitted = []
-        while self.waiting and len(self.running) + len(admitted) < self.max_running:
-            req = self.waiting[0]
+        order = self.waiting
+        if self.policy == "lspf" and self.waiting:
+            lens = [B.rt_match_prefix(rt.tree, r.prompt)[0].size for r in self.waiting]
+            order = [self.waiting[i] for i in np.lexsort((np.arange(len(lens)), -np.asarray(lens)))]
+        for req in list(order):
+            if len(self.running) + len(admitted) >= self.max_running:
+                break
             slots, node = B.rt_match_prefix(rt.tree, req.prompt)
             B.rt_lock(rt.tree, node)
             p = len(slots)
@@ -222,7 +235,7 @@ class Scheduler:
             if need > avail or (admitted and e > budget):
                 B.rt_unlock(rt.tree, node)
                 break
-            self.waiting.pop(0)
+            self.waiting.remove(req)
             row = rt.free_rows.pop(0)
             rt.r2t_host[row, :p] = slots
             admitted.append(_Run(req, row, p, node, it))

@@ -14,15 +14,17 @@ from prefix_shared_kv_rt_amd.runtime import RadixRuntime, Scheduler
 from synth import workloads
 
 
-def _host_compare(wl, max_running=256, max_extend_tokens=16384):
+def _host_compare(wl, max_running=256, max_extend_tokens=16384, policy="fcfs"):
     t0 = time.time()
-    ora = run_workload(wl, attention=False, max_running=max_running, max_extend_tokens=max_extend_tokens)
+    ora = run_workload(wl, attention=False, max_running=max_running, max_extend_tokens=max_extend_tokens,
+                       policy=policy)
     t1 = time.time()
     rt = RadixRuntime(wl.num_slots, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, None,
                       max(max_running, 8), wl.max_ctx, device=None)
-    sch = Scheduler(rt, wl.requests, None, max_running=max_running, max_extend_tokens=max_extend_tokens).run()
+    sch = Scheduler(rt, wl.requests, None, max_running=max_running, max_extend_tokens=max_extend_tokens,
+                    policy=policy).run()
     t2 = time.time()
-    print(f"{wl.name}: oracle {t1 - t0:.1f}s, runtime {t2 - t1:.1f}s, {len(ora.iterations)} iterations, "
+    print(f"{wl.name} ({policy}): oracle {t1 - t0:.1f}s, runtime {t2 - t1:.1f}s, {len(ora.iterations)} iterations, "
           f"hit {ora.cached_tokens}/{ora.prefill_tokens}", flush=True)
     assert (sch.cached_tokens, sch.prefill_tokens) == (ora.cached_tokens, ora.prefill_tokens)
     assert len(sch.iterations) == len(ora.iterations)
@@ -73,3 +75,18 @@ def test_chat_full_with_eviction():
     redo = [r.rid for r in wl.requests if r.after and r.after[0] != 0 and
             matched[r.rid] < len(by_rid[r.after[0]].prompt) + len(by_rid[r.after[0]].gen)]
     assert redo
+
+
+@pytest.mark.parametrize("pool", [512, 160])
+def test_tiny_lspf(pool):
+    _host_compare(workloads.tiny(pool), policy="lspf")
+
+
+def test_chat_full_lspf():
+    """Longest-shared-prefix-first on the full chat workload: identical host
+    decisions, and the cache-aware order keeps more of the history cached
+    than arrival order does."""
+    wl = workloads.chat()
+    lspf = _host_compare(wl, policy="lspf")
+    fcfs = run_workload(wl, attention=False)
+    assert lspf.cached_tokens > fcfs.cached_tokens

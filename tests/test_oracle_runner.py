@@ -2,9 +2,12 @@
 Theorem 3.1, conservation of slots, and the eviction script of the tiny
 workload with a 160-slot pool."""
 
-import numpy as np
+import random
 
-from oracle.hit_rate import optimal_hit_rate
+import numpy as np
+import pytest
+
+from oracle.hit_rate import distinct_prefix_tokens, hit_rate, optimal_hit_rate
 from oracle.runner import run_workload
 from synth import workloads
 
@@ -73,3 +76,52 @@ def test_outputs_are_recomputed_rows():
     r1 = wl.requests[1]
     full = recompute_rows(r1.prompt, np.arange(48), 4, 4, 64, wl.seed, wl.sm_scale)
     assert np.max(np.abs(full[32:] - tr.outputs[("ext", 1, 0)])) < 1e-13
+
+
+def _trie_prompts(rng, n):
+    """Prompts that share prefixes at several depths: each extends a random
+    earlier prompt's prefix (or starts fresh) with new tokens."""
+    prompts = []
+    for _ in range(n):
+        if prompts and rng.random() < 0.8:
+            base = rng.choice(prompts)
+            head = base[:rng.randint(1, len(base))]
+        else:
+            head = []
+        prompts.append(head + [rng.randrange(1000) for _ in range(rng.randint(1, 12))])
+    return [p for i, p in enumerate(prompts) if p not in prompts[:i]]
+
+
+def _batch(prompts):
+    reqs = [workloads.Request(i, list(p), [], ()) for i, p in enumerate(prompts)]
+    return workloads.Workload("batch", 0, 1, 1, 8, "f32", max(len(p) for p in prompts), reqs,
+                              max_ctx=max(len(p) for p in prompts))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_lspf_offline_batch_reaches_theorem_optimum(seed):
+    """Theorem 3.1 through the scheduler: a whole batch waiting at once,
+    served one request per iteration in longest-shared-prefix-first order
+    with a pool exactly as large as the longest request, computes every
+    edge of the prompt tree once -- hit rate == H_opt -- whatever the
+    arrival order."""
+    rng = random.Random(seed)
+    prompts = _trie_prompts(rng, 30)
+    rng.shuffle(prompts)
+    tr = run_workload(_batch(prompts), attention=False, max_running=1, policy="lspf")
+    assert tr.prefill_tokens - tr.cached_tokens == distinct_prefix_tokens(prompts)
+    assert hit_rate(tr.cached_tokens, tr.prefill_tokens) == optimal_hit_rate(prompts)
+
+
+def test_lspf_groups_the_explainers_interleaved_queue():
+    """The explainer's A1, B1, A2, B2 queue with room for one prefix: arrival
+    order recomputes both prefixes, longest-shared-prefix-first serves A2
+    right after A1 and B2 right after B1."""
+    a, b = list(range(0, 20)), list(range(100, 120))
+    prompts = [a + [1], b + [1], a + [2], b + [2]]
+    fcfs = run_workload(_batch(prompts), attention=False, max_running=1)
+    lspf = run_workload(_batch(prompts), attention=False, max_running=1, policy="lspf")
+    assert fcfs.cached_tokens == 0
+    assert lspf.cached_tokens == 40
+    order = [it["admitted"][0][0] for it in lspf.iterations]
+    assert order == [0, 2, 1, 3]
