@@ -63,7 +63,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="few_shot", choices=["few_shot", "long_context", "fork", "chat"])
+    ap.add_argument("--workload", default="few_shot", choices=["few_shot", "long_context", "fork", "chat", "decode_graph"])
     ap.add_argument("--policy", default="fcfs", choices=["fcfs", "lspf"],
                     help="admission order of the chat workload's scheduler")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -552,6 +552,66 @@ def run_chat(args, torch):
     }
 
 
+def run_decode_graph(args, torch):
+    """Decode-step latency, eager launches against replayed HIP graphs, at the
+    Llama-3-8B shape with 2048-token contexts and batch 1..128.  A step is what
+    a serving loop does per generated token: stage the batch's rows,
+    positions and new slots, append the new tokens, attend, synchronise.  The
+    eager step also uploads its index vectors one by one; the graph step reads
+    the new Q/K/V from its static buffers, where a producer writes them."""
+    from prefix_shared_kv_rt_amd.graphs import DecodeGraphs
+    from prefix_shared_kv_rt_amd.runtime import RadixRuntime
+    HQ, HKV, D, CTX, SLOTS = 32, 8, 128, 2304, 1 << 19
+    sizes = [1, 4, 16, 64, 128]
+    rt = RadixRuntime(SLOTS, HQ, HKV, D, torch.bfloat16, 129, CTX)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    rt.k_pool[1:] = torch.randn(rt.k_pool[1:].shape, generator=g, device="cuda").to(torch.bfloat16)
+    rt.v_pool[1:] = torch.randn(rt.v_pool[1:].shape, generator=g, device="cuda").to(torch.bfloat16)
+    rng = np.random.default_rng(7)
+    for r in range(128):
+        rt.r2t_host[r, :] = rng.integers(1, SLOTS // 2, CTX)
+    rt.r2t_dev.copy_(torch.from_numpy(rt.r2t_host))
+    t0 = time.perf_counter()
+    graphs = DecodeGraphs(rt, max_batch=128)
+    capture_s = time.perf_counter() - t0
+    table = {}
+    steps = max(args.steps, 20)
+    for n in sizes:
+        rows = np.arange(n, dtype=np.int32)
+        pos = np.full(n, 2047, dtype=np.int32)
+        slots = (SLOTS // 2 + np.arange(n)).astype(np.int32)
+        q = torch.randn((n, HQ, D), device="cuda").to(torch.bfloat16)
+        k = torch.randn((n, HKV, D), device="cuda").to(torch.bfloat16)
+        v = torch.randn((n, HKV, D), device="cuda").to(torch.bfloat16)
+        res = {}
+        gq, gk, gv = graphs.inputs(n)  # a producer would write the new tokens' Q/K/V here
+        gq.copy_(q), gk.copy_(k), gv.copy_(v)
+        for mode in ("eager", "graph"):
+            run = (lambda: rt.run_decode(rows, pos, slots, q, k, v)) if mode == "eager" else \
+                  (lambda: graphs.run(rows, pos, slots))
+            for _ in range(args.warmup + 2):
+                run()
+                rt.stream.synchronize()
+            t1 = time.perf_counter()
+            for _ in range(steps):
+                run()
+                rt.stream.synchronize()
+            res[mode] = (time.perf_counter() - t1) / steps * 1e6
+        table[n] = {"eager_us": res["eager"], "graph_us": res["graph"], "speedup": res["eager"] / res["graph"]}
+    rt.close()
+    return {
+        "metric": METRIC + " (decode step latency, graphs)", "value": 1e6 / table[1]["graph_us"],
+        "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": table[1]["graph_us"] / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode steps of batch 1..128 at 2048-token contexts, Hq 32 / Hkv 8 / D 128; "
+                               "value = batch-1 tokens/s with graphs; each step synchronised",
+                   "num_q_heads": HQ, "num_kv_heads": HKV, "head_dim": D, "graph_sizes": graphs.sizes},
+        "capture_s": capture_s,
+        "latency": table,
+    }
+
+
 def cpu_baseline(args):
     """The oracle, unchanged, on a bounded sample of the same workload: a
     batch of --cpu-sample requests (1024 shared + 128 distinct tokens, one
@@ -586,6 +646,8 @@ def main():
         result, _ = run_few_shot(args, torch)
     elif args.workload == "chat":
         result = run_chat(args, torch)
+    elif args.workload == "decode_graph":
+        result = run_decode_graph(args, torch)
     else:
         result = run_decode_bench(args, torch)
     if not args.no_cpu_baseline and args.workload == "few_shot":

@@ -200,8 +200,9 @@ int rt_finish_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_o
 /* Scatter new rows into the pool [P4 out_cache_loc]:
  * k_pool[out_cache_loc[t]] = k_new[t], v_pool[...] = v_new[t] for
  * t < n_tokens; k_new / v_new (device) [n_tokens, num_kv_heads, head_dim].
- * Bit-exact copy.  Repeated slots (e.g. padding to slot 0) leave one of the
- * written rows there. */
+ * Bit-exact copy.  Repeated slots (e.g. padding to slot 0) race: each
+ * 16-byte piece of such a slot ends up holding that piece of one of the rows
+ * written to it. */
 int kv_store(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
              const int32_t* out_cache_loc, int32_t n_tokens, int32_t num_kv_heads,
              int32_t head_dim, int dtype, void* stream);
@@ -212,6 +213,19 @@ int kv_store(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
  * be < stride and rows inside the table (not checked on the device). */
 int req_to_token_scatter(int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* rows,
                          const int32_t* positions, const int32_t* slots, int32_t n, void* stream);
+
+/* One decode step's writes in a single launch: req_to_token_scatter of
+ * (rows, positions, slots) and kv_store of (k_new, v_new) at slots, for i < n
+ * [P4 the decode step writes its new token's slot into req_to_token and its
+ * K/V into the pool before attention].  rows, positions, slots: (device)
+ * int32 [n]; k_new, v_new: (device) [n, num_kv_heads, head_dim].  Same
+ * results as the two calls; same unchecked device contents.  Repeated
+ * slots (padding to slot 0) race: each 16-byte piece of such a slot ends up
+ * holding that piece of one of the rows written to it. */
+int decode_append(int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* rows,
+                  const int32_t* positions, const int32_t* slots, int32_t n, void* k_pool, void* v_pool,
+                  const void* k_new, const void* v_new, int32_t num_kv_heads, int32_t head_dim, int dtype,
+                  void* stream);
 
 /* Extend (prefill of the uncached suffix) attention [P2 "match the longest
  * prefix, reference the shared KV, prefill only the missed suffix"].

@@ -23,7 +23,7 @@ EXPORTS = [
     "rt_tree_create", "rt_tree_destroy", "rt_match_prefix", "rt_insert", "rt_lock", "rt_unlock",
     "rt_evict_lru_leaves", "rt_alloc_with_evict", "rt_evictable_size", "rt_protected_size",
     "rt_tree_num_nodes", "rt_tree_dump", "rt_admit_batch", "rt_decode_slots_batch", "rt_finish_batch",
-    "kv_store", "req_to_token_scatter", "radix_extend_attention", "radix_decode_workspace_bytes", "radix_decode_attention",
+    "kv_store", "req_to_token_scatter", "decode_append", "radix_extend_attention", "radix_decode_workspace_bytes", "radix_decode_attention",
 ]
 
 
@@ -84,6 +84,8 @@ def lib():
             "kv_store": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int, _vp]),
             "req_to_token_scatter": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int32, _vp]),
+            "decode_append": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp]),
             "radix_extend_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
@@ -305,6 +307,13 @@ def kv_store(k_pool, v_pool, k_new, v_new, out_cache_loc, stream=None):
 def req_to_token_scatter(req_to_token, rows, positions, slots, stream=None):
     _check(lib().req_to_token_scatter(_dptr(req_to_token), req_to_token.shape[1], _dptr(rows), _dptr(positions),
                                       _dptr(slots), rows.shape[0], _stream(stream)))
+
+
+def decode_append(req_to_token, rows, positions, slots, k_pool, v_pool, k_new, v_new, stream=None):
+    n, hkv, d = k_new.shape
+    _check(lib().decode_append(_dptr(req_to_token), req_to_token.shape[1], _dptr(rows), _dptr(positions),
+                               _dptr(slots), n, _dptr(k_pool), _dptr(v_pool), _dptr(k_new), _dptr(v_new), hkv, d,
+                               _dtype_code(k_new), _stream(stream)))
 
 
 def radix_extend_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens, extend_lens,

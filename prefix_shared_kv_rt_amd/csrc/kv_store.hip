@@ -34,7 +34,51 @@ __global__ void __launch_bounds__(256) kv_store_kernel(char* __restrict__ k_pool
   }
 }
 
+// One decode step's appends: block t writes token t's slot into the slot
+// table and copies its K and V rows into the pool.
+__global__ void __launch_bounds__(256) decode_append_kernel(int32_t* __restrict__ r2t, int64_t stride,
+                                                            const int32_t* __restrict__ rows,
+                                                            const int32_t* __restrict__ pos,
+                                                            const int32_t* __restrict__ slots,
+                                                            char* __restrict__ k_pool, char* __restrict__ v_pool,
+                                                            const char* __restrict__ k_new,
+                                                            const char* __restrict__ v_new, int n,
+                                                            int64_t row_bytes) {
+  const int64_t pieces = row_bytes >> 4;
+  for (int t = blockIdx.x; t < n; t += gridDim.x) {
+    const int64_t slot = slots[t];
+    if (threadIdx.x == 0) r2t[int64_t(rows[t]) * stride + pos[t]] = int32_t(slot);
+    for (int64_t p = threadIdx.x; p < pieces; p += blockDim.x) {
+      const int64_t off = p << 4;
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(k_new + t * row_bytes + off);
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(v_new + t * row_bytes + off);
+      *reinterpret_cast<u32x4*>(k_pool + slot * row_bytes + off) = kv;
+      *reinterpret_cast<u32x4*>(v_pool + slot * row_bytes + off) = vv;
+    }
+  }
+}
+
 }  // namespace
+
+extern "C" int decode_append(int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* rows,
+                             const int32_t* positions, const int32_t* slots, int32_t n, void* k_pool,
+                             void* v_pool, const void* k_new, const void* v_new, int32_t num_kv_heads,
+                             int32_t head_dim, int dtype, void* stream) {
+  if (n < 0 || req_to_token_stride < 1 || num_kv_heads < 1 || (head_dim != 64 && head_dim != 128) ||
+      (dtype != RT_F32 && dtype != RT_BF16))
+    return rt::fail(RT_ERR_INVALID, "decode_append: bad size, shape or dtype");
+  if (n == 0) return RT_OK;
+  if (!req_to_token || !rows || !positions || !slots || !k_pool || !v_pool || !k_new || !v_new)
+    return rt::fail(RT_ERR_INVALID, "decode_append: null pointer");
+  const int64_t row_bytes = int64_t(num_kv_heads) * head_dim * (dtype == RT_BF16 ? 2 : 4);
+  const uint32_t grid = uint32_t(n < 4096 ? n : 4096);
+  hipLaunchKernelGGL(decode_append_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, req_to_token,
+                     int64_t(req_to_token_stride), rows, positions, slots, (char*)k_pool, (char*)v_pool,
+                     (const char*)k_new, (const char*)v_new, int(n), row_bytes);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return rt::fail(RT_ERR_HIP, std::string("decode_append launch: ") + hipGetErrorString(e));
+  return RT_OK;
+}
 
 extern "C" int kv_store(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                         const int32_t* out_cache_loc, int32_t n_tokens, int32_t num_kv_heads,

@@ -67,7 +67,7 @@ class RadixRuntime:
         self._ws = torch.empty(0, dtype=torch.uint8, device=self.device)
         # When a list, every device step appends (kind, start event, end event,
         # info) for the kernels it launches; kind is 'kv_store', 'extend' or
-        # 'decode' (the decode entry covers its scatter and store too).
+        # 'decode' (the decode entry covers its slot-table and K/V writes too).
         self.events = None
 
     def _event(self):
@@ -141,8 +141,8 @@ class RadixRuntime:
             max_kv = int(max(positions)) + 1
             ws = self.workspace(n, max_kv)
             e0 = self._event() if self.events is not None else None
-            B.req_to_token_scatter(self.r2t_dev, rows_d, pos_d, slots_d, stream=self.stream)
-            B.kv_store(self.k_pool, self.v_pool, k_new, v_new, slots_d, stream=self.stream)
+            B.decode_append(self.r2t_dev, rows_d, pos_d, slots_d, self.k_pool, self.v_pool, k_new, v_new,
+                            stream=self.stream)
             B.radix_decode_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, max_kv,
                                      self.sm_scale, ws, stream=self.stream)
             if e0 is not None:
@@ -169,12 +169,13 @@ class Scheduler:
     output (kind 'ext' or 'dec'); ``trace`` collects the host decisions."""
 
     def __init__(self, rt, requests, qkv_source, max_running=256, max_extend_tokens=16384,
-                 skip_extend_attention=False, record=None, keep_dumps=False, policy="fcfs"):
+                 skip_extend_attention=False, record=None, keep_dumps=False, policy="fcfs", graphs=None):
         if rt.max_reqs < max_running:
             raise ValueError("the slot table needs a row per running request")
         if policy not in ("fcfs", "lspf"):
             raise ValueError(f"unknown policy {policy!r}")
         self.policy = policy
+        self.graphs = graphs  # a DecodeGraphs: decode steps replay captured graphs when the batch fits
         self.rt = rt
         self.pending = list(requests)
         self.qkv = qkv_source
@@ -301,7 +302,10 @@ class Scheduler:
                     qs.append(q)
                     ks.append(k)
                     vs.append(v)
-                o = rt.run_decode(rows, positions, slots, torch.cat(qs), torch.cat(ks), torch.cat(vs))
+                q, k, v = torch.cat(qs), torch.cat(ks), torch.cat(vs)
+                o = self.graphs.run(rows, positions, slots, q, k, v) if self.graphs is not None else None
+                if o is None:
+                    o = rt.run_decode(rows, positions, slots, q, k, v)
             if o is not None and self.record is not None:
                 for i, r in enumerate(dec):
                     self.record("dec", r.req.rid, r.generated, o[i:i + 1])

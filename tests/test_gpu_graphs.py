@@ -1,0 +1,91 @@
+"""Decode steps replayed from captured HIP graphs: every replay against an
+eager launch of the same step and against a float32 reference gathered from
+the pool, with eager work and synchronisation between replays; padding to
+the captured sizes; fallback beyond the largest size."""
+
+import numpy as np
+import pytest
+import torch
+
+from prefix_shared_kv_rt_amd.graphs import DecodeGraphs, default_batch_sizes
+from prefix_shared_kv_rt_amd.runtime import RadixRuntime
+
+pytestmark = pytest.mark.gpu
+
+HQ, HKV, D, SLOTS, ROWS, CTX = 8, 2, 128, 8192, 20, 300
+
+
+def _runtime(seed):
+    rt = RadixRuntime(SLOTS, HQ, HKV, D, torch.bfloat16, ROWS, CTX)
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    rt.k_pool[1:] = torch.randn(rt.k_pool[1:].shape, generator=g, device="cuda").to(torch.bfloat16)
+    rt.v_pool[1:] = torch.randn(rt.v_pool[1:].shape, generator=g, device="cuda").to(torch.bfloat16)
+    rng = np.random.default_rng(seed)
+    # each row's context: distinct slots from the first half of the pool; the
+    # new tokens' slots come from the second half
+    for r in range(ROWS):
+        rt.r2t_host[r, :] = rng.permutation(np.arange(1, SLOTS // 2))[:CTX]
+    rt.r2t_dev.copy_(torch.from_numpy(rt.r2t_host))
+    return rt
+
+
+def _reference(rt, rows, positions, q):
+    """float32 decode attention gathered through the device slot table."""
+    r2t = rt.r2t_dev.cpu().numpy()
+    kp, vp = rt.k_pool.float().cpu(), rt.v_pool.float().cpu()
+    out = []
+    for i, (r, p) in enumerate(zip(rows, positions)):
+        sl = torch.from_numpy(r2t[r, :p + 1].astype(np.int64))
+        k = kp[sl].repeat_interleave(HQ // HKV, dim=1).permute(1, 0, 2)   # [Hq, L, D]
+        v = vp[sl].repeat_interleave(HQ // HKV, dim=1).permute(1, 0, 2)
+        s = torch.einsum("hd,hld->hl", q[i].float().cpu(), k) * rt.sm_scale
+        out.append(torch.einsum("hl,hld->hd", torch.softmax(s, -1), v))
+    return torch.stack(out)
+
+
+def test_default_sizes_follow_the_handbook_list():
+    assert default_batch_sizes(128) == [1, 2, 4] + list(range(8, 129, 8))
+    assert default_batch_sizes(20) == [1, 2, 4, 8, 16, 20]
+
+
+def test_graph_replays_match_eager_and_reference():
+    rt = _runtime(0)
+    graphs = DecodeGraphs(rt, max_batch=16)
+    assert graphs.sizes == [1, 2, 4, 8, 16]
+    rng = np.random.default_rng(1)
+    free = np.arange(SLOTS // 2, SLOTS + 1)
+    for trial, n in enumerate([1, 3, 8, 13, 16, 5, 2, 16]):
+        print(f"trial {trial}: batch {n}", flush=True)
+        rows = rng.choice(np.array(rt.free_rows), n, replace=False).astype(np.int32)
+        positions = rng.integers(0, CTX - 1, n).astype(np.int32)
+        slots = rng.choice(free, n, replace=False).astype(np.int32)
+        q = torch.randn((n, HQ, D), device="cuda").to(torch.bfloat16)
+        k = torch.randn((n, HKV, D), device="cuda").to(torch.bfloat16)
+        v = torch.randn((n, HKV, D), device="cuda").to(torch.bfloat16)
+        eager = rt.run_decode(rows, positions, slots, q, k, v).float()
+        rt.stream.synchronize()
+        # eager work between replays
+        _ = (torch.randn(1024, device="cuda") * 2).sum().item()
+        out = graphs.run(rows, positions, slots, q, k, v).float()
+        rt.stream.synchronize()
+        assert graphs.replays == trial + 1
+        ref = _reference(rt, rows, positions, q)
+        assert (out.cpu() - ref).abs().max().item() <= 2e-2
+        assert (out - eager).abs().max().item() <= 2e-2
+    # past the largest captured size: the caller falls back to eager
+    n = 17
+    rows = np.array(rt.free_rows[:n], dtype=np.int32)
+    assert graphs.run(rows, np.zeros(n, np.int32), np.arange(1, n + 1, dtype=np.int32),
+                      torch.zeros((n, HQ, D), device="cuda", dtype=torch.bfloat16),
+                      torch.zeros((n, HKV, D), device="cuda", dtype=torch.bfloat16),
+                      torch.zeros((n, HKV, D), device="cuda", dtype=torch.bfloat16)) is None
+    rt.close()
+
+
+def test_graphs_reserve_the_dummy_row():
+    rt = _runtime(2)
+    DecodeGraphs(rt, max_batch=4)
+    assert ROWS - 1 not in rt.free_rows
+    # the dummy requests read and write only slot 0 through that row
+    assert int(rt.r2t_dev[ROWS - 1, 0].item()) == 0
+    rt.close()

@@ -39,6 +39,37 @@ def test_kv_store_bit_exact(dtype, hkv, d):
                        want_v.view(torch.int16 if dtype == "bf16" else torch.int32))
 
 
+@pytest.mark.parametrize("dtype,hkv,d", [("bf16", 8, 128), ("f32", 2, 64)])
+def test_decode_append_bit_exact(dtype, hkv, d):
+    """The fused append equals the slot-table scatter plus kv_store, bit for
+    bit, including padding rows that all write slot 0 through one row."""
+    _announce(f"decode_append {dtype} hkv={hkv} d={d}")
+    rng = np.random.default_rng(5 + d)
+    n_slots, n, stride, rows_n = 2000, 300, 97, 400
+    kp = torch.from_numpy(rng.standard_normal((n_slots + 1, hkv, d)).astype(np.float32)).to(DT[dtype]).cuda()
+    vp = torch.from_numpy(rng.standard_normal((n_slots + 1, hkv, d)).astype(np.float32)).to(DT[dtype]).cuda()
+    kn = torch.from_numpy(rng.standard_normal((n, hkv, d)).astype(np.float32)).to(DT[dtype]).cuda()
+    vn = torch.from_numpy(rng.standard_normal((n, hkv, d)).astype(np.float32)).to(DT[dtype]).cuda()
+    rows = rng.permutation(rows_n - 1)[:n].astype(np.int32)
+    pos = rng.integers(0, stride, n).astype(np.int32)
+    slots = rng.permutation(np.arange(1, n_slots + 1))[:n].astype(np.int32)
+    rows[-5:], pos[-5:], slots[-5:] = rows_n - 1, 0, 0  # padding: one dummy row, slot 0
+    r2t = torch.from_numpy(rng.integers(1, n_slots, (rows_n, stride)).astype(np.int32)).cuda()
+    want_r2t, want_k, want_v = r2t.clone(), kp.clone(), vp.clone()
+    B.req_to_token_scatter(want_r2t, i32(rows), i32(pos), i32(slots))
+    B.kv_store(want_k, want_v, kn[:-5], vn[:-5], i32(slots[:-5]))
+    B.decode_append(r2t, i32(rows), i32(pos), i32(slots), kp, vp, kn, vn)
+    torch.cuda.synchronize()
+    view = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(r2t.cpu(), want_r2t.cpu())
+    # every row but slot 0 must match exactly; slot 0 holds, element by
+    # element, the value of one of the padding rows that all wrote it
+    assert torch.equal(kp[1:].cpu().view(view), want_k[1:].cpu().view(view))
+    assert torch.equal(vp[1:].cpu().view(view), want_v[1:].cpu().view(view))
+    pad_k, got = kn[-5:].cpu().view(view), kp[0].cpu().view(view)
+    assert bool((got[None] == pad_k).any(dim=0).all())
+
+
 def _run_extend(case, q_host, prefix_lens, extend_lens, hq, hkv, d, dtype, use_rows=True):
     qo = np.zeros(len(prefix_lens) + 1, dtype=np.int32)
     qo[1:] = np.cumsum(extend_lens)

@@ -7,6 +7,7 @@ import pytest
 import torch
 
 from oracle.runner import run_workload
+from prefix_shared_kv_rt_amd.graphs import DecodeGraphs
 from prefix_shared_kv_rt_amd.runtime import RadixRuntime, Scheduler
 from synth import workloads
 from synth.sources import QKVSource
@@ -17,7 +18,7 @@ TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
-def run_both(wl, want=None, max_running=256, max_extend_tokens=16384, max_reqs=None, policy="fcfs"):
+def run_both(wl, want=None, max_running=256, max_extend_tokens=16384, max_reqs=None, policy="fcfs", graphs=False):
     ora = run_workload(wl, want=want, max_running=max_running, max_extend_tokens=max_extend_tokens, policy=policy)
     outs = {}
 
@@ -28,8 +29,11 @@ def run_both(wl, want=None, max_running=256, max_extend_tokens=16384, max_reqs=N
     rt = RadixRuntime(wl.num_slots, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, TORCH_DT[wl.dtype],
                       max_reqs or max(max_running, 8), wl.max_ctx)
     src = QKVSource(wl.seed, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, TORCH_DT[wl.dtype])
+    dg = DecodeGraphs(rt, max_batch=max_running) if graphs else None
     sch = Scheduler(rt, wl.requests, src, max_running=max_running, max_extend_tokens=max_extend_tokens,
-                    skip_extend_attention=wl.skip_extend_attention, record=record, policy=policy).run()
+                    skip_extend_attention=wl.skip_extend_attention, record=record, policy=policy, graphs=dg).run()
+    if graphs:
+        assert dg.replays > 0
     from prefix_shared_kv_rt_amd import binding as B
     final_dump = B.rt_tree_dump(rt.tree)
     free_list = list(B.rt_pool_free_list(rt.pool))
@@ -88,12 +92,13 @@ def test_small_few_shot_bf16():
     check_outputs(ora, outs, TOL["bf16"])
 
 
-@pytest.mark.parametrize("policy", ["fcfs", "lspf"])
-def test_small_chat_with_eviction_bf16(policy):
-    print(f"chat (6 sessions x 3 turns, pool 60%, {policy})", flush=True)
+@pytest.mark.parametrize("policy,graphs", [("fcfs", False), ("lspf", False), ("fcfs", True)])
+def test_small_chat_with_eviction_bf16(policy, graphs):
+    print(f"chat (6 sessions x 3 turns, pool 60%, {policy}, graphs {graphs})", flush=True)
     wl = workloads.chat(sessions=6, turns=3, system_len=64, user_lo=16, user_hi=48, gen_len=6)
     sel = lambda kind, rid, step: kind == "ext" or step in (0, 5)
-    ora, sch, outs, dump, free = run_both(wl, want=sel, max_running=4, max_extend_tokens=128, policy=policy)
+    ora, sch, outs, dump, free = run_both(wl, want=sel, max_running=4, max_extend_tokens=128, policy=policy,
+                                          graphs=graphs)
     check_host_identical(ora, sch, dump, free)
     check_outputs(ora, outs, TOL["bf16"])
     assert any(len(it["extend_freed"]) or len(it["decode_freed"]) for it in ora.iterations)
