@@ -51,6 +51,10 @@ constexpr int kBN = 64;        // keys per LDS tile
 // 32-row query blocks per wave.  2 halves the LDS reads per MFMA but needs
 // more than 256 registers (one wave per SIMD); on gfx950 1 measures faster.
 constexpr int kRB = 1;
+// Waves per workgroup.  A work item's K/V tiles are gathered once for all of
+// its kWaves * 32 query rows.  8 waves halve that gather traffic but measure
+// slower than 4 on MI355X: the gather is not what bounds the kernel.
+constexpr int kWaves = 4;
 constexpr int kSeg = 2048;     // keys whose slot indices are staged in LDS at a time
 constexpr float kSlack = 8.f;  // log2 headroom of the lazy softmax rescale
 
@@ -59,7 +63,7 @@ struct ExtendCfg {
   static constexpr int kRowBytes = D * 2;                 // one K or V row of one head
   static constexpr int kCPR = kRowBytes / 16;             // 16-byte chunks per row
   static constexpr int kKPI = 64 / kCPR;                  // rows per 64-lane LDS load (1 KiB)
-  static constexpr int kLoadsPerWave = kBN / kKPI / 4;    // per wave per tile, K and V each
+  static constexpr int kLoadsPerWave = kBN / kKPI / kWaves;  // per wave per tile, K and V each
   static constexpr int kKB = kBN / 32;                    // 32-key blocks per tile
   static constexpr int kTile = kBN * kRowBytes;           // bytes of one K (or V) tile
   static constexpr int kKS = D / 16;                      // 16-dim steps of Q K^T
@@ -87,7 +91,7 @@ __device__ __forceinline__ int swz(int key, int chunk) {
 }
 
 template <int D, int RB>
-__global__ void __launch_bounds__(256, RB == 1 ? 2 : 1) extend_bf16(
+__global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_bf16(
     const char* __restrict__ q, char* __restrict__ o, const char* __restrict__ k_pool,
     const char* __restrict__ v_pool, const int32_t* __restrict__ req_to_token, int64_t stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
@@ -95,7 +99,7 @@ __global__ void __launch_bounds__(256, RB == 1 ? 2 : 1) extend_bf16(
     int G, int n_qt, float scale_log2) {
   using C = ExtendCfg<D>;
   constexpr int kWaveRows = 32 * RB;          // query rows per wave (RB blocks of 32)
-  constexpr int kItemRows = 4 * kWaveRows;    // query rows per work item
+  constexpr int kItemRows = kWaves * kWaveRows;  // query rows per work item
   // Two stages of K and V tiles: the next tile streams into one stage while
   // the other is used.  Separate arrays let the compiler see that LDS reads of
   // one stage never wait on the loads still landing in the other.
@@ -138,7 +142,9 @@ __global__ void __launch_bounds__(256, RB == 1 ? 2 : 1) extend_bf16(
   const int wj_first = min((row0 + wave * kWaveRows) / G, E - 1);
   const int wj_last = min((row0 + wave * kWaveRows + kWaveRows - 1) / G, E - 1);
   const int w_min_limit = P + wj_first;       // keys <= this are visible to every row of the wave
-  const int w_end = P + wj_last + 1;          // keys >= this are invisible to every row of the wave
+  // Keys >= w_end are invisible to every row of the wave; a wave whose rows
+  // all lie past the request's extend rows computes nothing.
+  const int w_end = (row0 + wave * kWaveRows) / G < E ? P + wj_last + 1 : 0;
 
   const int32_t* idx_row = req_to_token + int64_t(rpi ? rpi[b] : b) * stride;
   const uint32_t pool_row = uint32_t(Hkv) * C::kRowBytes;
@@ -172,7 +178,7 @@ __global__ void __launch_bounds__(256, RB == 1 ? 2 : 1) extend_bf16(
 
   // Tile loads go straight from HBM to LDS (global_load_lds_dwordx4): one
   // 64-lane load fills kKPI consecutive rows (1 KiB).  Wave w issues loads
-  // n = w + 4*it; lane i takes row kKPI*n + i/kCPR and the logical chunk that
+  // n = w + kWaves*it; lane i takes row kKPI*n + i/kCPR and the logical chunk that
   // the swizzle stores at physical chunk i%kCPR.  Keys past kv_end are clamped
   // to the last valid key (masked later; a real row keeps the tile finite).
   // Slot indices come from s_slot, staged per segment of kSeg keys.
@@ -182,14 +188,15 @@ __global__ void __launch_bounds__(256, RB == 1 ? 2 : 1) extend_bf16(
   // Loads of one wave read the slot indices at s_slot[tile_key + krow]; the
   // staging pads the segment's last tile with the last valid key, so no clamp.
   const int krow0 = C::kKPI * wave + ld_row;
-  const int lchunk = ld_pchunk ^ (swz_f(krow0) & (C::kCPR - 1));  // same for every it: krow = krow0 + 16*kKPI*it
+  // krow = krow0 + kWaves*kKPI*it, a multiple of 16 apart: same swizzle
+  const int lchunk = ld_pchunk ^ (swz_f(krow0) & (C::kCPR - 1));
   const uint64_t lane_off = uint64_t(lchunk << 4);
   auto issue = [&](int tile, char* sk, char* sv) {
     const uint32_t* srow = s_slot + (tile * kBN - seg0) + krow0;
 #pragma unroll
     for (int it = 0; it < C::kLoadsPerWave; ++it) {
-      const uint64_t off = uint64_t(srow[4 * C::kKPI * it]) * pool_row + lane_off;
-      const int dst = C::kKPI * (wave + 4 * it) * C::kRowBytes;
+      const uint64_t off = uint64_t(srow[kWaves * C::kKPI * it]) * pool_row + lane_off;
+      const int dst = C::kKPI * (wave + kWaves * it) * C::kRowBytes;
       __builtin_amdgcn_global_load_lds(kbase + off, (__attribute__((address_space(3))) void*)(sk + dst), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vbase + off, (__attribute__((address_space(3))) void*)(sv + dst), 16, 0, 0);
     }
@@ -308,7 +315,7 @@ __global__ void __launch_bounds__(256, RB == 1 ? 2 : 1) extend_bf16(
     seg0 = seg_tile * kBN;
     seg_end = min(n_tiles, seg_tile + tiles_per_seg);
     __syncthreads();  // previous segment fully consumed
-    for (int i = tid; i < (seg_end - seg_tile) * kBN; i += 256) s_slot[i] = uint32_t(idx_row[min(seg0 + i, kv_end - 1)]);
+    for (int i = tid; i < (seg_end - seg_tile) * kBN; i += 64 * kWaves) s_slot[i] = uint32_t(idx_row[min(seg0 + i, kv_end - 1)]);
     __syncthreads();
     issue(seg_tile, sk0, sv0);
     for (int tile = seg_tile; tile < seg_end; tile += 2) {
@@ -405,17 +412,17 @@ extern "C" int radix_extend_attention(const void* q, void* o, const void* k_pool
   const float scale_log2 = sm_scale * kLog2e;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == RT_BF16) {
-    const int64_t item_rows = 4 * 32 * kRB;
+    const int64_t item_rows = kWaves * 32 * kRB;
     const int64_t n_qt = (int64_t(max_extend_len) * G + item_rows - 1) / item_rows;
     const int64_t grid = n_qt * batch * num_kv_heads;
     if (grid > INT32_MAX) return rt::fail(RT_ERR_INVALID, "radix_extend_attention: grid too large");
     if (head_dim == 128)
-      hipLaunchKernelGGL((extend_bf16<128, kRB>), dim3(uint32_t(grid)), dim3(256), 0, st, (const char*)q, (char*)o,
+      hipLaunchKernelGGL((extend_bf16<128, kRB>), dim3(uint32_t(grid)), dim3(64 * kWaves), 0, st, (const char*)q, (char*)o,
                          (const char*)k_pool, (const char*)v_pool, req_to_token, int64_t(req_to_token_stride),
                          req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch, num_q_heads, num_kv_heads,
                          G, int(n_qt), scale_log2);
     else
-      hipLaunchKernelGGL((extend_bf16<64, kRB>), dim3(uint32_t(grid)), dim3(256), 0, st, (const char*)q, (char*)o,
+      hipLaunchKernelGGL((extend_bf16<64, kRB>), dim3(uint32_t(grid)), dim3(64 * kWaves), 0, st, (const char*)q, (char*)o,
                          (const char*)k_pool, (const char*)v_pool, req_to_token, int64_t(req_to_token_stride),
                          req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch, num_q_heads, num_kv_heads,
                          G, int(n_qt), scale_log2);
