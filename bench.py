@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--workload", default="few_shot", choices=["few_shot", "long_context", "fork", "chat", "decode_graph"])
     ap.add_argument("--policy", default="fcfs", choices=["fcfs", "lspf"],
                     help="admission order of the chat workload's scheduler")
+    ap.add_argument("--chunk-size", type=int, default=None,
+                    help="chunked prefill for the chat workload: extend tokens per scheduler iteration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=192, help="requests in the oracle's timed sample")
     ap.add_argument("--check", action="store_true", help="check sampled outputs of the last step against the oracle")
@@ -505,12 +507,26 @@ def run_chat(args, torch):
     rt = RadixRuntime(wl.num_slots, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, torch.bfloat16, 256, wl.max_ctx)
     src = QKVSource(wl.seed, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, torch.bfloat16)
     rt.events = []
-    sch = Scheduler(rt, wl.requests, src, max_running=256, max_extend_tokens=16384, policy=args.policy)
+    sch = Scheduler(rt, wl.requests, src, max_running=256, max_extend_tokens=16384, policy=args.policy,
+                    chunk_size=args.chunk_size)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    sch.run()
+    marks = [0]
+    sch._arrive()
+    it = 0
+    while sch.waiting or sch.running or sch.pending or sch.prefilling:
+        sch.step(it)
+        sch._arrive()
+        marks.append(len(rt.events))
+        it += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # GPU time of each iteration that decoded: how long running requests wait per token
+    it_ms = []
+    for a, b in zip(marks[:-1], marks[1:]):
+        evs = rt.events[a:b]
+        if any(kind == "decode" for kind, _, _, _ in evs):
+            it_ms.append(sum(x.elapsed_time(y) for _, x, y, _ in evs))
     per = {}
     for kind, a, b, info in rt.events:
         d = per.setdefault(kind, {"launches": 0, "ms": 0.0, "tokens": 0, "flops": 0.0, "bytes": 0.0, "rows": 0})
@@ -539,7 +555,7 @@ def run_chat(args, torch):
         "config": {"workload": "multi-turn chat: 512-token system prompt, 256 sessions x 4 turns, "
                                "U{128..384} user + 128 generated tokens per turn, pool 60% of the working set; "
                                "one pass of the whole workload, a step = one scheduler iteration",
-                   "policy": args.policy,
+                   "policy": args.policy, "chunk_size": args.chunk_size,
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "pool_slots": wl.num_slots},
         "wall_tokens_per_s": tokens / wall,
@@ -549,6 +565,8 @@ def run_chat(args, torch):
         "hit_rate": {"cached": sch.cached_tokens, "prefill": sch.prefill_tokens,
                      "ratio": sch.cached_tokens / max(sch.prefill_tokens, 1)},
         "evicted_tokens": evicted, "re_extended_tokens": re_extended,
+        "decode_iteration_gpu_ms": {"p50": float(np.percentile(it_ms, 50)), "p99": float(np.percentile(it_ms, 99)),
+                                    "max": float(np.max(it_ms))} if it_ms else None,
     }
 
 

@@ -25,6 +25,16 @@ split an edge, as any match does), and admission walks the waiting requests
 by matched length, longest first, ties in arrival order, still stopping at
 the first that does not fit.
 
+Chunked prefill (``chunk_size``; v0.2 handbook, the #800 entry of the
+release timeline: long prompts are cut into chunks of a fixed size that run
+beside decode, and admission changes with it).  Reading taken: each
+iteration extends at most chunk_size prompt tokens, first the next chunks of
+requests still being prefilled (in admission order), then the first chunks
+of newly admitted requests; admission stops once the budget is spent or a
+request does not fit.  A request's whole remaining prompt and output are
+reserved at admission; its slots are allocated chunk by chunk.  It decodes
+from the iteration after its last chunk.
+
 Attention outputs come from ``recompute_rows`` (full recompute, float64).
 """
 
@@ -41,9 +51,10 @@ class _Running:
     req: object
     prefix_len: int
     node: int
-    slots: list
-    admit_iter: int
+    slots: list       # slot of every position computed so far
+    admit_iter: int   # the iteration that completed the prompt
     generated: int = 0
+    n_chunks: int = 0
 
 
 @dataclass
@@ -58,7 +69,8 @@ class OracleTrace:
 
 
 def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
-                 attention=True, want=None, keep_dumps=False, max_iterations=100000, policy="fcfs"):
+                 attention=True, want=None, keep_dumps=False, max_iterations=100000, policy="fcfs",
+                 chunk_size=None):
     """Drive workload ``wl`` through the naive tree.  ``want(kind, rid, step)``
     (kind 'ext' or 'dec') selects which attention outputs are recomputed;
     by default all of them when ``attention`` is true."""
@@ -67,7 +79,7 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
     tr = OracleTrace()
     pending = list(wl.requests)
     finished = set()
-    waiting, running = [], []
+    waiting, running, prefilling = [], [], []
 
     def arrive():
         nonlocal pending
@@ -96,7 +108,7 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
 
     arrive()
     it = 0
-    while waiting or running or pending:
+    while waiting or running or pending or prefilling:
         if it >= max_iterations:
             raise RuntimeError("workload did not drain")
         rec = {"admitted": [], "extend_loc": [], "extend_freed": [], "decode": [],
@@ -109,48 +121,52 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
             order = [waiting[i] for i in sorted(range(len(waiting)), key=lambda i: (-matched[i], i))]
         else:
             raise ValueError(f"unknown policy {policy!r}")
-        reserved = sum(len(r.req.gen) - r.generated for r in running)
-        budget = max_extend_tokens
-        admitted = []
-        for req in order:
-            if len(running) + len(admitted) >= max_running:
-                break
-            slots, node = tree.match_prefix(req.prompt)
-            tree.lock(node)
-            p = len(slots)
-            e = len(req.prompt) - p
-            need = e + len(req.gen)
-            avail = pool.available() + tree.evictable_size() - reserved
-            if need > avail or (admitted and e > budget):
-                tree.unlock(node)
-                break
-            waiting.remove(req)
-            admitted.append(_Running(req, p, node, list(slots), it))
-            reserved += need
-            budget -= e
-        # 2. extend the admitted batch
-        if admitted:
-            total = sum(len(r.req.prompt) - r.prefix_len for r in admitted)
-            loc, freed = tree.alloc_with_evict(total) if total > 0 else ([], [])
-            rec["extend_loc"], rec["extend_freed"] = list(loc), list(freed)
-            off = 0
-            for r in admitted:
-                e = len(r.req.prompt) - r.prefix_len
-                r.slots += loc[off:off + e]
-                off += e
-                rec["admitted"].append((r.req.rid, r.prefix_len, e))
-                tr.cached_tokens += r.prefix_len
-                tr.prefill_tokens += len(r.req.prompt)
-                if e > 0 and not wl.skip_extend_attention and selected("ext", r.req.rid, 0):
-                    pos = np.arange(r.prefix_len, len(r.req.prompt))
-                    tr.outputs[("ext", r.req.rid, 0)] = recompute_rows(
-                        r.req.prompt, pos, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                        wl.seed, wl.sm_scale)
-            for r in admitted:
-                if len(r.req.gen) == 0:
-                    finish(r, rec)
-                else:
-                    running.append(r)
+        if chunk_size is not None:
+            _chunked_admit_and_extend(wl, tree, pool, tr, rec, it, order, waiting, running, prefilling,
+                                      max_running, chunk_size, selected, finish)
+        else:
+            reserved = sum(len(r.req.gen) - r.generated for r in running)
+            budget = max_extend_tokens
+            admitted = []
+            for req in order:
+                if len(running) + len(admitted) >= max_running:
+                    break
+                slots, node = tree.match_prefix(req.prompt)
+                tree.lock(node)
+                p = len(slots)
+                e = len(req.prompt) - p
+                need = e + len(req.gen)
+                avail = pool.available() + tree.evictable_size() - reserved
+                if need > avail or (admitted and e > budget):
+                    tree.unlock(node)
+                    break
+                waiting.remove(req)
+                admitted.append(_Running(req, p, node, list(slots), it))
+                reserved += need
+                budget -= e
+            # 2. extend the admitted batch
+            if admitted:
+                total = sum(len(r.req.prompt) - r.prefix_len for r in admitted)
+                loc, freed = tree.alloc_with_evict(total) if total > 0 else ([], [])
+                rec["extend_loc"], rec["extend_freed"] = list(loc), list(freed)
+                off = 0
+                for r in admitted:
+                    e = len(r.req.prompt) - r.prefix_len
+                    r.slots += loc[off:off + e]
+                    off += e
+                    rec["admitted"].append((r.req.rid, r.prefix_len, e))
+                    tr.cached_tokens += r.prefix_len
+                    tr.prefill_tokens += len(r.req.prompt)
+                    if e > 0 and not wl.skip_extend_attention and selected("ext", r.req.rid, 0):
+                        pos = np.arange(r.prefix_len, len(r.req.prompt))
+                        tr.outputs[("ext", r.req.rid, 0)] = recompute_rows(
+                            r.req.prompt, pos, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                            wl.seed, wl.sm_scale)
+                for r in admitted:
+                    if len(r.req.gen) == 0:
+                        finish(r, rec)
+                    else:
+                        running.append(r)
         # 3. one decode step for requests admitted in earlier iterations
         dec = [r for r in running if r.admit_iter < it]
         if dec:
@@ -178,3 +194,69 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
     tr.free_list = list(pool.free)
     tr.final_dump = tree.dump()
     return tr
+
+
+def _chunked_admit_and_extend(wl, tree, pool, tr, rec, it, order, waiting, running, prefilling,
+                              max_running, chunk_size, selected, finish):
+    """One iteration's admission and extend under chunked prefill."""
+    budget = chunk_size
+    plan = []  # (request, first position, token count), in launch order
+    for r in prefilling:
+        if budget <= 0:
+            break
+        cnt = min(len(r.req.prompt) - len(r.slots), budget)
+        plan.append((r, len(r.slots), cnt))
+        budget -= cnt
+    reserved = sum(len(r.req.gen) - r.generated for r in running)
+    reserved += sum(len(r.req.prompt) - len(r.slots) + len(r.req.gen) for r in prefilling)
+    admitted = []
+    for req in order:
+        if len(running) + len(prefilling) + len(admitted) >= max_running or budget <= 0:
+            break
+        slots, node = tree.match_prefix(req.prompt)
+        tree.lock(node)
+        p = len(slots)
+        e = len(req.prompt) - p
+        need = e + len(req.gen)
+        if need > pool.available() + tree.evictable_size() - reserved:
+            tree.unlock(node)
+            break
+        waiting.remove(req)
+        run = _Running(req, p, node, list(slots), it)
+        admitted.append(run)
+        reserved += need
+        rec["admitted"].append((req.rid, p, e))
+        tr.cached_tokens += p
+        tr.prefill_tokens += len(req.prompt)
+        cnt = min(e, budget)
+        if cnt > 0:
+            plan.append((run, p, cnt))
+            budget -= cnt
+    total = sum(cnt for _, _, cnt in plan)
+    loc, freed = tree.alloc_with_evict(total) if total > 0 else ([], [])
+    rec["extend_loc"], rec["extend_freed"] = list(loc), list(freed)
+    rec["chunks"] = [(r.req.rid, first, cnt) for r, first, cnt in plan]
+    off = 0
+    for r, first, cnt in plan:
+        r.slots += loc[off:off + cnt]
+        off += cnt
+        if not wl.skip_extend_attention and selected("ext", r.req.rid, r.n_chunks):
+            tr.outputs[("ext", r.req.rid, r.n_chunks)] = recompute_rows(
+                r.req.prompt, np.arange(first, first + cnt), wl.num_q_heads, wl.num_kv_heads,
+                wl.head_dim, wl.seed, wl.sm_scale)
+        r.n_chunks += 1
+    continuing = [r for r, _, _ in plan if all(r is not a for a in admitted)]
+    for r in continuing + admitted:
+        complete = len(r.slots) == len(r.req.prompt)
+        is_new = any(r is a for a in admitted)
+        if not complete:
+            if is_new:
+                prefilling.append(r)
+            continue
+        if not is_new:
+            prefilling[:] = [x for x in prefilling if x is not r]
+        r.admit_iter = it
+        if len(r.req.gen) == 0:
+            finish(r, rec)
+        else:
+            running.append(r)

@@ -19,6 +19,16 @@ request is exempt from the token cap), a request extended in iteration k
 decodes from iteration k+1, and a request enters the tree only when it
 finishes (its duplicate slots are freed, then its admission lock released).
 
+``chunk_size=C`` is chunked prefill (v0.2 handbook, the #800 entry of the
+release timeline: long prompts no longer take a whole step, they are cut
+into chunks of a fixed size that run beside decode, and admission changes
+with it).  Each iteration extends at most C prompt tokens: first the next
+chunks of requests still being prefilled, in admission order, then the
+first chunks of newly admitted requests; admission stops when the budget is
+spent.  Admission reserves a request's whole remaining prompt and output,
+and slots are allocated chunk by chunk.  A request decodes from the
+iteration after its last chunk.
+
 ``policy="lspf"`` is the paper's cache-aware order (SGLang paper summary,
 section 3 "Cache-aware scheduling", appendix A.3): each iteration matches
 every waiting request against the tree in arrival order, then admits by
@@ -159,8 +169,10 @@ class _Run:
     row: int
     prefix_len: int
     node: int
-    admit_iter: int
+    admit_iter: int  # iteration whose extend completed the prompt (decode starts after it)
     generated: int = 0
+    done: int = 0    # prompt tokens whose K/V are in the pool
+    chunks: int = 0  # extend chunks run so far
 
 
 class Scheduler:
@@ -169,12 +181,17 @@ class Scheduler:
     output (kind 'ext' or 'dec'); ``trace`` collects the host decisions."""
 
     def __init__(self, rt, requests, qkv_source, max_running=256, max_extend_tokens=16384,
-                 skip_extend_attention=False, record=None, keep_dumps=False, policy="fcfs", graphs=None):
+                 skip_extend_attention=False, record=None, keep_dumps=False, policy="fcfs", graphs=None,
+                 chunk_size=None):
         if rt.max_reqs < max_running:
             raise ValueError("the slot table needs a row per running request")
         if policy not in ("fcfs", "lspf"):
             raise ValueError(f"unknown policy {policy!r}")
         self.policy = policy
+        if chunk_size is not None and chunk_size < 1:
+            raise ValueError("chunk_size must be positive")
+        self.chunk_size = chunk_size
+        self.prefilling = []  # admitted requests with prompt tokens still to extend
         self.graphs = graphs  # a DecodeGraphs: decode steps replay captured graphs when the batch fits
         self.rt = rt
         self.pending = list(requests)
@@ -217,15 +234,26 @@ class Scheduler:
         rt = self.rt
         rec = {"admitted": [], "extend_loc": [], "extend_freed": [], "decode": [], "decode_freed": [],
                "finished": []}
+        chunked = self.chunk_size is not None
         reserved = sum(len(r.req.gen) - r.generated for r in self.running)
-        budget = self.max_extend_tokens
+        reserved += sum(len(r.req.prompt) - r.done + len(r.req.gen) for r in self.prefilling)
+        budget = self.chunk_size if chunked else self.max_extend_tokens
+        chunks = []  # (run, first token, tokens) of this iteration's extend, in launch order
+        for r in self.prefilling:
+            if budget <= 0:
+                break
+            n = min(len(r.req.prompt) - r.done, budget)
+            chunks.append((r, r.done, n))
+            budget -= n
         admitted = []
         order = self.waiting
         if self.policy == "lspf" and self.waiting:
             lens = [B.rt_match_prefix(rt.tree, r.prompt)[0].size for r in self.waiting]
             order = [self.waiting[i] for i in np.lexsort((np.arange(len(lens)), -np.asarray(lens)))]
         for req in list(order):
-            if len(self.running) + len(admitted) >= self.max_running:
+            if len(self.running) + len(self.prefilling) + len(admitted) >= self.max_running:
+                break
+            if chunked and budget <= 0:
                 break
             slots, node = B.rt_match_prefix(rt.tree, req.prompt)
             B.rt_lock(rt.tree, node)
@@ -233,56 +261,70 @@ class Scheduler:
             e = len(req.prompt) - p
             need = e + len(req.gen)
             avail = B.rt_pool_available(rt.pool) + B.rt_evictable_size(rt.tree) - reserved
-            if need > avail or (admitted and e > budget):
+            if need > avail or (not chunked and admitted and e > budget):
                 B.rt_unlock(rt.tree, node)
                 break
             self.waiting.remove(req)
             row = rt.free_rows.pop(0)
             rt.r2t_host[row, :p] = slots
-            admitted.append(_Run(req, row, p, node, it))
+            run = _Run(req, row, p, node, it, done=p)
+            admitted.append(run)
             reserved += need
-            budget -= e
+            n = min(e, budget) if chunked else e
+            if n > 0:
+                chunks.append((run, p, n))
+            budget -= n
+            rec["admitted"].append((req.rid, p, e))
+            self.cached_tokens += p
+            self.prefill_tokens += len(req.prompt)
 
-        if admitted:
-            ext = [len(r.req.prompt) - r.prefix_len for r in admitted]
-            total = sum(ext)
-            if total > 0:
-                loc, evicted = B.rt_alloc_with_evict(rt.tree, total)
-                rec["extend_loc"] = [int(x) for x in loc]
-                rec["extend_freed_tokens"] = evicted
+        total = sum(n for _, _, n in chunks)
+        if total > 0:
+            loc, evicted = B.rt_alloc_with_evict(rt.tree, total)
+            rec["extend_loc"] = [int(x) for x in loc]
+            rec["extend_freed_tokens"] = evicted
+        else:
+            loc = np.zeros(0, dtype=np.int32)
+        if chunked:
+            rec["chunks"] = [(r.req.rid, start, n) for r, start, n in chunks]
+        off = 0
+        for r, start, n in chunks:
+            rt.r2t_host[r.row, start:start + n] = loc[off:off + n]
+            off += n
+            r.done = start + n
+        # device rows: the computed prefix of every request touched this iteration
+        touched = list({id(r): r for r in [c[0] for c in chunks] + admitted}.values())
+        rt.upload_rows([r.row for r in touched], [r.done for r in touched])
+        if total > 0 and rt.device is not None:
+            qs, ks, vs = [], [], []
+            for r, start, n in chunks:
+                q, k, v = self.qkv(r.req.rid, r.req.prompt, np.arange(start, start + n))
+                qs.append(q)
+                ks.append(k)
+                vs.append(v)
+            q, k, v = torch.cat(qs), torch.cat(ks), torch.cat(vs)
+            o = rt.run_extend([r.row for r, _, _ in chunks], [start for _, start, _ in chunks],
+                              [n for _, _, n in chunks], q, k, v, loc, attention=not self.skip_extend_attention)
+            if o is not None and self.record is not None:
+                off = 0
+                for r, start, n in chunks:
+                    self.record("ext", r.req.rid, r.chunks, o[off:off + n])
+                    off += n
+        for r, _, _ in chunks:
+            r.chunks += 1
+        new_ids = {id(r) for r in admitted}
+        for r in [c[0] for c in chunks if id(c[0]) not in new_ids] + admitted:
+            if r.done < len(r.req.prompt):
+                if id(r) in new_ids:
+                    self.prefilling.append(r)
+                continue
+            if id(r) not in new_ids:
+                self.prefilling = [x for x in self.prefilling if x is not r]
+            r.admit_iter = it
+            if len(r.req.gen) == 0:
+                self._finish(r, rec)
             else:
-                loc = np.zeros(0, dtype=np.int32)
-            off = 0
-            for r, e in zip(admitted, ext):
-                rt.r2t_host[r.row, r.prefix_len:r.prefix_len + e] = loc[off:off + e]
-                off += e
-                rec["admitted"].append((r.req.rid, r.prefix_len, e))
-                self.cached_tokens += r.prefix_len
-                self.prefill_tokens += len(r.req.prompt)
-            rt.upload_rows([r.row for r in admitted], [len(r.req.prompt) for r in admitted])
-            if total > 0 and rt.device is not None:
-                qs, ks, vs = [], [], []
-                for r, e in zip(admitted, ext):
-                    if e == 0:
-                        continue
-                    q, k, v = self.qkv(r.req.rid, r.req.prompt, np.arange(r.prefix_len, len(r.req.prompt)))
-                    qs.append(q)
-                    ks.append(k)
-                    vs.append(v)
-                q, k, v = torch.cat(qs), torch.cat(ks), torch.cat(vs)
-                o = rt.run_extend([r.row for r in admitted], [r.prefix_len for r in admitted], ext, q, k, v, loc,
-                                  attention=not self.skip_extend_attention)
-                if o is not None and self.record is not None:
-                    off = 0
-                    for r, e in zip(admitted, ext):
-                        if e:
-                            self.record("ext", r.req.rid, 0, o[off:off + e])
-                        off += e
-            for r in admitted:
-                if len(r.req.gen) == 0:
-                    self._finish(r, rec)
-                else:
-                    self.running.append(r)
+                self.running.append(r)
 
         dec = [r for r in self.running if r.admit_iter < it]
         if dec:
@@ -325,7 +367,7 @@ class Scheduler:
     def run(self, max_iterations=100000):
         self._arrive()
         it = 0
-        while self.waiting or self.running or self.pending:
+        while self.waiting or self.running or self.pending or self.prefilling:
             if it >= max_iterations:
                 raise RuntimeError("workload did not drain")
             self.step(it)

@@ -18,8 +18,10 @@ TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
-def run_both(wl, want=None, max_running=256, max_extend_tokens=16384, max_reqs=None, policy="fcfs", graphs=False):
-    ora = run_workload(wl, want=want, max_running=max_running, max_extend_tokens=max_extend_tokens, policy=policy)
+def run_both(wl, want=None, max_running=256, max_extend_tokens=16384, max_reqs=None, policy="fcfs", graphs=False,
+             chunk_size=None):
+    ora = run_workload(wl, want=want, max_running=max_running, max_extend_tokens=max_extend_tokens, policy=policy,
+                       chunk_size=chunk_size)
     outs = {}
 
     def record(kind, rid, step, o):
@@ -31,7 +33,8 @@ def run_both(wl, want=None, max_running=256, max_extend_tokens=16384, max_reqs=N
     src = QKVSource(wl.seed, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, TORCH_DT[wl.dtype])
     dg = DecodeGraphs(rt, max_batch=max_running) if graphs else None
     sch = Scheduler(rt, wl.requests, src, max_running=max_running, max_extend_tokens=max_extend_tokens,
-                    skip_extend_attention=wl.skip_extend_attention, record=record, policy=policy, graphs=dg).run()
+                    skip_extend_attention=wl.skip_extend_attention, record=record, policy=policy, graphs=dg,
+                    chunk_size=chunk_size).run()
     if graphs:
         assert dg.replays > 0
     from prefix_shared_kv_rt_amd import binding as B
@@ -51,6 +54,7 @@ def check_host_identical(ora, sch, final_dump, free_list):
         assert a["decode"] == b["decode"]
         assert a.get("decode_freed_tokens", 0) == len(b["decode_freed"])
         assert a["finished"] == b["finished"]
+        assert a.get("chunks") == b.get("chunks")
     assert sch.request_slots == ora.request_slots
     assert final_dump == ora.final_dump
     assert free_list == ora.free_list
@@ -92,13 +96,14 @@ def test_small_few_shot_bf16():
     check_outputs(ora, outs, TOL["bf16"])
 
 
-@pytest.mark.parametrize("policy,graphs", [("fcfs", False), ("lspf", False), ("fcfs", True)])
-def test_small_chat_with_eviction_bf16(policy, graphs):
-    print(f"chat (6 sessions x 3 turns, pool 60%, {policy}, graphs {graphs})", flush=True)
+@pytest.mark.parametrize("policy,graphs,chunk", [("fcfs", False, None), ("lspf", False, None), ("fcfs", True, None),
+                                                 ("fcfs", False, 24)])
+def test_small_chat_with_eviction_bf16(policy, graphs, chunk):
+    print(f"chat (6 sessions x 3 turns, pool 60%, {policy}, graphs {graphs}, chunk {chunk})", flush=True)
     wl = workloads.chat(sessions=6, turns=3, system_len=64, user_lo=16, user_hi=48, gen_len=6)
     sel = lambda kind, rid, step: kind == "ext" or step in (0, 5)
     ora, sch, outs, dump, free = run_both(wl, want=sel, max_running=4, max_extend_tokens=128, policy=policy,
-                                          graphs=graphs)
+                                          graphs=graphs, chunk_size=chunk)
     check_host_identical(ora, sch, dump, free)
     check_outputs(ora, outs, TOL["bf16"])
     assert any(len(it["extend_freed"]) or len(it["decode_freed"]) for it in ora.iterations)
@@ -115,3 +120,14 @@ def test_chat_full_size_sampled():
     ora, sch, outs, dump, free = run_both(wl, want=sel)
     check_host_identical(ora, sch, dump, free)
     check_outputs(ora, outs, TOL["bf16"])
+
+
+def test_chunked_prefill_few_shot_bf16():
+    """Prompts of 1024 + 96 tokens through 160-token chunks beside decode:
+    every chunk's rows against the oracle's rows of the same positions."""
+    print("few-shot 6 x (1024 + 96), chunks of 160", flush=True)
+    wl = workloads.few_shot(batch=6, suffix_len=96, decode_steps=4, num_slots=8192)
+    ora, sch, outs, dump, free = run_both(wl, chunk_size=160)
+    check_host_identical(ora, sch, dump, free)
+    check_outputs(ora, outs, TOL["bf16"])
+    assert max(len(it["chunks"]) for it in ora.iterations) > 1

@@ -14,15 +14,15 @@ from prefix_shared_kv_rt_amd.runtime import RadixRuntime, Scheduler
 from synth import workloads
 
 
-def _host_compare(wl, max_running=256, max_extend_tokens=16384, policy="fcfs"):
+def _host_compare(wl, max_running=256, max_extend_tokens=16384, policy="fcfs", chunk_size=None):
     t0 = time.time()
     ora = run_workload(wl, attention=False, max_running=max_running, max_extend_tokens=max_extend_tokens,
-                       policy=policy)
+                       policy=policy, chunk_size=chunk_size)
     t1 = time.time()
     rt = RadixRuntime(wl.num_slots, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, None,
                       max(max_running, 8), wl.max_ctx, device=None)
     sch = Scheduler(rt, wl.requests, None, max_running=max_running, max_extend_tokens=max_extend_tokens,
-                    policy=policy).run()
+                    policy=policy, chunk_size=chunk_size).run()
     t2 = time.time()
     print(f"{wl.name} ({policy}): oracle {t1 - t0:.1f}s, runtime {t2 - t1:.1f}s, {len(ora.iterations)} iterations, "
           f"hit {ora.cached_tokens}/{ora.prefill_tokens}", flush=True)
@@ -35,6 +35,7 @@ def _host_compare(wl, max_running=256, max_extend_tokens=16384, policy="fcfs"):
         assert a["decode"] == b["decode"], i
         assert a.get("decode_freed_tokens", 0) == len(b["decode_freed"]), i
         assert a["finished"] == b["finished"], i
+        assert a.get("chunks") == b.get("chunks"), i
     assert sch.request_slots == ora.request_slots
     assert B.rt_tree_dump(rt.tree) == ora.final_dump
     assert list(B.rt_pool_free_list(rt.pool)) == ora.free_list
@@ -90,3 +91,20 @@ def test_chat_full_lspf():
     lspf = _host_compare(wl, policy="lspf")
     fcfs = run_workload(wl, attention=False)
     assert lspf.cached_tokens > fcfs.cached_tokens
+
+
+@pytest.mark.parametrize("pool,chunk", [(512, 7), (160, 16), (160, 5)])
+def test_tiny_chunked(pool, chunk):
+    _host_compare(workloads.tiny(pool), chunk_size=chunk)
+
+
+def test_chat_full_chunked():
+    _host_compare(workloads.chat(), chunk_size=512)
+
+
+def test_long_context_chunked():
+    """32 prompts of 32768 tokens through 8192-token chunks: every prompt
+    takes four iterations, and decode runs beside the next prompts' chunks."""
+    ora = _host_compare(workloads.long_context(), chunk_size=8192)
+    assert all(sum(n for _, _, n in it["chunks"]) <= 8192 for it in ora.iterations)
+    assert any(it["chunks"] and it["decode"] for it in ora.iterations)

@@ -125,3 +125,44 @@ def test_lspf_groups_the_explainers_interleaved_queue():
     assert lspf.cached_tokens == 40
     order = [it["admitted"][0][0] for it in lspf.iterations]
     assert order == [0, 2, 1, 3]
+
+
+def test_chunked_prefill_script():
+    """Chunked prefill on a hand-worked case: A (100-token prompt, 3 output
+    tokens) and B (10-token prompt, 2 output tokens) arrive together, chunks
+    of 32.  A takes the whole budget for three iterations, its 4-token tail
+    leaves room for B's whole prompt in the fourth, both decode from the
+    fifth; B finishes after 2 steps and A after 3."""
+    a = workloads.Request(0, list(range(1, 101)), [7, 8, 9], ())
+    b = workloads.Request(1, list(range(500, 510)), [5, 6], ())
+    wl = workloads.Workload("chunks", 0, 1, 1, 8, "f32", 1000, [a, b], max_ctx=110)
+    tr = run_workload(wl, attention=False, chunk_size=32)
+    chunks = [it["chunks"] for it in tr.iterations]
+    assert chunks[:4] == [[(0, 0, 32)], [(0, 32, 32)], [(0, 64, 32)], [(0, 96, 4), (1, 0, 10)]]
+    assert [it["admitted"] for it in tr.iterations[:4]] == [[(0, 0, 100)], [], [], [(1, 0, 10)]]
+    dec = [[(rid, pos) for rid, pos, _ in it["decode"]] for it in tr.iterations]
+    assert dec[:4] == [[], [], [], []]
+    assert dec[4:] == [[(0, 100), (1, 10)], [(0, 101), (1, 11)], [(0, 102)]]
+    fin = [[f[0] for f in it["finished"]] for it in tr.iterations]
+    assert fin[5] == [1] and fin[6] == [0]
+    # the slots of A's chunks are consecutive allocations from the FIFO pool
+    assert tr.request_slots[0][:100] == list(range(1, 101))
+
+
+@pytest.mark.parametrize("chunk", [7, 64, 100000])
+def test_chunked_prefill_keeps_hit_rate_and_slots(chunk):
+    """On the tiny workload (no eviction at 512 slots) chunking changes when
+    tokens are computed, not what is cached: the hit-rate integers, every
+    request's final slot count and the conservation of slots hold for any
+    chunk size; a chunk larger than every iteration's demand reproduces the
+    unchunked extend allocations."""
+    wl = workloads.tiny(512)
+    base = run_workload(wl, attention=False)
+    tr = run_workload(wl, attention=False, chunk_size=chunk)
+    assert (tr.cached_tokens, tr.prefill_tokens) == (base.cached_tokens, base.prefill_tokens)
+    assert {k: len(v) for k, v in tr.request_slots.items()} == {k: len(v) for k, v in base.request_slots.items()}
+    _slots_conserved(tr, 512)
+    for it in tr.iterations:
+        assert sum(n for _, _, n in it["chunks"]) <= chunk
+    if chunk == 100000:
+        assert [it["extend_loc"] for it in tr.iterations] == [it["extend_loc"] for it in base.iterations]
