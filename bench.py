@@ -27,6 +27,7 @@ CPU oracle baseline on a bounded sample).  ``--workload long_context`` or
 """
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -252,6 +253,8 @@ def run_few_shot(args, torch):
         fb.step(i, timed=False)
     fb.stream.synchronize()
     torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()  # a collector pass inside the timed steps would stall the host, not the path
     t0 = time.perf_counter()
     tokens = 0
     for i in range(args.warmup, n):
@@ -259,6 +262,7 @@ def run_few_shot(args, torch):
     fb.stream.synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     ext_ms = [a.elapsed_time(b) for a, b in fb.ext_events]
     dec_ms = [a.elapsed_time(b) for a, b in fb.dec_events]
     ext_avg_s = float(np.mean(ext_ms)) / 1e3
@@ -460,6 +464,8 @@ def run_decode_bench(args, torch):
         db.step(s, timed=False)
     db.stream.synchronize()
     torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()
     t0 = time.perf_counter()
     tokens = 0
     for s in range(args.warmup, n):
@@ -467,6 +473,7 @@ def run_decode_bench(args, torch):
     db.stream.synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     ms = [a.elapsed_time(b) for a, b, _ in db.events]
     avg_s = float(np.mean(ms)) / 1e3
     kv = np.mean([k for _, _, k in db.events])
