@@ -13,6 +13,8 @@ What it holds (each function cites the passage it follows):
 * ``attention`` -- causal scaled-dot-product attention in float64, evaluated
   from freshly regenerated Q/K/V for every position (no pool, no cache).
 * ``kv_store`` -- the pool after a scatter of new rows.
+* ``fp8`` -- the FP8 (OCP E4M3) pool format: codes, rounding, the stored
+  values that attention then reads.
 * ``hit_rate`` -- token-weighted cache hit rate and the Theorem 3.1 optimum.
 * ``runner`` -- the batch scheduler that drives the naive tree through a
   workload and records every observable decision.

@@ -55,11 +55,17 @@ def regenerate_qkv(tokens, positions, num_q_heads, num_kv_heads, head_dim, seed)
     return q, k, v
 
 
-def recompute_rows(tokens, positions, num_q_heads, num_kv_heads, head_dim, seed, sm_scale):
+def recompute_rows(tokens, positions, num_q_heads, num_kv_heads, head_dim, seed, sm_scale, kv_fp8_scales=None):
     """Attention output (float64 [len(positions), Hq, D]) of the given
-    positions of one sequence, from fully recomputed Q/K/V."""
+    positions of one sequence, from fully recomputed Q/K/V.  With
+    ``kv_fp8_scales = (k_scale, v_scale)`` the K and V rows are first
+    replaced by what an FP8 (E4M3) pool holds for them (``oracle.fp8``)."""
     positions = np.asarray(positions, dtype=np.int64)
     if positions.size == 0:
         return np.zeros((0, num_q_heads, head_dim))
     q, k, v = regenerate_qkv(tokens, positions, num_q_heads, num_kv_heads, head_dim, seed)
+    if kv_fp8_scales is not None:
+        from .fp8 import stored_values
+        k = stored_values(k, kv_fp8_scales[0])
+        v = stored_values(v, kv_fp8_scales[1])
     return causal_attention(q, k, v, positions, sm_scale)

@@ -70,7 +70,7 @@ class OracleTrace:
 
 def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
                  attention=True, want=None, keep_dumps=False, max_iterations=100000, policy="fcfs",
-                 chunk_size=None):
+                 chunk_size=None, kv_fp8_scales=None):
     """Drive workload ``wl`` through the naive tree.  ``want(kind, rid, step)``
     (kind 'ext' or 'dec') selects which attention outputs are recomputed;
     by default all of them when ``attention`` is true."""
@@ -123,7 +123,7 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
             raise ValueError(f"unknown policy {policy!r}")
         if chunk_size is not None:
             _chunked_admit_and_extend(wl, tree, pool, tr, rec, it, order, waiting, running, prefilling,
-                                      max_running, chunk_size, selected, finish)
+                                      max_running, chunk_size, selected, finish, kv_fp8_scales)
         else:
             reserved = sum(len(r.req.gen) - r.generated for r in running)
             budget = max_extend_tokens
@@ -161,7 +161,7 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
                         pos = np.arange(r.prefix_len, len(r.req.prompt))
                         tr.outputs[("ext", r.req.rid, 0)] = recompute_rows(
                             r.req.prompt, pos, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                            wl.seed, wl.sm_scale)
+                            wl.seed, wl.sm_scale, kv_fp8_scales)
                 for r in admitted:
                     if len(r.req.gen) == 0:
                         finish(r, rec)
@@ -180,7 +180,7 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
                     seq = list(r.req.prompt) + list(r.req.gen[:r.generated + 1])
                     tr.outputs[("dec", r.req.rid, r.generated)] = recompute_rows(
                         seq, [pos], wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                        wl.seed, wl.sm_scale)
+                        wl.seed, wl.sm_scale, kv_fp8_scales)
                 r.generated += 1
             done = [r for r in dec if r.generated == len(r.req.gen)]
             for r in done:
@@ -197,7 +197,7 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
 
 
 def _chunked_admit_and_extend(wl, tree, pool, tr, rec, it, order, waiting, running, prefilling,
-                              max_running, chunk_size, selected, finish):
+                              max_running, chunk_size, selected, finish, kv_fp8_scales=None):
     """One iteration's admission and extend under chunked prefill."""
     budget = chunk_size
     plan = []  # (request, first position, token count), in launch order
@@ -243,7 +243,7 @@ def _chunked_admit_and_extend(wl, tree, pool, tr, rec, it, order, waiting, runni
         if not wl.skip_extend_attention and selected("ext", r.req.rid, r.n_chunks):
             tr.outputs[("ext", r.req.rid, r.n_chunks)] = recompute_rows(
                 r.req.prompt, np.arange(first, first + cnt), wl.num_q_heads, wl.num_kv_heads,
-                wl.head_dim, wl.seed, wl.sm_scale)
+                wl.head_dim, wl.seed, wl.sm_scale, kv_fp8_scales)
         r.n_chunks += 1
     continuing = [r for r, _, _ in plan if all(r is not a for a in admitted)]
     for r in continuing + admitted:
