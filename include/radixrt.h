@@ -271,6 +271,32 @@ int radix_decode_attention(const void* q, void* o, const void* k_pool, const voi
                            float sm_scale, int dtype, void* workspace, int64_t workspace_bytes,
                            void* stream);
 
+/* FP8 K/V pool [P4 the v0.2 release was measured in FP8 as well as bf16;
+ * the pool format is OCP 8-bit floating point E4M3: sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits, no infinity, S.1111.111 NaN, largest finite
+ * 448].  Pools are uint8 [N+1, num_kv_heads, head_dim]; a stored code c
+ * stands for E4M3(c) * scale, with one k_scale for the K pool and one
+ * v_scale for the V pool (both > 0).
+ *
+ * kv_store_fp8: k_new, v_new (device) bf16 [n_tokens, num_kv_heads,
+ * head_dim]; row t is written at slot out_cache_loc[t] as
+ * E4M3(x * fl32(1 / scale)) with x * fl32(1 / scale) rounded in fp32, then
+ * to the nearest E4M3 value with ties to the even mantissa; magnitudes of
+ * 448 and above saturate to 448, NaN stays NaN.  Otherwise as kv_store. */
+int kv_store_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                 const int32_t* out_cache_loc, int32_t n_tokens, int32_t num_kv_heads, int32_t head_dim,
+                 float k_scale, float v_scale, void* stream);
+
+/* radix_decode_attention over FP8 pools: q, o bf16; keys and values read as
+ * E4M3(code) * k_scale and E4M3(code) * v_scale.  Same arguments, workspace
+ * (radix_decode_workspace_bytes) and checks otherwise. */
+int radix_decode_attention_fp8kv(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                 const int32_t* req_to_token, int32_t req_to_token_stride,
+                                 const int32_t* req_pool_indices, const int32_t* prefix_lens, int32_t batch,
+                                 int32_t max_kv_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 float sm_scale, float k_scale, float v_scale, void* workspace,
+                                 int64_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

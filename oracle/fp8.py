@@ -43,26 +43,21 @@ _POS_VALUES = _VALUES[_POS_CODES]
 def quantize_e4m3(x):
     """Nearest E4M3 code of each value (uint8 array of x's shape)."""
     x = np.asarray(x, dtype=np.float64)
-    flat = x.reshape(-1)
-    out = np.empty(flat.size, dtype=np.uint8)
-    for i, v in enumerate(flat):
-        sign = 0x80 if np.signbit(v) else 0
-        if np.isnan(v):
-            out[i] = sign | 0x7F
-            continue
-        a = abs(v)
-        if a >= _POS_VALUES[-1]:
-            out[i] = sign | _POS_CODES[-1]
-            continue
-        j = int(np.searchsorted(_POS_VALUES, a))        # _POS_VALUES[j-1] < a <= _POS_VALUES[j]
-        lo, hi = j - 1, j
-        if _POS_VALUES[hi] == a or lo < 0:
-            c = hi
-        else:
-            dl, dh = a - _POS_VALUES[lo], _POS_VALUES[hi] - a
-            c = lo if dl < dh else hi if dh < dl else (lo if _POS_CODES[lo] % 2 == 0 else hi)
-        out[i] = sign | int(_POS_CODES[c])
-    return out.reshape(x.shape)
+    sign = np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+    a = np.abs(x)
+    nan = np.isnan(x)
+    a_f = np.where(nan, 0.0, a)
+    # candidates: the largest finite value <= a and the smallest >= a
+    hi = np.clip(np.searchsorted(_POS_VALUES, a_f), 0, len(_POS_VALUES) - 1)
+    lo = np.clip(hi - 1, 0, len(_POS_VALUES) - 1)
+    d_lo, d_hi = a_f - _POS_VALUES[lo], _POS_VALUES[hi] - a_f
+    exact = _POS_VALUES[hi] == a_f
+    even_lo = (_POS_CODES[lo] % 2) == 0
+    pick_lo = ~exact & ((d_lo < d_hi) | ((d_lo == d_hi) & even_lo))
+    code = np.where(pick_lo, _POS_CODES[lo], _POS_CODES[hi])
+    code = np.where(a_f >= _POS_VALUES[-1], _POS_CODES[-1], code)   # saturate
+    code = np.where(nan, 0x7F, code)
+    return (sign | code.astype(np.uint8)).astype(np.uint8)
 
 
 def store_codes(rows, scale):

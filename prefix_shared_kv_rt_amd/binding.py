@@ -23,7 +23,8 @@ EXPORTS = [
     "rt_tree_create", "rt_tree_destroy", "rt_match_prefix", "rt_insert", "rt_lock", "rt_unlock",
     "rt_evict_lru_leaves", "rt_alloc_with_evict", "rt_evictable_size", "rt_protected_size",
     "rt_tree_num_nodes", "rt_tree_dump", "rt_admit_batch", "rt_decode_slots_batch", "rt_finish_batch",
-    "kv_store", "req_to_token_scatter", "decode_append", "radix_extend_attention", "radix_decode_workspace_bytes", "radix_decode_attention",
+    "kv_store", "req_to_token_scatter", "decode_append", "kv_store_fp8", "radix_decode_attention_fp8kv",
+    "radix_extend_attention", "radix_decode_workspace_bytes", "radix_decode_attention",
 ]
 
 
@@ -84,6 +85,13 @@ def lib():
             "kv_store": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int, _vp]),
             "req_to_token_scatter": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int32, _vp]),
+            "kv_store_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_float, ctypes.c_float, _vp]),
+            "radix_decode_attention_fp8kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp,
+                                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                                            ctypes.c_float, ctypes.c_float, _vp, ctypes.c_int64,
+                                                            _vp]),
             "decode_append": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp]),
             "radix_extend_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
@@ -307,6 +315,24 @@ def kv_store(k_pool, v_pool, k_new, v_new, out_cache_loc, stream=None):
 def req_to_token_scatter(req_to_token, rows, positions, slots, stream=None):
     _check(lib().req_to_token_scatter(_dptr(req_to_token), req_to_token.shape[1], _dptr(rows), _dptr(positions),
                                       _dptr(slots), rows.shape[0], _stream(stream)))
+
+
+def kv_store_fp8(k_pool, v_pool, k_new, v_new, out_cache_loc, k_scale=1.0, v_scale=1.0, stream=None):
+    """k_pool, v_pool: uint8 (FP8 E4M3 codes); k_new, v_new: bf16."""
+    n, hkv, d = k_new.shape
+    _check(lib().kv_store_fp8(_dptr(k_pool), _dptr(v_pool), _dptr(k_new), _dptr(v_new), _dptr(out_cache_loc), n, hkv,
+                              d, float(k_scale), float(v_scale), _stream(stream)))
+
+
+def radix_decode_attention_fp8kv(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens, max_kv_len,
+                                 sm_scale, workspace, k_scale=1.0, v_scale=1.0, stream=None):
+    batch, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    _check(lib().radix_decode_attention_fp8kv(_dptr(q), _dptr(o), _dptr(k_pool), _dptr(v_pool), _dptr(req_to_token),
+                                              req_to_token.shape[1], _dptr(req_pool_indices), _dptr(prefix_lens),
+                                              batch, int(max_kv_len), hq, hkv, d, float(sm_scale), float(k_scale),
+                                              float(v_scale), _dptr(workspace), workspace.numel() * workspace.element_size(),
+                                              _stream(stream)))
 
 
 def decode_append(req_to_token, rows, positions, slots, k_pool, v_pool, k_new, v_new, stream=None):

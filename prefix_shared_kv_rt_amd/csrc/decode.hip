@@ -69,26 +69,34 @@ DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len) 
 // into 8 contiguous slices, one per XCD (the hardware places block i on XCD
 // i % 8).  Requests that share a cached prefix read the same slots for the
 // same (s, h), so their concurrent waves on one XCD meet those rows in L2.
-template <int D>
+// One 16-key block's operands as loaded: bf16 pools hold them as the MFMA
+// takes them; FP8 pools hold half the bytes, widened to bf16 when consumed.
+template <int D, bool KV8>
 struct DecBlock {
   u32x4 k[D / 32];        // K operand rows: key kb + col, dims 32*ks + 8*grp .. +7
   u32x2 v[D / 64][4];     // V rows kb + 4*grp + t, dims 64*h + 4*col .. +3
 };
-
 template <int D>
+struct DecBlock<D, true> {
+  u32x2 k[D / 32];
+  uint32_t v[D / 64][4];
+};
+
+template <int D, bool KV8>
 __global__ void __launch_bounds__(64) decode_split_bf16(
     const char* __restrict__ q, const char* __restrict__ k_pool, const char* __restrict__ v_pool,
     const int32_t* __restrict__ req_to_token, int64_t stride, const int32_t* __restrict__ rpi,
     const int32_t* __restrict__ prefix_lens, int B, int Hq, int Hkv, int G, int S, int chunk, float scale_log2,
-    float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
+    float v_scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
   constexpr int KS = D / 32;      // 32-dim steps of the score contraction
   constexpr int VH = D / 64;      // 64-dim halves of the PV update
+  constexpr int EB = KV8 ? 1 : 2; // bytes per pool element
   __shared__ int32_t s_idx[kMaxChunk];
 
   const int lane = threadIdx.x;
   const int col = lane & 15;      // MFMA column: query head within the group / key within block
   const int grp = lane >> 4;      // MFMA k-group
-  const int64_t row_bytes = int64_t(Hkv) * D * 2;
+  const int64_t row_bytes = int64_t(Hkv) * D * EB;
 
   // This wave's share of its XCD's slice of the item list.
   const int n_items = B * Hkv * S;
@@ -105,8 +113,8 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
     const int start = s * chunk;
     const int end = min(kv_len, start + chunk);
     const int32_t* idx_row = req_to_token + int64_t(rpi ? rpi[b] : b) * stride;
-    const char* kbase = k_pool + int64_t(kvh) * D * 2 + (8 * grp) * 2;
-    const char* vbase = v_pool + int64_t(kvh) * D * 2 + (4 * col) * 2;
+    const char* kbase = k_pool + (int64_t(kvh) * D + 8 * grp) * EB;
+    const char* vbase = v_pool + (int64_t(kvh) * D + 4 * col) * EB;
 
     // Slot indices of the whole chunk into this wave's LDS, once.
     __syncthreads();  // the previous item's index reads are complete
@@ -131,24 +139,39 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
 
     // Keys past `end` are clamped to the chunk's last key (masked below), so
     // every load is valid and the loop needs no tail branches.
-    auto load = [&](DecBlock<D>& blk, int kb) {
+    auto load = [&](DecBlock<D, KV8>& blk, int kb) {
       const int kk = min(kb + col, end - 1) - start;
       const char* kp = kbase + int64_t(uint32_t(s_idx[kk])) * row_bytes;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) blk.k[ks] = ld16(kp + 64 * ks);
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (KV8)
+          blk.k[ks] = ld8(kp + 32 * ks);
+        else
+          blk.k[ks] = ld16(kp + 64 * ks);
+      }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int kv = min(kb + 4 * grp + t, end - 1) - start;
         const char* vp = vbase + int64_t(uint32_t(s_idx[kv])) * row_bytes;
 #pragma unroll
-        for (int h = 0; h < VH; ++h) blk.v[h][t] = ld8(vp + 128 * h);
+        for (int h = 0; h < VH; ++h) {
+          if constexpr (KV8)
+            blk.v[h][t] = ld4(vp + 64 * h);
+          else
+            blk.v[h][t] = ld8(vp + 128 * h);
+        }
       }
     };
 
-    auto consume = [&](const DecBlock<D>& cur, int kb) {
+    auto consume = [&](const DecBlock<D, KV8>& cur, int kb) {
       floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sacc = mfma_16x16x32(as_bf16x8(cur.k[ks]), qop[ks], sacc);
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (KV8)
+          sacc = mfma_16x16x32(fp8x8_to_bf16x8(cur.k[ks]), qop[ks], sacc);
+        else
+          sacc = mfma_16x16x32(as_bf16x8(cur.k[ks]), qop[ks], sacc);
+      }
       // Scores of keys kb + 4*grp + v for head `col` (log2 domain); keys at or
       // past `end` (a block wholly past it included) contribute nothing.
       float sv[4];
@@ -173,7 +196,14 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
       const bf16x4 pop = as_bf16x4(u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
 #pragma unroll
       for (int h = 0; h < VH; ++h) {
-        const u32x2* w = cur.v[h];
+        u32x2 w[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if constexpr (KV8)
+            w[t] = fp8x4_to_bf16x4(cur.v[h][t]);
+          else
+            w[t] = cur.v[h][t];
+        }
         o[h * 4 + 0] = mfma_16x16x16(as_bf16x4(u32x2{pack_lo16(w[0].x, w[1].x), pack_lo16(w[2].x, w[3].x)}), pop, o[h * 4 + 0]);
         o[h * 4 + 1] = mfma_16x16x16(as_bf16x4(u32x2{pack_hi16(w[0].x, w[1].x), pack_hi16(w[2].x, w[3].x)}), pop, o[h * 4 + 1]);
         o[h * 4 + 2] = mfma_16x16x16(as_bf16x4(u32x2{pack_lo16(w[0].y, w[1].y), pack_lo16(w[2].y, w[3].y)}), pop, o[h * 4 + 2]);
@@ -185,7 +215,7 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
     // one is consumed (past `end` the loads repeat the clamped last row).
     const int nb = end > start ? (end - start + 15) >> 4 : 0;
     if (nb > 0) {
-      DecBlock<D> cur, nxt;
+      DecBlock<D, KV8> cur, nxt;
       load(cur, start);
       for (int i = 0; i < nb; ++i) {
         const int kb = start + 16 * i;
@@ -210,6 +240,7 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           floatx4 w = {o[h * 4 + 0][v], o[h * 4 + 1][v], o[h * 4 + 2][v], o[h * 4 + 3][v]};
+          if constexpr (KV8) w *= v_scale;
           *reinterpret_cast<floatx4*>(acc + 64 * h + 16 * grp + 4 * v) = w;
         }
     }
@@ -305,14 +336,14 @@ __global__ void __launch_bounds__(64) decode_combine(const float* __restrict__ w
 
 // Resident 64-thread blocks of the bf16 split kernel on this device
 // (occupancy x compute units, a multiple of 8), queried once per device.
-template <int D>
+template <int D, bool KV8>
 int resident_waves() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 2048;
   if (cached[dev] == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_bf16<D>, 64, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_bf16<D, KV8>, 64, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 ||
         cus < 1)
       return 2048;
@@ -321,17 +352,29 @@ int resident_waves() {
   return cached[dev];
 }
 
+// Pool formats of launch_decode: the two public dtypes plus FP8 K/V under
+// bf16 q/o.
+constexpr int kModeFp8Kv = 100;
+
 template <int D>
 void launch_decode(const void* q, void* o, const void* k_pool, const void* v_pool, const int32_t* r2t,
                    int64_t stride, const int32_t* rpi, const int32_t* plens, int B, int Hq, int Hkv,
-                   DecodePlan pl, float scale_log2, int dtype, float* ws_acc, float* ws_ml, hipStream_t st) {
+                   DecodePlan pl, float scale_log2, float v_scale, int mode, float* ws_acc, float* ws_ml,
+                   hipStream_t st) {
   const int G = Hq / Hkv;
-  if (dtype == RT_BF16) {
+  if (mode == RT_BF16 || mode == kModeFp8Kv) {
     const int64_t items = int64_t(B) * Hkv * pl.splits;
-    const int64_t grid = std::min<int64_t>(resident_waves<D>(), (items + 7) / 8 * 8);
-    hipLaunchKernelGGL(decode_split_bf16<D>, dim3(uint32_t(grid)), dim3(64), 0, st, (const char*)q, (const char*)k_pool,
-                       (const char*)v_pool, r2t, stride, rpi, plens, B, Hq, Hkv, G, pl.splits, pl.chunk, scale_log2,
-                       ws_acc, ws_ml);
+    if (mode == RT_BF16) {
+      const int64_t grid = std::min<int64_t>(resident_waves<D, false>(), (items + 7) / 8 * 8);
+      hipLaunchKernelGGL((decode_split_bf16<D, false>), dim3(uint32_t(grid)), dim3(64), 0, st, (const char*)q,
+                         (const char*)k_pool, (const char*)v_pool, r2t, stride, rpi, plens, B, Hq, Hkv, G, pl.splits,
+                         pl.chunk, scale_log2, 1.0f, ws_acc, ws_ml);
+    } else {
+      const int64_t grid = std::min<int64_t>(resident_waves<D, true>(), (items + 7) / 8 * 8);
+      hipLaunchKernelGGL((decode_split_bf16<D, true>), dim3(uint32_t(grid)), dim3(64), 0, st, (const char*)q,
+                         (const char*)k_pool, (const char*)v_pool, r2t, stride, rpi, plens, B, Hq, Hkv, G, pl.splits,
+                         pl.chunk, scale_log2, v_scale, ws_acc, ws_ml);
+    }
     hipLaunchKernelGGL((decode_combine<D, true>), dim3(uint32_t(int64_t(B) * Hq)), dim3(64), 0, st, ws_acc,
                        ws_ml, pl.splits, o);
   } else {
@@ -342,6 +385,42 @@ void launch_decode(const void* q, void* o, const void* k_pool, const void* v_poo
     hipLaunchKernelGGL((decode_combine<D, false>), dim3(uint32_t(int64_t(B) * Hq)), dim3(64), 0, st, ws_acc,
                        ws_ml, pl.splits, o);
   }
+}
+
+int decode_entry(const char* name, const void* q, void* o, const void* k_pool, const void* v_pool,
+                 const int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* req_pool_indices,
+                 const int32_t* prefix_lens, int32_t batch, int32_t max_kv_len, int32_t num_q_heads,
+                 int32_t num_kv_heads, int32_t head_dim, float sm_scale, float k_scale, float v_scale, int mode,
+                 void* workspace, int64_t workspace_bytes, void* stream) {
+  const std::string fn(name);
+  if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
+      (head_dim != 64 && head_dim != 128) || max_kv_len < 1 || req_to_token_stride < max_kv_len ||
+      !(sm_scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
+    return rt::fail(RT_ERR_INVALID, fn + ": bad shape, stride or scale");
+  if (int64_t(max_kv_len) > int64_t(kMaxChunk) * 1024)
+    return rt::fail(RT_ERR_INVALID, fn + ": max_kv_len above 2097152");
+  if (mode != RT_F32 && num_q_heads / num_kv_heads > 16)
+    return rt::fail(RT_ERR_INVALID, fn + ": the bf16 path supports at most 16 query heads per KV head");
+  if (batch == 0) return RT_OK;
+  if (!q || !o || !k_pool || !v_pool || !req_to_token || !prefix_lens || !workspace)
+    return rt::fail(RT_ERR_INVALID, fn + ": null pointer");
+  const int64_t need = radix_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_kv_len);
+  if (workspace_bytes < need)
+    return rt::fail(RT_ERR_INVALID, fn + ": workspace too small (need " + std::to_string(need) + ")");
+  const DecodePlan pl = plan_decode(batch, num_kv_heads, max_kv_len);
+  float* ws_acc = static_cast<float*>(workspace);
+  float* ws_ml = ws_acc + int64_t(batch) * num_q_heads * pl.splits * head_dim;
+  const float scale_log2 = sm_scale * k_scale * kLog2e;
+  hipStream_t st = (hipStream_t)stream;
+  if (head_dim == 128)
+    launch_decode<128>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
+                       batch, num_q_heads, num_kv_heads, pl, scale_log2, v_scale, mode, ws_acc, ws_ml, st);
+  else
+    launch_decode<64>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
+                      batch, num_q_heads, num_kv_heads, pl, scale_log2, v_scale, mode, ws_acc, ws_ml, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return rt::fail(RT_ERR_HIP, fn + " launch: " + hipGetErrorString(e));
+  return RT_OK;
 }
 
 }  // namespace
@@ -364,33 +443,19 @@ extern "C" int radix_decode_attention(const void* q, void* o, const void* k_pool
                                       float sm_scale, int dtype, void* workspace, int64_t workspace_bytes,
                                       void* stream) {
   (void)extend_lens;  // decode rows are one token each by definition
-  if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
-      (head_dim != 64 && head_dim != 128) || (dtype != RT_F32 && dtype != RT_BF16) || max_kv_len < 1 ||
-      req_to_token_stride < max_kv_len || !(sm_scale > 0.f))
-    return rt::fail(RT_ERR_INVALID, "radix_decode_attention: bad shape, dtype, stride or scale");
-  if (int64_t(max_kv_len) > int64_t(kMaxChunk) * 1024)
-    return rt::fail(RT_ERR_INVALID, "radix_decode_attention: max_kv_len above 2097152");
-  if (dtype == RT_BF16 && num_q_heads / num_kv_heads > 16)
-    return rt::fail(RT_ERR_INVALID, "radix_decode_attention: bf16 path supports at most 16 query heads per KV head");
-  if (batch == 0) return RT_OK;
-  if (!q || !o || !k_pool || !v_pool || !req_to_token || !prefix_lens || !workspace)
-    return rt::fail(RT_ERR_INVALID, "radix_decode_attention: null pointer");
-  const int64_t need = radix_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_kv_len);
-  if (workspace_bytes < need)
-    return rt::fail(RT_ERR_INVALID, "radix_decode_attention: workspace too small (need " + std::to_string(need) + ")");
-  const DecodePlan pl = plan_decode(batch, num_kv_heads, max_kv_len);
-  float* ws_acc = static_cast<float*>(workspace);
-  float* ws_ml = ws_acc + int64_t(batch) * num_q_heads * pl.splits * head_dim;
-  const float scale_log2 = sm_scale * kLog2e;
-  hipStream_t st = (hipStream_t)stream;
-  if (head_dim == 128)
-    launch_decode<128>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
-                       batch, num_q_heads, num_kv_heads, pl, scale_log2, dtype, ws_acc, ws_ml, st);
-  else
-    launch_decode<64>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
-                      batch, num_q_heads, num_kv_heads, pl, scale_log2, dtype, ws_acc, ws_ml, st);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess)
-    return rt::fail(RT_ERR_HIP, std::string("radix_decode_attention launch: ") + hipGetErrorString(e));
-  return RT_OK;
+  if (dtype != RT_F32 && dtype != RT_BF16) return rt::fail(RT_ERR_INVALID, "radix_decode_attention: bad dtype");
+  return decode_entry("radix_decode_attention", q, o, k_pool, v_pool, req_to_token, req_to_token_stride,
+                      req_pool_indices, prefix_lens, batch, max_kv_len, num_q_heads, num_kv_heads, head_dim,
+                      sm_scale, 1.0f, 1.0f, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" int radix_decode_attention_fp8kv(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                            const int32_t* req_to_token, int32_t req_to_token_stride,
+                                            const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                            int32_t batch, int32_t max_kv_len, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim, float sm_scale, float k_scale,
+                                            float v_scale, void* workspace, int64_t workspace_bytes, void* stream) {
+  return decode_entry("radix_decode_attention_fp8kv", q, o, k_pool, v_pool, req_to_token, req_to_token_stride,
+                      req_pool_indices, prefix_lens, batch, max_kv_len, num_q_heads, num_kv_heads, head_dim,
+                      sm_scale, k_scale, v_scale, kModeFp8Kv, workspace, workspace_bytes, stream);
 }

@@ -76,8 +76,49 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const void* lds_ptr) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Global loads; 16 / 8 byte vectors.
+// Global loads; 16 / 8 / 4 byte vectors.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ uint32_t ld4(const void* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+// FP8 (OCP E4M3: sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+// infinity, S.1111.111 = NaN, largest finite 448).
+//
+// Decode: bytes 0-1 (HI = false) or 2-3 (HI = true) of w to a bf16 pair, with
+// gfx950's v_cvt_scalef32_pk_bf16_fp8 at scale 1 (exact: every E4M3 value is
+// a bf16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// Four FP8 values of a dword (byte order = element order) to four bf16.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  return u32x2{fp8x2_to_bf16x2<false>(w), fp8x2_to_bf16x2<true>(w)};
+}
+// Eight FP8 values (two dwords) to eight bf16.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 w) {
+  return as_bf16x8(u32x4{fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x), fp8x2_to_bf16x2<false>(w.y),
+                         fp8x2_to_bf16x2<true>(w.y)});
+}
+// Encode: nearest E4M3 value, ties to the even mantissa; magnitudes of 448
+// and beyond (infinity included) saturate to 448; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t s = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return s | 0x7fu;       // NaN
+  if (a >= 0x43e00000u) return s | 0x7eu;      // >= 448
+  if (a < 0x3c800000u) {                        // below 2^-6: multiples of 2^-9
+    return s | uint32_t(__builtin_rintf(__uint_as_float(a) * 512.f));  // 0..8; 8 is 2^-6
+  }
+  const uint32_t m = a & 0x7fffffu;
+  uint32_t e = (a >> 23) - 120u;                // exponent re-biased from 127 to 7: 1..15
+  uint32_t r = (m + 0x7ffffu + ((m >> 20) & 1u)) >> 20;
+  if (r == 8u) {
+    r = 0u;
+    ++e;
+  }
+  return s | (e << 3) | r;                      // below 448: never reaches e = 15 with r = 7
+}
 
 }  // namespace rtk

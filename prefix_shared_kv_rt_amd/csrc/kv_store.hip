@@ -13,6 +13,7 @@
 
 namespace {
 
+using rtk::u32x2;
 using rtk::u32x4;
 
 __global__ void __launch_bounds__(256) kv_store_kernel(char* __restrict__ k_pool, char* __restrict__ v_pool,
@@ -58,7 +59,57 @@ __global__ void __launch_bounds__(256) decode_append_kernel(int32_t* __restrict_
   }
 }
 
+// bf16 rows in, FP8 rows out: 8 values per piece (16 bytes read, 8 written).
+__global__ void __launch_bounds__(256) kv_store_fp8_kernel(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                                                           const char* __restrict__ k_new,
+                                                           const char* __restrict__ v_new,
+                                                           const int32_t* __restrict__ loc, int64_t n_tokens,
+                                                           int64_t row_elems, float k_inv, float v_inv) {
+  const int64_t pieces_per_row = row_elems >> 3;
+  const int64_t total = n_tokens * pieces_per_row;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t p = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; p < total; p += stride) {
+    const int64_t t = p / pieces_per_row;
+    const int64_t e = (p - t * pieces_per_row) << 3;
+    const int64_t slot = loc[t];
+    const u32x4 kw = *reinterpret_cast<const u32x4*>(k_new + (t * row_elems + e) * 2);
+    const u32x4 vw = *reinterpret_cast<const u32x4*>(v_new + (t * row_elems + e) * 2);
+    u32x2 ko = {0u, 0u}, vo = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t kb = (kw[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+      const uint32_t vb = (vw[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+      ko[i >> 2] |= rtk::f32_to_e4m3(__uint_as_float(kb << 16) * k_inv) << (8 * (i & 3));
+      vo[i >> 2] |= rtk::f32_to_e4m3(__uint_as_float(vb << 16) * v_inv) << (8 * (i & 3));
+    }
+    *reinterpret_cast<u32x2*>(k_pool + slot * row_elems + e) = ko;
+    *reinterpret_cast<u32x2*>(v_pool + slot * row_elems + e) = vo;
+  }
+}
+
 }  // namespace
+
+extern "C" int kv_store_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                            const int32_t* out_cache_loc, int32_t n_tokens, int32_t num_kv_heads, int32_t head_dim,
+                            float k_scale, float v_scale, void* stream) {
+  if (n_tokens < 0 || num_kv_heads < 1 || (head_dim != 64 && head_dim != 128) || !(k_scale > 0.f) ||
+      !(v_scale > 0.f))
+    return rt::fail(RT_ERR_INVALID, "kv_store_fp8: bad shape or scale");
+  if (n_tokens == 0) return RT_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !out_cache_loc)
+    return rt::fail(RT_ERR_INVALID, "kv_store_fp8: null pointer");
+  const int64_t row_elems = int64_t(num_kv_heads) * head_dim;
+  const int64_t total = int64_t(n_tokens) * (row_elems >> 3);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;
+  hipLaunchKernelGGL(kv_store_fp8_kernel, dim3(uint32_t(blocks)), dim3(256), 0, (hipStream_t)stream,
+                     (uint8_t*)k_pool, (uint8_t*)v_pool, (const char*)k_new, (const char*)v_new, out_cache_loc,
+                     int64_t(n_tokens), row_elems, k_inv, v_inv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return rt::fail(RT_ERR_HIP, std::string("kv_store_fp8 launch: ") + hipGetErrorString(e));
+  return RT_OK;
+}
 
 extern "C" int decode_append(int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* rows,
                              const int32_t* positions, const int32_t* slots, int32_t n, void* k_pool,

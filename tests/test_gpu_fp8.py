@@ -1,0 +1,86 @@
+"""FP8 (E4M3) K/V pools on the GPU: the store kernel against the oracle's
+codes bit for bit, and decode attention over FP8 pools against float64
+attention on the values those codes stand for."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.fp8 import dequantize, kv_store_fp8 as oracle_store, store_codes
+from prefix_shared_kv_rt_amd import binding as B
+from tests.gpu_util import host_values, i32, make_pool_case, max_err, oracle_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("hkv,d,k_scale,v_scale", [(8, 128, 1.0, 1.0), (2, 64, 0.37, 3.0)])
+def test_kv_store_fp8_bit_exact(hkv, d, k_scale, v_scale):
+    _announce(f"kv_store_fp8 hkv={hkv} d={d} scales {k_scale} {v_scale}")
+    rng = np.random.default_rng(hkv + d)
+    n_slots, T = 1500, 611
+    mags = np.array([1e-4, 1e-2, 1.0, 30.0, 300.0, 3000.0])
+    k = rng.standard_normal((T, hkv, d)) * mags[rng.integers(0, len(mags), (T, hkv, 1))]
+    v = rng.standard_normal((T, hkv, d)) * mags[rng.integers(0, len(mags), (T, hkv, 1))]
+    k[0, 0, :4] = [np.inf, -np.inf, np.nan, -0.0]
+    kn = torch.from_numpy(k.astype(np.float32)).to(torch.bfloat16)
+    vn = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16)
+    loc = rng.permutation(np.arange(1, n_slots + 1))[:T].astype(np.int32)
+    pool0 = rng.integers(0, 256, (n_slots + 1, hkv, d)).astype(np.uint8)
+    kp, vp = torch.from_numpy(pool0).cuda(), torch.from_numpy(pool0.copy()).cuda()
+    B.kv_store_fp8(kp, vp, kn.cuda(), vn.cuda(), i32(loc), k_scale, v_scale)
+    torch.cuda.synchronize()
+    want_k = oracle_store(pool0, kn.float().numpy(), loc, k_scale)
+    want_v = oracle_store(pool0, vn.float().numpy(), loc, v_scale)
+    got_k, got_v = kp.cpu().numpy(), vp.cpu().numpy()
+    # NaN codes agree up to the sign bit (the NaN's sign is not specified)
+    nan_k = (want_k & 0x7F) == 0x7F
+    assert np.array_equal((got_k & 0x7F) == 0x7F, nan_k)
+    assert np.array_equal(got_k[~nan_k], want_k[~nan_k])
+    assert np.array_equal(got_v, want_v)
+
+
+FP8_DECODE_CASES = [
+    ([0, 1, 15, 16, 17, 63, 64, 65], 32, 8, 128, 1.0, 1.0),
+    ([2048, 2100, 2303, 1], 32, 8, 128, 0.5, 2.0),
+    ([5000, 777, 3333], 64, 8, 128, 1.0, 0.25),
+    ([40, 600, 1200], 16, 16, 64, 1.5, 1.0),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(FP8_DECODE_CASES)))
+def test_decode_fp8_matches_oracle(ci):
+    prefix_lens, hq, hkv, d, ks, vs = FP8_DECODE_CASES[ci]
+    _announce(f"decode fp8 case {ci}: P={prefix_lens} hq={hq} hkv={hkv} d={d} scales {ks} {vs}")
+    rng = np.random.default_rng(500 + ci)
+    case = make_pool_case(rng, prefix_lens, [1] * len(prefix_lens), hq, hkv, d, "bf16")
+    kc, vc = store_codes(case["kpool"], ks), store_codes(case["vpool"], vs)
+    q_host = host_values(rng, (len(prefix_lens), hq, d), "bf16")
+    q = to_dev(q_host, "bf16")
+    o = torch.full_like(q, float("nan"))
+    max_kv = max(prefix_lens) + 1
+    ws = torch.empty(B.radix_decode_workspace_bytes(len(prefix_lens), hq, hkv, d, max_kv), dtype=torch.uint8,
+                     device="cuda")
+    B.radix_decode_attention_fp8kv(q, o, torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda(), i32(case["r2t"]),
+                                   i32(case["rows"]), i32(prefix_lens), max_kv, 1.0 / np.sqrt(d), ws, ks, vs)
+    torch.cuda.synchronize()
+    kvals, vvals = dequantize(kc, ks), dequantize(vc, vs)
+    worst = 0.0
+    for b, p in enumerate(prefix_lens):
+        sl = case["r2t"][case["rows"][b], :p + 1]
+        want = oracle_rows(q_host[b:b + 1], kvals[sl], vvals[sl], np.array([p]), 1.0 / np.sqrt(d))
+        worst = max(worst, max_err(o[b:b + 1], want))
+    print(f"  max abs err {worst:.3e}")
+    assert worst <= 2e-2
+
+
+def test_decode_fp8_rejects_bad_scale():
+    q = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
+    pool = torch.zeros((4, 1, 128), dtype=torch.uint8, device="cuda")
+    r2t = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.RadixRTError):
+        B.radix_decode_attention_fp8kv(q, q.clone(), pool, pool, r2t, None, i32([0]), 1, 0.1, ws, 0.0, 1.0)
