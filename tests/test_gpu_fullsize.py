@@ -15,6 +15,23 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-2
 
 
+def check_few_shot(fb, i):
+    """Sampled outputs of batch i against the oracle's full recompute."""
+    o_ext = fb.o_ext.float().cpu().numpy()
+    o_dec = fb.o_dec.float().cpu().numpy()
+    worst = 0.0
+    for b in (0, 31, 63):
+        toks = list(fb.prefix) + list(fb.suffix[i][b])
+        p = int(fb.last_prefix_lens[b])  # rows below p were cached, not recomputed
+        rows = sorted({p, (p + fb.PREFIX + fb.SUFFIX) // 2, fb.PREFIX + fb.SUFFIX - 1})
+        want = recompute_rows(toks, rows, fb.HQ, fb.HKV, fb.D, fb.SEED, fb.sm_scale)
+        got = o_ext[[b * fb.SUFFIX + (r - fb.PREFIX) for r in rows]]
+        worst = max(worst, float(np.abs(got - want).max()))
+        want_d = recompute_rows(toks, [fb.PREFIX + fb.SUFFIX], fb.HQ, fb.HKV, fb.D, fb.SEED, fb.sm_scale)
+        worst = max(worst, float(np.abs(o_dec[b:b + 1] - want_d).max()))
+    return {"max_abs_err": worst, "tol": TOL, "ok": worst <= TOL}
+
+
 def test_few_shot_full_size_bench_path():
     """64 requests x (1024 shared + 128 distinct) per step, three steps: the
     extend rows actually computed (position >= matched prefix) and the
@@ -27,20 +44,21 @@ def test_few_shot_full_size_bench_path():
     for i in range(3):
         fb.step(i, timed=False)
         fb.stream.synchronize()
-        res = bench.check_few_shot(fb, i)
+        res = check_few_shot(fb, i)
         print(f"  step {i}: {res}", flush=True)
         worst = max(worst, res["max_abs_err"])
     assert worst <= TOL
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,steps,sample_steps", [
-    ("fork", 256, (0, 127, 255)),
-    ("long_context", 128, (0, 64, 127)),
+@pytest.mark.parametrize("name,steps,sample_steps,kv_dtype", [
+    ("fork", 256, (0, 127, 255), "bf16"),
+    ("long_context", 128, (0, 64, 127), "bf16"),
+    ("long_context", 128, (0, 127), "fp8"),
 ])
-def test_decode_full_size_bench_path(name, steps, sample_steps):
-    print(f"{name} full size, {steps} decode steps", flush=True)
-    db = bench.DecodeBench(name, torch, B, torch_gen, steps)
+def test_decode_full_size_bench_path(name, steps, sample_steps, kv_dtype):
+    print(f"{name} full size, {steps} decode steps, {kv_dtype} pool", flush=True)
+    db = bench.DecodeBench(name, torch, B, torch_gen, steps, kv_dtype=kv_dtype)
     db.setup()
     saved = {}
     for s in range(steps):
@@ -53,7 +71,8 @@ def test_decode_full_size_bench_path(name, steps, sample_steps):
     for b in (0, db.B - 1):
         toks = list(db.shared_toks[b // per]) + list(db.private_toks[b]) + list(db.gen_toks[b])
         pos = [db.prompt_len + s for s in sample_steps]
-        want = recompute_rows(toks, pos, db.HQ, db.HKV, db.D, db.SEED, db.sm_scale)
+        want = recompute_rows(toks, pos, db.HQ, db.HKV, db.D, db.SEED, db.sm_scale,
+                              kv_fp8_scales=(1.0, 1.0) if kv_dtype == "fp8" else None)
         for k, s in enumerate(sample_steps):
             worst = max(worst, float(np.abs(saved[s][b] - want[k]).max()))
     print(f"  max abs err {worst:.3e}", flush=True)
