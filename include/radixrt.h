@@ -290,6 +290,16 @@ int kv_store_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_ne
 /* radix_decode_attention over FP8 pools: q, o bf16; keys and values read as
  * E4M3(code) * k_scale and E4M3(code) * v_scale.  Same arguments, workspace
  * (radix_decode_workspace_bytes) and checks otherwise. */
+/* radix_extend_attention over FP8 pools: q, o bf16; keys and values read as
+ * E4M3(code) * k_scale and E4M3(code) * v_scale.  Same arguments and checks
+ * otherwise. */
+int radix_extend_attention_fp8kv(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                 const int32_t* req_to_token, int32_t req_to_token_stride,
+                                 const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                 const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
+                                 int32_t max_extend_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, float sm_scale, float k_scale, float v_scale, void* stream);
+
 int radix_decode_attention_fp8kv(const void* q, void* o, const void* k_pool, const void* v_pool,
                                  const int32_t* req_to_token, int32_t req_to_token_stride,
                                  const int32_t* req_pool_indices, const int32_t* prefix_lens, int32_t batch,

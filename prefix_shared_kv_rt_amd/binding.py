@@ -24,6 +24,7 @@ EXPORTS = [
     "rt_evict_lru_leaves", "rt_alloc_with_evict", "rt_evictable_size", "rt_protected_size",
     "rt_tree_num_nodes", "rt_tree_dump", "rt_admit_batch", "rt_decode_slots_batch", "rt_finish_batch",
     "kv_store", "req_to_token_scatter", "decode_append", "kv_store_fp8", "radix_decode_attention_fp8kv",
+    "radix_extend_attention_fp8kv",
     "radix_extend_attention", "radix_decode_workspace_bytes", "radix_decode_attention",
 ]
 
@@ -92,6 +93,10 @@ def lib():
                                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                                             ctypes.c_float, ctypes.c_float, _vp, ctypes.c_int64,
                                                             _vp]),
+            "radix_extend_attention_fp8kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
+                                                            _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                                            ctypes.c_float, ctypes.c_float, _vp]),
             "decode_append": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp]),
             "radix_extend_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
@@ -333,6 +338,17 @@ def radix_decode_attention_fp8kv(q, o, k_pool, v_pool, req_to_token, req_pool_in
                                               batch, int(max_kv_len), hq, hkv, d, float(sm_scale), float(k_scale),
                                               float(v_scale), _dptr(workspace), workspace.numel() * workspace.element_size(),
                                               _stream(stream)))
+
+
+def radix_extend_attention_fp8kv(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens, extend_lens,
+                                 qo_indptr, max_extend_len, sm_scale, k_scale=1.0, v_scale=1.0, stream=None):
+    batch = prefix_lens.shape[0]
+    _, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    _check(lib().radix_extend_attention_fp8kv(_dptr(q), _dptr(o), _dptr(k_pool), _dptr(v_pool), _dptr(req_to_token),
+                                              req_to_token.shape[1], _dptr(req_pool_indices), _dptr(prefix_lens),
+                                              _dptr(extend_lens), _dptr(qo_indptr), batch, int(max_extend_len), hq, hkv,
+                                              d, float(sm_scale), float(k_scale), float(v_scale), _stream(stream)))
 
 
 def decode_append(req_to_token, rows, positions, slots, k_pool, v_pool, k_new, v_new, stream=None):

@@ -90,23 +90,32 @@ __device__ __forceinline__ int swz(int key, int chunk) {
   return key * ExtendCfg<D>::kRowBytes + ((chunk ^ (swz_f(key) & (ExtendCfg<D>::kCPR - 1))) << 4);
 }
 
-template <int D, int RB>
+template <int D, int RB, bool KV8>
 __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_bf16(
     const char* __restrict__ q, char* __restrict__ o, const char* __restrict__ k_pool,
     const char* __restrict__ v_pool, const int32_t* __restrict__ req_to_token, int64_t stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
     const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ qo_indptr, int B, int Hq, int Hkv,
-    int G, int n_qt, float scale_log2) {
+    int G, int n_qt, float scale_log2, float v_scale) {
   using C = ExtendCfg<D>;
   constexpr int kWaveRows = 32 * RB;          // query rows per wave (RB blocks of 32)
   constexpr int kItemRows = kWaves * kWaveRows;  // query rows per work item
+  // Staged rows: bf16 pools stage rows as the MFMA code reads them (swizzled);
+  // FP8 pools stage their D-byte rows as they are, and each tile is widened
+  // once into the bf16 layout (skw / svw) for all waves.
+  constexpr int kSRow = KV8 ? D : C::kRowBytes;  // staged bytes per row
+  constexpr int kSCPR = kSRow / 16;              // 16-byte chunks per staged row
+  constexpr int kSKPI = 64 / kSCPR;              // staged rows per 64-lane load
+  constexpr int kSLoads = kBN / kSKPI / kWaves;  // loads per wave per tile, K and V each
   // Two stages of K and V tiles: the next tile streams into one stage while
   // the other is used.  Separate arrays let the compiler see that LDS reads of
   // one stage never wait on the loads still landing in the other.
-  __shared__ __attribute__((aligned(1024))) char sk0[C::kTile];
-  __shared__ __attribute__((aligned(1024))) char sv0[C::kTile];
-  __shared__ __attribute__((aligned(1024))) char sk1[C::kTile];
-  __shared__ __attribute__((aligned(1024))) char sv1[C::kTile];
+  __shared__ __attribute__((aligned(1024))) char sk0[kBN * kSRow];
+  __shared__ __attribute__((aligned(1024))) char sv0[kBN * kSRow];
+  __shared__ __attribute__((aligned(1024))) char sk1[kBN * kSRow];
+  __shared__ __attribute__((aligned(1024))) char sv1[kBN * kSRow];
+  __shared__ __attribute__((aligned(1024))) char skw[KV8 ? C::kTile : 16];
+  __shared__ __attribute__((aligned(1024))) char svw[KV8 ? C::kTile : 16];
   __shared__ uint32_t s_slot[kSeg];
 
   const int work = xcd_slice(blockIdx.x, gridDim.x);
@@ -147,9 +156,9 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
   const int w_end = (row0 + wave * kWaveRows) / G < E ? P + wj_last + 1 : 0;
 
   const int32_t* idx_row = req_to_token + int64_t(rpi ? rpi[b] : b) * stride;
-  const uint32_t pool_row = uint32_t(Hkv) * C::kRowBytes;
-  const char* kbase = k_pool + int64_t(kvh) * C::kRowBytes;
-  const char* vbase = v_pool + int64_t(kvh) * C::kRowBytes;
+  const uint32_t pool_row = uint32_t(Hkv) * kSRow;
+  const char* kbase = k_pool + int64_t(kvh) * kSRow;
+  const char* vbase = v_pool + int64_t(kvh) * kSRow;
 
   // Q^T operands (B of S^T = K Q^T): column r32 = query row, k = dims 16*ks + 8*hi + t.
   bf16x8 qop[RB][C::kKS];
@@ -182,21 +191,21 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
   // the swizzle stores at physical chunk i%kCPR.  Keys past kv_end are clamped
   // to the last valid key (masked later; a real row keeps the tile finite).
   // Slot indices come from s_slot, staged per segment of kSeg keys.
-  const int ld_row = lane / C::kCPR;
-  const int ld_pchunk = lane % C::kCPR;
+  const int ld_row = lane / kSCPR;
+  const int ld_pchunk = lane % kSCPR;
   int seg0 = 0;  // first key of the segment whose slot indices are in s_slot
   // Loads of one wave read the slot indices at s_slot[tile_key + krow]; the
   // staging pads the segment's last tile with the last valid key, so no clamp.
-  const int krow0 = C::kKPI * wave + ld_row;
-  // krow = krow0 + kWaves*kKPI*it, a multiple of 16 apart: same swizzle
-  const int lchunk = ld_pchunk ^ (swz_f(krow0) & (C::kCPR - 1));
+  const int krow0 = kSKPI * wave + ld_row;
+  // krow = krow0 + kWaves*kSKPI*it, a multiple of 16 apart: same swizzle
+  const int lchunk = KV8 ? ld_pchunk : ld_pchunk ^ (swz_f(krow0) & (C::kCPR - 1));
   const uint64_t lane_off = uint64_t(lchunk << 4);
   auto issue = [&](int tile, char* sk, char* sv) {
     const uint32_t* srow = s_slot + (tile * kBN - seg0) + krow0;
 #pragma unroll
-    for (int it = 0; it < C::kLoadsPerWave; ++it) {
-      const uint64_t off = uint64_t(srow[kWaves * C::kKPI * it]) * pool_row + lane_off;
-      const int dst = C::kKPI * (wave + kWaves * it) * C::kRowBytes;
+    for (int it = 0; it < kSLoads; ++it) {
+      const uint64_t off = uint64_t(srow[kWaves * kSKPI * it]) * pool_row + lane_off;
+      const int dst = kSKPI * (wave + kWaves * it) * kSRow;
       __builtin_amdgcn_global_load_lds(kbase + off, (__attribute__((address_space(3))) void*)(sk + dst), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vbase + off, (__attribute__((address_space(3))) void*)(sv + dst), 16, 0, 0);
     }
@@ -209,13 +218,35 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
   const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int tr_half = (lane & 1) * 8;
 
+  // FP8 pools: widen a staged tile into the swizzled bf16 layout, 16 codes
+  // (two bf16 chunks) per unit of work.
+  auto widen = [&](const char* s8, char* sw) {
+    for (int u = tid; u < kBN * kSCPR; u += 64 * kWaves) {
+      const int row = u / kSCPR, c = u - (u / kSCPR) * kSCPR;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(s8 + row * kSRow + 16 * c);
+      const u32x4 lo = {fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x), fp8x2_to_bf16x2<false>(w.y),
+                        fp8x2_to_bf16x2<true>(w.y)};
+      const u32x4 hi = {fp8x2_to_bf16x2<false>(w.z), fp8x2_to_bf16x2<true>(w.z), fp8x2_to_bf16x2<false>(w.w),
+                        fp8x2_to_bf16x2<true>(w.w)};
+      *reinterpret_cast<u32x4*>(sw + swz<D>(row, 2 * c)) = lo;
+      *reinterpret_cast<u32x4*>(sw + swz<D>(row, 2 * c + 1)) = hi;
+    }
+  };
+
   // One tile: barrier (this tile's loads have landed everywhere and the other
   // stage is free), start the next tile's loads into the other stage, then
-  // compute from this one.
+  // compute from this one (FP8: widen it first, then a second barrier).
   int seg_end = 0;  // tiles below seg_end have their slot indices staged
   auto step = [&](int tile, const char* sk, const char* sv, char* sk_next, char* sv_next) {
     __syncthreads();
     if (tile + 1 < seg_end) issue(tile + 1, sk_next, sv_next);
+    if constexpr (KV8) {
+      widen(sk, skw);
+      widen(sv, svw);
+      __syncthreads();
+      sk = skw;
+      sv = svw;
+    }
     const int base = tile * kBN;
     if (base >= w_end) return;                // wave-uniform: every row of this wave is done
 
@@ -330,7 +361,7 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
   for (int rb = 0; rb < RB; ++rb) {
     const float lsum = l[rb] + __shfl_xor(l[rb], 32, 64);
     if (!row_ok[rb]) continue;
-    const float inv = 1.f / lsum;
+    const float inv = (KV8 ? v_scale : 1.f) / lsum;
     const int64_t tok = int64_t(qo_indptr[b]) + jrow[rb];
     char* op = o + (tok * Hq + int64_t(kvh) * G + grow[rb]) * C::kRowBytes;
 #pragma unroll
@@ -393,7 +424,56 @@ __global__ void __launch_bounds__(64) extend_f32(const float* __restrict__ q, fl
   for (int i = 0; i < PER; ++i) o[qo * D + lane + 64 * i] = acc[i] * inv;
 }
 
+template <bool KV8>
+int launch_extend_bf16(const void* q, void* o, const void* k_pool, const void* v_pool, const int32_t* req_to_token,
+                       int32_t req_to_token_stride, const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                       const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch, int32_t max_extend_len,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale_log2, float v_scale,
+                       hipStream_t st) {
+  const int G = num_q_heads / num_kv_heads;
+  const int64_t item_rows = kWaves * 32 * kRB;
+  const int64_t n_qt = (int64_t(max_extend_len) * G + item_rows - 1) / item_rows;
+  const int64_t grid = n_qt * batch * num_kv_heads;
+  if (grid > INT32_MAX) return rt::fail(RT_ERR_INVALID, "radix_extend_attention: grid too large");
+  if (head_dim == 128)
+    hipLaunchKernelGGL((extend_bf16<128, kRB, KV8>), dim3(uint32_t(grid)), dim3(64 * kWaves), 0, st,
+                       (const char*)q, (char*)o, (const char*)k_pool, (const char*)v_pool, req_to_token,
+                       int64_t(req_to_token_stride), req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch,
+                       num_q_heads, num_kv_heads, G, int(n_qt), scale_log2, v_scale);
+  else
+    hipLaunchKernelGGL((extend_bf16<64, kRB, KV8>), dim3(uint32_t(grid)), dim3(64 * kWaves), 0, st,
+                       (const char*)q, (char*)o, (const char*)k_pool, (const char*)v_pool, req_to_token,
+                       int64_t(req_to_token_stride), req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch,
+                       num_q_heads, num_kv_heads, G, int(n_qt), scale_log2, v_scale);
+  return RT_OK;
+}
+
 }  // namespace
+
+extern "C" int radix_extend_attention_fp8kv(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                            const int32_t* req_to_token, int32_t req_to_token_stride,
+                                            const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                            const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
+                                            int32_t max_extend_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, float sm_scale, float k_scale, float v_scale,
+                                            void* stream) {
+  if (batch < 0 || max_extend_len < 0 || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_q_heads % num_kv_heads != 0 || (head_dim != 64 && head_dim != 128) || req_to_token_stride < 1 ||
+      !(sm_scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
+    return rt::fail(RT_ERR_INVALID, "radix_extend_attention_fp8kv: bad shape, stride or scale");
+  if (batch == 0 || max_extend_len == 0) return RT_OK;
+  if (!q || !o || !k_pool || !v_pool || !req_to_token || !prefix_lens || !extend_lens || !qo_indptr)
+    return rt::fail(RT_ERR_INVALID, "radix_extend_attention_fp8kv: null pointer");
+  const int rc = launch_extend_bf16<true>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices,
+                                          prefix_lens, extend_lens, qo_indptr, batch, max_extend_len, num_q_heads,
+                                          num_kv_heads, head_dim, sm_scale * k_scale * kLog2e, v_scale,
+                                          (hipStream_t)stream);
+  if (rc != RT_OK) return rc;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return rt::fail(RT_ERR_HIP, std::string("radix_extend_attention_fp8kv launch: ") + hipGetErrorString(e));
+  return RT_OK;
+}
 
 extern "C" int radix_extend_attention(const void* q, void* o, const void* k_pool, const void* v_pool,
                                       const int32_t* req_to_token, int32_t req_to_token_stride,
@@ -412,20 +492,11 @@ extern "C" int radix_extend_attention(const void* q, void* o, const void* k_pool
   const float scale_log2 = sm_scale * kLog2e;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == RT_BF16) {
-    const int64_t item_rows = kWaves * 32 * kRB;
-    const int64_t n_qt = (int64_t(max_extend_len) * G + item_rows - 1) / item_rows;
-    const int64_t grid = n_qt * batch * num_kv_heads;
-    if (grid > INT32_MAX) return rt::fail(RT_ERR_INVALID, "radix_extend_attention: grid too large");
-    if (head_dim == 128)
-      hipLaunchKernelGGL((extend_bf16<128, kRB>), dim3(uint32_t(grid)), dim3(64 * kWaves), 0, st, (const char*)q, (char*)o,
-                         (const char*)k_pool, (const char*)v_pool, req_to_token, int64_t(req_to_token_stride),
-                         req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch, num_q_heads, num_kv_heads,
-                         G, int(n_qt), scale_log2);
-    else
-      hipLaunchKernelGGL((extend_bf16<64, kRB>), dim3(uint32_t(grid)), dim3(64 * kWaves), 0, st, (const char*)q, (char*)o,
-                         (const char*)k_pool, (const char*)v_pool, req_to_token, int64_t(req_to_token_stride),
-                         req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch, num_q_heads, num_kv_heads,
-                         G, int(n_qt), scale_log2);
+    const int rc = launch_extend_bf16<false>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride,
+                                             req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch,
+                                             max_extend_len, num_q_heads, num_kv_heads, head_dim, scale_log2, 1.f,
+                                             st);
+    if (rc != RT_OK) return rc;
   } else {
     if (max_extend_len > 65535 * 16 || num_q_heads > 65535 || batch > 65535)
       return rt::fail(RT_ERR_INVALID, "radix_extend_attention: fp32 grid too large");

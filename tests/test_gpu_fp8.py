@@ -1,6 +1,6 @@
 """FP8 (E4M3) K/V pools on the GPU: the store kernel against the oracle's
-codes bit for bit, and decode attention over FP8 pools against float64
-attention on the values those codes stand for."""
+codes bit for bit, and extend and decode attention over FP8 pools against
+float64 attention on the values those codes stand for."""
 
 import numpy as np
 import pytest
@@ -84,3 +84,41 @@ def test_decode_fp8_rejects_bad_scale():
     ws = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
     with pytest.raises(B.RadixRTError):
         B.radix_decode_attention_fp8kv(q, q.clone(), pool, pool, r2t, None, i32([0]), 1, 0.1, ws, 0.0, 1.0)
+
+
+FP8_EXTEND_CASES = [
+    # (prefix_lens, extend_lens, hq, hkv, d, k_scale, v_scale)
+    ([0, 5, 70, 130], [200, 1, 63, 129], 32, 8, 128, 1.0, 1.0),
+    ([1024, 1024], [128, 77], 32, 8, 128, 0.5, 2.0),
+    ([10, 200, 0], [90, 45, 130], 12, 4, 64, 1.0, 0.25),
+    ([50, 3], [0, 70], 32, 8, 128, 3.0, 1.0),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(FP8_EXTEND_CASES)))
+def test_extend_fp8_matches_oracle(ci):
+    prefix_lens, extend_lens, hq, hkv, d, ks, vs = FP8_EXTEND_CASES[ci]
+    _announce(f"extend fp8 case {ci}: P={prefix_lens} E={extend_lens} hq={hq} hkv={hkv} d={d} scales {ks} {vs}")
+    rng = np.random.default_rng(700 + ci)
+    case = make_pool_case(rng, prefix_lens, extend_lens, hq, hkv, d, "bf16")
+    kc, vc = store_codes(case["kpool"], ks), store_codes(case["vpool"], vs)
+    q_host = host_values(rng, (sum(extend_lens), hq, d), "bf16")
+    qo = np.zeros(len(prefix_lens) + 1, dtype=np.int32)
+    qo[1:] = np.cumsum(extend_lens)
+    q = to_dev(q_host, "bf16")
+    o = torch.full_like(q, float("nan"))
+    B.radix_extend_attention_fp8kv(q, o, torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda(), i32(case["r2t"]),
+                                   i32(case["rows"]), i32(prefix_lens), i32(extend_lens), i32(qo), max(extend_lens),
+                                   1.0 / np.sqrt(d), ks, vs)
+    torch.cuda.synchronize()
+    kvals, vvals = dequantize(kc, ks), dequantize(vc, vs)
+    off, worst = 0, 0.0
+    for b, (p, e) in enumerate(zip(prefix_lens, extend_lens)):
+        if e == 0:
+            continue
+        sl = case["r2t"][case["rows"][b], :p + e]
+        want = oracle_rows(q_host[off:off + e], kvals[sl], vvals[sl], np.arange(p, p + e), 1.0 / np.sqrt(d))
+        worst = max(worst, max_err(o[off:off + e], want))
+        off += e
+    print(f"  max abs err {worst:.3e}")
+    assert worst <= 2e-2
