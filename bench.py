@@ -68,7 +68,7 @@ def parse():
     ap.add_argument("--policy", default="fcfs", choices=["fcfs", "lspf"],
                     help="admission order of the chat workload's scheduler")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
-                    help="K/V pool format of the decode workloads (fp8 = OCP E4M3, scales 1)")
+                    help="K/V pool format (fp8 = OCP E4M3 codes, scales 1)")
     ap.add_argument("--chunk-size", type=int, default=None,
                     help="chunked prefill for the chat workload: extend tokens per scheduler iteration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -83,7 +83,8 @@ class FewShotBench:
     SLOTS = 262144
     SEED = 1
 
-    def __init__(self, n_batches, torch, B_mod, gen_t):
+    def __init__(self, n_batches, torch, B_mod, gen_t, kv_dtype="bf16"):
+        self.fp8 = kv_dtype == "fp8"
         self.torch = torch
         self.Bm = B_mod
         self.gen_t = gen_t
@@ -97,7 +98,8 @@ class FewShotBench:
         bf16 = torch.bfloat16
         self.pool = B_mod.rt_pool_create(self.SLOTS)
         self.tree = B_mod.rt_tree_create(self.pool)
-        self.k_pool = torch.zeros((self.SLOTS + 1, self.HKV, self.D), dtype=bf16, device=self.dev)
+        pool_dt = torch.uint8 if self.fp8 else bf16
+        self.k_pool = torch.zeros((self.SLOTS + 1, self.HKV, self.D), dtype=pool_dt, device=self.dev)
         self.v_pool = torch.zeros_like(self.k_pool)
         # two row sets of 64 so that host writes for step i+1 never touch rows still being copied for step i
         self.r2t_host_t = torch.zeros((2 * self.B, self.stride), dtype=torch.int32, pin_memory=True)
@@ -158,13 +160,22 @@ class FewShotBench:
         with torch.cuda.stream(self.stream):
             self.r2t_dev[0, :self.PREFIX].copy_(self.r2t_host_t[0, :self.PREFIX])
             dloc = torch.from_numpy(loc).to(self.dev)
-            Bm.kv_store(self.k_pool, self.v_pool, k, v, dloc, stream=self.stream)
+            self._store(k, v, dloc)
             o = torch.empty_like(q)
             meta = torch.tensor([0, self.PREFIX, 0, self.PREFIX, 0], dtype=torch.int32, device=self.dev)
-            Bm.radix_extend_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, meta[4:5], meta[0:1], meta[1:2],
-                                      meta[2:4], self.PREFIX, self.sm_scale, stream=self.stream)
+            self._extend(q, o, meta[4:5], meta[0:1], meta[1:2], meta[2:4], self.PREFIX)
         self.stream.synchronize()
         Bm.rt_finish_batch(self.tree, toks, off, self.r2t_host, rows, pl, nodes)
+
+    def _store(self, k, v, loc):
+        if self.fp8:
+            self.Bm.kv_store_fp8(self.k_pool, self.v_pool, k, v, loc, stream=self.stream)
+        else:
+            self.Bm.kv_store(self.k_pool, self.v_pool, k, v, loc, stream=self.stream)
+
+    def _extend(self, q, o, rows, pl, el, qo, max_e):
+        f = self.Bm.radix_extend_attention_fp8kv if self.fp8 else self.Bm.radix_extend_attention
+        f(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows, pl, el, qo, max_e, self.sm_scale, stream=self.stream)
 
     def step(self, i, timed):
         torch, Bm = self.torch, self.Bm
@@ -209,23 +220,23 @@ class FewShotBench:
             self.copy_done[rs] = ev
             d_pl, d_el, d_qo, d_rows = md[0:B], md[B:2 * B], md[2 * B:3 * B + 1], md[3 * B + 1:4 * B + 1]
             d_dslots, d_loc = md[4 * B + 1:5 * B + 1], md[base:base + B * S]
-            Bm.kv_store(self.k_pool, self.v_pool, k, v, d_loc, stream=self.stream)
+            self._store(k, v, d_loc)
             if timed:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(self.stream)
-            Bm.radix_extend_attention(q, self.o_ext, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pl, d_el, d_qo,
-                                      int(el.max()), self.sm_scale, stream=self.stream)
+            self._extend(q, self.o_ext, d_rows, d_pl, d_el, d_qo, int(el.max()))
             if timed:
                 e1.record(self.stream)
                 self.ext_events.append((e0, e1))
             d_pos = self.pos_dev
             Bm.req_to_token_scatter(self.r2t_dev, d_rows, d_pos, d_dslots, stream=self.stream)
-            Bm.kv_store(self.k_pool, self.v_pool, kd, vd, d_dslots, stream=self.stream)
+            self._store(kd, vd, d_dslots)
             if timed:
                 e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e2.record(self.stream)
-            Bm.radix_decode_attention(qd, self.o_dec, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pos,
-                                      P0 + S + 1, self.sm_scale, self.ws, stream=self.stream)
+            dec = Bm.radix_decode_attention_fp8kv if self.fp8 else Bm.radix_decode_attention
+            dec(qd, self.o_dec, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pos, P0 + S + 1, self.sm_scale,
+                self.ws, stream=self.stream)
             if timed:
                 e3.record(self.stream)
                 self.dec_events.append((e2, e3))
@@ -239,7 +250,8 @@ class FewShotBench:
             self.flops.append(4.0 * self.D * self.HQ * rows_keys)
             self.ext_tokens.append(int(el.sum()) + B)
             kv_len = P0 + S + 1
-            self.dec_bytes.append(B * kv_len * (self.HKV * self.D * 2 * 2 + 4) + 2 * B * self.HQ * self.D * 2)
+            eb = 1 if self.fp8 else 2
+            self.dec_bytes.append(B * kv_len * (self.HKV * self.D * eb * 2 + 4) + 2 * B * self.HQ * self.D * 2)
         return int(el.sum()) + B
 
 
@@ -247,7 +259,7 @@ def run_few_shot(args, torch):
     from prefix_shared_kv_rt_amd import binding as Bm
     from synth import torch_gen
     n = args.warmup + args.steps
-    fb = FewShotBench(n, torch, Bm, torch_gen)
+    fb = FewShotBench(n, torch, Bm, torch_gen, kv_dtype=args.kv_dtype)
     fb.gen_inputs(n)
     fb.warm_prefix()
     for i in range(args.warmup):
@@ -288,15 +300,17 @@ def run_few_shot(args, torch):
                         "distinct tokens) per step, one extend pass + one decode step, tree match/insert on host",
             "batch": fb.B, "prefix_len": fb.PREFIX, "suffix_len": fb.SUFFIX, "num_q_heads": fb.HQ,
             "num_kv_heads": fb.HKV, "head_dim": fb.D, "pool_slots": fb.SLOTS,
+            "kv_dtype": "fp8_e4m3" if fb.fp8 else "bf16",
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "radix_extend_attention (extend_bf16<128>)",
+            "kernel": "radix_extend_attention_fp8kv (extend_bf16<128, 1, true>)" if fb.fp8 else
+                      "radix_extend_attention (extend_bf16<128, 1, false>)",
             "achieved": achieved_tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved_tflops / PEAK_BF16_TFLOPS,
-            "traffic": profiled_traffic("extend_bf16"),
+            "traffic": None if fb.fp8 else profiled_traffic("extend_bf16"),
             "flops_per_launch": flops_avg,
             "avg_launch_us": ext_avg_s * 1e6,
         },

@@ -48,6 +48,8 @@ class DecodeGraphs:
     def __init__(self, rt, max_batch=None, batch_sizes=None):
         if rt.device is None:
             raise ValueError("decode graphs need a device runtime")
+        if rt.kv_fp8_scales:
+            raise ValueError("decode graphs run over bf16 pools")
         if rt.max_reqs - 1 in rt.free_rows:
             rt.free_rows.remove(rt.max_reqs - 1)
         else:

@@ -50,13 +50,17 @@ from . import binding as B
 class RadixRuntime:
     """device=None runs the host half only (tree, pool, slot table): the
     device steps are skipped and return None.  Used to check host decisions
-    on machines without a GPU."""
+    on machines without a GPU.  ``kv_fp8_scales=(k_scale, v_scale)`` keeps the
+    K/V pools in FP8 (E4M3 codes, uint8) under bf16 queries and outputs."""
 
     def __init__(self, num_slots, num_q_heads, num_kv_heads, head_dim, dtype, max_reqs, max_ctx,
-                 device="cuda", stream=None):
+                 device="cuda", stream=None, kv_fp8_scales=None):
         self.num_slots = int(num_slots)
         self.hq, self.hkv, self.d = int(num_q_heads), int(num_kv_heads), int(head_dim)
         self.dtype = dtype
+        if kv_fp8_scales is not None and dtype not in (None, torch.bfloat16):
+            raise ValueError("FP8 pools run under bf16 queries")
+        self.kv_fp8_scales = None if kv_fp8_scales is None else (float(kv_fp8_scales[0]), float(kv_fp8_scales[1]))
         self.max_reqs, self.max_ctx = int(max_reqs), int(max_ctx)
         self.pool = B.rt_pool_create(self.num_slots)
         self.tree = B.rt_tree_create(self.pool)
@@ -69,7 +73,8 @@ class RadixRuntime:
             return
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         # Slot 0 stays zero: padded writes land there and it is never read as data.
-        self.k_pool = torch.zeros((self.num_slots + 1, self.hkv, self.d), dtype=dtype, device=self.device)
+        pool_dtype = torch.uint8 if self.kv_fp8_scales else dtype
+        self.k_pool = torch.zeros((self.num_slots + 1, self.hkv, self.d), dtype=pool_dtype, device=self.device)
         self.v_pool = torch.zeros_like(self.k_pool)
         self.r2t_host_t = torch.zeros((self.max_reqs, self.max_ctx), dtype=torch.int32, pin_memory=True)
         self.r2t_host = self.r2t_host_t.numpy()
@@ -102,6 +107,13 @@ class RadixRuntime:
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._ws
 
+    def _store(self, k_new, v_new, loc):
+        """Write new K/V rows at pool slots, in the pool's format."""
+        if self.kv_fp8_scales:
+            B.kv_store_fp8(self.k_pool, self.v_pool, k_new, v_new, loc, *self.kv_fp8_scales, stream=self.stream)
+        else:
+            B.kv_store(self.k_pool, self.v_pool, k_new, v_new, loc, stream=self.stream)
+
     def upload_rows(self, rows, lens):
         """Copy the first lens[i] entries of host rows rows[i] to the device table."""
         if self.device is None:
@@ -121,7 +133,7 @@ class RadixRuntime:
             loc = self._to_dev(out_cache_loc)
             if loc.numel() > 0:
                 e0 = self._event() if self.events is not None else None
-                B.kv_store(self.k_pool, self.v_pool, k_new, v_new, loc, stream=self.stream)
+                self._store(k_new, v_new, loc)
                 if e0 is not None:
                     self.events.append(("kv_store", e0, self._event(), {"rows": int(loc.numel())}))
             if not attention or loc.numel() == 0:
@@ -131,8 +143,13 @@ class RadixRuntime:
             o = torch.empty_like(q)
             args = (self._to_dev(rows), self._to_dev(prefix_lens), self._to_dev(extend_lens), self._to_dev(qo))
             e0 = self._event() if self.events is not None else None
-            B.radix_extend_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, *args,
-                                     int(max(extend_lens)), self.sm_scale, stream=self.stream)
+            if self.kv_fp8_scales:
+                B.radix_extend_attention_fp8kv(q, o, self.k_pool, self.v_pool, self.r2t_dev, *args,
+                                               int(max(extend_lens)), self.sm_scale, *self.kv_fp8_scales,
+                                               stream=self.stream)
+            else:
+                B.radix_extend_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, *args,
+                                         int(max(extend_lens)), self.sm_scale, stream=self.stream)
             if e0 is not None:
                 pl = np.asarray(prefix_lens, dtype=np.float64)
                 el = np.asarray(extend_lens, dtype=np.float64)
@@ -151,10 +168,16 @@ class RadixRuntime:
             max_kv = int(max(positions)) + 1
             ws = self.workspace(n, max_kv)
             e0 = self._event() if self.events is not None else None
-            B.decode_append(self.r2t_dev, rows_d, pos_d, slots_d, self.k_pool, self.v_pool, k_new, v_new,
-                            stream=self.stream)
-            B.radix_decode_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, max_kv,
-                                     self.sm_scale, ws, stream=self.stream)
+            if self.kv_fp8_scales:
+                B.req_to_token_scatter(self.r2t_dev, rows_d, pos_d, slots_d, stream=self.stream)
+                self._store(k_new, v_new, slots_d)
+                B.radix_decode_attention_fp8kv(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, max_kv,
+                                               self.sm_scale, ws, *self.kv_fp8_scales, stream=self.stream)
+            else:
+                B.decode_append(self.r2t_dev, rows_d, pos_d, slots_d, self.k_pool, self.v_pool, k_new, v_new,
+                                stream=self.stream)
+                B.radix_decode_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, max_kv,
+                                         self.sm_scale, ws, stream=self.stream)
             if e0 is not None:
                 kv = np.asarray(positions, dtype=np.float64) + 1
                 eb = q.element_size()

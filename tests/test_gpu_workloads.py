@@ -19,9 +19,9 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
 def run_both(wl, want=None, max_running=256, max_extend_tokens=16384, max_reqs=None, policy="fcfs", graphs=False,
-             chunk_size=None):
+             chunk_size=None, kv_fp8_scales=None):
     ora = run_workload(wl, want=want, max_running=max_running, max_extend_tokens=max_extend_tokens, policy=policy,
-                       chunk_size=chunk_size)
+                       chunk_size=chunk_size, kv_fp8_scales=kv_fp8_scales)
     outs = {}
 
     def record(kind, rid, step, o):
@@ -29,7 +29,7 @@ def run_both(wl, want=None, max_running=256, max_extend_tokens=16384, max_reqs=N
             outs[(kind, rid, step)] = o.float().cpu().numpy()
 
     rt = RadixRuntime(wl.num_slots, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, TORCH_DT[wl.dtype],
-                      max_reqs or max(max_running, 8), wl.max_ctx)
+                      max_reqs or max(max_running, 8), wl.max_ctx, kv_fp8_scales=kv_fp8_scales)
     src = QKVSource(wl.seed, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, TORCH_DT[wl.dtype])
     dg = DecodeGraphs(rt, max_batch=max_running) if graphs else None
     sch = Scheduler(rt, wl.requests, src, max_running=max_running, max_extend_tokens=max_extend_tokens,
@@ -131,3 +131,15 @@ def test_chunked_prefill_few_shot_bf16():
     check_host_identical(ora, sch, dump, free)
     check_outputs(ora, outs, TOL["bf16"])
     assert max(len(it["chunks"]) for it in ora.iterations) > 1
+
+
+@pytest.mark.parametrize("scales", [(1.0, 1.0), (0.5, 2.0)])
+def test_small_chat_fp8_pool(scales):
+    """The small chat workload with FP8 pools: host decisions as with bf16,
+    attention against the oracle over the values the FP8 pool holds."""
+    print(f"chat (6 sessions x 3 turns, pool 60%, fp8 pool {scales})", flush=True)
+    wl = workloads.chat(sessions=6, turns=3, system_len=64, user_lo=16, user_hi=48, gen_len=6)
+    sel = lambda kind, rid, step: kind == "ext" or step in (0, 5)
+    ora, sch, outs, dump, free = run_both(wl, want=sel, max_running=4, max_extend_tokens=128, kv_fp8_scales=scales)
+    check_host_identical(ora, sch, dump, free)
+    check_outputs(ora, outs, TOL["bf16"])
