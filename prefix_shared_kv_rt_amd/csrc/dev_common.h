@@ -56,6 +56,18 @@ __device__ __forceinline__ bf16x4 as_bf16x4(u32x2 v) { return __builtin_bit_cast
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// max(x, x of lane ^ 32) with one v_permlane32_swap (no LDS round trip).
+__device__ __forceinline__ float max_lane_pair(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// acc + lo + hi of a packed bfloat16 pair (v_dot2_f32_bf16 against {1, 1}).
+__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w), __builtin_bit_cast(bf16x2v, 0x3f803f80u), acc,
+                                         false);
+}
+
 __device__ __forceinline__ floatx4 mfma_16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -22,7 +22,12 @@
 //     as MFMA rows, each lane owns one query row, so the softmax max/sum
 //     need only one cross-lane exchange (lane ^ 32).
 //   * Online softmax in the log2 domain with a lazy rescale: the running max
-//     moves only when a tile's max exceeds it by more than 2^8.
+//     moves only when a tile's max exceeds it by more than 2^8.  Q is
+//     multiplied by scale * log2(e) once (and rounded back to bf16), and the
+//     score accumulators start at -m instead of 0, so the MFMA hands back
+//     scores already shifted by the running max and each probability costs
+//     one v_exp_f32.  Row sums add the bf16-rounded probabilities that the
+//     P V product uses, two per v_dot2_f32_bf16.
 //   * O^T += V^T P^T with the same MFMA.  P^T comes straight from the score
 //     registers (the key order of the contraction is chosen to match the
 //     score layout); V^T operands come from LDS through gfx950's transpose
@@ -167,8 +172,13 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
     const int64_t tok = int64_t(qo_indptr[b]) + jrow[rb];
     const char* qp = q + (tok * Hq + int64_t(kvh) * G + grow[rb]) * C::kRowBytes + hi * 16;
 #pragma unroll
-    for (int ks = 0; ks < C::kKS; ++ks)
-      qop[rb][ks] = as_bf16x8(row_ok[rb] ? ld16(qp + ks * 32) : u32x4{0, 0, 0, 0});
+    for (int ks = 0; ks < C::kKS; ++ks) {
+      const u32x4 w = row_ok[rb] ? ld16(qp + ks * 32) : u32x4{0, 0, 0, 0};
+      u32x4 s;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = pack_bf16x2(bf16_lo(w[i]) * scale_log2, bf16_hi(w[i]) * scale_log2);
+      qop[rb][ks] = as_bf16x8(s);
+    }
   }
 
   floatx16 oacc[RB][C::kR];
@@ -178,12 +188,20 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
     for (int r = 0; r < C::kR; ++r)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[rb][r][i] = 0.f;
+  // Scores come out of the MFMA already shifted by the running max: the
+  // accumulator starts at cm = -m (all 16 entries of a lane belong to one
+  // query row), so p = exp2(acc) needs no per-score arithmetic.  m starts at
+  // 0 with the first computed tile forced through the rescale path.
   float m[RB], l[RB];
+  floatx16 cm[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    m[rb] = -INFINITY;
+    m[rb] = 0.f;
     l[rb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cm[rb][i] = 0.f;
   }
+  bool first = true;  // wave-uniform
 
   // Tile loads go straight from HBM to LDS (global_load_lds_dwordx4): one
   // 64-lane load fills kKPI consecutive rows (1 KiB).  Wave w issues loads
@@ -210,6 +228,13 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
       __builtin_amdgcn_global_load_lds(vbase + off, (__attribute__((address_space(3))) void*)(sv + dst), 16, 0, 0);
     }
   };
+
+  // K operand sources of this lane: key r32 of a 32-key block (+32 rows per
+  // block), 16-byte chunk 2*ks + hi under the swizzle (which depends only on
+  // the key's low 4 bits).
+  int kofs[C::kKS];
+#pragma unroll
+  for (int ks = 0; ks < C::kKS; ++ks) kofs[ks] = swz<D>(r32, 2 * ks + hi);
 
   // V transpose-read source of this lane: lane s = lane%16 of group gr = lane/16
   // addresses key 4*(gr/2) + s/4 and the 4-dim run at dims 16*(gr%2) + 4*(s%4)
@@ -258,20 +283,18 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
       u32x4 ka[C::kKS];
 #pragma unroll
       for (int ks = 0; ks < C::kKS; ++ks)
-        ka[ks] = *reinterpret_cast<const u32x4*>(sk + swz<D>(kb * 32 + r32, 2 * ks + hi));
+        ka[ks] = *reinterpret_cast<const u32x4*>(sk + kb * 32 * C::kRowBytes + kofs[ks]);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
+        sacc[rb][kb] = mfma_32x32x16(as_bf16x8(ka[0]), qop[rb][0], cm[rb]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[rb][kb][i] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < C::kKS; ++ks)
+        for (int ks = 1; ks < C::kKS; ++ks)
           sacc[rb][kb] = mfma_32x32x16(as_bf16x8(ka[ks]), qop[rb][ks], sacc[rb][kb]);
       }
     }
     // Lane holds keys base + 32*kb + 8*(v/4) + 4*hi + (v%4) of its query rows.
     // Only tiles that cross this wave's diagonal (or its last key) need a mask.
     const bool masked = base + kBN - 1 > w_min_limit;
-    float neg_m[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if (masked) {
@@ -282,28 +305,35 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
           for (int v = 0; v < 16; ++v)
             if (rel + 32 * kb + 8 * (v >> 2) + (v & 3) > 0) sacc[rb][kb][v] = -INFINITY;
       }
-      float mx = -INFINITY;
+      float mx = sacc[rb][0][0];
 #pragma unroll
       for (int kb = 0; kb < C::kKB; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[rb][kb][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        for (int v = (kb == 0); v < 16; ++v) mx = fmaxf(mx, sacc[rb][kb][v]);
+      mx = max_lane_pair(mx);  // row max of the tile minus m
       // Lazy rescale: the reference max m only moves when some row's max
       // exceeds it by more than 2^kSlack, so probabilities stay <= 2^kSlack
       // (harmless in fp32 and bf16) and the accumulator rescale is rare.
-      const float m_tile = mx * scale_log2;
-      if (__any(m_tile > m[rb] + kSlack)) {
-        const float m_new = fmaxf(m[rb], m_tile);
-        const float alpha = __builtin_amdgcn_exp2f(m[rb] - m_new);
+      if (first || __any(mx > kSlack)) {
+        const float m_old = first ? -INFINITY : m[rb];
+        const float m_new = fmaxf(m_old, m[rb] + mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
+        const float shift = m_new - m[rb];
         l[rb] *= alpha;
 #pragma unroll
         for (int r = 0; r < C::kR; ++r)
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[rb][r][i] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sacc[rb][kb][v] -= shift;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) cm[rb][i] = -m_new;
         m[rb] = m_new;
       }
-      neg_m[rb] = -m[rb];
     }
+    first = false;
 
     // ---- O^T += V^T P^T, 16 keys per MFMA; each V operand read feeds the
     // wave's RB row blocks
@@ -325,10 +355,11 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
         for (int rb = 0; rb < RB; ++rb) {
           float p[8];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) p[t] = __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][8 * sh + t], scale_log2, neg_m[rb]));
+          for (int t = 0; t < 8; ++t) p[t] = __builtin_amdgcn_exp2f(sacc[rb][kb][8 * sh + t]);
           const u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+          // row sum of the rounded probabilities the MFMA uses
 #pragma unroll
-          for (int t = 0; t < 8; ++t) l[rb] += p[t];
+          for (int t = 0; t < 4; ++t) l[rb] = sum_bf16x2(pk[t], l[rb]);
           const bf16x8 pop = as_bf16x8(pk);
 #pragma unroll
           for (int dt = 0; dt < C::kR; ++dt)
