@@ -111,6 +111,8 @@ class FewShotBench:
         self.meta_host = self.meta_host_t.numpy()
         self.meta_dev = torch.zeros((2, self.meta_n), dtype=torch.int32, device=self.dev)
         self.copy_done = [None, None]
+        self.rows = [np.arange(rs * self.B, rs * self.B + self.B, dtype=np.int32) for rs in range(2)]
+        self.dec_pos = np.full(self.B, self.PREFIX + self.SUFFIX, dtype=np.int32)
         self.ws = torch.empty(B_mod.radix_decode_workspace_bytes(self.B, self.HQ, self.HKV, self.D, self.stride),
                               dtype=torch.uint8, device=self.dev)
         self.o_ext = torch.empty((self.B * self.SUFFIX, self.HQ, self.D), dtype=bf16, device=self.dev)
@@ -122,6 +124,7 @@ class FewShotBench:
         self.flops = []
         self.ext_tokens = []
         self.dec_bytes = []
+        self.host_s = []
 
     def gen_inputs(self, n_batches):
         """Q/K/V of every suffix position and of the generated token, in HBM."""
@@ -130,6 +133,10 @@ class FewShotBench:
         bf16 = torch.bfloat16
         ph = prefix_hashes_rows_np(self.prefix[None, :], [chain_start(self.SEED)])
         self.inputs = []
+        self.tokens = []
+        n = self.PREFIX + self.SUFFIX
+        self.tok_off = np.arange(0, self.B * n + 1, n, dtype=np.int64)
+        self.full_off = np.arange(0, self.B * (n + 1) + 1, n + 1, dtype=np.int64)
         for i in range(n_batches):
             hn = prefix_hashes_rows_np(self.suffix[i], np.full(self.B, ph[0, -1], dtype=np.uint64))
             h = torch.from_numpy(hn.view(np.int64)).to(self.dev)    # [64, 129]
@@ -141,6 +148,11 @@ class FewShotBench:
             kd = T.qkv_values_t(hd, 2, range(self.HKV), self.D, self.SEED, bf16)
             vd = T.qkv_values_t(hd, 3, range(self.HKV), self.D, self.SEED, bf16)
             self.inputs.append((q, k, v, qd, kd, vd))
+            # the batch's token ids as the requests arrive: prompts, then prompts + generated token
+            prompts = np.concatenate([np.broadcast_to(self.prefix, (self.B, self.PREFIX)),
+                                      self.suffix[i][:, :self.SUFFIX]], axis=1)
+            full = np.concatenate([prompts, self.suffix[i][:, self.SUFFIX:self.SUFFIX + 1]], axis=1)
+            self.tokens.append((prompts.reshape(-1).copy(), full.reshape(-1).copy()))
         torch.cuda.synchronize()
 
     def warm_prefix(self):
@@ -178,17 +190,16 @@ class FewShotBench:
         f(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows, pl, el, qo, max_e, self.sm_scale, stream=self.stream)
 
     def step(self, i, timed):
+        t_host = time.perf_counter()
         torch, Bm = self.torch, self.Bm
         B, S, P0 = self.B, self.SUFFIX, self.PREFIX
         q, k, v, qd, kd, vd = self.inputs[i]
         rs = i % 2
         if self.copy_done[rs] is not None:
             self.copy_done[rs].synchronize()       # host staging of this row set is free again
-        rows = np.arange(rs * B, rs * B + B, dtype=np.int32)
-        prompts = np.concatenate([np.broadcast_to(self.prefix, (B, P0)), self.suffix[i][:, :S]], axis=1)
-        toks = prompts.reshape(-1)
-        off = np.arange(0, B * (P0 + S) + 1, P0 + S, dtype=np.int64)
-        pl, el, nodes, loc = Bm.rt_admit_batch(self.tree, toks, off, self.r2t_host, rows)
+        rows = self.rows[rs]
+        toks, full = self.tokens[i]
+        pl, el, nodes, loc = Bm.rt_admit_batch(self.tree, toks, self.tok_off, self.r2t_host, rows)
         if int(pl.min()) < P0:
             raise RuntimeError("the shared prefix left the cache; the pool is too small for this run")
         # scatter targets: already-cached suffix rows go to the dummy slot 0
@@ -200,16 +211,13 @@ class FewShotBench:
         meta[3 * B] = B * S
         meta[3 * B + 1:4 * B + 1] = rows
         base = 5 * B + 1
-        pad = np.zeros(B * S, dtype=np.int32)
-        o = 0
-        for b in range(B):
-            e = int(el[b])
-            pad[b * S + S - e:(b + 1) * S] = loc[o:o + e]
-            o += e
-        meta[base:base + B * S] = pad
+        # request b's new rows are the last el[b] of its S rows; the rest write slot 0
+        pad = meta[base:base + B * S]
+        pad[:] = 0
+        starts = np.arange(B, dtype=np.int64) * S + S - el
+        pad[np.repeat(starts - (np.cumsum(el) - el), el) + np.arange(loc.size)] = loc
         # one decode slot per request, at position P0 + S
-        pos = np.full(B, P0 + S, dtype=np.int32)
-        dslots = Bm.rt_decode_slots_batch(self.tree, rows, pos, self.r2t_host)
+        dslots = Bm.rt_decode_slots_batch(self.tree, rows, self.dec_pos, self.r2t_host)
         meta[4 * B + 1:5 * B + 1] = dslots
         md = self.meta_dev[rs]
         with torch.cuda.stream(self.stream):
@@ -229,8 +237,12 @@ class FewShotBench:
                 e1.record(self.stream)
                 self.ext_events.append((e0, e1))
             d_pos = self.pos_dev
-            Bm.req_to_token_scatter(self.r2t_dev, d_rows, d_pos, d_dslots, stream=self.stream)
-            self._store(kd, vd, d_dslots)
+            if self.fp8:
+                Bm.req_to_token_scatter(self.r2t_dev, d_rows, d_pos, d_dslots, stream=self.stream)
+                self._store(kd, vd, d_dslots)
+            else:  # slot-table entry and K/V row of the new token in one launch
+                Bm.decode_append(self.r2t_dev, d_rows, d_pos, d_dslots, self.k_pool, self.v_pool, kd, vd,
+                                 stream=self.stream)
             if timed:
                 e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e2.record(self.stream)
@@ -241,9 +253,7 @@ class FewShotBench:
                 e3.record(self.stream)
                 self.dec_events.append((e2, e3))
         # finish: prompt + generated token into the tree
-        full = np.concatenate([prompts, self.suffix[i][:, S:S + 1]], axis=1)
-        foff = np.arange(0, B * (P0 + S + 1) + 1, P0 + S + 1, dtype=np.int64)
-        Bm.rt_finish_batch(self.tree, full.reshape(-1), foff, self.r2t_host, rows, pl, nodes)
+        Bm.rt_finish_batch(self.tree, full, self.full_off, self.r2t_host, rows, pl, nodes)
         self.last_prefix_lens = pl.copy()
         if timed:
             rows_keys = sum(int(p) * int(e) + int(e) * (int(e) + 1) // 2 for p, e in zip(pl, el))
@@ -252,6 +262,7 @@ class FewShotBench:
             kv_len = P0 + S + 1
             eb = 1 if self.fp8 else 2
             self.dec_bytes.append(B * kv_len * (self.HKV * self.D * eb * 2 + 4) + 2 * B * self.HQ * self.D * 2)
+            self.host_s.append(time.perf_counter() - t_host)
         return int(el.sum()) + B
 
 
@@ -319,6 +330,9 @@ def run_few_shot(args, torch):
             "extend_tokens_per_s": (fb.B * fb.SUFFIX) / ext_avg_s,
             "decode_us": dec_avg_s * 1e6,
             "decode_hbm_gbs": float(np.mean(fb.dec_bytes)) / dec_avg_s / 1e9,
+            # host time to run one step's tree work and enqueue its GPU work
+            # (the step is host-bound when this is near ms_per_step)
+            "host_us_per_step": float(np.mean(fb.host_s)) * 1e6,
         },
     }
     return result, fb

@@ -251,10 +251,14 @@ def rt_tree_dump(tree):
     return buf.raw[:need.value].decode()
 
 
+_loc_scratch = np.empty(1, dtype=np.int32)
+
+
 def rt_admit_batch(tree, tokens, token_offsets, req_to_token, rows):
     """tokens: int32 concat; token_offsets: int64 [n+1]; req_to_token: int32
     [R, stride] host array (written in place).  Returns (prefix_lens,
     extend_lens, nodes, out_cache_loc)."""
+    global _loc_scratch
     t = _i32(tokens)
     off = np.ascontiguousarray(token_offsets, dtype=np.int64)
     rows = _i32(rows)
@@ -265,7 +269,9 @@ def rt_admit_batch(tree, tokens, token_offsets, req_to_token, rows):
     el = np.empty(n, dtype=np.int32)
     nodes = np.empty(n, dtype=np.int64)
     cap = int(off[-1] - off[0]) if n else 0
-    loc = np.empty(max(cap, 1), dtype=np.int32)
+    if _loc_scratch.size < max(cap, 1):   # reused between calls: only the new slots are copied out
+        _loc_scratch = np.empty(max(cap, 1), dtype=np.int32)
+    loc = _loc_scratch
     nnew = ctypes.c_int64()
     _check(lib().rt_admit_batch(tree, _p32(t), _p64(off), n, _p32(req_to_token), stride, _p32(rows), _p32(pl),
                                 _p32(el), _p64(nodes), _p32(loc), cap, ctypes.byref(nnew)))

@@ -8,10 +8,13 @@
 // parent once it is an unlocked leaf).  Locks and the shared pool follow the
 // SGLang paper summary, section 3 ("Cache management").
 //
-// Data layout: nodes own their key and slot runs in std::vector; children
-// sit in a hash map keyed by first token; a side set tracks the unlocked
-// leaves so that eviction heapifies only the candidates; evictable and
-// protected token counts are kept incrementally.
+// Data layout: nodes own their key and slot runs in std::vector; children are
+// keyed by first token, in a short array while a node has few of them and
+// in a hash map beyond that; nodes are found by id through a vector (ids are
+// handed out in order and never reused) and their storage is recycled after
+// eviction; the unlocked leaves sit in an array with back-indices so that
+// eviction heapifies only the candidates; evictable and protected token
+// counts are kept incrementally.
 
 #include <algorithm>
 #include <cstdint>
@@ -20,7 +23,6 @@
 #include <queue>
 #include <string>
 #include <unordered_map>
-#include <unordered_set>
 #include <vector>
 
 #include "radixrt.h"
@@ -39,21 +41,18 @@ struct Pool {
     for (int32_t i = 0; i < n; ++i) ring[i] = i + 1;
     count = n;
   }
-  int32_t take_one() {
-    int32_t s = ring[head];
-    head = (head + 1) % capacity;
-    --count;
-    return s;
-  }
-  void put_one(int32_t s) {
-    ring[(head + count) % capacity] = s;
-    ++count;
-  }
+  // The free list is a ring: slots leave at head and return at head + count
+  // (mod capacity).  Runs are moved with at most two block copies.
   int alloc(int32_t n, int32_t* out) {
     if (n < 0) return fail(RT_ERR_INVALID, "negative allocation");
     if (n > count) return fail(RT_ERR_OOM, "pool: need " + std::to_string(n) + ", free " +
                                                std::to_string(count));
-    for (int32_t i = 0; i < n; ++i) out[i] = take_one();
+    const int64_t first = std::min<int64_t>(n, capacity - head);
+    std::memcpy(out, ring.data() + head, sizeof(int32_t) * first);
+    std::memcpy(out + first, ring.data(), sizeof(int32_t) * (n - first));
+    head += n;
+    if (head >= capacity) head -= capacity;
+    count -= n;
     return RT_OK;
   }
   int release(const int32_t* slots, int64_t n) {
@@ -62,20 +61,89 @@ struct Pool {
     for (int64_t i = 0; i < n; ++i)
       if (slots[i] < 1 || slots[i] > capacity)
         return fail(RT_ERR_INVALID, "pool: slot " + std::to_string(slots[i]) + " out of range");
-    for (int64_t i = 0; i < n; ++i) put_one(slots[i]);
+    int64_t tail = head + count;
+    if (tail >= capacity) tail -= capacity;
+    const int64_t first = std::min<int64_t>(n, capacity - tail);
+    std::memcpy(ring.data() + tail, slots, sizeof(int32_t) * first);
+    std::memcpy(ring.data(), slots + first, sizeof(int32_t) * (n - first));
+    count += int32_t(n);
     return RT_OK;
   }
 };
 
 // ------------------------------------------------------------------ tree --
+struct Node;
+
+// Children by first token: a short array up to kSmall entries, then a hash map.
+class ChildMap {
+ public:
+  static constexpr size_t kSmall = 8;
+  Node* find(int32_t tok) const {
+    if (!big_.empty()) {
+      auto it = big_.find(tok);
+      return it == big_.end() ? nullptr : it->second;
+    }
+    for (const auto& kv : small_)
+      if (kv.first == tok) return kv.second;
+    return nullptr;
+  }
+  // Inserts or replaces.
+  void set(int32_t tok, Node* n) {
+    if (!big_.empty()) {
+      big_[tok] = n;
+      return;
+    }
+    for (auto& kv : small_)
+      if (kv.first == tok) {
+        kv.second = n;
+        return;
+      }
+    if (small_.size() < kSmall) {
+      small_.emplace_back(tok, n);
+      return;
+    }
+    big_.reserve(2 * kSmall);
+    for (const auto& kv : small_) big_.emplace(kv.first, kv.second);
+    big_.emplace(tok, n);
+    small_.clear();
+  }
+  void erase(int32_t tok) {
+    if (!big_.empty()) {
+      big_.erase(tok);
+      return;
+    }
+    for (size_t i = 0; i < small_.size(); ++i)
+      if (small_[i].first == tok) {
+        small_[i] = small_.back();
+        small_.pop_back();
+        return;
+      }
+  }
+  bool empty() const { return small_.empty() && big_.empty(); }
+  void clear() {
+    small_.clear();
+    big_.clear();
+  }
+  template <typename F>
+  void for_each(F f) const {
+    for (const auto& kv : small_) f(kv.first, kv.second);
+    for (const auto& kv : big_) f(kv.first, kv.second);
+  }
+
+ private:
+  std::vector<std::pair<int32_t, Node*>> small_;
+  std::unordered_map<int32_t, Node*> big_;
+};
+
 struct Node {
-  int64_t id;
+  int64_t id = 0;
   std::vector<int32_t> key;
   std::vector<int32_t> value;
-  std::unordered_map<int32_t, Node*> children;
+  ChildMap children;
   Node* parent = nullptr;
   int32_t lock_ref = 0;
   uint64_t last_access = 0;
+  int64_t leaf_pos = -1;  // index in Tree::leaves while an eviction candidate
 };
 
 struct Tree {
@@ -84,8 +152,11 @@ struct Tree {
   int64_t next_id = 1;
   std::unique_ptr<Node> root_owner;
   Node* root;
-  std::unordered_map<int64_t, std::unique_ptr<Node>> nodes;  // non-root nodes by id
-  std::unordered_set<Node*> evictable_leaves;                // unlocked, childless, non-root
+  std::vector<Node*> by_id;                    // by_id[id - 1]: live node or null
+  std::vector<std::unique_ptr<Node>> storage;  // every node object ever made
+  std::vector<Node*> spare;                    // evicted node objects, reused
+  int64_t live = 0;                            // non-root nodes in the tree
+  std::vector<Node*> leaves;                   // unlocked, childless, non-root
   int64_t evictable = 0;
   int64_t protected_ = 0;
 
@@ -97,30 +168,59 @@ struct Tree {
   bool is_candidate(const Node* n) const {
     return n != root && n->children.empty() && n->lock_ref == 0;
   }
+  void leaf_add(Node* n) {
+    if (n->leaf_pos >= 0) return;
+    n->leaf_pos = int64_t(leaves.size());
+    leaves.push_back(n);
+  }
+  void leaf_remove(Node* n) {
+    if (n->leaf_pos < 0) return;
+    Node* last = leaves.back();
+    leaves[n->leaf_pos] = last;
+    last->leaf_pos = n->leaf_pos;
+    leaves.pop_back();
+    n->leaf_pos = -1;
+  }
   void refresh(Node* n) {
     if (n == root) return;
     if (is_candidate(n))
-      evictable_leaves.insert(n);
+      leaf_add(n);
     else
-      evictable_leaves.erase(n);
+      leaf_remove(n);
   }
 
   Node* make_node(Node* parent, const int32_t* key, const int32_t* val, int64_t len, uint64_t stamp) {
-    auto owned = std::make_unique<Node>();
-    Node* n = owned.get();
+    Node* n;
+    if (!spare.empty()) {
+      n = spare.back();
+      spare.pop_back();
+    } else {
+      storage.push_back(std::make_unique<Node>());
+      n = storage.back().get();
+    }
     n->id = next_id++;
     n->key.assign(key, key + len);
     n->value.assign(val, val + len);
+    n->children.clear();
     n->parent = parent;
+    n->lock_ref = 0;
     n->last_access = stamp;
-    nodes.emplace(n->id, std::move(owned));
+    n->leaf_pos = -1;
+    by_id.push_back(n);  // by_id[id - 1]
+    ++live;
     return n;
+  }
+  void drop_node(Node* n) {
+    by_id[size_t(n->id - 1)] = nullptr;
+    n->parent = nullptr;
+    --live;
+    spare.push_back(n);
   }
 
   Node* find(int64_t id) {
     if (id == 0) return root;
-    auto it = nodes.find(id);
-    return it == nodes.end() ? nullptr : it->second.get();
+    if (id < 0 || id > int64_t(by_id.size())) return nullptr;
+    return by_id[size_t(id - 1)];
   }
 
   // Cut child's edge after k tokens (0 < k < len); the upper part becomes a
@@ -129,20 +229,24 @@ struct Tree {
     Node* parent = child->parent;
     Node* upper = make_node(parent, child->key.data(), child->value.data(), k, child->last_access);
     upper->lock_ref = child->lock_ref;
-    parent->children[child->key[0]] = upper;
+    parent->children.set(child->key[0], upper);
     child->key.erase(child->key.begin(), child->key.begin() + k);
     child->value.erase(child->value.begin(), child->value.begin() + k);
     child->parent = upper;
-    upper->children.emplace(child->key[0], child);
+    upper->children.set(child->key[0], child);
     // token counts are unchanged (same lock count on both parts)
     refresh(upper);
     return upper;
   }
 
+  // Length of the common prefix of an edge key and a token run; long runs
+  // are compared 64 tokens at a time with memcmp.
   static int64_t common_len(const std::vector<int32_t>& a, const int32_t* b, int64_t nb) {
-    int64_t m = std::min<int64_t>(int64_t(a.size()), nb);
+    const int64_t m = std::min<int64_t>(int64_t(a.size()), nb);
+    const int32_t* pa = a.data();
     int64_t k = 0;
-    while (k < m && a[k] == b[k]) ++k;
+    while (k + 64 <= m && std::memcmp(pa + k, b + k, 64 * sizeof(int32_t)) == 0) k += 64;
+    while (k < m && pa[k] == b[k]) ++k;
     return k;
   }
 
@@ -152,9 +256,8 @@ struct Tree {
     Node* node = root;
     int64_t pos = 0, len = 0;
     while (pos < n) {
-      auto it = node->children.find(tokens[pos]);
-      if (it == node->children.end()) break;
-      Node* child = it->second;
+      Node* child = node->children.find(tokens[pos]);
+      if (!child) break;
       child->last_access = stamp;
       int64_t k = common_len(child->key, tokens + pos, n - pos);
       if (k < int64_t(child->key.size())) {
@@ -178,9 +281,8 @@ struct Tree {
     Node* node = root;
     int64_t pos = 0;
     while (pos < n) {
-      auto it = node->children.find(tokens[pos]);
-      if (it == node->children.end()) break;
-      Node* child = it->second;
+      Node* child = node->children.find(tokens[pos]);
+      if (!child) break;
       child->last_access = stamp;
       int64_t k = common_len(child->key, tokens + pos, n - pos);
       if (k < int64_t(child->key.size())) child = split(child, k);
@@ -189,7 +291,7 @@ struct Tree {
     }
     if (pos < n) {
       Node* leaf = make_node(node, tokens + pos, slots + pos, n - pos, stamp);
-      node->children.emplace(tokens[pos], leaf);
+      node->children.set(tokens[pos], leaf);
       evictable += n - pos;
       refresh(node);
       refresh(leaf);
@@ -225,8 +327,8 @@ struct Tree {
     using Key = std::pair<std::pair<uint64_t, int64_t>, Node*>;
     auto cmp = [](const Key& a, const Key& b) { return a.first > b.first; };  // min-heap
     std::vector<Key> init;
-    init.reserve(evictable_leaves.size());
-    for (Node* n : evictable_leaves) init.push_back({{n->last_access, n->id}, n});
+    init.reserve(leaves.size());
+    for (Node* n : leaves) init.push_back({{n->last_access, n->id}, n});
     std::priority_queue<Key, std::vector<Key>, decltype(cmp)> heap(cmp, std::move(init));
     int64_t evicted = 0;
     while (evicted < num_tokens && !heap.empty()) {
@@ -239,10 +341,10 @@ struct Tree {
       evictable -= len;
       Node* parent = x->parent;
       parent->children.erase(x->key[0]);
-      evictable_leaves.erase(x);
-      nodes.erase(x->id);
+      leaf_remove(x);
+      drop_node(x);
       if (is_candidate(parent)) {
-        evictable_leaves.insert(parent);
+        leaf_add(parent);
         heap.push({{parent->last_access, parent->id}, parent});
       }
     }
@@ -279,7 +381,8 @@ struct Tree {
       s += std::to_string(n->value[i]);
     }
     s += '\n';
-    std::vector<std::pair<int32_t, const Node*>> kids(n->children.begin(), n->children.end());
+    std::vector<std::pair<int32_t, const Node*>> kids;
+    n->children.for_each([&](int32_t tok, const Node* c) { kids.emplace_back(tok, c); });
     std::sort(kids.begin(), kids.end(),
               [](const auto& a, const auto& b) { return a.first < b.first; });
     for (auto& kv : kids) dump_node(kv.second, n->id, s);
@@ -418,7 +521,7 @@ int rt_alloc_with_evict(rt_tree* tree, int32_t n, int32_t* out_slots, int32_t* o
 
 int64_t rt_evictable_size(const rt_tree* tree) { return tree ? tree->impl.evictable : 0; }
 int64_t rt_protected_size(const rt_tree* tree) { return tree ? tree->impl.protected_ : 0; }
-int64_t rt_tree_num_nodes(const rt_tree* tree) { return tree ? int64_t(tree->impl.nodes.size()) + 1 : 0; }
+int64_t rt_tree_num_nodes(const rt_tree* tree) { return tree ? tree->impl.live + 1 : 0; }
 
 int rt_tree_dump(const rt_tree* tree, char* buf, int64_t cap, int64_t* out_len) {
   if (!tree || !out_len) return fail(RT_ERR_INVALID, "rt_tree_dump: null argument");
