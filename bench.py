@@ -590,10 +590,16 @@ def run_decode_graph(args, torch):
     from prefix_shared_kv_rt_amd.runtime import RadixRuntime
     HQ, HKV, D, CTX, SLOTS = 32, 8, 128, 2304, 1 << 19
     sizes = [1, 4, 16, 64, 128]
-    rt = RadixRuntime(SLOTS, HQ, HKV, D, torch.bfloat16, 129, CTX)
+    fp8 = args.kv_dtype == "fp8"
+    rt = RadixRuntime(SLOTS, HQ, HKV, D, torch.bfloat16, 129, CTX, kv_fp8_scales=(1.0, 1.0) if fp8 else None)
     g = torch.Generator(device="cuda").manual_seed(7)
-    rt.k_pool[1:] = torch.randn(rt.k_pool[1:].shape, generator=g, device="cuda").to(torch.bfloat16)
-    rt.v_pool[1:] = torch.randn(rt.v_pool[1:].shape, generator=g, device="cuda").to(torch.bfloat16)
+    if fp8:  # codes of N(0, 1) values, as an FP8 store leaves them
+        for pool in (rt.k_pool, rt.v_pool):
+            vals = torch.randn(pool[1:].shape, generator=g, device="cuda")
+            pool[1:] = vals.to(torch.float8_e4m3fn).view(torch.uint8)
+    else:
+        rt.k_pool[1:] = torch.randn(rt.k_pool[1:].shape, generator=g, device="cuda").to(torch.bfloat16)
+        rt.v_pool[1:] = torch.randn(rt.v_pool[1:].shape, generator=g, device="cuda").to(torch.bfloat16)
     rng = np.random.default_rng(7)
     for r in range(128):
         rt.r2t_host[r, :] = rng.integers(1, SLOTS // 2, CTX)
@@ -633,7 +639,8 @@ def run_decode_graph(args, torch):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "decode steps of batch 1..128 at 2048-token contexts, Hq 32 / Hkv 8 / D 128; "
                                "value = batch-1 tokens/s with graphs; each step synchronised",
-                   "num_q_heads": HQ, "num_kv_heads": HKV, "head_dim": D, "graph_sizes": graphs.sizes},
+                   "num_q_heads": HQ, "num_kv_heads": HKV, "head_dim": D, "graph_sizes": graphs.sizes,
+                   "kv_dtype": "fp8_e4m3" if fp8 else "bf16"},
         "capture_s": capture_s,
         "latency": table,
     }

@@ -287,9 +287,17 @@ int kv_store_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_ne
                  const int32_t* out_cache_loc, int32_t n_tokens, int32_t num_kv_heads, int32_t head_dim,
                  float k_scale, float v_scale, void* stream);
 
-/* radix_decode_attention over FP8 pools: q, o bf16; keys and values read as
- * E4M3(code) * k_scale and E4M3(code) * v_scale.  Same arguments, workspace
- * (radix_decode_workspace_bytes) and checks otherwise. */
+/* decode_append for FP8 pools: req_to_token_scatter of (rows, positions,
+ * slots) and kv_store_fp8 of (k_new, v_new) at slots, in one launch, with the
+ * encoding and scales of kv_store_fp8.  k_new, v_new: (device) bf16 [n,
+ * num_kv_heads, head_dim].  Repeated slots (padding to slot 0) race: each
+ * 8-byte piece of such a slot ends up holding that piece of one of the rows
+ * written to it. */
+int decode_append_fp8(int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* rows,
+                      const int32_t* positions, const int32_t* slots, int32_t n, void* k_pool, void* v_pool,
+                      const void* k_new, const void* v_new, int32_t num_kv_heads, int32_t head_dim,
+                      float k_scale, float v_scale, void* stream);
+
 /* radix_extend_attention over FP8 pools: q, o bf16; keys and values read as
  * E4M3(code) * k_scale and E4M3(code) * v_scale.  Same arguments and checks
  * otherwise. */
@@ -300,6 +308,9 @@ int radix_extend_attention_fp8kv(const void* q, void* o, const void* k_pool, con
                                  int32_t max_extend_len, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, float sm_scale, float k_scale, float v_scale, void* stream);
 
+/* radix_decode_attention over FP8 pools: q, o bf16; keys and values read as
+ * E4M3(code) * k_scale and E4M3(code) * v_scale.  Same arguments, workspace
+ * (radix_decode_workspace_bytes) and checks otherwise. */
 int radix_decode_attention_fp8kv(const void* q, void* o, const void* k_pool, const void* v_pool,
                                  const int32_t* req_to_token, int32_t req_to_token_stride,
                                  const int32_t* req_pool_indices, const int32_t* prefix_lens, int32_t batch,

@@ -24,7 +24,7 @@ EXPORTS = [
     "rt_evict_lru_leaves", "rt_alloc_with_evict", "rt_evictable_size", "rt_protected_size",
     "rt_tree_num_nodes", "rt_tree_dump", "rt_admit_batch", "rt_decode_slots_batch", "rt_finish_batch",
     "kv_store", "req_to_token_scatter", "decode_append", "kv_store_fp8", "radix_decode_attention_fp8kv",
-    "radix_extend_attention_fp8kv",
+    "radix_extend_attention_fp8kv", "decode_append_fp8",
     "radix_extend_attention", "radix_decode_workspace_bytes", "radix_decode_attention",
 ]
 
@@ -99,6 +99,9 @@ def lib():
                                                             ctypes.c_float, ctypes.c_float, _vp]),
             "decode_append": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp]),
+            "decode_append_fp8": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
+                                                 _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                                                 _vp]),
             "radix_extend_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
@@ -362,6 +365,15 @@ def decode_append(req_to_token, rows, positions, slots, k_pool, v_pool, k_new, v
     _check(lib().decode_append(_dptr(req_to_token), req_to_token.shape[1], _dptr(rows), _dptr(positions),
                                _dptr(slots), n, _dptr(k_pool), _dptr(v_pool), _dptr(k_new), _dptr(v_new), hkv, d,
                                _dtype_code(k_new), _stream(stream)))
+
+
+def decode_append_fp8(req_to_token, rows, positions, slots, k_pool, v_pool, k_new, v_new, k_scale=1.0, v_scale=1.0,
+                      stream=None):
+    """decode_append into FP8 pools (uint8 codes); k_new, v_new bf16."""
+    n, hkv, d = k_new.shape
+    _check(lib().decode_append_fp8(_dptr(req_to_token), req_to_token.shape[1], _dptr(rows), _dptr(positions),
+                                   _dptr(slots), n, _dptr(k_pool), _dptr(v_pool), _dptr(k_new), _dptr(v_new), hkv, d,
+                                   float(k_scale), float(v_scale), _stream(stream)))
 
 
 def radix_extend_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens, extend_lens,

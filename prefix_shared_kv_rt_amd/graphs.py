@@ -15,7 +15,8 @@ scheme this follows:
 A decode step here is one host-to-device copy of the batch's indices (rows,
 positions, new slots: one pinned block) and the replay of three kernels on
 the runtime's stream: the append of the new tokens (slot table and K/V in
-one launch) and decode attention (split and combine).  The new tokens' Q/K/V
+one launch; for FP8 pools the K/V rows are encoded on the way) and decode
+attention (split and combine).  The new tokens' Q/K/V
 are read from static buffers that a producer fills in place (``inputs``) or
 that ``run`` copies into.  The decode kernels' split plan depends on the batch
 size and the maximum context length, both fixed at capture: the graphs use
@@ -48,8 +49,6 @@ class DecodeGraphs:
     def __init__(self, rt, max_batch=None, batch_sizes=None):
         if rt.device is None:
             raise ValueError("decode graphs need a device runtime")
-        if rt.kv_fp8_scales:
-            raise ValueError("decode graphs run over bf16 pools")
         if rt.max_reqs - 1 in rt.free_rows:
             rt.free_rows.remove(rt.max_reqs - 1)
         else:
@@ -83,9 +82,16 @@ class DecodeGraphs:
     def _launch(self, bs, stream):
         rt = self.rt
         rows, pos, slots = self.idx[0, :bs], self.idx[1, :bs], self.idx[2, :bs]
-        B.decode_append(rt.r2t_dev, rows, pos, slots, rt.k_pool, rt.v_pool, self.k[:bs], self.v[:bs], stream=stream)
-        B.radix_decode_attention(self.q[:bs], self.o[:bs], rt.k_pool, rt.v_pool, rt.r2t_dev, rows, pos,
-                                 self.max_kv, rt.sm_scale, self.ws, stream=stream)
+        if rt.kv_fp8_scales:
+            B.decode_append_fp8(rt.r2t_dev, rows, pos, slots, rt.k_pool, rt.v_pool, self.k[:bs], self.v[:bs],
+                                *rt.kv_fp8_scales, stream=stream)
+            B.radix_decode_attention_fp8kv(self.q[:bs], self.o[:bs], rt.k_pool, rt.v_pool, rt.r2t_dev, rows, pos,
+                                           self.max_kv, rt.sm_scale, self.ws, *rt.kv_fp8_scales, stream=stream)
+        else:
+            B.decode_append(rt.r2t_dev, rows, pos, slots, rt.k_pool, rt.v_pool, self.k[:bs], self.v[:bs],
+                            stream=stream)
+            B.radix_decode_attention(self.q[:bs], self.o[:bs], rt.k_pool, rt.v_pool, rt.r2t_dev, rows, pos,
+                                     self.max_kv, rt.sm_scale, self.ws, stream=stream)
 
     def _capture_all(self):
         rt = self.rt
@@ -146,8 +152,8 @@ class DecodeGraphs:
             self.graphs[bs].replay()
             if e0 is not None:
                 kv = np.asarray(positions, dtype=np.float64) + 1
-                eb = self.q.element_size()
-                nbytes = float(np.sum(kv * (2 * rt.hkv * rt.d * eb + 4))) + 2.0 * n * rt.hq * rt.d * eb
+                eb, ekv = self.q.element_size(), rt.k_pool.element_size()
+                nbytes = float(np.sum(kv * (2 * rt.hkv * rt.d * ekv + 4))) + 2.0 * n * rt.hq * rt.d * eb
                 rt.events.append(("decode", e0, rt._event(), {"tokens": n, "bytes": nbytes, "graph_batch": bs}))
         self.replays += 1
         return self.o[:n]

@@ -169,8 +169,8 @@ class RadixRuntime:
             ws = self.workspace(n, max_kv)
             e0 = self._event() if self.events is not None else None
             if self.kv_fp8_scales:
-                B.req_to_token_scatter(self.r2t_dev, rows_d, pos_d, slots_d, stream=self.stream)
-                self._store(k_new, v_new, slots_d)
+                B.decode_append_fp8(self.r2t_dev, rows_d, pos_d, slots_d, self.k_pool, self.v_pool, k_new, v_new,
+                                    *self.kv_fp8_scales, stream=self.stream)
                 B.radix_decode_attention_fp8kv(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, max_kv,
                                                self.sm_scale, ws, *self.kv_fp8_scales, stream=self.stream)
             else:
@@ -180,8 +180,8 @@ class RadixRuntime:
                                          self.sm_scale, ws, stream=self.stream)
             if e0 is not None:
                 kv = np.asarray(positions, dtype=np.float64) + 1
-                eb = q.element_size()
-                nbytes = float(np.sum(kv * (2 * self.hkv * self.d * eb + 4))) + 2.0 * n * self.hq * self.d * eb
+                eb, ekv = q.element_size(), self.k_pool.element_size()
+                nbytes = float(np.sum(kv * (2 * self.hkv * self.d * ekv + 4))) + 2.0 * n * self.hq * self.d * eb
                 self.events.append(("decode", e0, self._event(), {"tokens": n, "bytes": nbytes}))
             return o
 

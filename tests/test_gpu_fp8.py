@@ -43,6 +43,46 @@ def test_kv_store_fp8_bit_exact(hkv, d, k_scale, v_scale):
     assert np.array_equal(got_v, want_v)
 
 
+@pytest.mark.parametrize("hkv,d,k_scale,v_scale", [(8, 128, 1.0, 1.0), (2, 64, 0.37, 3.0)])
+def test_decode_append_fp8_bit_exact(hkv, d, k_scale, v_scale):
+    """The fused FP8 append writes the slot-table entries and the oracle's
+    E4M3 codes of the new rows; padding rows that all write slot 0 through
+    one row leave there, 8-byte piece by piece, the codes of one of them."""
+    _announce(f"decode_append_fp8 hkv={hkv} d={d} scales {k_scale} {v_scale}")
+    rng = np.random.default_rng(40 + d)
+    n_slots, n, stride, rows_n = 2000, 300, 97, 400
+    pool0 = rng.integers(0, 256, (n_slots + 1, hkv, d)).astype(np.uint8)
+    kn = torch.from_numpy((rng.standard_normal((n, hkv, d)) * 5).astype(np.float32)).to(torch.bfloat16)
+    vn = torch.from_numpy((rng.standard_normal((n, hkv, d)) * 5).astype(np.float32)).to(torch.bfloat16)
+    rows = rng.permutation(rows_n - 1)[:n].astype(np.int32)
+    pos = rng.integers(0, stride, n).astype(np.int32)
+    slots = rng.permutation(np.arange(1, n_slots + 1))[:n].astype(np.int32)
+    rows[-5:], pos[-5:], slots[-5:] = rows_n - 1, 0, 0
+    r2t0 = rng.integers(1, n_slots, (rows_n, stride)).astype(np.int32)
+    r2t = torch.from_numpy(r2t0).cuda()
+    kp, vp = torch.from_numpy(pool0).cuda(), torch.from_numpy(pool0.copy()).cuda()
+    B.decode_append_fp8(r2t, i32(rows), i32(pos), i32(slots), kp, vp, kn.cuda(), vn.cuda(), k_scale, v_scale)
+    torch.cuda.synchronize()
+    want_r2t = r2t0.copy()
+    want_r2t[rows, pos] = slots
+    assert np.array_equal(r2t.cpu().numpy(), want_r2t)
+    for pool, new, scale in ((kp, kn, k_scale), (vp, vn, v_scale)):
+        got = pool.cpu().numpy()
+        want = oracle_store(pool0, new[:-5].float().numpy(), slots[:-5], scale)
+        assert np.array_equal(got[1:], want[1:])
+        pad = store_codes(new[-5:].float().numpy(), scale).reshape(5, -1, 8)
+        g0 = got[0].reshape(-1, 8)
+        assert bool((g0[None] == pad).all(axis=2).any(axis=0).all())
+
+
+def test_decode_append_fp8_rejects_bad_scale():
+    r2t = torch.zeros((2, 4), dtype=torch.int32, device="cuda")
+    pool = torch.zeros((4, 1, 128), dtype=torch.uint8, device="cuda")
+    kn = torch.zeros((1, 1, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B.RadixRTError):
+        B.decode_append_fp8(r2t, i32([0]), i32([0]), i32([1]), pool, pool, kn, kn, -1.0, 1.0)
+
+
 FP8_DECODE_CASES = [
     ([0, 1, 15, 16, 17, 63, 64, 65], 32, 8, 128, 1.0, 1.0),
     ([2048, 2100, 2303, 1], 32, 8, 128, 0.5, 2.0),

@@ -19,25 +19,29 @@ def check_few_shot(fb, i):
     """Sampled outputs of batch i against the oracle's full recompute."""
     o_ext = fb.o_ext.float().cpu().numpy()
     o_dec = fb.o_dec.float().cpu().numpy()
+    fp8 = (1.0, 1.0) if fb.fp8 else None
     worst = 0.0
     for b in (0, 31, 63):
         toks = list(fb.prefix) + list(fb.suffix[i][b])
         p = int(fb.last_prefix_lens[b])  # rows below p were cached, not recomputed
         rows = sorted({p, (p + fb.PREFIX + fb.SUFFIX) // 2, fb.PREFIX + fb.SUFFIX - 1})
-        want = recompute_rows(toks, rows, fb.HQ, fb.HKV, fb.D, fb.SEED, fb.sm_scale)
+        want = recompute_rows(toks, rows, fb.HQ, fb.HKV, fb.D, fb.SEED, fb.sm_scale, kv_fp8_scales=fp8)
         got = o_ext[[b * fb.SUFFIX + (r - fb.PREFIX) for r in rows]]
         worst = max(worst, float(np.abs(got - want).max()))
-        want_d = recompute_rows(toks, [fb.PREFIX + fb.SUFFIX], fb.HQ, fb.HKV, fb.D, fb.SEED, fb.sm_scale)
+        want_d = recompute_rows(toks, [fb.PREFIX + fb.SUFFIX], fb.HQ, fb.HKV, fb.D, fb.SEED, fb.sm_scale,
+                                kv_fp8_scales=fp8)
         worst = max(worst, float(np.abs(o_dec[b:b + 1] - want_d).max()))
     return {"max_abs_err": worst, "tol": TOL, "ok": worst <= TOL}
 
 
-def test_few_shot_full_size_bench_path():
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_few_shot_full_size_bench_path(kv_dtype):
     """64 requests x (1024 shared + 128 distinct) per step, three steps: the
     extend rows actually computed (position >= matched prefix) and the
-    decode row of sampled requests."""
-    print("few-shot full size", flush=True)
-    fb = bench.FewShotBench(3, torch, B, torch_gen)
+    decode row of sampled requests (bf16 pool, or FP8 E4M3 pool at unit
+    scales against attention over the values the FP8 pool holds)."""
+    print(f"few-shot full size, {kv_dtype} pool", flush=True)
+    fb = bench.FewShotBench(3, torch, B, torch_gen, kv_dtype=kv_dtype)
     fb.gen_inputs(3)
     fb.warm_prefix()
     worst = 0.0

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle.fp8 import dequantize, store_codes
 from prefix_shared_kv_rt_amd.graphs import DecodeGraphs, default_batch_sizes
 from prefix_shared_kv_rt_amd.runtime import RadixRuntime
 
@@ -29,10 +30,27 @@ def _runtime(seed):
     return rt
 
 
+def _runtime_fp8(seed, scales):
+    rt = RadixRuntime(SLOTS, HQ, HKV, D, torch.bfloat16, ROWS, CTX, kv_fp8_scales=scales)
+    rng = np.random.default_rng(seed)
+    # pools hold the codes of N(0, 1) rows, as kv_store_fp8 would leave them
+    for pool, scale in ((rt.k_pool, scales[0]), (rt.v_pool, scales[1])):
+        pool[1:] = torch.from_numpy(store_codes(rng.standard_normal((SLOTS, HKV, D)), scale)).cuda()
+    for r in range(ROWS):
+        rt.r2t_host[r, :] = rng.permutation(np.arange(1, SLOTS // 2))[:CTX]
+    rt.r2t_dev.copy_(torch.from_numpy(rt.r2t_host))
+    return rt
+
+
 def _reference(rt, rows, positions, q):
-    """float32 decode attention gathered through the device slot table."""
+    """float32 decode attention gathered through the device slot table (for
+    FP8 pools: over the values the stored codes stand for)."""
     r2t = rt.r2t_dev.cpu().numpy()
-    kp, vp = rt.k_pool.float().cpu(), rt.v_pool.float().cpu()
+    if rt.kv_fp8_scales:
+        kp = torch.from_numpy(dequantize(rt.k_pool.cpu().numpy(), rt.kv_fp8_scales[0])).float()
+        vp = torch.from_numpy(dequantize(rt.v_pool.cpu().numpy(), rt.kv_fp8_scales[1])).float()
+    else:
+        kp, vp = rt.k_pool.float().cpu(), rt.v_pool.float().cpu()
     out = []
     for i, (r, p) in enumerate(zip(rows, positions)):
         sl = torch.from_numpy(r2t[r, :p + 1].astype(np.int64))
@@ -48,8 +66,9 @@ def test_default_sizes_follow_the_handbook_list():
     assert default_batch_sizes(20) == [1, 2, 4, 8, 16, 20]
 
 
-def test_graph_replays_match_eager_and_reference():
-    rt = _runtime(0)
+@pytest.mark.parametrize("pool", ["bf16", "fp8"])
+def test_graph_replays_match_eager_and_reference(pool):
+    rt = _runtime(0) if pool == "bf16" else _runtime_fp8(0, (0.5, 2.0))
     graphs = DecodeGraphs(rt, max_batch=16)
     assert graphs.sizes == [1, 2, 4, 8, 16]
     rng = np.random.default_rng(1)

@@ -133,13 +133,15 @@ def test_chunked_prefill_few_shot_bf16():
     assert max(len(it["chunks"]) for it in ora.iterations) > 1
 
 
-@pytest.mark.parametrize("scales", [(1.0, 1.0), (0.5, 2.0)])
-def test_small_chat_fp8_pool(scales):
-    """The small chat workload with FP8 pools: host decisions as with bf16,
-    attention against the oracle over the values the FP8 pool holds."""
-    print(f"chat (6 sessions x 3 turns, pool 60%, fp8 pool {scales})", flush=True)
+@pytest.mark.parametrize("scales,graphs", [((1.0, 1.0), False), ((0.5, 2.0), False), ((0.5, 2.0), True)])
+def test_small_chat_fp8_pool(scales, graphs):
+    """The small chat workload with FP8 pools (decode steps eager or replayed
+    from HIP graphs): host decisions as with bf16, attention against the
+    oracle over the values the FP8 pool holds."""
+    print(f"chat (6 sessions x 3 turns, pool 60%, fp8 pool {scales}, graphs {graphs})", flush=True)
     wl = workloads.chat(sessions=6, turns=3, system_len=64, user_lo=16, user_hi=48, gen_len=6)
     sel = lambda kind, rid, step: kind == "ext" or step in (0, 5)
-    ora, sch, outs, dump, free = run_both(wl, want=sel, max_running=4, max_extend_tokens=128, kv_fp8_scales=scales)
+    ora, sch, outs, dump, free = run_both(wl, want=sel, max_running=4, max_extend_tokens=128, kv_fp8_scales=scales,
+                                          graphs=graphs)
     check_host_identical(ora, sch, dump, free)
     check_outputs(ora, outs, TOL["bf16"])
