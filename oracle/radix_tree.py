@@ -27,6 +27,23 @@ logical counter advanced once per match or insert call; ties break on the
 node creation id; a split's upper node gets a fresh id, the walk's stamp
 and a copy of the child's lock count; evicted leaves are not re-merged.
 
+Pages (page_size p > 1; the explainer's source excerpt compares a child's
+key with the remaining key under the tree's page size, and the engine makes
+the page size configurable).  Readings taken, all reducing to the above at
+p = 1:
+
+* the pool hands out whole pages: page j holds slots 1 + j*p .. (j+1)*p,
+  the free list is a FIFO of pages (ascending at start), an allocation of n
+  slots takes n / p pages, and a free returns the distinct pages of the
+  given slots in order of first appearance;
+* keys are compared page by page: a child is found by its first page, a
+  common length counts whole pages only, so matches and splits fall on page
+  boundaries; a trailing partial page of a key never matches; inserts carry
+  whole pages only;
+* positions get slots by the page rule (``alloc_positions``): a position
+  that starts a page takes a fresh page and its first slot, any other
+  position takes the slot after the previous position's.
+
 Everything here is written for obviousness, not speed: children are a list
 scanned linearly, sizes are recomputed by full traversal, and the eviction
 candidate is found by scanning every node.
@@ -44,25 +61,46 @@ class OracleInvalid(Exception):
 
 
 class NaivePool:
-    """FIFO free list of KV slots 1..num_slots (slot 0 reserved)."""
+    """FIFO free list of pages of KV slots 1..num_slots (slot 0 reserved);
+    page j holds slots 1 + j*p .. (j+1)*p."""
 
-    def __init__(self, num_slots):
+    def __init__(self, num_slots, page_size=1):
+        if page_size < 1 or num_slots % page_size:
+            raise OracleInvalid("num_slots must be a positive multiple of page_size")
         self.num_slots = num_slots
-        self.free = deque(range(1, num_slots + 1))
+        self.page_size = page_size
+        self.free_pages = deque(range(num_slots // page_size))
+
+    def page_slots(self, j):
+        return [1 + j * self.page_size + i for i in range(self.page_size)]
+
+    @property
+    def free(self):
+        """Free slots in free-list order (each free page's slots in order)."""
+        return [s for j in self.free_pages for s in self.page_slots(j)]
 
     def available(self):
-        return len(self.free)
+        return len(self.free_pages) * self.page_size
 
     def alloc(self, n):
-        if n < 0:
-            raise OracleInvalid("negative allocation")
-        if n > len(self.free):
-            raise OracleOOM(f"need {n}, have {len(self.free)}")
-        return [self.free.popleft() for _ in range(n)]
+        if n < 0 or n % self.page_size:
+            raise OracleInvalid("allocation must be a non-negative multiple of the page size")
+        if n > self.available():
+            raise OracleOOM(f"need {n}, have {self.available()}")
+        out = []
+        for _ in range(n // self.page_size):
+            out += self.page_slots(self.free_pages.popleft())
+        return out
 
     def release(self, slots):
+        """Frees the distinct pages of the given slots, in order of first
+        appearance."""
+        seen = set()
         for s in slots:
-            self.free.append(int(s))
+            j = (int(s) - 1) // self.page_size
+            if j not in seen:
+                seen.add(j)
+                self.free_pages.append(j)
 
 
 class _Node:
@@ -79,6 +117,7 @@ class _Node:
 class NaiveRadixTree:
     def __init__(self, pool):
         self.pool = pool
+        self.page_size = pool.page_size
         self.clock = 0
         self.next_id = 1
         self.root = _Node(0, [], [], None, 0)
@@ -103,19 +142,22 @@ class NaiveRadixTree:
                 return n
         raise OracleInvalid(f"no node {node_id}")
 
-    @staticmethod
-    def _child_starting_with(node, token):
+    def _child_starting_with(self, node, page):
+        """The child whose key begins with this page (its first p tokens)."""
         for c in node.children:
-            if c.key[0] == token:
+            if c.key[:self.page_size] == list(page):
                 return c
         return None
 
-    @staticmethod
-    def _common_len(a, b):
+    def _common_len(self, a, b):
+        """Common prefix length of a and b in whole pages."""
         k = 0
         while k < len(a) and k < len(b) and a[k] == b[k]:
             k += 1
-        return k
+        return k - k % self.page_size
+
+    def _aligned(self, tokens):
+        return list(tokens)[:len(tokens) - len(tokens) % self.page_size]
 
     def _split(self, child, k, stamp):
         """Cut child's edge after k tokens; the upper part becomes a new node."""
@@ -135,9 +177,9 @@ class NaiveRadixTree:
         """Returns (slots of the longest cached prefix, id of its last node)."""
         self.clock += 1
         stamp = self.clock
-        node, key, slots = self.root, list(tokens), []
+        node, key, slots = self.root, self._aligned(tokens), []
         while key:
-            child = self._child_starting_with(node, key[0])
+            child = self._child_starting_with(node, key[:self.page_size])
             if child is None:
                 break
             child.last_access = stamp
@@ -154,14 +196,17 @@ class NaiveRadixTree:
 
     def insert(self, tokens, slots):
         """Insert tokens with their slots; returns the length already present.
-        Where the tree already holds a token, the tree's slot is kept."""
+        Where the tree already holds a token, the tree's slot is kept.  The
+        length must be a whole number of pages."""
         if len(tokens) != len(slots):
             raise OracleInvalid("tokens/slots length mismatch")
+        if len(tokens) % self.page_size:
+            raise OracleInvalid("insert of a partial page")
         self.clock += 1
         stamp = self.clock
         node, key, val, present = self.root, list(tokens), list(slots), 0
         while key:
-            child = self._child_starting_with(node, key[0])
+            child = self._child_starting_with(node, key[:self.page_size])
             if child is None:
                 break
             child.last_access = stamp
@@ -223,24 +268,48 @@ class NaiveRadixTree:
         return evicted, freed
 
     def alloc_with_evict(self, n):
-        """Allocate n slots, evicting the deficit first if the pool is short.
-        Raises OracleOOM (allocating nothing) if still short."""
+        """Allocate n slots (whole pages), evicting the deficit first if the
+        pool is short.  Raises OracleOOM (allocating nothing) if still short."""
         short = n - self.pool.available()
         freed = []
         if short > 0:
             _, freed = self.evict(short)
         return self.pool.alloc(n), freed
 
+    def alloc_positions(self, runs):
+        """Slots for runs of positions by the page rule.  runs: list of
+        (slots of the request's positions 0 .. first-1, first, count), in
+        order.  Pages for every position that starts a page are allocated
+        together (evicting first if short), taken in run order.  Returns
+        (slots of every run's positions, concatenated; slots freed by
+        eviction)."""
+        p = self.page_size
+        starts = sum(1 for _, first, cnt in runs for x in range(first, first + cnt) if x % p == 0)
+        fresh, freed = self.alloc_with_evict(starts * p)
+        out, nxt = [], 0
+        for prev, first, cnt in runs:
+            mine = list(prev)
+            for x in range(first, first + cnt):
+                if x % p == 0:
+                    s = fresh[nxt * p]
+                    nxt += 1
+                else:
+                    s = mine[x - 1] + 1
+                mine.append(s)
+                out.append(s)
+        return out, freed
+
     def dump(self):
-        """Canonical text: pre-order, children by first token ascending; one
-        line per node: id parent lock_ref last_access k=<tokens> v=<slots>."""
+        """Canonical text: pre-order, children by first page ascending
+        (lexicographic); one line per node: id parent lock_ref last_access
+        k=<tokens> v=<slots>."""
         lines = []
 
         def visit(n, parent_id):
             lines.append("%d %d %d %d k=%s v=%s\n" % (
                 n.id, parent_id, n.lock_ref, n.last_access,
                 ",".join(str(t) for t in n.key), ",".join(str(s) for s in n.value)))
-            for c in sorted(n.children, key=lambda c: c.key[0]):
+            for c in sorted(n.children, key=lambda c: c.key[:self.page_size]):
                 visit(c, n.id)
 
         visit(self.root, -1)

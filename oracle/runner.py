@@ -35,6 +35,15 @@ request does not fit.  A request's whole remaining prompt and output are
 reserved at admission; its slots are allocated chunk by chunk.  It decodes
 from the iteration after its last chunk.
 
+Pages (``wl.page_size`` p; see ``radix_tree``): matches and inserts are
+page-aligned, every position's slot follows the page rule, and a request's
+need counts whole pages: a request holding x of its L = prompt + generated
+positions still needs ceil(L / p) - ceil(x / p) pages, p slots each (at
+admission x is its page-aligned matched length).  On finish only the
+page-aligned part ceil-down(L / p) * p is inserted; the request's pages that
+the tree already held and the page of its trailing partial page are freed.
+At p = 1 all of this is the token-granular behaviour above.
+
 Attention outputs come from ``recompute_rows`` (full recompute, float64).
 """
 
@@ -74,8 +83,14 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
     """Drive workload ``wl`` through the naive tree.  ``want(kind, rid, step)``
     (kind 'ext' or 'dec') selects which attention outputs are recomputed;
     by default all of them when ``attention`` is true."""
-    pool = NaivePool(num_slots if num_slots is not None else wl.num_slots)
+    page = getattr(wl, "page_size", 1)
+    pool = NaivePool(num_slots if num_slots is not None else wl.num_slots, page)
     tree = NaiveRadixTree(pool)
+
+    def pages_left(total_len, held):
+        """Slots still to be allocated for a request of total_len positions
+        that holds held of them: whole pages."""
+        return (-(-total_len // page) - (-(-held // page))) * page
     tr = OracleTrace()
     pending = list(wl.requests)
     finished = set()
@@ -93,8 +108,10 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
 
     def finish(run, it_rec):
         full = list(run.req.prompt) + list(run.req.gen)
-        present = tree.insert(full, run.slots[:len(full)])
+        aligned = len(full) - len(full) % page
+        present = tree.insert(full[:aligned], run.slots[:aligned])
         dups = run.slots[run.prefix_len:present] if present > run.prefix_len else []
+        dups = list(dups) + list(run.slots[aligned:len(full)])  # and the trailing partial page
         pool.release(dups)
         tree.unlock(run.node)
         tr.request_slots[run.req.rid] = list(run.slots[:len(full)])
@@ -125,7 +142,7 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
             _chunked_admit_and_extend(wl, tree, pool, tr, rec, it, order, waiting, running, prefilling,
                                       max_running, chunk_size, selected, finish, kv_fp8_scales)
         else:
-            reserved = sum(len(r.req.gen) - r.generated for r in running)
+            reserved = sum(pages_left(len(r.req.prompt) + len(r.req.gen), len(r.slots)) for r in running)
             budget = max_extend_tokens
             admitted = []
             for req in order:
@@ -135,7 +152,7 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
                 tree.lock(node)
                 p = len(slots)
                 e = len(req.prompt) - p
-                need = e + len(req.gen)
+                need = pages_left(len(req.prompt) + len(req.gen), p)
                 avail = pool.available() + tree.evictable_size() - reserved
                 if need > avail or (admitted and e > budget):
                     tree.unlock(node)
@@ -146,8 +163,8 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
                 budget -= e
             # 2. extend the admitted batch
             if admitted:
-                total = sum(len(r.req.prompt) - r.prefix_len for r in admitted)
-                loc, freed = tree.alloc_with_evict(total) if total > 0 else ([], [])
+                runs = [(r.slots, r.prefix_len, len(r.req.prompt) - r.prefix_len) for r in admitted]
+                loc, freed = tree.alloc_positions(runs)
                 rec["extend_loc"], rec["extend_freed"] = list(loc), list(freed)
                 off = 0
                 for r in admitted:
@@ -170,7 +187,7 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
         # 3. one decode step for requests admitted in earlier iterations
         dec = [r for r in running if r.admit_iter < it]
         if dec:
-            loc, freed = tree.alloc_with_evict(len(dec))
+            loc, freed = tree.alloc_positions([(r.slots, len(r.slots), 1) for r in dec])
             rec["decode_freed"] = list(freed)
             for r, s in zip(dec, loc):
                 pos = len(r.req.prompt) + r.generated
@@ -199,6 +216,8 @@ def run_workload(wl, num_slots=None, max_running=256, max_extend_tokens=16384,
 def _chunked_admit_and_extend(wl, tree, pool, tr, rec, it, order, waiting, running, prefilling,
                               max_running, chunk_size, selected, finish, kv_fp8_scales=None):
     """One iteration's admission and extend under chunked prefill."""
+    page = tree.page_size
+    pages_left = lambda total_len, held: (-(-total_len // page) - (-(-held // page))) * page
     budget = chunk_size
     plan = []  # (request, first position, token count), in launch order
     for r in prefilling:
@@ -207,8 +226,7 @@ def _chunked_admit_and_extend(wl, tree, pool, tr, rec, it, order, waiting, runni
         cnt = min(len(r.req.prompt) - len(r.slots), budget)
         plan.append((r, len(r.slots), cnt))
         budget -= cnt
-    reserved = sum(len(r.req.gen) - r.generated for r in running)
-    reserved += sum(len(r.req.prompt) - len(r.slots) + len(r.req.gen) for r in prefilling)
+    reserved = sum(pages_left(len(r.req.prompt) + len(r.req.gen), len(r.slots)) for r in running + prefilling)
     admitted = []
     for req in order:
         if len(running) + len(prefilling) + len(admitted) >= max_running or budget <= 0:
@@ -217,7 +235,7 @@ def _chunked_admit_and_extend(wl, tree, pool, tr, rec, it, order, waiting, runni
         tree.lock(node)
         p = len(slots)
         e = len(req.prompt) - p
-        need = e + len(req.gen)
+        need = pages_left(len(req.prompt) + len(req.gen), p)
         if need > pool.available() + tree.evictable_size() - reserved:
             tree.unlock(node)
             break
@@ -232,8 +250,7 @@ def _chunked_admit_and_extend(wl, tree, pool, tr, rec, it, order, waiting, runni
         if cnt > 0:
             plan.append((run, p, cnt))
             budget -= cnt
-    total = sum(cnt for _, _, cnt in plan)
-    loc, freed = tree.alloc_with_evict(total) if total > 0 else ([], [])
+    loc, freed = tree.alloc_positions([(r.slots, first, cnt) for r, first, cnt in plan])
     rec["extend_loc"], rec["extend_freed"] = list(loc), list(freed)
     rec["chunks"] = [(r.req.rid, first, cnt) for r, first, cnt in plan]
     off = 0

@@ -37,6 +37,7 @@ class Workload:
     requests: list
     max_ctx: int
     skip_extend_attention: bool = False  # K/V written by kv_store only
+    page_size: int = 1  # KV slots per page of the pool (num_slots a multiple of it)
 
     @property
     def sm_scale(self):
@@ -161,3 +162,13 @@ def long_context(seed=4, batch=32, shared_len=16384, private_len=16384, decode_s
     return Workload("long_context", seed, 64, 8, 128, "bf16", num_slots, reqs,
                     max_ctx=shared_len + private_len + decode_steps,
                     skip_extend_attention=True)
+
+
+def paged(wl, page_size):
+    """The same workload over a pool of page_size-slot pages: the pool is
+    rounded up to whole pages."""
+    import copy
+    out = copy.copy(wl)
+    out.page_size = int(page_size)
+    out.num_slots = -(-wl.num_slots // page_size) * page_size
+    return out
