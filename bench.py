@@ -71,6 +71,8 @@ def parse():
                     help="K/V pool format (fp8 = OCP E4M3 codes, scales 1)")
     ap.add_argument("--chunk-size", type=int, default=None,
                     help="chunked prefill for the chat workload: extend tokens per scheduler iteration")
+    ap.add_argument("--page-size", type=int, default=1,
+                    help="KV slots per pool page (few_shot and chat); 1 = token-granular")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=192, help="requests in the oracle's timed sample")
     return ap.parse_args()
@@ -83,8 +85,9 @@ class FewShotBench:
     SLOTS = 262144
     SEED = 1
 
-    def __init__(self, n_batches, torch, B_mod, gen_t, kv_dtype="bf16"):
+    def __init__(self, n_batches, torch, B_mod, gen_t, kv_dtype="bf16", page_size=1):
         self.fp8 = kv_dtype == "fp8"
+        self.page_size = int(page_size)
         self.torch = torch
         self.Bm = B_mod
         self.gen_t = gen_t
@@ -96,7 +99,7 @@ class FewShotBench:
         self.suffix = [rng.integers(0, 1000, size=(self.B, self.SUFFIX + 1)).astype(np.int32) for _ in range(n_batches)]
         self.stride = self.PREFIX + self.SUFFIX + 1
         bf16 = torch.bfloat16
-        self.pool = B_mod.rt_pool_create(self.SLOTS)
+        self.pool = B_mod.rt_pool_create(self.SLOTS, self.page_size)
         self.tree = B_mod.rt_tree_create(self.pool)
         pool_dt = torch.uint8 if self.fp8 else bf16
         self.k_pool = torch.zeros((self.SLOTS + 1, self.HKV, self.D), dtype=pool_dt, device=self.dev)
@@ -270,7 +273,7 @@ def run_few_shot(args, torch):
     from prefix_shared_kv_rt_amd import binding as Bm
     from synth import torch_gen
     n = args.warmup + args.steps
-    fb = FewShotBench(n, torch, Bm, torch_gen, kv_dtype=args.kv_dtype)
+    fb = FewShotBench(n, torch, Bm, torch_gen, kv_dtype=args.kv_dtype, page_size=args.page_size)
     fb.gen_inputs(n)
     fb.warm_prefix()
     for i in range(args.warmup):
@@ -311,7 +314,7 @@ def run_few_shot(args, torch):
                         "distinct tokens) per step, one extend pass + one decode step, tree match/insert on host",
             "batch": fb.B, "prefix_len": fb.PREFIX, "suffix_len": fb.SUFFIX, "num_q_heads": fb.HQ,
             "num_kv_heads": fb.HKV, "head_dim": fb.D, "pool_slots": fb.SLOTS,
-            "kv_dtype": "fp8_e4m3" if fb.fp8 else "bf16",
+            "kv_dtype": "fp8_e4m3" if fb.fp8 else "bf16", "page_size": fb.page_size,
         },
         "roofline": {
             "bound": "mfma",
@@ -512,8 +515,9 @@ def run_chat(args, torch):
     from prefix_shared_kv_rt_amd.runtime import RadixRuntime, Scheduler
     from synth import workloads
     from synth.sources import QKVSource
-    wl = workloads.chat()
-    rt = RadixRuntime(wl.num_slots, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, torch.bfloat16, 256, wl.max_ctx)
+    wl = workloads.paged(workloads.chat(), args.page_size)
+    rt = RadixRuntime(wl.num_slots, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, torch.bfloat16, 256, wl.max_ctx,
+                      kv_fp8_scales=(1.0, 1.0) if args.kv_dtype == "fp8" else None, page_size=wl.page_size)
     src = QKVSource(wl.seed, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, torch.bfloat16)
     rt.events = []
     sch = Scheduler(rt, wl.requests, src, max_running=256, max_extend_tokens=16384, policy=args.policy,
@@ -564,7 +568,8 @@ def run_chat(args, torch):
         "config": {"workload": "multi-turn chat: 512-token system prompt, 256 sessions x 4 turns, "
                                "U{128..384} user + 128 generated tokens per turn, pool 60% of the working set; "
                                "one pass of the whole workload, a step = one scheduler iteration",
-                   "policy": args.policy, "chunk_size": args.chunk_size,
+                   "policy": args.policy, "chunk_size": args.chunk_size, "page_size": wl.page_size,
+                   "kv_dtype": "fp8_e4m3" if args.kv_dtype == "fp8" else "bf16",
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "pool_slots": wl.num_slots},
         "wall_tokens_per_s": tokens / wall,

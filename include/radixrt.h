@@ -70,32 +70,46 @@ int rt_abi_version(void);
 
 /* ---------------------------------------------------------------- pool --
  * Token-slot allocator [P1 "one shared pool"; P2 freeing a leaf's slots].
- * Free slots form a FIFO list that starts as 1..num_slots ascending;
- * allocation takes from the head, frees append at the tail in the order
- * given. */
+ * Slots come in pages of page_size (1 unless created paged): page j holds
+ * slots 1 + j*page_size .. (j+1)*page_size [P2 prefix-match excerpt: the
+ * engine compares keys under a configurable page size].  Free pages form a
+ * FIFO list that starts ascending; allocation takes whole pages from the
+ * head, a free appends the distinct pages of the given slots at the tail in
+ * order of first appearance.  With one-slot pages: a FIFO of slots, frees
+ * appended in the order given. */
 
 /* num_slots >= 1.  *out receives the pool (free with rt_pool_destroy). */
 int rt_pool_create(int32_t num_slots, rt_pool** out);
+/* A pool of pages: num_slots a positive multiple of page_size >= 1. */
+int rt_pool_create_paged(int32_t num_slots, int32_t page_size, rt_pool** out);
 void rt_pool_destroy(rt_pool* pool);
-/* Take n slots (host out_slots[n]); RT_ERR_OOM if fewer are free (nothing
- * taken).  Never evicts: see rt_alloc_with_evict. */
+int32_t rt_pool_page_size(const rt_pool* pool);
+/* Take n slots (host out_slots[n]): n / page_size whole pages, each page's
+ * slots in order.  RT_ERR_INVALID if n is not a whole number of pages;
+ * RT_ERR_OOM if fewer are free (nothing taken).  Never evicts: see
+ * rt_alloc_with_evict. */
 int rt_pool_alloc(rt_pool* pool, int32_t n, int32_t* out_slots);
-/* Return n slots (host).  Each must be in 1..num_slots; RT_ERR_INVALID if a
- * slot is out of range or the free list would exceed num_slots (nothing is
- * freed then). */
+/* Return the pages of n slots (host).  Each must be in 1..num_slots;
+ * RT_ERR_INVALID if a slot is out of range or the free list would exceed
+ * the pool (nothing is freed then). */
 int rt_pool_free(rt_pool* pool, const int32_t* slots, int32_t n);
+/* Free slots (whole free pages times page_size) and all usable slots. */
 int32_t rt_pool_available(const rt_pool* pool);
 int32_t rt_pool_capacity(const rt_pool* pool);
-/* Copy the free list, head first, into host out[cap]; *out_len = its length
- * (RT_ERR_INVALID, nothing copied, if cap < length). */
+/* Copy the free list as slots, head page first, each page's slots in
+ * order, into host out[cap]; *out_len = its length (RT_ERR_INVALID, nothing
+ * copied, if cap < length). */
 int rt_pool_free_list(const rt_pool* pool, int32_t* out, int32_t cap, int32_t* out_len);
 
 /* ---------------------------------------------------------------- tree --
  * Radix tree of cached prefixes bound to a pool [P1, P2].  A node holds a
  * run of tokens and the KV slot of each; children are keyed by their first
- * token.  An LRU clock advances by one per rt_match_prefix / rt_insert
- * call; every node such a call walks through or creates is stamped with it.
- * Eviction order is (last access, node id) ascending. */
+ * page of tokens (their first token with one-slot pages).  Keys are compared
+ * in whole pages of the pool's page size: matches, splits and inserts fall
+ * on page boundaries and a trailing partial page never matches.  An LRU
+ * clock advances by one per rt_match_prefix / rt_insert call; every node
+ * such a call walks through or creates is stamped with it.  Eviction order
+ * is (last access, node id) ascending. */
 
 int rt_tree_create(rt_pool* pool, rt_tree** out);
 /* Destroys the tree; its slots are NOT returned to the pool. */
@@ -110,7 +124,8 @@ void rt_tree_destroy(rt_tree* tree);
 int rt_match_prefix(rt_tree* tree, const int32_t* tokens, int32_t n, int32_t* out_slots,
                     int32_t out_cap, int32_t* out_len, rt_node* out_last);
 
-/* Insert tokens[n] with their slots[n] (host) [P2 walkthrough step 2].
+/* Insert tokens[n] with their slots[n] (host) [P2 walkthrough step 2]; n
+ * must be a whole number of pages (RT_ERR_INVALID otherwise).
  * Diverging edges are split; the unmatched rest becomes a new leaf.  Where
  * the tree already holds a token its slot is kept; *out_present_len (may be
  * NULL) receives how many leading tokens were already present, and the
@@ -135,10 +150,26 @@ int rt_unlock(rt_tree* tree, rt_node node);
 int rt_evict_lru_leaves(rt_tree* tree, int32_t num_tokens, int32_t* out_evicted,
                         int32_t* out_freed_slots, int32_t freed_cap);
 
-/* Allocate n slots, first evicting the deficit (n - free) if the pool is
- * short.  RT_ERR_OOM if still short: nothing is allocated, but evictions
- * already made stand.  *out_evicted (may be NULL) = tokens evicted. */
+/* Allocate n slots (whole pages), first evicting the deficit (n - free) if
+ * the pool is short.  RT_ERR_OOM if still short: nothing is allocated, but
+ * evictions already made stand.  *out_evicted (may be NULL) = tokens
+ * evicted. */
 int rt_alloc_with_evict(rt_tree* tree, int32_t n, int32_t* out_slots, int32_t* out_evicted);
+
+/* Slots for runs of positions of requests, by the page rule: run i is
+ * positions first_positions[i] .. + counts[i] - 1 of slot-table row rows[i]
+ * (host table req_to_token, row stride `stride`).  A position that starts a
+ * page (position % page_size == 0) takes a fresh page and its first slot;
+ * the fresh pages for all runs are allocated at once (evicting first if
+ * short, as rt_alloc_with_evict) and taken in run order.  Any other position
+ * takes the slot after the previous position's, read from its row (which
+ * must hold that request's slot).  Every slot is written into its row and,
+ * concatenated in run order, into host out_slots (out_cap entries).
+ * *out_evicted (may be NULL) = tokens evicted.  With one-slot pages this is
+ * rt_alloc_with_evict of all positions, in order. */
+int rt_alloc_positions(rt_tree* tree, int32_t n_runs, const int32_t* rows, const int32_t* first_positions,
+                       const int32_t* counts, int32_t* req_to_token, int64_t stride, int32_t* out_slots,
+                       int64_t out_cap, int32_t* out_evicted);
 
 /* Tokens held by unlocked nodes / by locked nodes (root excluded). */
 int64_t rt_evictable_size(const rt_tree* tree);
@@ -146,7 +177,7 @@ int64_t rt_protected_size(const rt_tree* tree);
 int64_t rt_tree_num_nodes(const rt_tree* tree);
 
 /* Canonical text dump into host buf[cap]: pre-order from the root, children
- * by first token ascending, one line per node
+ * by first page ascending (lexicographic), one line per node
  *   "<id> <parent id> <lock count> <last access> k=<t,t,...> v=<s,s,...>\n"
  * with the root as "0 -1 0 0 k= v=".  *out_len = bytes needed (without a
  * terminating NUL, which is written when it fits); RT_ERR_INVALID if cap is
@@ -159,10 +190,11 @@ int rt_tree_dump(const rt_tree* tree, char* buf, int64_t cap, int64_t* out_len);
  * tokens[token_offsets[i] .. token_offsets[i+1]) (host).  Row r of the slot
  * table is req_to_token[r * stride .. r * stride + stride) (host). */
 
-/* For i in order: rt_match_prefix, rt_lock; then one rt_alloc_with_evict of
- * sum_i (len_i - prefix_len_i) slots, split among the requests in order.
- * Row rows[i] of req_to_token receives the matched slots followed by the
- * new ones.  Outputs (host, n entries): prefix_lens, extend_lens, nodes;
+/* For i in order: rt_match_prefix, rt_lock; then one rt_alloc_positions of
+ * positions prefix_len_i .. len_i - 1 of every request (with one-slot
+ * pages: sum_i (len_i - prefix_len_i) slots split among the requests in
+ * order).  Row rows[i] of req_to_token receives the matched slots followed
+ * by the new ones.  Outputs (host, n entries): prefix_lens, extend_lens, nodes;
  * out_cache_loc receives the new slots (cap out_cache_cap), *out_num_new
  * their count.  On RT_ERR_OOM every lock taken here is released (the
  * matches' splits and stamps remain).  RT_ERR_INVALID if a request is
@@ -172,16 +204,20 @@ int rt_admit_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_of
                    int32_t* prefix_lens, int32_t* extend_lens, rt_node* nodes,
                    int32_t* out_cache_loc, int64_t out_cache_cap, int64_t* out_num_new);
 
-/* One decode step's slots: rt_alloc_with_evict(n), then
+/* One decode step's slots: rt_alloc_positions of one position
+ * positions[i] per row rows[i], which sets
  * req_to_token[rows[i] * stride + positions[i]] = slot i (host).
  * out_cache_loc (host, n) receives the slots. */
 int rt_decode_slots_batch(rt_tree* tree, int32_t n, const int32_t* rows, const int32_t* positions,
                           int32_t* req_to_token, int64_t stride, int32_t* out_cache_loc);
 
-/* Finish requests: for i in order, rt_insert(tokens_i, row rows[i] of
- * req_to_token), free the row's slots in [prefix_lens[i], present_len)
- * (the duplicates the tree already held), then rt_unlock(nodes[i]).
- * *out_freed (may be NULL) = total duplicate slots freed. */
+/* Finish requests: for i in order, rt_insert of the whole pages of tokens_i
+ * (the first len_i - len_i % page_size) with row rows[i] of req_to_token,
+ * then one rt_pool_free of the row's slots in [prefix_lens[i],
+ * present_len) (the duplicates the tree already held) followed by those in
+ * [aligned len, len_i) (the trailing partial page), then
+ * rt_unlock(nodes[i]).  *out_freed (may be NULL) = total slots passed to
+ * those frees. */
 int rt_finish_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_offsets,
                     int32_t n, const int32_t* req_to_token, int64_t stride, const int32_t* rows,
                     const int32_t* prefix_lens, const rt_node* nodes, int64_t* out_freed);

@@ -19,7 +19,7 @@ RT_F32, RT_BF16 = 0, 1
 EXPORTS = [
     "rt_last_error", "rt_abi_version",
     "rt_pool_create", "rt_pool_destroy", "rt_pool_alloc", "rt_pool_free", "rt_pool_available",
-    "rt_pool_capacity", "rt_pool_free_list",
+    "rt_pool_capacity", "rt_pool_free_list", "rt_pool_create_paged", "rt_pool_page_size", "rt_alloc_positions",
     "rt_tree_create", "rt_tree_destroy", "rt_match_prefix", "rt_insert", "rt_lock", "rt_unlock",
     "rt_evict_lru_leaves", "rt_alloc_with_evict", "rt_evictable_size", "rt_protected_size",
     "rt_tree_num_nodes", "rt_tree_dump", "rt_admit_batch", "rt_decode_slots_batch", "rt_finish_batch",
@@ -59,6 +59,10 @@ def lib():
             "rt_last_error": (ctypes.c_char_p, []),
             "rt_abi_version": (ctypes.c_int, []),
             "rt_pool_create": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(_vp)]),
+            "rt_pool_create_paged": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_vp)]),
+            "rt_pool_page_size": (ctypes.c_int32, [_vp]),
+            "rt_alloc_positions": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p, _i32p, _i32p, _i32p, ctypes.c_int64,
+                                                  _i32p, ctypes.c_int64, _i32p]),
             "rt_pool_destroy": (None, [_vp]),
             "rt_pool_alloc": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p]),
             "rt_pool_free": (ctypes.c_int, [_vp, _i32p, ctypes.c_int32]),
@@ -143,10 +147,17 @@ def _i32(x):
 
 
 # ------------------------------------------------------------------ host --
-def rt_pool_create(num_slots):
+def rt_pool_create(num_slots, page_size=1):
     h = _vp()
-    _check(lib().rt_pool_create(int(num_slots), ctypes.byref(h)))
+    if page_size == 1:
+        _check(lib().rt_pool_create(int(num_slots), ctypes.byref(h)))
+    else:
+        _check(lib().rt_pool_create_paged(int(num_slots), int(page_size), ctypes.byref(h)))
     return h
+
+
+def rt_pool_page_size(pool):
+    return int(lib().rt_pool_page_size(pool))
 
 
 def rt_pool_destroy(pool):
@@ -232,6 +243,20 @@ def rt_alloc_with_evict(tree, n):
     ev = ctypes.c_int32()
     _check(lib().rt_alloc_with_evict(tree, int(n), _p32(out), ctypes.byref(ev)))
     return out[:int(n)].copy(), int(ev.value)
+
+
+def rt_alloc_positions(tree, rows, first_positions, counts, req_to_token):
+    """Slots of runs of positions by the page rule, written into the host
+    slot-table rows; returns (slots concatenated in run order, tokens
+    evicted)."""
+    rows, first, cnt = _i32(rows), _i32(first_positions), _i32(counts)
+    assert req_to_token.dtype == np.int32 and req_to_token.flags.c_contiguous
+    total = int(cnt.sum()) if cnt.size else 0
+    out = np.empty(max(total, 1), dtype=np.int32)
+    ev = ctypes.c_int32()
+    _check(lib().rt_alloc_positions(tree, rows.size, _p32(rows), _p32(first), _p32(cnt), _p32(req_to_token),
+                                    req_to_token.shape[1], _p32(out), out.size, ctypes.byref(ev)))
+    return out[:total].copy(), int(ev.value)
 
 
 def rt_evictable_size(tree):

@@ -31,42 +31,90 @@
 namespace rt {
 
 // ------------------------------------------------------------------ pool --
+// Slots 1..capacity in pages of `page` slots: page j holds slots
+// 1 + j*page .. (j+1)*page.  The free list is a FIFO ring of pages, each held
+// as its first slot (with one-slot pages that is the slot itself).  An
+// allocation takes whole pages from the head; a free appends the distinct
+// pages of the given slots at the tail, in order of first appearance.
 struct Pool {
-  int32_t capacity = 0;
-  std::vector<int32_t> ring;  // FIFO free list of capacity slots
-  int64_t head = 0;           // index of the first free slot in ring
-  int32_t count = 0;          // number of free slots
+  int32_t capacity = 0;       // slots
+  int32_t page = 1;           // slots per page
+  int32_t pages = 0;          // capacity / page
+  std::vector<int32_t> ring;  // first slot of each free page, FIFO
+  int64_t head = 0;           // index of the first free page in ring
+  int32_t count = 0;          // number of free pages
+  std::vector<uint32_t> mark; // per page: call number of its last free (page > 1)
+  uint32_t epoch = 0;
 
-  explicit Pool(int32_t n) : capacity(n), ring(n) {
-    for (int32_t i = 0; i < n; ++i) ring[i] = i + 1;
-    count = n;
+  Pool(int32_t n, int32_t page_size) : capacity(n), page(page_size), pages(n / page_size), ring(n / page_size) {
+    for (int32_t j = 0; j < pages; ++j) ring[j] = 1 + j * page;
+    count = pages;
+    if (page > 1) mark.assign(size_t(pages), 0u);
   }
-  // The free list is a ring: slots leave at head and return at head + count
-  // (mod capacity).  Runs are moved with at most two block copies.
+  int64_t free_slots() const { return int64_t(count) * page; }
   int alloc(int32_t n, int32_t* out) {
-    if (n < 0) return fail(RT_ERR_INVALID, "negative allocation");
-    if (n > count) return fail(RT_ERR_OOM, "pool: need " + std::to_string(n) + ", free " +
-                                               std::to_string(count));
-    const int64_t first = std::min<int64_t>(n, capacity - head);
-    std::memcpy(out, ring.data() + head, sizeof(int32_t) * first);
-    std::memcpy(out + first, ring.data(), sizeof(int32_t) * (n - first));
-    head += n;
-    if (head >= capacity) head -= capacity;
-    count -= n;
+    if (n < 0 || n % page) return fail(RT_ERR_INVALID, "pool: allocation must be a whole number of pages");
+    const int32_t k = n / page;
+    if (k > count) return fail(RT_ERR_OOM, "pool: need " + std::to_string(n) + ", free " +
+                                               std::to_string(free_slots()));
+    if (page == 1) {  // runs of slots move with at most two block copies
+      const int64_t first = std::min<int64_t>(k, pages - head);
+      std::memcpy(out, ring.data() + head, sizeof(int32_t) * first);
+      std::memcpy(out + first, ring.data(), sizeof(int32_t) * (k - first));
+    } else {
+      for (int32_t i = 0; i < k; ++i) {
+        const int32_t f = ring[(head + i) % pages];
+        for (int32_t t = 0; t < page; ++t) out[int64_t(i) * page + t] = f + t;
+      }
+    }
+    head += k;
+    if (head >= pages) head -= pages;
+    count -= k;
     return RT_OK;
   }
   int release(const int32_t* slots, int64_t n) {
     if (n < 0) return fail(RT_ERR_INVALID, "negative free");
-    if (int64_t(count) + n > capacity) return fail(RT_ERR_INVALID, "pool: free list overflow (double free?)");
     for (int64_t i = 0; i < n; ++i)
       if (slots[i] < 1 || slots[i] > capacity)
         return fail(RT_ERR_INVALID, "pool: slot " + std::to_string(slots[i]) + " out of range");
     int64_t tail = head + count;
-    if (tail >= capacity) tail -= capacity;
-    const int64_t first = std::min<int64_t>(n, capacity - tail);
-    std::memcpy(ring.data() + tail, slots, sizeof(int32_t) * first);
-    std::memcpy(ring.data(), slots + first, sizeof(int32_t) * (n - first));
-    count += int32_t(n);
+    if (tail >= pages) tail -= pages;
+    if (page == 1) {
+      if (int64_t(count) + n > pages) return fail(RT_ERR_INVALID, "pool: free list overflow (double free?)");
+      const int64_t first = std::min<int64_t>(n, pages - tail);
+      std::memcpy(ring.data() + tail, slots, sizeof(int32_t) * first);
+      std::memcpy(ring.data(), slots + first, sizeof(int32_t) * (n - first));
+      count += int32_t(n);
+      return RT_OK;
+    }
+    // distinct pages in order of first appearance
+    if (++epoch == 0) {
+      std::fill(mark.begin(), mark.end(), 0u);
+      epoch = 1;
+    }
+    int64_t k = 0;
+    for (int64_t i = 0; i < n; ++i) {
+      const int32_t j = (slots[i] - 1) / page;
+      if (mark[j] != epoch) {
+        mark[j] = epoch;
+        ++k;
+      }
+    }
+    if (int64_t(count) + k > pages) return fail(RT_ERR_INVALID, "pool: free list overflow (double free?)");
+    ++epoch;  // second pass appends each page at its first appearance
+    if (epoch == 0) {
+      std::fill(mark.begin(), mark.end(), 0u);
+      epoch = 1;
+    }
+    for (int64_t i = 0; i < n; ++i) {
+      const int32_t j = (slots[i] - 1) / page;
+      if (mark[j] != epoch) {
+        mark[j] = epoch;
+        ring[tail] = 1 + j * page;
+        if (++tail == pages) tail = 0;
+      }
+    }
+    count += int32_t(k);
     return RT_OK;
   }
 };
@@ -74,51 +122,24 @@ struct Pool {
 // ------------------------------------------------------------------ tree --
 struct Node;
 
-// Children by first token: a short array up to kSmall entries, then a hash map.
+// Hash of a key's first page (one-token pages hash to the token itself).
+inline uint64_t page_hash(const int32_t* t, int32_t p) {
+  if (p == 1) return uint32_t(t[0]);
+  uint64_t h = 1469598103934665603ull;
+  for (int32_t i = 0; i < p; ++i) h = (h ^ uint32_t(t[i])) * 1099511628211ull;
+  return h;
+}
+
+// Children by their first page: a short array up to kSmall entries, then a
+// hash multimap; every lookup confirms the page itself.
 class ChildMap {
  public:
   static constexpr size_t kSmall = 8;
-  Node* find(int32_t tok) const {
-    if (!big_.empty()) {
-      auto it = big_.find(tok);
-      return it == big_.end() ? nullptr : it->second;
-    }
-    for (const auto& kv : small_)
-      if (kv.first == tok) return kv.second;
-    return nullptr;
-  }
-  // Inserts or replaces.
-  void set(int32_t tok, Node* n) {
-    if (!big_.empty()) {
-      big_[tok] = n;
-      return;
-    }
-    for (auto& kv : small_)
-      if (kv.first == tok) {
-        kv.second = n;
-        return;
-      }
-    if (small_.size() < kSmall) {
-      small_.emplace_back(tok, n);
-      return;
-    }
-    big_.reserve(2 * kSmall);
-    for (const auto& kv : small_) big_.emplace(kv.first, kv.second);
-    big_.emplace(tok, n);
-    small_.clear();
-  }
-  void erase(int32_t tok) {
-    if (!big_.empty()) {
-      big_.erase(tok);
-      return;
-    }
-    for (size_t i = 0; i < small_.size(); ++i)
-      if (small_[i].first == tok) {
-        small_[i] = small_.back();
-        small_.pop_back();
-        return;
-      }
-  }
+  Node* find(uint64_t h, const int32_t* page, int32_t p) const;
+  // Puts n (whose key starts with the page hashed to h) in place of the child
+  // with the same first page, or adds it.
+  void set(uint64_t h, Node* n, int32_t p);
+  void erase(uint64_t h, const int32_t* page, int32_t p);
   bool empty() const { return small_.empty() && big_.empty(); }
   void clear() {
     small_.clear();
@@ -126,13 +147,13 @@ class ChildMap {
   }
   template <typename F>
   void for_each(F f) const {
-    for (const auto& kv : small_) f(kv.first, kv.second);
-    for (const auto& kv : big_) f(kv.first, kv.second);
+    for (const auto& kv : small_) f(kv.second);
+    for (const auto& kv : big_) f(kv.second);
   }
 
  private:
-  std::vector<std::pair<int32_t, Node*>> small_;
-  std::unordered_map<int32_t, Node*> big_;
+  std::vector<std::pair<uint64_t, Node*>> small_;
+  std::unordered_multimap<uint64_t, Node*> big_;
 };
 
 struct Node {
@@ -146,8 +167,70 @@ struct Node {
   int64_t leaf_pos = -1;  // index in Tree::leaves while an eviction candidate
 };
 
+inline bool same_page(const Node* n, const int32_t* page, int32_t p) {
+  return p == 1 ? n->key[0] == page[0] : std::memcmp(n->key.data(), page, sizeof(int32_t) * p) == 0;
+}
+
+inline Node* ChildMap::find(uint64_t h, const int32_t* page, int32_t p) const {
+  if (!big_.empty()) {
+    auto range = big_.equal_range(h);
+    for (auto it = range.first; it != range.second; ++it)
+      if (same_page(it->second, page, p)) return it->second;
+    return nullptr;
+  }
+  for (const auto& kv : small_)
+    if (kv.first == h && same_page(kv.second, page, p)) return kv.second;
+  return nullptr;
+}
+
+inline void ChildMap::set(uint64_t h, Node* n, int32_t p) {
+  const int32_t* page = n->key.data();
+  if (!big_.empty()) {
+    auto range = big_.equal_range(h);
+    for (auto it = range.first; it != range.second; ++it)
+      if (same_page(it->second, page, p)) {
+        it->second = n;
+        return;
+      }
+    big_.emplace(h, n);
+    return;
+  }
+  for (auto& kv : small_)
+    if (kv.first == h && same_page(kv.second, page, p)) {
+      kv.second = n;
+      return;
+    }
+  if (small_.size() < kSmall) {
+    small_.emplace_back(h, n);
+    return;
+  }
+  big_.reserve(2 * kSmall);
+  for (const auto& kv : small_) big_.emplace(kv.first, kv.second);
+  big_.emplace(h, n);
+  small_.clear();
+}
+
+inline void ChildMap::erase(uint64_t h, const int32_t* page, int32_t p) {
+  if (!big_.empty()) {
+    auto range = big_.equal_range(h);
+    for (auto it = range.first; it != range.second; ++it)
+      if (same_page(it->second, page, p)) {
+        big_.erase(it);
+        return;
+      }
+    return;
+  }
+  for (size_t i = 0; i < small_.size(); ++i)
+    if (small_[i].first == h && same_page(small_[i].second, page, p)) {
+      small_[i] = small_.back();
+      small_.pop_back();
+      return;
+    }
+}
+
 struct Tree {
   Pool* pool;
+  int32_t P;                                   // slots per page (the pool's)
   uint64_t clock = 0;
   int64_t next_id = 1;
   std::unique_ptr<Node> root_owner;
@@ -160,7 +243,7 @@ struct Tree {
   int64_t evictable = 0;
   int64_t protected_ = 0;
 
-  explicit Tree(Pool* p) : pool(p), root_owner(new Node()) {
+  explicit Tree(Pool* p) : pool(p), P(p->page), root_owner(new Node()) {
     root = root_owner.get();
     root->id = 0;
   }
@@ -229,11 +312,11 @@ struct Tree {
     Node* parent = child->parent;
     Node* upper = make_node(parent, child->key.data(), child->value.data(), k, child->last_access);
     upper->lock_ref = child->lock_ref;
-    parent->children.set(child->key[0], upper);
+    parent->children.set(page_hash(upper->key.data(), P), upper, P);
     child->key.erase(child->key.begin(), child->key.begin() + k);
     child->value.erase(child->value.begin(), child->value.begin() + k);
     child->parent = upper;
-    upper->children.set(child->key[0], child);
+    upper->children.set(page_hash(child->key.data(), P), child, P);
     // token counts are unchanged (same lock count on both parts)
     refresh(upper);
     return upper;
@@ -251,15 +334,18 @@ struct Tree {
   }
 
   // Returns the last matched node; appends matched slots to out (if given).
+  // Keys are compared in whole pages: a trailing partial page never matches.
   Node* match(const int32_t* tokens, int64_t n, int32_t* out, int64_t* out_len) {
     uint64_t stamp = ++clock;
     Node* node = root;
     int64_t pos = 0, len = 0;
+    n -= n % P;
     while (pos < n) {
-      Node* child = node->children.find(tokens[pos]);
+      Node* child = node->children.find(page_hash(tokens + pos, P), tokens + pos, P);
       if (!child) break;
       child->last_access = stamp;
       int64_t k = common_len(child->key, tokens + pos, n - pos);
+      k -= k % P;  // at least one page: the first page matched
       if (k < int64_t(child->key.size())) {
         Node* upper = split(child, k);
         if (out) std::memcpy(out + len, upper->value.data(), sizeof(int32_t) * k);
@@ -276,22 +362,24 @@ struct Tree {
     return node;
   }
 
+  // n must be a whole number of pages (checked by the callers).
   int64_t insert(const int32_t* tokens, const int32_t* slots, int64_t n) {
     uint64_t stamp = ++clock;
     Node* node = root;
     int64_t pos = 0;
     while (pos < n) {
-      Node* child = node->children.find(tokens[pos]);
+      Node* child = node->children.find(page_hash(tokens + pos, P), tokens + pos, P);
       if (!child) break;
       child->last_access = stamp;
       int64_t k = common_len(child->key, tokens + pos, n - pos);
+      k -= k % P;
       if (k < int64_t(child->key.size())) child = split(child, k);
       pos += k;
       node = child;
     }
     if (pos < n) {
       Node* leaf = make_node(node, tokens + pos, slots + pos, n - pos, stamp);
-      node->children.set(tokens[pos], leaf);
+      node->children.set(page_hash(leaf->key.data(), P), leaf, P);
       evictable += n - pos;
       refresh(node);
       refresh(leaf);
@@ -340,7 +428,7 @@ struct Tree {
       evicted += len;
       evictable -= len;
       Node* parent = x->parent;
-      parent->children.erase(x->key[0]);
+      parent->children.erase(page_hash(x->key.data(), P), x->key.data(), P);
       leaf_remove(x);
       drop_node(x);
       if (is_candidate(parent)) {
@@ -351,15 +439,49 @@ struct Tree {
     return evicted;
   }
 
+  // n slots (whole pages); the deficit is evicted first.
   int alloc_with_evict(int32_t n, int32_t* out, int32_t* out_evicted) {
-    if (n < 0) return fail(RT_ERR_INVALID, "negative allocation");
+    if (n < 0 || n % P) return fail(RT_ERR_INVALID, "allocation must be a whole number of pages");
     int64_t ev = 0;
-    if (n > pool->count) ev = evict(int64_t(n) - pool->count, nullptr);
+    if (n > pool->free_slots()) ev = evict(int64_t(n) - pool->free_slots(), nullptr);
     if (out_evicted) *out_evicted = int32_t(ev);
-    if (n > pool->count)
-      return fail(RT_ERR_OOM, "need " + std::to_string(n) + " slots, " + std::to_string(pool->count) +
+    if (n > pool->free_slots())
+      return fail(RT_ERR_OOM, "need " + std::to_string(n) + " slots, " + std::to_string(pool->free_slots()) +
                                   " free after evicting " + std::to_string(ev));
     return pool->alloc(n, out);
+  }
+
+  // Slots of runs of positions by the page rule: a position that starts a
+  // page takes a fresh page (allocated for all runs at once, evicting first
+  // if short, taken in run order) and its first slot; any other position
+  // takes the slot after the previous position's, read from that request's
+  // row.  Writes every slot into its row and into out (concatenated).
+  int alloc_positions(int32_t n_runs, const int32_t* rows, const int32_t* first, const int32_t* counts,
+                      int32_t* req_to_token, int64_t stride, int32_t* out, int64_t out_cap,
+                      int32_t* out_evicted) {
+    int64_t starts = 0, total = 0;
+    for (int32_t i = 0; i < n_runs; ++i) {
+      if (rows[i] < 0 || first[i] < 0 || counts[i] < 0 || int64_t(first[i]) + counts[i] > stride)
+        return fail(RT_ERR_INVALID, "alloc_positions: bad run " + std::to_string(i));
+      for (int64_t x = first[i]; x < int64_t(first[i]) + counts[i]; ++x)
+        if (x % P == 0) ++starts;
+      total += counts[i];
+    }
+    if (total > out_cap || (total > 0 && !out)) return fail(RT_ERR_INVALID, "alloc_positions: out too small");
+    if (starts * P > INT32_MAX) return fail(RT_ERR_INVALID, "alloc_positions: too many pages");
+    std::vector<int32_t> fresh(size_t(starts * P));
+    int rc = alloc_with_evict(int32_t(starts * P), fresh.data(), out_evicted);
+    if (rc != RT_OK) return rc;
+    int64_t next = 0, o = 0;
+    for (int32_t i = 0; i < n_runs; ++i) {
+      int32_t* row = req_to_token + int64_t(rows[i]) * stride;
+      for (int64_t x = first[i]; x < int64_t(first[i]) + counts[i]; ++x) {
+        const int32_t sl = (x % P == 0) ? fresh[size_t(next++ * P)] : row[x - 1] + 1;
+        row[x] = sl;
+        out[o++] = sl;
+      }
+    }
+    return RT_OK;
   }
 
   void dump_node(const Node* n, int64_t parent_id, std::string& s) const {
@@ -381,11 +503,14 @@ struct Tree {
       s += std::to_string(n->value[i]);
     }
     s += '\n';
-    std::vector<std::pair<int32_t, const Node*>> kids;
-    n->children.for_each([&](int32_t tok, const Node* c) { kids.emplace_back(tok, c); });
-    std::sort(kids.begin(), kids.end(),
-              [](const auto& a, const auto& b) { return a.first < b.first; });
-    for (auto& kv : kids) dump_node(kv.second, n->id, s);
+    // children by first page, lexicographic
+    std::vector<const Node*> kids;
+    n->children.for_each([&](const Node* c) { kids.push_back(c); });
+    const int32_t p = P;
+    std::sort(kids.begin(), kids.end(), [p](const Node* a, const Node* b) {
+      return std::lexicographical_compare(a->key.begin(), a->key.begin() + p, b->key.begin(), b->key.begin() + p);
+    });
+    for (const Node* c : kids) dump_node(c, n->id, s);
   }
 };
 
@@ -396,7 +521,7 @@ using rt::fail;
 
 struct rt_pool {
   rt::Pool impl;
-  explicit rt_pool(int32_t n) : impl(n) {}
+  rt_pool(int32_t n, int32_t page) : impl(n, page) {}
 };
 struct rt_tree {
   rt::Tree impl;
@@ -415,13 +540,18 @@ struct rt_tree {
 
 extern "C" {
 
-int rt_pool_create(int32_t num_slots, rt_pool** out) {
-  if (!out || num_slots < 1) return fail(RT_ERR_INVALID, "rt_pool_create: num_slots >= 1 and out required");
+int rt_pool_create_paged(int32_t num_slots, int32_t page_size, rt_pool** out) {
+  if (!out || num_slots < 1 || page_size < 1 || num_slots % page_size)
+    return fail(RT_ERR_INVALID, "rt_pool_create_paged: num_slots a positive multiple of page_size, out required");
   RT_GUARD_BEGIN
-  *out = new rt_pool(num_slots);
+  *out = new rt_pool(num_slots, page_size);
   return RT_OK;
   RT_GUARD_END
 }
+
+int rt_pool_create(int32_t num_slots, rt_pool** out) { return rt_pool_create_paged(num_slots, 1, out); }
+
+int32_t rt_pool_page_size(const rt_pool* pool) { return pool ? pool->impl.page : 0; }
 
 void rt_pool_destroy(rt_pool* pool) { delete pool; }
 
@@ -435,15 +565,17 @@ int rt_pool_free(rt_pool* pool, const int32_t* slots, int32_t n) {
   return pool->impl.release(slots, n);
 }
 
-int32_t rt_pool_available(const rt_pool* pool) { return pool ? pool->impl.count : 0; }
+int32_t rt_pool_available(const rt_pool* pool) { return pool ? int32_t(pool->impl.free_slots()) : 0; }
 int32_t rt_pool_capacity(const rt_pool* pool) { return pool ? pool->impl.capacity : 0; }
 
 int rt_pool_free_list(const rt_pool* pool, int32_t* out, int32_t cap, int32_t* out_len) {
   if (!pool || !out_len) return fail(RT_ERR_INVALID, "rt_pool_free_list: null argument");
   const rt::Pool& p = pool->impl;
-  *out_len = p.count;
-  if (cap < p.count || (p.count > 0 && !out)) return fail(RT_ERR_INVALID, "rt_pool_free_list: buffer too small");
-  for (int32_t i = 0; i < p.count; ++i) out[i] = p.ring[(p.head + i) % p.capacity];
+  const int32_t n = int32_t(p.free_slots());
+  *out_len = n;
+  if (cap < n || (n > 0 && !out)) return fail(RT_ERR_INVALID, "rt_pool_free_list: buffer too small");
+  for (int32_t i = 0; i < p.count; ++i)
+    for (int32_t t = 0; t < p.page; ++t) out[int64_t(i) * p.page + t] = p.ring[(p.head + i) % p.pages] + t;
   return RT_OK;
 }
 
@@ -474,6 +606,7 @@ int rt_match_prefix(rt_tree* tree, const int32_t* tokens, int32_t n, int32_t* ou
 int rt_insert(rt_tree* tree, const int32_t* tokens, const int32_t* slots, int32_t n,
               int32_t* out_present_len) {
   if (!tree || n < 0 || (n > 0 && (!tokens || !slots))) return fail(RT_ERR_INVALID, "rt_insert: bad argument");
+  if (n % tree->impl.P) return fail(RT_ERR_INVALID, "rt_insert: length is not a whole number of pages");
   RT_GUARD_BEGIN
   int64_t present = tree->impl.insert(tokens, slots, n);
   if (out_present_len) *out_present_len = int32_t(present);
@@ -509,6 +642,17 @@ int rt_evict_lru_leaves(rt_tree* tree, int32_t num_tokens, int32_t* out_evicted,
     std::memcpy(out_freed_slots, freed.data(), sizeof(int32_t) * m);
   }
   return RT_OK;
+  RT_GUARD_END
+}
+
+int rt_alloc_positions(rt_tree* tree, int32_t n_runs, const int32_t* rows, const int32_t* first_positions,
+                       const int32_t* counts, int32_t* req_to_token, int64_t stride, int32_t* out_slots,
+                       int64_t out_cap, int32_t* out_evicted) {
+  if (!tree || n_runs < 0 || (n_runs > 0 && (!rows || !first_positions || !counts || !req_to_token)) || stride < 1)
+    return fail(RT_ERR_INVALID, "rt_alloc_positions: bad argument");
+  RT_GUARD_BEGIN
+  return tree->impl.alloc_positions(n_runs, rows, first_positions, counts, req_to_token, stride, out_slots, out_cap,
+                                    out_evicted);
   RT_GUARD_END
 }
 
@@ -578,16 +722,13 @@ int rt_admit_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_of
     unlock_all();
     return fail(RT_ERR_INVALID, "rt_admit_batch: too many new tokens");
   }
-  int rc = t.alloc_with_evict(int32_t(new_total), out_cache_loc, nullptr);
+  // slots of positions [prefix, prefix + extend) of every request, by the
+  // page rule, written into the rows and into out_cache_loc
+  int rc = t.alloc_positions(n, rows, prefix_lens, extend_lens, req_to_token, stride, out_cache_loc,
+                             out_cache_cap, nullptr);
   if (rc != RT_OK) {
     unlock_all();
     return rc;
-  }
-  int64_t off = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    int32_t* row = req_to_token + int64_t(rows[i]) * stride;
-    std::memcpy(row + prefix_lens[i], out_cache_loc + off, sizeof(int32_t) * extend_lens[i]);
-    off += extend_lens[i];
   }
   (void)total;
   return RT_OK;
@@ -602,10 +743,9 @@ int rt_decode_slots_batch(rt_tree* tree, int32_t n, const int32_t* rows, const i
     if (rows[i] < 0 || positions[i] < 0 || positions[i] >= stride)
       return fail(RT_ERR_INVALID, "rt_decode_slots_batch: row or position out of range");
   RT_GUARD_BEGIN
-  int rc = tree->impl.alloc_with_evict(n, out_cache_loc, nullptr);
-  if (rc != RT_OK) return rc;
-  for (int32_t i = 0; i < n; ++i) req_to_token[int64_t(rows[i]) * stride + positions[i]] = out_cache_loc[i];
-  return RT_OK;
+  std::vector<int32_t> ones(size_t(n), 1);
+  return tree->impl.alloc_positions(n, rows, positions, ones.data(), req_to_token, stride, out_cache_loc, n,
+                                    nullptr);
   RT_GUARD_END
 }
 
@@ -628,11 +768,17 @@ int rt_finish_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_o
     const int32_t* tk = tokens + token_offsets[i];
     int64_t len = token_offsets[i + 1] - token_offsets[i];
     const int32_t* row = req_to_token + int64_t(rows[i]) * stride;
-    int64_t present = t.insert(tk, row, len);
-    if (present > prefix_lens[i]) {
-      int rc = t.pool->release(row + prefix_lens[i], present - prefix_lens[i]);
+    // the whole pages go into the tree; pages the tree already held and the
+    // trailing partial page go back to the pool, in one free
+    const int64_t aligned = len - len % t.P;
+    const int64_t present = t.insert(tk, row, aligned);
+    std::vector<int32_t> rel;
+    if (present > prefix_lens[i]) rel.assign(row + prefix_lens[i], row + present);
+    rel.insert(rel.end(), row + aligned, row + len);
+    if (!rel.empty()) {
+      int rc = t.pool->release(rel.data(), int64_t(rel.size()));
       if (rc != RT_OK) return rc;
-      freed += present - prefix_lens[i];
+      freed += int64_t(rel.size());
     }
     rt::Node* node = t.find(nodes[i]);
     if (!node || !t.unlock(node)) return fail(RT_ERR_INVALID, "rt_finish_batch: unlock failed");

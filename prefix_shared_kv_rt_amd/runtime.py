@@ -54,15 +54,16 @@ class RadixRuntime:
     K/V pools in FP8 (E4M3 codes, uint8) under bf16 queries and outputs."""
 
     def __init__(self, num_slots, num_q_heads, num_kv_heads, head_dim, dtype, max_reqs, max_ctx,
-                 device="cuda", stream=None, kv_fp8_scales=None):
+                 device="cuda", stream=None, kv_fp8_scales=None, page_size=1):
         self.num_slots = int(num_slots)
+        self.page_size = int(page_size)
         self.hq, self.hkv, self.d = int(num_q_heads), int(num_kv_heads), int(head_dim)
         self.dtype = dtype
         if kv_fp8_scales is not None and dtype not in (None, torch.bfloat16):
             raise ValueError("FP8 pools run under bf16 queries")
         self.kv_fp8_scales = None if kv_fp8_scales is None else (float(kv_fp8_scales[0]), float(kv_fp8_scales[1]))
         self.max_reqs, self.max_ctx = int(max_reqs), int(max_ctx)
-        self.pool = B.rt_pool_create(self.num_slots)
+        self.pool = B.rt_pool_create(self.num_slots, self.page_size)
         self.tree = B.rt_tree_create(self.pool)
         self.free_rows = list(range(self.max_reqs))
         self.sm_scale = 1.0 / float(np.sqrt(self.d))
@@ -239,12 +240,22 @@ class Scheduler:
                 still.append(r)
         self.pending = still
 
+    def _pages_left(self, total_len, held):
+        """Slots a request of total_len positions holding held of them still
+        needs: whole pages."""
+        p = self.rt.page_size
+        return (-(-total_len // p) - (-(-held // p))) * p
+
     def _finish(self, run, rec):
         rt = self.rt
         full = list(run.req.prompt) + list(run.req.gen)
         row = rt.r2t_host[run.row, :len(full)].copy()
-        present = B.rt_insert(rt.tree, full, row)
+        # whole pages into the tree; the tree's duplicates and the trailing
+        # partial page back to the pool
+        aligned = len(full) - len(full) % rt.page_size
+        present = B.rt_insert(rt.tree, full[:aligned], row[:aligned])
         dups = row[run.prefix_len:present] if present > run.prefix_len else row[:0]
+        dups = np.concatenate([dups, row[aligned:]])
         if dups.size:
             B.rt_pool_free(rt.pool, dups)
         B.rt_unlock(rt.tree, run.node)
@@ -258,8 +269,9 @@ class Scheduler:
         rec = {"admitted": [], "extend_loc": [], "extend_freed": [], "decode": [], "decode_freed": [],
                "finished": []}
         chunked = self.chunk_size is not None
-        reserved = sum(len(r.req.gen) - r.generated for r in self.running)
-        reserved += sum(len(r.req.prompt) - r.done + len(r.req.gen) for r in self.prefilling)
+        reserved = sum(self._pages_left(len(r.req.prompt) + len(r.req.gen), len(r.req.prompt) + r.generated)
+                       for r in self.running)
+        reserved += sum(self._pages_left(len(r.req.prompt) + len(r.req.gen), r.done) for r in self.prefilling)
         budget = self.chunk_size if chunked else self.max_extend_tokens
         chunks = []  # (run, first token, tokens) of this iteration's extend, in launch order
         for r in self.prefilling:
@@ -282,7 +294,7 @@ class Scheduler:
             B.rt_lock(rt.tree, node)
             p = len(slots)
             e = len(req.prompt) - p
-            need = e + len(req.gen)
+            need = self._pages_left(len(req.prompt) + len(req.gen), p)
             avail = B.rt_pool_available(rt.pool) + B.rt_evictable_size(rt.tree) - reserved
             if need > avail or (not chunked and admitted and e > budget):
                 B.rt_unlock(rt.tree, node)
@@ -303,7 +315,10 @@ class Scheduler:
 
         total = sum(n for _, _, n in chunks)
         if total > 0:
-            loc, evicted = B.rt_alloc_with_evict(rt.tree, total)
+            # slots by the page rule, written into the host rows as well
+            loc, evicted = B.rt_alloc_positions(rt.tree, [r.row for r, _, _ in chunks],
+                                                [start for _, start, _ in chunks], [n for _, _, n in chunks],
+                                                rt.r2t_host)
             rec["extend_loc"] = [int(x) for x in loc]
             rec["extend_freed_tokens"] = evicted
         else:
@@ -351,12 +366,11 @@ class Scheduler:
 
         dec = [r for r in self.running if r.admit_iter < it]
         if dec:
-            slots, evicted = B.rt_alloc_with_evict(rt.tree, len(dec))
-            rec["decode_freed_tokens"] = evicted
             positions = np.array([len(r.req.prompt) + r.generated for r in dec], dtype=np.int32)
             rows = np.array([r.row for r in dec], dtype=np.int32)
+            slots, evicted = B.rt_alloc_positions(rt.tree, rows, positions, np.ones(len(dec), np.int32), rt.r2t_host)
+            rec["decode_freed_tokens"] = evicted
             for r, s, pos in zip(dec, slots, positions):
-                rt.r2t_host[r.row, pos] = s
                 rec["decode"].append((r.req.rid, int(pos), int(s)))
             o = None
             if rt.device is not None:

@@ -34,14 +34,15 @@ def check_few_shot(fb, i):
     return {"max_abs_err": worst, "tol": TOL, "ok": worst <= TOL}
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
-def test_few_shot_full_size_bench_path(kv_dtype):
+@pytest.mark.parametrize("kv_dtype,page", [("bf16", 1), ("fp8", 1), ("bf16", 16)])
+def test_few_shot_full_size_bench_path(kv_dtype, page):
     """64 requests x (1024 shared + 128 distinct) per step, three steps: the
     extend rows actually computed (position >= matched prefix) and the
     decode row of sampled requests (bf16 pool, or FP8 E4M3 pool at unit
-    scales against attention over the values the FP8 pool holds)."""
-    print(f"few-shot full size, {kv_dtype} pool", flush=True)
-    fb = bench.FewShotBench(3, torch, B, torch_gen, kv_dtype=kv_dtype)
+    scales against attention over the values the FP8 pool holds; token
+    slots or pages of 16)."""
+    print(f"few-shot full size, {kv_dtype} pool, pages of {page}", flush=True)
+    fb = bench.FewShotBench(3, torch, B, torch_gen, kv_dtype=kv_dtype, page_size=page)
     fb.gen_inputs(3)
     fb.warm_prefix()
     worst = 0.0

@@ -29,7 +29,8 @@ def run_both(wl, want=None, max_running=256, max_extend_tokens=16384, max_reqs=N
             outs[(kind, rid, step)] = o.float().cpu().numpy()
 
     rt = RadixRuntime(wl.num_slots, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, TORCH_DT[wl.dtype],
-                      max_reqs or max(max_running, 8), wl.max_ctx, kv_fp8_scales=kv_fp8_scales)
+                      max_reqs or max(max_running, 8), wl.max_ctx, kv_fp8_scales=kv_fp8_scales,
+                      page_size=wl.page_size)
     src = QKVSource(wl.seed, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, TORCH_DT[wl.dtype])
     dg = DecodeGraphs(rt, max_batch=max_running) if graphs else None
     sch = Scheduler(rt, wl.requests, src, max_running=max_running, max_extend_tokens=max_extend_tokens,
@@ -143,5 +144,28 @@ def test_small_chat_fp8_pool(scales, graphs):
     sel = lambda kind, rid, step: kind == "ext" or step in (0, 5)
     ora, sch, outs, dump, free = run_both(wl, want=sel, max_running=4, max_extend_tokens=128, kv_fp8_scales=scales,
                                           graphs=graphs)
+    check_host_identical(ora, sch, dump, free)
+    check_outputs(ora, outs, TOL["bf16"])
+
+
+@pytest.mark.parametrize("page,graphs,chunk", [(16, False, None), (4, True, None), (16, False, 24)])
+def test_small_chat_paged(page, graphs, chunk):
+    """Pools of pages: slots by the page rule in the slot table, the same
+    kernels; host decisions bit-exact and attention within tolerance."""
+    print(f"chat (6 sessions x 3 turns, pool 60%, pages of {page}, graphs {graphs}, chunk {chunk})", flush=True)
+    wl = workloads.paged(workloads.chat(sessions=6, turns=3, system_len=64, user_lo=16, user_hi=48, gen_len=6),
+                         page)
+    sel = lambda kind, rid, step: kind == "ext" or step in (0, 5)
+    ora, sch, outs, dump, free = run_both(wl, want=sel, max_running=4, max_extend_tokens=128, graphs=graphs,
+                                          chunk_size=chunk)
+    check_host_identical(ora, sch, dump, free)
+    check_outputs(ora, outs, TOL["bf16"])
+
+
+def test_small_few_shot_paged():
+    print("few-shot (8 x [256 + 64], 2 decode steps), pages of 16", flush=True)
+    wl = workloads.paged(workloads.few_shot(batch=8, prefix_len=256, suffix_len=64, decode_steps=2,
+                                            num_slots=4096), 16)
+    ora, sch, outs, dump, free = run_both(wl)
     check_host_identical(ora, sch, dump, free)
     check_outputs(ora, outs, TOL["bf16"])

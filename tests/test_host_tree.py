@@ -30,11 +30,12 @@ def test_library_exports_every_declared_symbol():
 class Pair:
     """The library tree and the oracle tree driven in lockstep."""
 
-    def __init__(self, num_slots):
+    def __init__(self, num_slots, page_size=1):
         self.num_slots = num_slots
-        self.cpool = B.rt_pool_create(num_slots)
+        self.page = page_size
+        self.cpool = B.rt_pool_create(num_slots, page_size)
         self.ctree = B.rt_tree_create(self.cpool)
-        self.opool = NaivePool(num_slots)
+        self.opool = NaivePool(num_slots, page_size)
         self.otree = NaiveRadixTree(self.opool)
 
     def close(self):
@@ -264,4 +265,63 @@ def test_batch_helpers_equal_the_primitive_sequence(seed):
                 pr.opool.release(row[pl[i]:present])
             pr.otree.unlock(onodes[i])
         pr.same()
+    pr.close()
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("page", [2, 4])
+def test_random_paged_operations_match_oracle(seed, page):
+    """Pages: page-aligned matches and inserts, slots by the page rule
+    (fresh pages at page starts, the next slot otherwise), finishes that free
+    the tree's duplicates and the trailing partial page, evictions of whole
+    pages; library and oracle in lockstep."""
+    rng = random.Random(1000 * page + seed)
+    pr = Pair(page * rng.choice([20, 40, 100]), page)
+    assert B.rt_pool_page_size(pr.cpool) == page
+    stride = 64
+    r2t = np.zeros((1, stride), dtype=np.int32)
+    running = []
+    for _ in range(200):
+        op = rng.random()
+        if op < 0.45:
+            p = _prompt(rng) + [rng.randrange(40) for _ in range(rng.randint(0, 6))]
+            slots, node = pr.match(p)
+            assert len(slots) % page == 0
+            pr.lock(node)
+            # positions len(slots) .. len(p)-1 by the page rule, both sides
+            r2t[0, :len(slots)] = slots
+            err_c = err_o = None
+            try:
+                cs, _ = B.rt_alloc_positions(pr.ctree, [0], [len(slots)], [len(p) - len(slots)], r2t)
+            except B.OOMError as e:
+                err_c, cs = e, None
+            try:
+                os_, _ = pr.otree.alloc_positions([(slots, len(slots), len(p) - len(slots))])
+            except OracleOOM as e:
+                err_o, os_ = e, None
+            assert (err_c is None) == (err_o is None)
+            if os_ is None:
+                pr.unlock(node)
+            else:
+                assert list(cs) == os_ and list(r2t[0, :len(p)]) == slots + os_
+                running.append((p, node, slots + os_, len(slots)))
+        elif op < 0.8 and running:
+            p, node, slots, plen = running.pop(rng.randrange(len(running)))
+            aligned = len(p) - len(p) % page
+            present = pr.insert(p[:aligned], slots[:aligned])
+            rel = (slots[plen:present] if present > plen else []) + slots[aligned:]
+            if rel:
+                pr.free(rel)
+            pr.unlock(node)
+        elif op < 0.9:
+            pr.evict(rng.randint(0, 25))
+        else:
+            _, node = pr.match(_prompt(rng))
+            if pr.unlock(node) and node != 0:
+                pr.lock(node)
+        pr.same()
+    with pytest.raises(B.RadixRTError):
+        B.rt_insert(pr.ctree, [1] * (page + 1), [1] * (page + 1))   # not whole pages
+    with pytest.raises(B.RadixRTError):
+        B.rt_alloc_with_evict(pr.ctree, page + 1)
     pr.close()

@@ -20,7 +20,7 @@ def _host_compare(wl, max_running=256, max_extend_tokens=16384, policy="fcfs", c
                        policy=policy, chunk_size=chunk_size)
     t1 = time.time()
     rt = RadixRuntime(wl.num_slots, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, None,
-                      max(max_running, 8), wl.max_ctx, device=None)
+                      max(max_running, 8), wl.max_ctx, device=None, page_size=wl.page_size)
     sch = Scheduler(rt, wl.requests, None, max_running=max_running, max_extend_tokens=max_extend_tokens,
                     policy=policy, chunk_size=chunk_size).run()
     t2 = time.time()
@@ -108,3 +108,29 @@ def test_long_context_chunked():
     ora = _host_compare(workloads.long_context(), chunk_size=8192)
     assert all(sum(n for _, _, n in it["chunks"]) <= 8192 for it in ora.iterations)
     assert any(it["chunks"] and it["decode"] for it in ora.iterations)
+
+
+@pytest.mark.parametrize("page", [2, 4])
+@pytest.mark.parametrize("pool", [512, 160])
+def test_tiny_paged(pool, page):
+    _host_compare(workloads.paged(workloads.tiny(pool), page))
+
+
+@pytest.mark.parametrize("page", [4, 16])
+def test_small_chat_paged(page):
+    wl = workloads.paged(workloads.chat(sessions=6, turns=3, system_len=64, user_lo=16, user_hi=48, gen_len=6), page)
+    ora = _host_compare(wl, max_running=4, max_extend_tokens=128)
+    assert any(it["extend_freed"] or it["decode_freed"] for it in ora.iterations)
+    ora = _host_compare(wl, max_running=4, max_extend_tokens=128, policy="lspf")
+    ora = _host_compare(wl, max_running=4, chunk_size=24)
+
+
+def test_few_shot_full_paged():
+    ora = _host_compare(workloads.paged(workloads.few_shot(), 16))
+    assert ora.cached_tokens == 64 * 1024 and ora.prefill_tokens == 1024 + 64 * 1152
+
+
+def test_chat_full_paged_with_eviction():
+    wl = workloads.paged(workloads.chat(), 16)
+    ora = _host_compare(wl)
+    assert sum(len(it["extend_freed"]) + len(it["decode_freed"]) for it in ora.iterations) > 0
