@@ -8,9 +8,16 @@
 // parent once it is an unlocked leaf).  Locks and the shared pool follow the
 // SGLang paper summary, section 3 ("Cache management").
 //
+// Pages: the pool may hand out slots in pages of p (the explainer's match
+// excerpt compares keys under a configurable page size); keys are then
+// compared in whole pages, children are keyed by their first page, and new
+// positions take slots by the page rule (a fresh page at a page start, the
+// next slot otherwise).  With p = 1 everything is token-granular.
+//
 // Data layout: nodes own their key and slot runs in std::vector; children are
-// keyed by first token, in a short array while a node has few of them and
-// in a hash map beyond that; nodes are found by id through a vector (ids are
+// keyed by a hash of their first page (checked against the page itself), in
+// a short array while a node has few of them and in a hash multimap beyond
+// that; nodes are found by id through a vector (ids are
 // handed out in order and never reused) and their storage is recycled after
 // eviction; the unlocked leaves sit in an array with back-indices so that
 // eviction heapifies only the candidates; evictable and protected token
