@@ -45,16 +45,24 @@ struct DecodePlan {
 };
 
 constexpr int kMaxChunk = 2048;      // slot indices of one chunk staged in LDS (8 KiB)
-constexpr int kTargetItems = 6144;   // about two work items per resident wave on 256 CUs
+// FP8 pools move half the bytes per key, so a wave streams a chunk's keys
+// with less in flight; shorter chunks (more items) keep HBM busier on long
+// contexts (32 x 32897 keys: 24 chunks in 327 us against 17 in 358 us).
+constexpr int kMaxChunkFp8 = 1408;
+// About six work items per CU: fewer, longer chunks amortise each item's
+// index staging, Q load and partial write.  On MI355X, 1536 is faster than
+// 6144 for few-shot (35 against 45 us), fork (108 against 112 us) and long
+// context (574 against 582 us) decode; 512 or fewer starve few-shot.
+constexpr int kTargetItems = 1536;
 constexpr float kSlack = 8.f;        // log2 headroom of the lazy softmax rescale
 
-// Chunk the context so that there are enough (chunk, KV head, request) work
-// items to keep every wave of the chip busy about twice over, chunks hold at
-// least 64 keys and at most kMaxChunk.  Depends only on the call's sizes.
-DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len) {
+// Chunk the context into about kTargetItems (chunk, KV head, request) work
+// items; chunks hold at least 64 keys and at most max_chunk (at most
+// kMaxChunk in any case).  Depends only on the call's sizes and pool format.
+DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len, int max_chunk = kMaxChunk) {
   const int64_t units = int64_t(batch) * num_kv_heads;
   int64_t s = (kTargetItems + units - 1) / units;
-  s = std::max<int64_t>(s, (max_kv_len + kMaxChunk - 1) / kMaxChunk);
+  s = std::max<int64_t>(s, (max_kv_len + max_chunk - 1) / max_chunk);
   s = std::min<int64_t>(s, std::max(1, (max_kv_len + 63) / 64));
   s = std::max<int64_t>(std::min<int64_t>(s, 1024), 1);
   int chunk = int((max_kv_len + s - 1) / s);
@@ -407,7 +415,7 @@ int decode_entry(const char* name, const void* q, void* o, const void* k_pool, c
   const int64_t need = radix_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_kv_len);
   if (workspace_bytes < need)
     return rt::fail(RT_ERR_INVALID, fn + ": workspace too small (need " + std::to_string(need) + ")");
-  const DecodePlan pl = plan_decode(batch, num_kv_heads, max_kv_len);
+  const DecodePlan pl = plan_decode(batch, num_kv_heads, max_kv_len, mode == kModeFp8Kv ? kMaxChunkFp8 : kMaxChunk);
   float* ws_acc = static_cast<float*>(workspace);
   float* ws_ml = ws_acc + int64_t(batch) * num_q_heads * pl.splits * head_dim;
   const float scale_log2 = sm_scale * k_scale * kLog2e;
@@ -431,8 +439,10 @@ extern "C" int64_t radix_decode_workspace_bytes(int32_t batch, int32_t num_q_hea
       (head_dim != 64 && head_dim != 128) || max_kv_len < 1)
     return -1;
   if (batch == 0) return 0;
-  DecodePlan pl = plan_decode(batch, num_kv_heads, max_kv_len);
-  return int64_t(batch) * num_q_heads * pl.splits * (head_dim + 2) * int64_t(sizeof(float));
+  // enough for either pool format's plan
+  const int splits = std::max(plan_decode(batch, num_kv_heads, max_kv_len).splits,
+                              plan_decode(batch, num_kv_heads, max_kv_len, kMaxChunkFp8).splits);
+  return int64_t(batch) * num_q_heads * splits * (head_dim + 2) * int64_t(sizeof(float));
 }
 
 extern "C" int radix_decode_attention(const void* q, void* o, const void* k_pool, const void* v_pool,
