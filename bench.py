@@ -105,16 +105,20 @@ class FewShotBench:
         self.k_pool = torch.zeros((self.SLOTS + 1, self.HKV, self.D), dtype=pool_dt, device=self.dev)
         self.v_pool = torch.zeros_like(self.k_pool)
         # two row sets of 64 so that host writes for step i+1 never touch rows still being copied for step i
-        self.r2t_host_t = torch.zeros((2 * self.B, self.stride), dtype=torch.int32, pin_memory=True)
-        self.r2t_host = self.r2t_host_t.numpy()
-        self.r2t_dev = torch.zeros((2 * self.B, self.stride), dtype=torch.int32, device=self.dev)
-        # pinned metadata staging per row set: prefix, extend, qo_indptr(65), rows, dec_pos, dec_slots, loc(8192)
+        # Per row set: B slot-table rows, then MR rows that carry the step's
+        # metadata, so that one host-to-device copy moves both.
         self.meta_n = 5 * self.B + 1 + self.B * self.SUFFIX
-        self.meta_host_t = torch.zeros((2, self.meta_n), dtype=torch.int32, pin_memory=True)
-        self.meta_host = self.meta_host_t.numpy()
-        self.meta_dev = torch.zeros((2, self.meta_n), dtype=torch.int32, device=self.dev)
+        self.MR = -(-self.meta_n // self.stride)
+        self.set_rows = self.B + self.MR
+        self.r2t_host_t = torch.zeros((2 * self.set_rows, self.stride), dtype=torch.int32, pin_memory=True)
+        self.r2t_host = self.r2t_host_t.numpy()
+        self.r2t_dev = torch.zeros((2 * self.set_rows, self.stride), dtype=torch.int32, device=self.dev)
+        # pinned metadata staging per row set: prefix, extend, qo_indptr(65), rows, dec_pos, dec_slots, loc(8192)
+        meta_rows = lambda t, rs: t[rs * self.set_rows + self.B:(rs + 1) * self.set_rows].reshape(-1)[:self.meta_n]
+        self.meta_host = [meta_rows(self.r2t_host, rs) for rs in range(2)]
+        self.meta_dev = [meta_rows(self.r2t_dev, rs) for rs in range(2)]
         self.copy_done = [None, None]
-        self.rows = [np.arange(rs * self.B, rs * self.B + self.B, dtype=np.int32) for rs in range(2)]
+        self.rows = [np.arange(rs * self.set_rows, rs * self.set_rows + self.B, dtype=np.int32) for rs in range(2)]
         self.dec_pos = np.full(self.B, self.PREFIX + self.SUFFIX, dtype=np.int32)
         self.ws = torch.empty(B_mod.radix_decode_workspace_bytes(self.B, self.HQ, self.HKV, self.D, self.stride),
                               dtype=torch.uint8, device=self.dev)
@@ -224,8 +228,8 @@ class FewShotBench:
         meta[4 * B + 1:5 * B + 1] = dslots
         md = self.meta_dev[rs]
         with torch.cuda.stream(self.stream):
-            self.r2t_dev[rs * B:(rs + 1) * B].copy_(self.r2t_host_t[rs * B:(rs + 1) * B], non_blocking=True)
-            md.copy_(self.meta_host_t[rs], non_blocking=True)
+            lo, hi = rs * self.set_rows, (rs + 1) * self.set_rows
+            self.r2t_dev[lo:hi].copy_(self.r2t_host_t[lo:hi], non_blocking=True)  # rows and metadata
             ev = torch.cuda.Event()
             ev.record(self.stream)
             self.copy_done[rs] = ev
