@@ -238,6 +238,7 @@ inline void ChildMap::erase(uint64_t h, const int32_t* page, int32_t p) {
 struct Tree {
   Pool* pool;
   int32_t P;                                   // slots per page (the pool's)
+  std::vector<int32_t> fresh_;                 // scratch of alloc_positions: the fresh pages' slots
   uint64_t clock = 0;
   int64_t next_id = 1;
   std::unique_ptr<Node> root_owner;
@@ -247,6 +248,9 @@ struct Tree {
   std::vector<Node*> spare;                    // evicted node objects, reused
   int64_t live = 0;                            // non-root nodes in the tree
   std::vector<Node*> leaves;                   // unlocked, childless, non-root
+  // (last_access, id) of leaves[i], kept beside it so that building the
+  // eviction heap reads one contiguous array instead of every leaf node.
+  std::vector<std::pair<uint64_t, int64_t>> leaf_keys;
   int64_t evictable = 0;
   int64_t protected_ = 0;
 
@@ -262,14 +266,21 @@ struct Tree {
     if (n->leaf_pos >= 0) return;
     n->leaf_pos = int64_t(leaves.size());
     leaves.push_back(n);
+    leaf_keys.push_back({n->last_access, n->id});
   }
   void leaf_remove(Node* n) {
     if (n->leaf_pos < 0) return;
     Node* last = leaves.back();
     leaves[n->leaf_pos] = last;
+    leaf_keys[n->leaf_pos] = leaf_keys.back();
     last->leaf_pos = n->leaf_pos;
     leaves.pop_back();
+    leaf_keys.pop_back();
     n->leaf_pos = -1;
+  }
+  void stamp(Node* n, uint64_t t) {
+    n->last_access = t;
+    if (n->leaf_pos >= 0) leaf_keys[n->leaf_pos].first = t;
   }
   void refresh(Node* n) {
     if (n == root) return;
@@ -350,7 +361,7 @@ struct Tree {
     while (pos < n) {
       Node* child = node->children.find(page_hash(tokens + pos, P), tokens + pos, P);
       if (!child) break;
-      child->last_access = stamp;
+      this->stamp(child, stamp);
       int64_t k = common_len(child->key, tokens + pos, n - pos);
       k -= k % P;  // at least one page: the first page matched
       if (k < int64_t(child->key.size())) {
@@ -377,7 +388,7 @@ struct Tree {
     while (pos < n) {
       Node* child = node->children.find(page_hash(tokens + pos, P), tokens + pos, P);
       if (!child) break;
-      child->last_access = stamp;
+      this->stamp(child, stamp);
       int64_t k = common_len(child->key, tokens + pos, n - pos);
       k -= k % P;
       if (k < int64_t(child->key.size())) child = split(child, k);
@@ -419,16 +430,10 @@ struct Tree {
 
   // Evicts leaves; appends freed slots to `freed` (if given).
   int64_t evict(int64_t num_tokens, std::vector<int32_t>* freed) {
-    using Key = std::pair<std::pair<uint64_t, int64_t>, Node*>;
-    auto cmp = [](const Key& a, const Key& b) { return a.first > b.first; };  // min-heap
-    std::vector<Key> init;
-    init.reserve(leaves.size());
-    for (Node* n : leaves) init.push_back({{n->last_access, n->id}, n});
-    std::priority_queue<Key, std::vector<Key>, decltype(cmp)> heap(cmp, std::move(init));
     int64_t evicted = 0;
-    while (evicted < num_tokens && !heap.empty()) {
-      Node* x = heap.top().second;
-      heap.pop();
+    // Frees leaf x; a parent that becomes an unlocked leaf joins the
+    // candidates (and the heap, once there is one).
+    auto evict_one = [&](Node* x) -> Node* {
       int64_t len = int64_t(x->value.size());
       pool->release(x->value.data(), len);  // cannot fail: the slots came from this pool
       if (freed) freed->insert(freed->end(), x->value.begin(), x->value.end());
@@ -440,8 +445,31 @@ struct Tree {
       drop_node(x);
       if (is_candidate(parent)) {
         leaf_add(parent);
-        heap.push({{parent->last_access, parent->id}, parent});
+        return parent;
       }
+      return nullptr;
+    };
+    // The first few victims: a scan of the contiguous candidate keys for the
+    // least recently used (ties by id) -- cheaper than a heap when only a
+    // few leaves go, as in a decode step's allocation.
+    for (int k = 0; k < 8 && evicted < num_tokens && !leaves.empty(); ++k) {
+      size_t best = 0;
+      for (size_t i = 1; i < leaf_keys.size(); ++i)
+        if (leaf_keys[i] < leaf_keys[best]) best = i;
+      evict_one(leaves[best]);
+    }
+    if (evicted >= num_tokens || leaves.empty()) return evicted;
+    // Many victims: a min-heap of all candidates.
+    using Key = std::pair<std::pair<uint64_t, int64_t>, Node*>;
+    auto cmp = [](const Key& a, const Key& b) { return a.first > b.first; };  // min-heap
+    std::vector<Key> init;
+    init.reserve(leaves.size());
+    for (size_t i = 0; i < leaves.size(); ++i) init.push_back({leaf_keys[i], leaves[i]});
+    std::priority_queue<Key, std::vector<Key>, decltype(cmp)> heap(cmp, std::move(init));
+    while (evicted < num_tokens && !heap.empty()) {
+      Node* x = heap.top().second;
+      heap.pop();
+      if (Node* parent = evict_one(x)) heap.push({{parent->last_access, parent->id}, parent});
     }
     return evicted;
   }
@@ -470,22 +498,33 @@ struct Tree {
     for (int32_t i = 0; i < n_runs; ++i) {
       if (rows[i] < 0 || first[i] < 0 || counts[i] < 0 || int64_t(first[i]) + counts[i] > stride)
         return fail(RT_ERR_INVALID, "alloc_positions: bad run " + std::to_string(i));
-      for (int64_t x = first[i]; x < int64_t(first[i]) + counts[i]; ++x)
-        if (x % P == 0) ++starts;
+      // multiples of P in [first, first + count)
+      starts += (int64_t(first[i]) + counts[i] + P - 1) / P - (int64_t(first[i]) + P - 1) / P;
       total += counts[i];
     }
     if (total > out_cap || (total > 0 && !out)) return fail(RT_ERR_INVALID, "alloc_positions: out too small");
     if (starts * P > INT32_MAX) return fail(RT_ERR_INVALID, "alloc_positions: too many pages");
-    std::vector<int32_t> fresh(size_t(starts * P));
-    int rc = alloc_with_evict(int32_t(starts * P), fresh.data(), out_evicted);
+    fresh_.resize(size_t(starts * P));
+    int rc = alloc_with_evict(int32_t(starts * P), fresh_.data(), out_evicted);
     if (rc != RT_OK) return rc;
+    const int32_t* fresh = fresh_.data();
     int64_t next = 0, o = 0;
     for (int32_t i = 0; i < n_runs; ++i) {
       int32_t* row = req_to_token + int64_t(rows[i]) * stride;
-      for (int64_t x = first[i]; x < int64_t(first[i]) + counts[i]; ++x) {
-        const int32_t sl = (x % P == 0) ? fresh[size_t(next++ * P)] : row[x - 1] + 1;
+      const int64_t x0 = first[i], cnt = counts[i];
+      if (P == 1) {  // every position starts a page: the fresh slots in order
+        std::memcpy(row + x0, fresh + next, sizeof(int32_t) * cnt);
+        std::memcpy(out + o, fresh + next, sizeof(int32_t) * cnt);
+        next += cnt;
+        o += cnt;
+        continue;
+      }
+      int64_t r = x0 % P;  // offset of position x within its page
+      for (int64_t x = x0; x < x0 + cnt; ++x) {
+        const int32_t sl = r == 0 ? fresh[next++ * P] : row[x - 1] + 1;
         row[x] = sl;
         out[o++] = sl;
+        if (++r == P) r = 0;
       }
     }
     return RT_OK;
