@@ -69,7 +69,7 @@ const char* rt_last_error(void);
 int rt_abi_version(void);
 
 /* ---------------------------------------------------------------- pool --
- * Token-slot allocator [P1 "one shared pool"; P2 freeing a leaf's slots].
+ * Token-slot allocator [P1 cache management: cached and running requests share one pool; P2 freeing a leaf's slots].
  * Slots come in pages of page_size (1 unless created paged): page j holds
  * slots 1 + j*page_size .. (j+1)*page_size [P2 prefix-match excerpt: the
  * engine compares keys under a configurable page size].  Free pages form a
@@ -135,7 +135,7 @@ int rt_insert(rt_tree* tree, const int32_t* tokens, const int32_t* slots, int32_
               int32_t* out_present_len);
 
 /* Reference counts on every non-root node from `node` up to the root
- * [P1 "reference counters"; P2 lifetime figure].  Locked nodes are never
+ * [P1 cache management: counts that keep running requests' nodes from eviction; P2 lifetime figure].  Locked nodes are never
  * evicted.  rt_unlock on a path with a zero count fails with
  * RT_ERR_INVALID and changes nothing.  Locking the root is a no-op. */
 int rt_lock(rt_tree* tree, rt_node node);
@@ -263,15 +263,37 @@ int decode_append(int32_t* req_to_token, int32_t req_to_token_stride, const int3
                   const void* k_new, const void* v_new, int32_t num_kv_heads, int32_t head_dim, int dtype,
                   void* stream);
 
-/* Extend (prefill of the uncached suffix) attention [P2 "match the longest
- * prefix, reference the shared KV, prefill only the missed suffix"].
+/* The extend batch's scatter with its targets read from the slot table [P4
+ * out_cache_loc; the new slots are the entries req_to_token[row_b][prefix_lens[b]
+ * .. prefix_lens[b] + extend_lens[b]) that the host already wrote]: for request
+ * b and j < extend_lens[b], row qo_indptr[b] + j of k_new / v_new goes to slot
+ * req_to_token[row_b][prefix_lens[b] + j], row_b = req_pool_indices[b] (or b
+ * when req_pool_indices is NULL).  The metadata arguments mean what they mean
+ * for radix_extend_attention, so one set of device arrays drives both calls;
+ * qo_indptr[b] only locates request b's first row (rows between requests are
+ * not read).  k_new, v_new: (device) [rows, num_kv_heads, head_dim] in the
+ * pool's dtype (RT_F32 or RT_BF16).  Same results as kv_store with
+ * out_cache_loc = those table entries in request order; the same race on
+ * repeated slots; table entries and lengths are not checked on the device.
+ * batch <= 65535; max_extend_len (host) bounds every extend_lens[b]. */
+int kv_store_extend(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                    const int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* req_pool_indices,
+                    const int32_t* prefix_lens, const int32_t* extend_lens, const int32_t* qo_indptr,
+                    int32_t batch, int32_t max_extend_len, int32_t num_kv_heads, int32_t head_dim, int dtype,
+                    void* stream);
+
+/* Extend (prefill of the uncached suffix) attention [P2 section 04: after the
+ * longest-prefix match only the tokens past the cached prefix are computed,
+ * attending to the cached K/V].
  * For request b, extend row j < extend_lens[b] and query head h:
  *   o[qo_indptr[b] + j][h] = sum_i softmax_i(sm_scale * q.k_i) v_i over keys
  *   i = 0 .. prefix_lens[b] + j, k_i / v_i = pool rows at slot
  *   req_to_token[row_b][i] of KV head h / (Hq / Hkv).
- * q, o: (device) [total extend rows, num_q_heads, head_dim], rows packed in
- * batch order with qo_indptr (device, int32 [batch + 1]) the exclusive
- * prefix sum of extend_lens.  prefix_lens, extend_lens (device, int32
+ * q, o: (device) [total extend rows, num_q_heads, head_dim]; request b's
+ * rows start at row qo_indptr[b] (device, int32 [batch + 1]), normally the
+ * exclusive prefix sum of extend_lens.  Only qo_indptr[0 .. batch - 1] is
+ * read, so rows between requests may be left out (they are neither read
+ * nor written).  prefix_lens, extend_lens (device, int32
  * [batch]).  max_extend_len (host) bounds every extend_lens[b] and sizes the
  * grid.  extend_lens[b] = 0 is allowed (no rows).  fp32 accumulation; o has
  * the input dtype. */
@@ -281,6 +303,25 @@ int radix_extend_attention(const void* q, void* o, const void* k_pool, const voi
                            const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
                            int32_t max_extend_len, int32_t num_q_heads, int32_t num_kv_heads,
                            int32_t head_dim, float sm_scale, int dtype, void* stream);
+
+/* One launch for a mixed batch [P4, the #800 entry of the release timeline:
+ * chunked prefill runs prompt chunks beside the running requests' decode
+ * steps]: requests 0 .. num_extend - 1 are extend requests with
+ * extend_lens[b] <= max_extend_len, requests num_extend .. batch - 1 are
+ * short ones with extend_lens[b] <= max_tail_len; a decode row is a short
+ * request with prefix_lens[b] = its position and extend_lens[b] = 1 (its new
+ * K/V already stored at req_to_token[row_b][prefix_lens[b]]).  The result is
+ * radix_extend_attention's over the whole batch; the grid sizes the extend
+ * requests by max_extend_len and the short ones by max_tail_len, so many
+ * decode rows beside a long chunk do not each pay for the chunk's length.
+ * 0 <= num_extend <= batch (both host). */
+int radix_mixed_attention(const void* q, void* o, const void* k_pool, const void* v_pool,
+                          const int32_t* req_to_token, int32_t req_to_token_stride,
+                          const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                          const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
+                          int32_t num_extend, int32_t max_extend_len, int32_t max_tail_len,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                          int dtype, void* stream);
 
 /* Bytes of device workspace radix_decode_attention needs for these sizes
  * (split-K partial maxima, sums and accumulators, fp32).  Negative on bad
@@ -334,6 +375,14 @@ int decode_append_fp8(int32_t* req_to_token, int32_t req_to_token_stride, const 
                       const void* k_new, const void* v_new, int32_t num_kv_heads, int32_t head_dim,
                       float k_scale, float v_scale, void* stream);
 
+/* kv_store_extend into FP8 pools: the rows and slots of kv_store_extend, the
+ * encoding and scales of kv_store_fp8.  k_new, v_new: (device) bf16. */
+int kv_store_extend_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                        const int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* req_pool_indices,
+                        const int32_t* prefix_lens, const int32_t* extend_lens, const int32_t* qo_indptr,
+                        int32_t batch, int32_t max_extend_len, int32_t num_kv_heads, int32_t head_dim,
+                        float k_scale, float v_scale, void* stream);
+
 /* radix_extend_attention over FP8 pools: q, o bf16; keys and values read as
  * E4M3(code) * k_scale and E4M3(code) * v_scale.  Same arguments and checks
  * otherwise. */
@@ -343,6 +392,16 @@ int radix_extend_attention_fp8kv(const void* q, void* o, const void* k_pool, con
                                  const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
                                  int32_t max_extend_len, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, float sm_scale, float k_scale, float v_scale, void* stream);
+
+/* radix_mixed_attention over FP8 pools (q, o bf16; pools and scales as in
+ * radix_extend_attention_fp8kv). */
+int radix_mixed_attention_fp8kv(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                const int32_t* req_to_token, int32_t req_to_token_stride,
+                                const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
+                                int32_t num_extend, int32_t max_extend_len, int32_t max_tail_len,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                                float k_scale, float v_scale, void* stream);
 
 /* radix_decode_attention over FP8 pools: q, o bf16; keys and values read as
  * E4M3(code) * k_scale and E4M3(code) * v_scale.  Same arguments, workspace

@@ -24,7 +24,8 @@ EXPORTS = [
     "rt_evict_lru_leaves", "rt_alloc_with_evict", "rt_evictable_size", "rt_protected_size",
     "rt_tree_num_nodes", "rt_tree_dump", "rt_admit_batch", "rt_decode_slots_batch", "rt_finish_batch",
     "kv_store", "req_to_token_scatter", "decode_append", "kv_store_fp8", "radix_decode_attention_fp8kv",
-    "radix_extend_attention_fp8kv", "decode_append_fp8",
+    "radix_extend_attention_fp8kv", "decode_append_fp8", "kv_store_extend", "kv_store_extend_fp8",
+    "radix_mixed_attention", "radix_mixed_attention_fp8kv",
     "radix_extend_attention", "radix_decode_workspace_bytes", "radix_decode_attention",
 ]
 
@@ -41,9 +42,12 @@ class OOMError(RadixRTError):
 
 _lib = None
 
-_i32p = ctypes.POINTER(ctypes.c_int32)
-_i64p = ctypes.POINTER(ctypes.c_int64)
+# Every pointer argument is declared void*: host arrays go in as their raw
+# address (numpy's .ctypes.data), which costs a fraction of building a typed
+# ctypes pointer per argument and per call.
 _vp = ctypes.c_void_p
+_i32p = _vp
+_i64p = _vp
 
 
 def lib():
@@ -106,6 +110,21 @@ def lib():
             "decode_append_fp8": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
                                                  _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
                                                  _vp]),
+            "kv_store_extend": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int, _vp]),
+            "kv_store_extend_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
+                                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.c_float, ctypes.c_float, _vp]),
+            "radix_mixed_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
+                                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                                     ctypes.c_int, _vp]),
+            "radix_mixed_attention_fp8kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
+                                                           _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                           ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                                                           ctypes.c_float, _vp]),
             "radix_extend_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
@@ -135,11 +154,10 @@ def _check(rc):
 
 
 def _p32(a):
-    return a.ctypes.data_as(_i32p) if a is not None else None
+    return a.ctypes.data if a is not None else None
 
 
-def _p64(a):
-    return a.ctypes.data_as(_i64p) if a is not None else None
+_p64 = _p32
 
 
 def _i32(x):
@@ -351,6 +369,25 @@ def kv_store(k_pool, v_pool, k_new, v_new, out_cache_loc, stream=None):
                           d, _dtype_code(k_new), _stream(stream)))
 
 
+def kv_store_extend(k_pool, v_pool, k_new, v_new, req_to_token, req_pool_indices, prefix_lens, extend_lens,
+                    qo_indptr, max_extend_len, stream=None):
+    _, hkv, d = k_new.shape
+    _check(lib().kv_store_extend(_dptr(k_pool), _dptr(v_pool), _dptr(k_new), _dptr(v_new), _dptr(req_to_token),
+                                 req_to_token.shape[1], _dptr(req_pool_indices), _dptr(prefix_lens),
+                                 _dptr(extend_lens), _dptr(qo_indptr), prefix_lens.shape[0], int(max_extend_len),
+                                 hkv, d, _dtype_code(k_new), _stream(stream)))
+
+
+def kv_store_extend_fp8(k_pool, v_pool, k_new, v_new, req_to_token, req_pool_indices, prefix_lens, extend_lens,
+                        qo_indptr, max_extend_len, k_scale=1.0, v_scale=1.0, stream=None):
+    """kv_store_extend into FP8 pools (uint8 codes); k_new, v_new bf16."""
+    _, hkv, d = k_new.shape
+    _check(lib().kv_store_extend_fp8(_dptr(k_pool), _dptr(v_pool), _dptr(k_new), _dptr(v_new), _dptr(req_to_token),
+                                     req_to_token.shape[1], _dptr(req_pool_indices), _dptr(prefix_lens),
+                                     _dptr(extend_lens), _dptr(qo_indptr), prefix_lens.shape[0],
+                                     int(max_extend_len), hkv, d, float(k_scale), float(v_scale), _stream(stream)))
+
+
 def req_to_token_scatter(req_to_token, rows, positions, slots, stream=None):
     _check(lib().req_to_token_scatter(_dptr(req_to_token), req_to_token.shape[1], _dptr(rows), _dptr(positions),
                                       _dptr(slots), rows.shape[0], _stream(stream)))
@@ -410,6 +447,31 @@ def radix_extend_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices,
                                         req_to_token.shape[1], _dptr(req_pool_indices), _dptr(prefix_lens),
                                         _dptr(extend_lens), _dptr(qo_indptr), batch, int(max_extend_len), hq, hkv, d,
                                         float(sm_scale), _dtype_code(q), _stream(stream)))
+
+
+def radix_mixed_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens, extend_lens,
+                          qo_indptr, num_extend, max_extend_len, max_tail_len, sm_scale, stream=None):
+    _, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    batch = prefix_lens.shape[0]
+    _check(lib().radix_mixed_attention(_dptr(q), _dptr(o), _dptr(k_pool), _dptr(v_pool), _dptr(req_to_token),
+                                       req_to_token.shape[1], _dptr(req_pool_indices), _dptr(prefix_lens),
+                                       _dptr(extend_lens), _dptr(qo_indptr), batch, int(num_extend),
+                                       int(max_extend_len), int(max_tail_len), hq, hkv, d, float(sm_scale),
+                                       _dtype_code(q), _stream(stream)))
+
+
+def radix_mixed_attention_fp8kv(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens, extend_lens,
+                                qo_indptr, num_extend, max_extend_len, max_tail_len, sm_scale, k_scale=1.0,
+                                v_scale=1.0, stream=None):
+    _, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    batch = prefix_lens.shape[0]
+    _check(lib().radix_mixed_attention_fp8kv(_dptr(q), _dptr(o), _dptr(k_pool), _dptr(v_pool), _dptr(req_to_token),
+                                             req_to_token.shape[1], _dptr(req_pool_indices), _dptr(prefix_lens),
+                                             _dptr(extend_lens), _dptr(qo_indptr), batch, int(num_extend),
+                                             int(max_extend_len), int(max_tail_len), hq, hkv, d, float(sm_scale),
+                                             float(k_scale), float(v_scale), _stream(stream)))
 
 
 def radix_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_kv_len):

@@ -44,6 +44,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "dev_common.h"
 #include "radixrt.h"
 #include "rt_internal.h"
@@ -100,8 +102,8 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
     const char* __restrict__ q, char* __restrict__ o, const char* __restrict__ k_pool,
     const char* __restrict__ v_pool, const int32_t* __restrict__ req_to_token, int64_t stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
-    const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ qo_indptr, int B, int Hq, int Hkv,
-    int G, int n_qt, float scale_log2, float v_scale) {
+    const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ qo_indptr, int B1, int B2, int Hq,
+    int Hkv, int G, int n_qt, int n_qt2, int seg2, float scale_log2, float v_scale) {
   using C = ExtendCfg<D>;
   constexpr int kWaveRows = 32 * RB;          // query rows per wave (RB blocks of 32)
   constexpr int kItemRows = kWaves * kWaveRows;  // query rows per work item
@@ -123,10 +125,24 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
   __shared__ __attribute__((aligned(1024))) char svw[KV8 ? C::kTile : 16];
   __shared__ uint32_t s_slot[kSeg];
 
-  const int work = xcd_slice(blockIdx.x, gridDim.x);
-  const int qt = work % n_qt;
-  const int b = (work / n_qt) % B;
-  const int kvh = work / (n_qt * B);
+  // Two segments of work: n_qt query tiles for each of requests 0 .. B1-1,
+  // then n_qt2 for each of the B2 short requests after them (decode rows of a
+  // mixed batch).  Each segment is spread over the XCDs on its own; the first
+  // ends at block seg2 (a multiple of 8 when a second segment follows, so the
+  // second starts on XCD 0), and its padding blocks have no work.
+  int qt, b, kvh;
+  if (int(blockIdx.x) < seg2) {
+    const int work = xcd_slice(blockIdx.x, seg2);
+    if (work >= n_qt * B1 * Hkv) return;
+    qt = work % n_qt;
+    b = (work / n_qt) % B1;
+    kvh = work / (n_qt * B1);
+  } else {
+    const int work = xcd_slice(int(blockIdx.x) - seg2, int(gridDim.x) - seg2);
+    qt = work % n_qt2;
+    b = B1 + (work / n_qt2) % B2;
+    kvh = work / (n_qt2 * B2);
+  }
 
   const int E = extend_lens[b];
   const int row0 = qt * kItemRows;            // first query row of this item
@@ -458,80 +474,69 @@ __global__ void __launch_bounds__(64) extend_f32(const float* __restrict__ q, fl
 template <bool KV8>
 int launch_extend_bf16(const void* q, void* o, const void* k_pool, const void* v_pool, const int32_t* req_to_token,
                        int32_t req_to_token_stride, const int32_t* req_pool_indices, const int32_t* prefix_lens,
-                       const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch, int32_t max_extend_len,
-                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale_log2, float v_scale,
-                       hipStream_t st) {
+                       const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch, int32_t num_extend,
+                       int32_t max_extend_len, int32_t max_tail_len, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, float scale_log2, float v_scale, hipStream_t st) {
   const int G = num_q_heads / num_kv_heads;
   const int64_t item_rows = kWaves * 32 * kRB;
+  const int64_t B2 = int64_t(batch) - num_extend;
   const int64_t n_qt = (int64_t(max_extend_len) * G + item_rows - 1) / item_rows;
-  const int64_t grid = n_qt * batch * num_kv_heads;
+  const int64_t n_qt2 = B2 > 0 ? (int64_t(max_tail_len) * G + item_rows - 1) / item_rows : 0;
+  const int64_t n1 = n_qt * num_extend * num_kv_heads;
+  const int64_t n2 = n_qt2 * B2 * num_kv_heads;
+  const int64_t seg2 = n2 > 0 ? (n1 + 7) / 8 * 8 : n1;
+  const int64_t grid = seg2 + n2;
   if (grid > INT32_MAX) return rt::fail(RT_ERR_INVALID, "radix_extend_attention: grid too large");
+  if (grid == 0) return RT_OK;
   if (head_dim == 128)
     hipLaunchKernelGGL((extend_bf16<128, kRB, KV8>), dim3(uint32_t(grid)), dim3(64 * kWaves), 0, st,
                        (const char*)q, (char*)o, (const char*)k_pool, (const char*)v_pool, req_to_token,
-                       int64_t(req_to_token_stride), req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch,
-                       num_q_heads, num_kv_heads, G, int(n_qt), scale_log2, v_scale);
+                       int64_t(req_to_token_stride), req_pool_indices, prefix_lens, extend_lens, qo_indptr,
+                       num_extend, int(B2), num_q_heads, num_kv_heads, G, int(n_qt), int(n_qt2), int(seg2),
+                       scale_log2, v_scale);
   else
     hipLaunchKernelGGL((extend_bf16<64, kRB, KV8>), dim3(uint32_t(grid)), dim3(64 * kWaves), 0, st,
                        (const char*)q, (char*)o, (const char*)k_pool, (const char*)v_pool, req_to_token,
-                       int64_t(req_to_token_stride), req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch,
-                       num_q_heads, num_kv_heads, G, int(n_qt), scale_log2, v_scale);
+                       int64_t(req_to_token_stride), req_pool_indices, prefix_lens, extend_lens, qo_indptr,
+                       num_extend, int(B2), num_q_heads, num_kv_heads, G, int(n_qt), int(n_qt2), int(seg2),
+                       scale_log2, v_scale);
   return RT_OK;
 }
 
-}  // namespace
-
-extern "C" int radix_extend_attention_fp8kv(const void* q, void* o, const void* k_pool, const void* v_pool,
-                                            const int32_t* req_to_token, int32_t req_to_token_stride,
-                                            const int32_t* req_pool_indices, const int32_t* prefix_lens,
-                                            const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
-                                            int32_t max_extend_len, int32_t num_q_heads, int32_t num_kv_heads,
-                                            int32_t head_dim, float sm_scale, float k_scale, float v_scale,
-                                            void* stream) {
-  if (batch < 0 || max_extend_len < 0 || num_q_heads < 1 || num_kv_heads < 1 ||
-      num_q_heads % num_kv_heads != 0 || (head_dim != 64 && head_dim != 128) || req_to_token_stride < 1 ||
-      !(sm_scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
-    return rt::fail(RT_ERR_INVALID, "radix_extend_attention_fp8kv: bad shape, stride or scale");
-  if (batch == 0 || max_extend_len == 0) return RT_OK;
+// Shared checks and dispatch of the four entry points.  kv8: FP8 pools.
+int extend_entry(const char* name, bool kv8, const void* q, void* o, const void* k_pool, const void* v_pool,
+                 const int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* req_pool_indices,
+                 const int32_t* prefix_lens, const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
+                 int32_t num_extend, int32_t max_extend_len, int32_t max_tail_len, int32_t num_q_heads,
+                 int32_t num_kv_heads, int32_t head_dim, float sm_scale, int dtype, float k_scale, float v_scale,
+                 hipStream_t st) {
+  if (batch < 0 || num_extend < 0 || num_extend > batch || max_extend_len < 0 || max_tail_len < 0 ||
+      num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
+      (head_dim != 64 && head_dim != 128) || (dtype != RT_F32 && dtype != RT_BF16) || (kv8 && dtype != RT_BF16) ||
+      req_to_token_stride < 1 || !(sm_scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
+    return rt::fail(RT_ERR_INVALID, std::string(name) + ": bad shape, count, dtype, stride or scale");
+  if (batch == 0 || (max_extend_len == 0 && (max_tail_len == 0 || num_extend == batch))) return RT_OK;
   if (!q || !o || !k_pool || !v_pool || !req_to_token || !prefix_lens || !extend_lens || !qo_indptr)
-    return rt::fail(RT_ERR_INVALID, "radix_extend_attention_fp8kv: null pointer");
-  const int rc = launch_extend_bf16<true>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices,
-                                          prefix_lens, extend_lens, qo_indptr, batch, max_extend_len, num_q_heads,
-                                          num_kv_heads, head_dim, sm_scale * k_scale * kLog2e, v_scale,
-                                          (hipStream_t)stream);
-  if (rc != RT_OK) return rc;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess)
-    return rt::fail(RT_ERR_HIP, std::string("radix_extend_attention_fp8kv launch: ") + hipGetErrorString(e));
-  return RT_OK;
-}
-
-extern "C" int radix_extend_attention(const void* q, void* o, const void* k_pool, const void* v_pool,
-                                      const int32_t* req_to_token, int32_t req_to_token_stride,
-                                      const int32_t* req_pool_indices, const int32_t* prefix_lens,
-                                      const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
-                                      int32_t max_extend_len, int32_t num_q_heads, int32_t num_kv_heads,
-                                      int32_t head_dim, float sm_scale, int dtype, void* stream) {
-  if (batch < 0 || max_extend_len < 0 || num_q_heads < 1 || num_kv_heads < 1 ||
-      num_q_heads % num_kv_heads != 0 || (head_dim != 64 && head_dim != 128) ||
-      (dtype != RT_F32 && dtype != RT_BF16) || req_to_token_stride < 1 || !(sm_scale > 0.f))
-    return rt::fail(RT_ERR_INVALID, "radix_extend_attention: bad shape, dtype, stride or scale");
-  if (batch == 0 || max_extend_len == 0) return RT_OK;
-  if (!q || !o || !k_pool || !v_pool || !req_to_token || !prefix_lens || !extend_lens || !qo_indptr)
-    return rt::fail(RT_ERR_INVALID, "radix_extend_attention: null pointer");
-  const int G = num_q_heads / num_kv_heads;
-  const float scale_log2 = sm_scale * kLog2e;
-  hipStream_t st = (hipStream_t)stream;
+    return rt::fail(RT_ERR_INVALID, std::string(name) + ": null pointer");
+  const float scale_log2 = sm_scale * k_scale * kLog2e;
   if (dtype == RT_BF16) {
-    const int rc = launch_extend_bf16<false>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride,
-                                             req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch,
-                                             max_extend_len, num_q_heads, num_kv_heads, head_dim, scale_log2, 1.f,
-                                             st);
+    const int rc = kv8 ? launch_extend_bf16<true>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride,
+                                                  req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch,
+                                                  num_extend, max_extend_len, max_tail_len, num_q_heads,
+                                                  num_kv_heads, head_dim, scale_log2, v_scale, st)
+                       : launch_extend_bf16<false>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride,
+                                                   req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch,
+                                                   num_extend, max_extend_len, max_tail_len, num_q_heads,
+                                                   num_kv_heads, head_dim, scale_log2, 1.f, st);
     if (rc != RT_OK) return rc;
   } else {
-    if (max_extend_len > 65535 * 16 || num_q_heads > 65535 || batch > 65535)
-      return rt::fail(RT_ERR_INVALID, "radix_extend_attention: fp32 grid too large");
-    const dim3 grid{uint32_t(max_extend_len), uint32_t(num_q_heads), uint32_t(batch)};
+    // fp32: one wave per (extend row, query head, request); one dense grid
+    // over the longest extend of either part.
+    const int32_t max_len = num_extend < batch ? std::max(max_extend_len, max_tail_len) : max_extend_len;
+    if (max_len > 65535 * 16 || num_q_heads > 65535 || batch > 65535)
+      return rt::fail(RT_ERR_INVALID, std::string(name) + ": fp32 grid too large");
+    const int G = num_q_heads / num_kv_heads;
+    const dim3 grid{uint32_t(max_len), uint32_t(num_q_heads), uint32_t(batch)};
     if (head_dim == 128)
       hipLaunchKernelGGL(extend_f32<128>, grid, dim3(64), 0, st, (const float*)q, (float*)o,
                          (const float*)k_pool, (const float*)v_pool, req_to_token, int64_t(req_to_token_stride),
@@ -544,7 +549,58 @@ extern "C" int radix_extend_attention(const void* q, void* o, const void* k_pool
                          scale_log2);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess)
-    return rt::fail(RT_ERR_HIP, std::string("radix_extend_attention launch: ") + hipGetErrorString(e));
+  if (e != hipSuccess) return rt::fail(RT_ERR_HIP, std::string(name) + " launch: " + hipGetErrorString(e));
   return RT_OK;
+}
+
+}  // namespace
+
+extern "C" int radix_extend_attention(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                      const int32_t* req_to_token, int32_t req_to_token_stride,
+                                      const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                      const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
+                                      int32_t max_extend_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, float sm_scale, int dtype, void* stream) {
+  return extend_entry("radix_extend_attention", false, q, o, k_pool, v_pool, req_to_token, req_to_token_stride,
+                      req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch, batch, max_extend_len, 0,
+                      num_q_heads, num_kv_heads, head_dim, sm_scale, dtype, 1.f, 1.f, (hipStream_t)stream);
+}
+
+extern "C" int radix_extend_attention_fp8kv(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                            const int32_t* req_to_token, int32_t req_to_token_stride,
+                                            const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                            const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
+                                            int32_t max_extend_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, float sm_scale, float k_scale, float v_scale,
+                                            void* stream) {
+  return extend_entry("radix_extend_attention_fp8kv", true, q, o, k_pool, v_pool, req_to_token,
+                      req_to_token_stride, req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch, batch,
+                      max_extend_len, 0, num_q_heads, num_kv_heads, head_dim, sm_scale, RT_BF16, k_scale, v_scale,
+                      (hipStream_t)stream);
+}
+
+extern "C" int radix_mixed_attention(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                     const int32_t* req_to_token, int32_t req_to_token_stride,
+                                     const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                     const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
+                                     int32_t num_extend, int32_t max_extend_len, int32_t max_tail_len,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                                     int dtype, void* stream) {
+  return extend_entry("radix_mixed_attention", false, q, o, k_pool, v_pool, req_to_token, req_to_token_stride,
+                      req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch, num_extend, max_extend_len,
+                      max_tail_len, num_q_heads, num_kv_heads, head_dim, sm_scale, dtype, 1.f, 1.f,
+                      (hipStream_t)stream);
+}
+
+extern "C" int radix_mixed_attention_fp8kv(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                           const int32_t* req_to_token, int32_t req_to_token_stride,
+                                           const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                           const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
+                                           int32_t num_extend, int32_t max_extend_len, int32_t max_tail_len,
+                                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                           float sm_scale, float k_scale, float v_scale, void* stream) {
+  return extend_entry("radix_mixed_attention_fp8kv", true, q, o, k_pool, v_pool, req_to_token, req_to_token_stride,
+                      req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch, num_extend, max_extend_len,
+                      max_tail_len, num_q_heads, num_kv_heads, head_dim, sm_scale, RT_BF16, k_scale, v_scale,
+                      (hipStream_t)stream);
 }

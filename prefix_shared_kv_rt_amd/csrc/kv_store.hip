@@ -120,6 +120,71 @@ __global__ void __launch_bounds__(256) decode_append_fp8_kernel(int32_t* __restr
   }
 }
 
+
+// Extend scatter driven by the slot table: block (x, b) moves extend rows
+// j0 .. j0 + kExtTok - 1 of request b (j0 = x * kExtTok); row j of request b
+// is source row qo[b] + j and lands at slot r2t[row_b][prefix_lens[b] + j].
+// Threads walk the block's rows as consecutive 16-byte source pieces, so a
+// wave reads and writes whole lines.  FP8 pools take 8 bf16 values per piece
+// and store their 8 codes.
+constexpr int kExtTok = 8;
+
+template <bool FP8>
+__global__ void __launch_bounds__(256) kv_store_extend_kernel(
+    char* __restrict__ k_pool, char* __restrict__ v_pool, const char* __restrict__ k_new,
+    const char* __restrict__ v_new, const int32_t* __restrict__ r2t, int64_t stride,
+    const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
+    const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ qo_indptr, uint32_t pieces,
+    int64_t src_row_bytes, int64_t dst_row_bytes, float k_inv, float v_inv) {
+  const int b = blockIdx.y;
+  const int j0 = blockIdx.x * kExtTok;
+  const int E = extend_lens[b];
+  if (j0 >= E) return;
+  const uint32_t n = uint32_t(min(kExtTok, E - j0));
+  const int64_t row = rpi ? rpi[b] : b;
+  const int32_t* slots = r2t + row * stride + prefix_lens[b] + j0;
+  const int64_t src0 = int64_t(qo_indptr[b]) + j0;
+  const uint32_t total = n * pieces;
+  // kUnroll pieces per thread per round, all loaded before any is stored, so
+  // each thread keeps 2 * kUnroll 16-byte loads in flight.
+  constexpr int kUnroll = 4;
+  for (uint32_t base = threadIdx.x; base < total; base += kUnroll * blockDim.x) {
+    u32x4 kw[kUnroll], vw[kUnroll];
+    int64_t dst[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t idx = base + u * blockDim.x;
+      if (idx < total) {
+        const uint32_t t = idx / pieces;
+        const uint32_t pc = idx - t * pieces;
+        const int64_t src = (src0 + t) * src_row_bytes + int64_t(pc) * 16;
+        kw[u] = *reinterpret_cast<const u32x4*>(k_new + src);
+        vw[u] = *reinterpret_cast<const u32x4*>(v_new + src);
+        dst[u] = int64_t(slots[t]) * dst_row_bytes + int64_t(pc) * (FP8 ? 8 : 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (base + u * blockDim.x >= total) break;
+      if constexpr (!FP8) {
+        *reinterpret_cast<u32x4*>(k_pool + dst[u]) = kw[u];
+        *reinterpret_cast<u32x4*>(v_pool + dst[u]) = vw[u];
+      } else {
+        u32x2 ko = {0u, 0u}, vo = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t kb = (kw[u][i >> 1] >> (16 * (i & 1))) & 0xffffu;
+          const uint32_t vb = (vw[u][i >> 1] >> (16 * (i & 1))) & 0xffffu;
+          ko[i >> 2] |= rtk::f32_to_e4m3(__uint_as_float(kb << 16) * k_inv) << (8 * (i & 3));
+          vo[i >> 2] |= rtk::f32_to_e4m3(__uint_as_float(vb << 16) * v_inv) << (8 * (i & 3));
+        }
+        *reinterpret_cast<u32x2*>(k_pool + dst[u]) = ko;
+        *reinterpret_cast<u32x2*>(v_pool + dst[u]) = vo;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" int decode_append_fp8(int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* rows,
@@ -206,4 +271,62 @@ extern "C" int kv_store(void* k_pool, void* v_pool, const void* k_new, const voi
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return rt::fail(RT_ERR_HIP, std::string("kv_store launch: ") + hipGetErrorString(e));
   return RT_OK;
+}
+
+namespace {
+
+int store_extend(const char* name, bool fp8, void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                 const int32_t* req_to_token, int32_t stride, const int32_t* req_pool_indices,
+                 const int32_t* prefix_lens, const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
+                 int32_t max_extend_len, int32_t num_kv_heads, int32_t head_dim, int64_t eb, float k_inv,
+                 float v_inv, void* stream) {
+  if (batch < 0 || max_extend_len < 0 || stride < 1 || num_kv_heads < 1 || (head_dim != 64 && head_dim != 128))
+    return rt::fail(RT_ERR_INVALID, std::string(name) + ": bad size or shape");
+  if (batch > 65535) return rt::fail(RT_ERR_INVALID, std::string(name) + ": batch above 65535");
+  if (batch == 0 || max_extend_len == 0) return RT_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !req_to_token || !prefix_lens || !extend_lens || !qo_indptr)
+    return rt::fail(RT_ERR_INVALID, std::string(name) + ": null pointer");
+  const int64_t row_elems = int64_t(num_kv_heads) * head_dim;
+  const int64_t src_row_bytes = row_elems * eb;
+  const uint32_t pieces = uint32_t(src_row_bytes / 16);
+  const dim3 grid{uint32_t((int64_t(max_extend_len) + kExtTok - 1) / kExtTok), uint32_t(batch)};
+  if (fp8)
+    hipLaunchKernelGGL(kv_store_extend_kernel<true>, grid, dim3(256), 0, (hipStream_t)stream, (char*)k_pool,
+                       (char*)v_pool, (const char*)k_new, (const char*)v_new, req_to_token, int64_t(stride),
+                       req_pool_indices, prefix_lens, extend_lens, qo_indptr, pieces, src_row_bytes, row_elems,
+                       k_inv, v_inv);
+  else
+    hipLaunchKernelGGL(kv_store_extend_kernel<false>, grid, dim3(256), 0, (hipStream_t)stream, (char*)k_pool,
+                       (char*)v_pool, (const char*)k_new, (const char*)v_new, req_to_token, int64_t(stride),
+                       req_pool_indices, prefix_lens, extend_lens, qo_indptr, pieces, src_row_bytes, src_row_bytes,
+                       k_inv, v_inv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return rt::fail(RT_ERR_HIP, std::string(name) + " launch: " + hipGetErrorString(e));
+  return RT_OK;
+}
+
+}  // namespace
+
+extern "C" int kv_store_extend(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                               const int32_t* req_to_token, int32_t req_to_token_stride,
+                               const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                               const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
+                               int32_t max_extend_len, int32_t num_kv_heads, int32_t head_dim, int dtype,
+                               void* stream) {
+  if (dtype != RT_F32 && dtype != RT_BF16) return rt::fail(RT_ERR_INVALID, "kv_store_extend: bad dtype");
+  return store_extend("kv_store_extend", false, k_pool, v_pool, k_new, v_new, req_to_token, req_to_token_stride,
+                      req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch, max_extend_len, num_kv_heads,
+                      head_dim, dtype == RT_BF16 ? 2 : 4, 1.f, 1.f, stream);
+}
+
+extern "C" int kv_store_extend_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                                   const int32_t* req_to_token, int32_t req_to_token_stride,
+                                   const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                   const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
+                                   int32_t max_extend_len, int32_t num_kv_heads, int32_t head_dim, float k_scale,
+                                   float v_scale, void* stream) {
+  if (!(k_scale > 0.f) || !(v_scale > 0.f)) return rt::fail(RT_ERR_INVALID, "kv_store_extend_fp8: bad scale");
+  return store_extend("kv_store_extend_fp8", true, k_pool, v_pool, k_new, v_new, req_to_token, req_to_token_stride,
+                      req_pool_indices, prefix_lens, extend_lens, qo_indptr, batch, max_extend_len, num_kv_heads,
+                      head_dim, 2, 1.0f / k_scale, 1.0f / v_scale, stream);
 }

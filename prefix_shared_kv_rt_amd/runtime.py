@@ -186,6 +186,56 @@ class RadixRuntime:
                 self.events.append(("decode", e0, self._event(), {"tokens": n, "bytes": nbytes}))
             return o
 
+    def run_mixed(self, ext_rows, prefix_lens, extend_lens, q, k_new, v_new, out_cache_loc, dec_rows, positions,
+                  slots, qd, kd, vd):
+        """An iteration with extend chunks and decode rows as one attention
+        launch: store the chunks' K/V, append the decode rows' slots and K/V,
+        then radix_mixed_attention over the extend requests followed by the
+        decode rows (prefix = position, one row each).  Returns (extend o,
+        decode o)."""
+        if self.device is None:
+            return None, None
+        n_e, n_d = len(ext_rows), len(dec_rows)
+        with torch.cuda.stream(self.stream):
+            loc = self._to_dev(out_cache_loc)
+            e0 = self._event() if self.events is not None else None
+            self._store(k_new, v_new, loc)
+            if e0 is not None:
+                self.events.append(("kv_store", e0, self._event(), {"rows": int(loc.numel())}))
+            rows_all = np.concatenate([np.asarray(ext_rows, np.int32), np.asarray(dec_rows, np.int32)])
+            pl_all = np.concatenate([np.asarray(prefix_lens, np.int32), np.asarray(positions, np.int32)])
+            el_all = np.concatenate([np.asarray(extend_lens, np.int32), np.ones(n_d, np.int32)])
+            qo = np.zeros(n_e + n_d + 1, dtype=np.int32)
+            qo[1:] = np.cumsum(el_all)
+            n = n_e + n_d
+            meta = self._to_dev(np.concatenate([rows_all, pl_all, el_all, qo, np.asarray(slots, np.int32)]))
+            d_rows, d_pl, d_el = meta[:n], meta[n:2 * n], meta[2 * n:3 * n]
+            d_qo, d_slots = meta[3 * n:4 * n + 1], meta[4 * n + 1:]
+            d_drows, d_pos = d_rows[n_e:], d_pl[n_e:]   # a decode row's prefix length is its position
+            qall = torch.cat([q, qd])
+            o = torch.empty_like(qall)
+            e0 = self._event() if self.events is not None else None
+            if self.kv_fp8_scales:
+                B.decode_append_fp8(self.r2t_dev, d_drows, d_pos, d_slots, self.k_pool, self.v_pool, kd, vd,
+                                    *self.kv_fp8_scales, stream=self.stream)
+                B.radix_mixed_attention_fp8kv(qall, o, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pl, d_el,
+                                              d_qo, n_e, int(max(extend_lens)), 1, self.sm_scale,
+                                              *self.kv_fp8_scales, stream=self.stream)
+            else:
+                B.decode_append(self.r2t_dev, d_drows, d_pos, d_slots, self.k_pool, self.v_pool, kd, vd,
+                                stream=self.stream)
+                B.radix_mixed_attention(qall, o, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pl, d_el, d_qo,
+                                        n_e, int(max(extend_lens)), 1, self.sm_scale, stream=self.stream)
+            if e0 is not None:
+                pl = np.asarray(prefix_lens, dtype=np.float64)
+                el = np.asarray(extend_lens, dtype=np.float64)
+                kv = np.asarray(positions, dtype=np.float64) + 1
+                flops = 4.0 * self.d * self.hq * float(np.sum(el * pl + el * (el + 1) / 2) + np.sum(kv))
+                self.events.append(("mixed", e0, self._event(), {"tokens": int(el.sum()) + n_d,
+                                                                  "ext_tokens": int(el.sum()), "dec_tokens": n_d,
+                                                                  "flops": flops}))
+            t_e = int(np.sum(extend_lens))
+            return o[:t_e], o[t_e:]
 
 @dataclass
 class _Run:
@@ -206,7 +256,7 @@ class Scheduler:
 
     def __init__(self, rt, requests, qkv_source, max_running=256, max_extend_tokens=16384,
                  skip_extend_attention=False, record=None, keep_dumps=False, policy="fcfs", graphs=None,
-                 chunk_size=None):
+                 chunk_size=None, mixed=False):
         if rt.max_reqs < max_running:
             raise ValueError("the slot table needs a row per running request")
         if policy not in ("fcfs", "lspf"):
@@ -217,6 +267,12 @@ class Scheduler:
         self.chunk_size = chunk_size
         self.prefilling = []  # admitted requests with prompt tokens still to extend
         self.graphs = graphs  # a DecodeGraphs: decode steps replay captured graphs when the batch fits
+        # mixed: an iteration's extend chunks and decode rows share one
+        # attention launch (radix_mixed_attention) unless a request finishes
+        # right after its extend: its freed slots could be handed to this
+        # iteration's decode rows and overwritten before the launch reads them.
+        self.mixed = bool(mixed)
+        self.mixed_launches = 0
         self.rt = rt
         self.pending = list(requests)
         self.qkv = qkv_source
@@ -333,6 +389,7 @@ class Scheduler:
         # device rows: the computed prefix of every request touched this iteration
         touched = list({id(r): r for r in [c[0] for c in chunks] + admitted}.values())
         rt.upload_rows([r.row for r in touched], [r.done for r in touched])
+        ext = None  # this iteration's extend launch, deferred when it may join the decode rows
         if total > 0 and rt.device is not None:
             qs, ks, vs = [], [], []
             for r, start, n in chunks:
@@ -340,17 +397,17 @@ class Scheduler:
                 qs.append(q)
                 ks.append(k)
                 vs.append(v)
-            q, k, v = torch.cat(qs), torch.cat(ks), torch.cat(vs)
-            o = rt.run_extend([r.row for r, _, _ in chunks], [start for _, start, _ in chunks],
-                              [n for _, _, n in chunks], q, k, v, loc, attention=not self.skip_extend_attention)
-            if o is not None and self.record is not None:
-                off = 0
-                for r, start, n in chunks:
-                    self.record("ext", r.req.rid, r.chunks, o[off:off + n])
-                    off += n
+            ext = ([r.row for r, _, _ in chunks], [start for _, start, _ in chunks], [n for _, _, n in chunks],
+                   torch.cat(qs), torch.cat(ks), torch.cat(vs), loc, [(r.req.rid, r.chunks, n) for r, _, n in chunks])
         for r, _, _ in chunks:
             r.chunks += 1
         new_ids = {id(r) for r in admitted}
+        completing = [r for r in [c[0] for c in chunks if id(c[0]) not in new_ids] + admitted
+                      if r.done == len(r.req.prompt)]
+        if ext is not None and not (self.mixed and not self.skip_extend_attention and
+                                    all(len(r.req.gen) > 0 for r in completing)):
+            self._launch_extend(ext)
+            ext = None
         for r in [c[0] for c in chunks if id(c[0]) not in new_ids] + admitted:
             if r.done < len(r.req.prompt):
                 if id(r) in new_ids:
@@ -382,9 +439,16 @@ class Scheduler:
                     ks.append(k)
                     vs.append(v)
                 q, k, v = torch.cat(qs), torch.cat(ks), torch.cat(vs)
-                o = self.graphs.run(rows, positions, slots, q, k, v) if self.graphs is not None else None
-                if o is None:
-                    o = rt.run_decode(rows, positions, slots, q, k, v)
+                if ext is not None:
+                    rows_e, starts, ns, qe, ke, ve, loc_e, tags = ext
+                    o_e, o = rt.run_mixed(rows_e, starts, ns, qe, ke, ve, loc_e, rows, positions, slots, q, k, v)
+                    self._record_extend(o_e, tags)
+                    self.mixed_launches += 1
+                    ext = None
+                else:
+                    o = self.graphs.run(rows, positions, slots, q, k, v) if self.graphs is not None else None
+                    if o is None:
+                        o = rt.run_decode(rows, positions, slots, q, k, v)
             if o is not None and self.record is not None:
                 for i, r in enumerate(dec):
                     self.record("dec", r.req.rid, r.generated, o[i:i + 1])
@@ -394,12 +458,27 @@ class Scheduler:
             for r in done:
                 self.running.remove(r)
                 self._finish(r, rec)
+        if ext is not None:  # no decode rows this iteration
+            self._launch_extend(ext)
         # Host rows and pinned staging are reused by later iterations.
         if rt.stream is not None:
             rt.stream.synchronize()
         self.iterations.append(rec)
         if self.keep_dumps:
             self.dumps.append(B.rt_tree_dump(rt.tree))
+
+    def _launch_extend(self, ext):
+        rows, starts, ns, q, k, v, loc, tags = ext
+        o = self.rt.run_extend(rows, starts, ns, q, k, v, loc, attention=not self.skip_extend_attention)
+        self._record_extend(o, tags)
+
+    def _record_extend(self, o, tags):
+        if o is None or self.record is None:
+            return
+        off = 0
+        for rid, chunk, n in tags:
+            self.record("ext", rid, chunk, o[off:off + n])
+            off += n
 
     def run(self, max_iterations=100000):
         self._arrive()

@@ -19,7 +19,7 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
 def run_both(wl, want=None, max_running=256, max_extend_tokens=16384, max_reqs=None, policy="fcfs", graphs=False,
-             chunk_size=None, kv_fp8_scales=None):
+             chunk_size=None, kv_fp8_scales=None, mixed=False):
     ora = run_workload(wl, want=want, max_running=max_running, max_extend_tokens=max_extend_tokens, policy=policy,
                        chunk_size=chunk_size, kv_fp8_scales=kv_fp8_scales)
     outs = {}
@@ -35,7 +35,7 @@ def run_both(wl, want=None, max_running=256, max_extend_tokens=16384, max_reqs=N
     dg = DecodeGraphs(rt, max_batch=max_running) if graphs else None
     sch = Scheduler(rt, wl.requests, src, max_running=max_running, max_extend_tokens=max_extend_tokens,
                     skip_extend_attention=wl.skip_extend_attention, record=record, policy=policy, graphs=dg,
-                    chunk_size=chunk_size).run()
+                    chunk_size=chunk_size, mixed=mixed).run()
     if graphs:
         assert dg.replays > 0
     from prefix_shared_kv_rt_amd import binding as B
@@ -167,5 +167,33 @@ def test_small_few_shot_paged():
     wl = workloads.paged(workloads.few_shot(batch=8, prefix_len=256, suffix_len=64, decode_steps=2,
                                             num_slots=4096), 16)
     ora, sch, outs, dump, free = run_both(wl)
+    check_host_identical(ora, sch, dump, free)
+    check_outputs(ora, outs, TOL["bf16"])
+
+
+@pytest.mark.parametrize("chunk,page,fp8,graphs", [(None, 1, False, False), (24, 1, False, True), (24, 16, False, False),
+                                                   (None, 4, True, False)])
+def test_small_chat_mixed_launch(chunk, page, fp8, graphs):
+    """Iterations with extend chunks and decode rows run them as one
+    radix_mixed_attention launch: host decisions as always, every extend
+    and decode output against the oracle's."""
+    print(f"chat mixed launch (chunk {chunk}, pages of {page}, fp8 {fp8}, graphs {graphs})", flush=True)
+    wl = workloads.paged(workloads.chat(sessions=6, turns=3, system_len=64, user_lo=16, user_hi=48, gen_len=6), page)
+    scales = (0.5, 2.0) if fp8 else None
+    ora, sch, outs, dump, free = run_both(wl, max_running=4, max_extend_tokens=128, chunk_size=chunk,
+                                          kv_fp8_scales=scales, mixed=True, graphs=graphs)
+    check_host_identical(ora, sch, dump, free)
+    check_outputs(ora, outs, TOL["bf16"])
+    print(f"  {sch.mixed_launches} mixed launches", flush=True)
+    assert sch.mixed_launches > 0
+
+
+def test_small_fork_mixed_falls_back_when_a_prompt_finishes():
+    """Fork heads finish right after their extend while earlier branches
+    decode: those iterations keep separate launches (the heads' freed slots
+    may be handed to the decode rows); results as the oracle's."""
+    print("fork 6 prompts x 200 tokens x 3 branches x 4 steps, mixed", flush=True)
+    wl = workloads.fork(prompts=6, prompt_len=200, branches=3, decode_steps=4, num_slots=4096)
+    ora, sch, outs, dump, free = run_both(wl, max_running=8, max_extend_tokens=400, mixed=True)
     check_host_identical(ora, sch, dump, free)
     check_outputs(ora, outs, TOL["bf16"])
