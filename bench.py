@@ -9,16 +9,21 @@ whole path:
   host   rt_admit_batch     match each request, lock its path, allocate the
                             suffix slots (evicting LRU leaves on a deficit),
                             fill its req_to_token row
-  device kv_store           scatter the suffix K/V into the pool
+  device kv_store_extend    scatter the suffix K/V into the pool at the slots
+                            the req_to_token rows hold
   device extend attention   suffix rows against prefix + suffix K/V
   host   rt_decode_slots    one slot per request for its first generated token
-  device req_to_token_scatter, kv_store, decode attention (split-K)
+  device decode_append      the new token's req_to_token entry and K/V row
+  device decode attention   split-K
   host   rt_finish_batch    insert prompt + token, free duplicates, unlock
 
-Q/K/V of every step are generated into HBM before the timed region.  A
+Q/K/V of every step are generated into HBM before the timed region.  Before
+the warm-up steps, about 200 ms of extend attention over the cached prefix
+lets the GPU's clocks settle at their level under sustained load (the first
+few dozen steps otherwise run 10-15 % slower).  A
 suffix that starts like an earlier finished request's suffix matches more
-than 1024 tokens; its already-cached rows are padded to slot 0 in the
-scatter and skipped by extend (they are not counted as work).
+than 1024 tokens; its already-cached rows are skipped by the scatter and by
+extend (they are not counted as work).
 
 Output: one JSON line (metric, value = extend + decode tokens per second of
 whole steps, roofline of the extend kernel from HIP events on its stream,
@@ -71,6 +76,8 @@ def parse():
                     help="K/V pool format (fp8 = OCP E4M3 codes, scales 1)")
     ap.add_argument("--chunk-size", type=int, default=None,
                     help="chunked prefill for the chat workload: extend tokens per scheduler iteration")
+    ap.add_argument("--mixed", action="store_true",
+                    help="chat workload: an iteration's extend chunks and decode rows share one attention launch")
     ap.add_argument("--page-size", type=int, default=1,
                     help="KV slots per pool page (few_shot and chat); 1 = token-granular")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -92,7 +99,12 @@ class FewShotBench:
         self.Bm = B_mod
         self.gen_t = gen_t
         self.dev = torch.device("cuda:0")
-        self.stream = torch.cuda.Stream(self.dev)
+        # One stream for the whole step: the stream current at construction,
+        # so that torch's row copy (on the current stream) and the library's
+        # launches (on self.stream) stay in order without a per-step stream
+        # switch.  (A separate copy stream that overlaps the copy with the
+        # previous step's kernels measured no faster.)
+        self.stream = torch.cuda.current_stream(self.dev)
         rng = np.random.Generator(np.random.PCG64(self.SEED))
         self.prefix = rng.integers(0, 1000, size=self.PREFIX).astype(np.int32)
         # every batch: 64 suffixes of 128 tokens + 1 generated token each
@@ -107,17 +119,22 @@ class FewShotBench:
         # two row sets of 64 so that host writes for step i+1 never touch rows still being copied for step i
         # Per row set: B slot-table rows, then MR rows that carry the step's
         # metadata, so that one host-to-device copy moves both.
-        self.meta_n = 5 * self.B + 1 + self.B * self.SUFFIX
+        self.meta_n = 5 * self.B + 1
         self.MR = -(-self.meta_n // self.stride)
         self.set_rows = self.B + self.MR
         self.r2t_host_t = torch.zeros((2 * self.set_rows, self.stride), dtype=torch.int32, pin_memory=True)
         self.r2t_host = self.r2t_host_t.numpy()
         self.r2t_dev = torch.zeros((2 * self.set_rows, self.stride), dtype=torch.int32, device=self.dev)
-        # pinned metadata staging per row set: prefix, extend, qo_indptr(65), rows, dec_pos, dec_slots, loc(8192)
+        # pinned metadata staging per row set: prefix, extend, qo_indptr(65), rows, dec_slots
         meta_rows = lambda t, rs: t[rs * self.set_rows + self.B:(rs + 1) * self.set_rows].reshape(-1)[:self.meta_n]
         self.meta_host = [meta_rows(self.r2t_host, rs) for rs in range(2)]
         self.meta_dev = [meta_rows(self.r2t_dev, rs) for rs in range(2)]
-        self.copy_done = [None, None]
+        B = self.B
+        # device views of each row set's metadata: prefix_lens, extend_lens, qo_indptr, rows, decode slots
+        self.meta_views = [(md[0:B], md[B:2 * B], md[2 * B:3 * B + 1], md[3 * B + 1:4 * B + 1],
+                            md[4 * B + 1:5 * B + 1]) for md in self.meta_dev]
+        self.copy_done = [torch.cuda.Event(), torch.cuda.Event()]
+        self.copy_used = [False, False]
         self.rows = [np.arange(rs * self.set_rows, rs * self.set_rows + self.B, dtype=np.int32) for rs in range(2)]
         self.dec_pos = np.full(self.B, self.PREFIX + self.SUFFIX, dtype=np.int32)
         self.ws = torch.empty(B_mod.radix_decode_workspace_bytes(self.B, self.HQ, self.HKV, self.D, self.stride),
@@ -126,12 +143,14 @@ class FewShotBench:
         self.o_dec = torch.empty((self.B, self.HQ, self.D), dtype=bf16, device=self.dev)
         self.sm_scale = 1.0 / np.sqrt(self.D)
         self.pos_dev = torch.full((self.B,), self.PREFIX + self.SUFFIX, dtype=torch.int32, device=self.dev)
+        self.row_base = np.arange(self.B, dtype=np.int32) * self.SUFFIX
         self.ext_events = []
         self.dec_events = []
         self.flops = []
         self.ext_tokens = []
         self.dec_bytes = []
         self.host_s = []
+        self.step_lens = []
 
     def gen_inputs(self, n_batches):
         """Q/K/V of every suffix position and of the generated token, in HBM."""
@@ -186,6 +205,38 @@ class FewShotBench:
         self.stream.synchronize()
         Bm.rt_finish_batch(self.tree, toks, off, self.r2t_host, rows, pl, nodes)
 
+    def settle_clocks(self, ms=200.0):
+        """Untimed: repeat an extend launch of the batch's own shape (64
+        requests x 128 rows over 1152 keys, the first batch's queries) for
+        about ``ms`` milliseconds, so that the GPU's clocks reach the level
+        they hold under this load before any step runs; without it the first
+        few dozen steps run 10-15 % slower.  Its requests use the second row
+        set, which no step has used yet: each row holds the prefix's slots
+        and, at the suffix positions, the slots of prefix positions 0..127
+        (cached K/V, read only); the output goes to scratch.  The first step
+        that uses that row set rewrites it."""
+        torch, B, P, S = self.torch, self.B, self.PREFIX, self.SUFFIX
+        rows = self.rows[1]
+        pre = self.r2t_host[0, :P].copy()
+        self.r2t_host[rows, :P] = pre
+        self.r2t_host[rows, P:P + S] = pre[:S]
+        lo, hi = self.set_rows, 2 * self.set_rows
+        self.r2t_dev[lo:hi].copy_(self.r2t_host_t[lo:hi])
+        meta = torch.from_numpy(np.concatenate([rows, np.full(B, P), np.full(B, S), np.arange(B + 1) * S])
+                                .astype(np.int32)).to(self.dev)
+        d_rows, d_pl, d_el, d_qo = meta[:B], meta[B:2 * B], meta[2 * B:3 * B], meta[3 * B:]
+        q = self.inputs[0][0]
+        o = torch.empty_like(q)
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(8):
+                self._extend(q, o, d_rows, d_pl, d_el, d_qo, S)
+            self.stream.synchronize()
+
+    def _store_extend(self, k, v, rows, pl, el, qo, max_e):
+        f = self.Bm.kv_store_extend_fp8 if self.fp8 else self.Bm.kv_store_extend
+        f(self.k_pool, self.v_pool, k, v, self.r2t_dev, rows, pl, el, qo, max_e, stream=self.stream)
+
     def _store(self, k, v, loc):
         if self.fp8:
             self.Bm.kv_store_fp8(self.k_pool, self.v_pool, k, v, loc, stream=self.stream)
@@ -196,81 +247,77 @@ class FewShotBench:
         f = self.Bm.radix_extend_attention_fp8kv if self.fp8 else self.Bm.radix_extend_attention
         f(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows, pl, el, qo, max_e, self.sm_scale, stream=self.stream)
 
-    def step(self, i, timed):
+    def step(self, i, timed, ev=None):
+        """One step; ``ev`` = three timing events (before extend, after
+        extend, after decode) recorded on the stream when given.  Each event
+        costs the stream a few microseconds, so there are only three."""
         t_host = time.perf_counter()
         torch, Bm = self.torch, self.Bm
         B, S, P0 = self.B, self.SUFFIX, self.PREFIX
         q, k, v, qd, kd, vd = self.inputs[i]
         rs = i % 2
-        if self.copy_done[rs] is not None:
+        if self.copy_used[rs]:
             self.copy_done[rs].synchronize()       # host staging of this row set is free again
         rows = self.rows[rs]
         toks, full = self.tokens[i]
         pl, el, nodes, loc = Bm.rt_admit_batch(self.tree, toks, self.tok_off, self.r2t_host, rows)
         if int(pl.min()) < P0:
             raise RuntimeError("the shared prefix left the cache; the pool is too small for this run")
-        # scatter targets: already-cached suffix rows go to the dummy slot 0
         meta = self.meta_host[rs]
         meta[0:B] = pl
         meta[B:2 * B] = el
-        qo = np.arange(B, dtype=np.int32) * S + (pl - P0)
-        meta[2 * B:3 * B] = qo
+        # request b's new rows are the last el[b] of its S rows of q / k / v
+        meta[2 * B:3 * B] = self.row_base + (pl - P0)
         meta[3 * B] = B * S
         meta[3 * B + 1:4 * B + 1] = rows
-        base = 5 * B + 1
-        # request b's new rows are the last el[b] of its S rows; the rest write slot 0
-        pad = meta[base:base + B * S]
-        pad[:] = 0
-        starts = np.arange(B, dtype=np.int64) * S + S - el
-        pad[np.repeat(starts - (np.cumsum(el) - el), el) + np.arange(loc.size)] = loc
         # one decode slot per request, at position P0 + S
-        dslots = Bm.rt_decode_slots_batch(self.tree, rows, self.dec_pos, self.r2t_host)
-        meta[4 * B + 1:5 * B + 1] = dslots
-        md = self.meta_dev[rs]
-        with torch.cuda.stream(self.stream):
-            lo, hi = rs * self.set_rows, (rs + 1) * self.set_rows
-            self.r2t_dev[lo:hi].copy_(self.r2t_host_t[lo:hi], non_blocking=True)  # rows and metadata
-            ev = torch.cuda.Event()
-            ev.record(self.stream)
-            self.copy_done[rs] = ev
-            d_pl, d_el, d_qo, d_rows = md[0:B], md[B:2 * B], md[2 * B:3 * B + 1], md[3 * B + 1:4 * B + 1]
-            d_dslots, d_loc = md[4 * B + 1:5 * B + 1], md[base:base + B * S]
-            self._store(k, v, d_loc)
-            if timed:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(self.stream)
-            self._extend(q, self.o_ext, d_rows, d_pl, d_el, d_qo, int(el.max()))
-            if timed:
-                e1.record(self.stream)
-                self.ext_events.append((e0, e1))
-            d_pos = self.pos_dev
-            if self.fp8:
-                Bm.req_to_token_scatter(self.r2t_dev, d_rows, d_pos, d_dslots, stream=self.stream)
-                self._store(kd, vd, d_dslots)
-            else:  # slot-table entry and K/V row of the new token in one launch
-                Bm.decode_append(self.r2t_dev, d_rows, d_pos, d_dslots, self.k_pool, self.v_pool, kd, vd,
+        meta[4 * B + 1:5 * B + 1] = Bm.rt_decode_slots_batch(self.tree, rows, self.dec_pos, self.r2t_host)
+        d_pl, d_el, d_qo, d_rows, d_dslots = self.meta_views[rs]
+        max_e = int(el.max())
+        # every launch names self.stream; the row copy goes on the current
+        # stream, which is self.stream (the stream current at construction)
+        lo, hi = rs * self.set_rows, (rs + 1) * self.set_rows
+        self.r2t_dev[lo:hi].copy_(self.r2t_host_t[lo:hi], non_blocking=True)  # rows and metadata
+        self.copy_done[rs].record(self.stream)
+        self.copy_used[rs] = True
+        self._store_extend(k, v, d_rows, d_pl, d_el, d_qo, max_e)
+        if ev is not None:
+            ev[0].record(self.stream)
+        self._extend(q, self.o_ext, d_rows, d_pl, d_el, d_qo, max_e)
+        if ev is not None:
+            ev[1].record(self.stream)
+        d_pos = self.pos_dev
+        if self.fp8:
+            Bm.decode_append_fp8(self.r2t_dev, d_rows, d_pos, d_dslots, self.k_pool, self.v_pool, kd, vd,
                                  stream=self.stream)
-            if timed:
-                e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e2.record(self.stream)
-            dec = Bm.radix_decode_attention_fp8kv if self.fp8 else Bm.radix_decode_attention
-            dec(qd, self.o_dec, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pos, P0 + S + 1, self.sm_scale,
-                self.ws, stream=self.stream)
-            if timed:
-                e3.record(self.stream)
-                self.dec_events.append((e2, e3))
+        else:  # slot-table entry and K/V row of the new token in one launch
+            Bm.decode_append(self.r2t_dev, d_rows, d_pos, d_dslots, self.k_pool, self.v_pool, kd, vd,
+                             stream=self.stream)
+        dec = Bm.radix_decode_attention_fp8kv if self.fp8 else Bm.radix_decode_attention
+        dec(qd, self.o_dec, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pos, P0 + S + 1, self.sm_scale,
+            self.ws, stream=self.stream)
+        if ev is not None:
+            ev[2].record(self.stream)
         # finish: prompt + generated token into the tree
         Bm.rt_finish_batch(self.tree, full, self.full_off, self.r2t_host, rows, pl, nodes)
-        self.last_prefix_lens = pl.copy()
+        self.last_prefix_lens = pl
         if timed:
-            rows_keys = sum(int(p) * int(e) + int(e) * (int(e) + 1) // 2 for p, e in zip(pl, el))
-            self.flops.append(4.0 * self.D * self.HQ * rows_keys)
-            self.ext_tokens.append(int(el.sum()) + B)
-            kv_len = P0 + S + 1
-            eb = 1 if self.fp8 else 2
-            self.dec_bytes.append(B * kv_len * (self.HKV * self.D * eb * 2 + 4) + 2 * B * self.HQ * self.D * 2)
+            # flops and bytes follow from (pl, el) after the timed region
+            self.ext_events.append((ev[0], ev[1]))
+            self.dec_events.append((ev[1], ev[2]))   # append + decode attention
+            self.step_lens.append((pl, el))
             self.host_s.append(time.perf_counter() - t_host)
         return int(el.sum()) + B
+
+    def accounting(self):
+        """Extend flops and decode bytes of every timed step."""
+        P0, S, B = self.PREFIX, self.SUFFIX, self.B
+        eb = 1 if self.fp8 else 2
+        for pl, el in self.step_lens:
+            rows_keys = float(np.sum(pl.astype(np.float64) * el + el.astype(np.float64) * (el + 1) / 2))
+            self.flops.append(4.0 * self.D * self.HQ * rows_keys)
+            self.ext_tokens.append(int(el.sum()) + B)
+            self.dec_bytes.append(B * (P0 + S + 1) * (self.HKV * self.D * eb * 2 + 4) + 2 * B * self.HQ * self.D * 2)
 
 
 def run_few_shot(args, torch):
@@ -280,20 +327,23 @@ def run_few_shot(args, torch):
     fb = FewShotBench(n, torch, Bm, torch_gen, kv_dtype=args.kv_dtype, page_size=args.page_size)
     fb.gen_inputs(n)
     fb.warm_prefix()
+    fb.settle_clocks()
     for i in range(args.warmup):
         fb.step(i, timed=False)
     fb.stream.synchronize()
     torch.cuda.synchronize()
     gc.collect()
     gc.disable()  # a collector pass inside the timed steps would stall the host, not the path
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     tokens = 0
     for i in range(args.warmup, n):
-        tokens += fb.step(i, timed=True)
+        tokens += fb.step(i, timed=True, ev=evs[i - args.warmup])
     fb.stream.synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gc.enable()
+    fb.accounting()
     ext_ms = [a.elapsed_time(b) for a, b in fb.ext_events]
     dec_ms = [a.elapsed_time(b) for a, b in fb.dec_events]
     ext_avg_s = float(np.mean(ext_ms)) / 1e3
@@ -335,7 +385,7 @@ def run_few_shot(args, torch):
         "kernels": {
             "extend_us": ext_avg_s * 1e6,
             "extend_tokens_per_s": (fb.B * fb.SUFFIX) / ext_avg_s,
-            "decode_us": dec_avg_s * 1e6,
+            "decode_us": dec_avg_s * 1e6,   # decode_append + split-K decode attention
             "decode_hbm_gbs": float(np.mean(fb.dec_bytes)) / dec_avg_s / 1e9,
             # host time to run one step's tree work and enqueue its GPU work
             # (the step is host-bound when this is near ms_per_step)
@@ -439,6 +489,21 @@ class DecodeBench:
         self.events = []
         torch.cuda.synchronize()
 
+    def settle_clocks(self, ms=200.0):
+        """Untimed: decode attention over the prompts alone (pool reads, a
+        scratch output) for about ``ms`` milliseconds, so that the clocks
+        reach their level under sustained load before any step runs."""
+        torch, Bm = self.torch, self.Bm
+        d_pos = torch.full((self.B,), self.prompt_len - 1, dtype=torch.int32, device=self.dev)
+        o = torch.empty_like(self.o)
+        decode = Bm.radix_decode_attention_fp8kv if self.fp8 else Bm.radix_decode_attention
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(8):
+                decode(self.q[0], o, self.k_pool, self.v_pool, self.r2t_dev, self.rows_dev, d_pos, self.prompt_len,
+                       self.sm_scale, self.ws, stream=self.stream)
+            self.stream.synchronize()
+
     def step(self, s, timed):
         torch, Bm = self.torch, self.Bm
         pos = np.full(self.B, self.prompt_len + s, dtype=np.int32)
@@ -468,6 +533,7 @@ def run_decode_bench(args, torch):
     n = args.warmup + args.steps
     db = DecodeBench(args.workload, torch, Bm, torch_gen, n, kv_dtype=args.kv_dtype)
     db.setup()
+    db.settle_clocks()
     for s in range(args.warmup):
         db.step(s, timed=False)
     db.stream.synchronize()
@@ -525,7 +591,7 @@ def run_chat(args, torch):
     src = QKVSource(wl.seed, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, torch.bfloat16)
     rt.events = []
     sch = Scheduler(rt, wl.requests, src, max_running=256, max_extend_tokens=16384, policy=args.policy,
-                    chunk_size=args.chunk_size)
+                    chunk_size=args.chunk_size, mixed=args.mixed)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     marks = [0]
@@ -542,7 +608,7 @@ def run_chat(args, torch):
     it_ms = []
     for a, b in zip(marks[:-1], marks[1:]):
         evs = rt.events[a:b]
-        if any(kind == "decode" for kind, _, _, _ in evs):
+        if any(kind in ("decode", "mixed") for kind, _, _, _ in evs):
             it_ms.append(sum(x.elapsed_time(y) for _, x, y, _ in evs))
     per = {}
     for kind, a, b, info in rt.events:
@@ -552,9 +618,9 @@ def run_chat(args, torch):
         for k in ("tokens", "flops", "bytes", "rows"):
             d[k] += info.get(k, 0)
     rt.close()
-    ext, dec = per.get("extend", {}), per.get("decode", {})
+    ext, dec, mix = per.get("extend", {}), per.get("decode", {}), per.get("mixed", {})
     kernel_s = sum(d["ms"] for d in per.values()) / 1e3
-    tokens = ext.get("tokens", 0) + dec.get("tokens", 0)
+    tokens = ext.get("tokens", 0) + dec.get("tokens", 0) + mix.get("tokens", 0)
     byrid = {r.rid: r for r in wl.requests}
     evicted = sum(it.get("extend_freed_tokens", 0) + it.get("decode_freed_tokens", 0) for it in sch.iterations)
     re_extended = 0
@@ -573,6 +639,7 @@ def run_chat(args, torch):
                                "U{128..384} user + 128 generated tokens per turn, pool 60% of the working set; "
                                "one pass of the whole workload, a step = one scheduler iteration",
                    "policy": args.policy, "chunk_size": args.chunk_size, "page_size": wl.page_size,
+                   "mixed_launch": bool(args.mixed),
                    "kv_dtype": "fp8_e4m3" if args.kv_dtype == "fp8" else "bf16",
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "pool_slots": wl.num_slots},
@@ -580,6 +647,8 @@ def run_chat(args, torch):
         "kernels": {k: {"launches": d["launches"], "ms": d["ms"]} for k, d in per.items()},
         "extend": {"tokens": ext.get("tokens", 0), "tflops": ext_tf, "mfma_frac": ext_tf / PEAK_BF16_TFLOPS},
         "decode": {"tokens": dec.get("tokens", 0), "gbs": dec_gbs, "hbm_frac": dec_gbs / PEAK_HBM_GBS},
+        "mixed": {"launches": mix.get("launches", 0), "tokens": mix.get("tokens", 0),
+                  "tflops": mix.get("flops", 0.0) / max(mix.get("ms", 0.0), 1e-9) / 1e9},
         "hit_rate": {"cached": sch.cached_tokens, "prefill": sch.prefill_tokens,
                      "ratio": sch.cached_tokens / max(sch.prefill_tokens, 1)},
         "evicted_tokens": evicted, "re_extended_tokens": re_extended,
