@@ -14,7 +14,10 @@ whole path:
   device extend attention   suffix rows against prefix + suffix K/V
   host   rt_decode_slots    one slot per request for its first generated token
   device decode_append      the new token's req_to_token entry and K/V row
-  device decode attention   split-K
+  device decode attention   radix_decode_attention_shared: the batch is one
+                            group sharing the prefix's slots, read once for
+                            all 64 queries; each request's own tail split-K
+                            (--decode plain: split-K over whole contexts)
   host   rt_finish_batch    insert prompt + token, free duplicates, unlock
 
 Q/K/V of every step are generated into HBM before the timed region.  Before
@@ -76,6 +79,11 @@ def parse():
                     help="K/V pool format (fp8 = OCP E4M3 codes, scales 1)")
     ap.add_argument("--chunk-size", type=int, default=None,
                     help="chunked prefill for the chat workload: extend tokens per scheduler iteration")
+    ap.add_argument("--decode", choices=["plain", "shared"], default=None,
+                    help="decode path of few_shot, long_context and fork: plain = radix_decode_attention (split-K "
+                         "over each request's whole context), shared = radix_decode_attention_shared (K/V that a "
+                         "group of requests shares read once per group); default shared for few_shot, plain for "
+                         "the decode workloads")
     ap.add_argument("--mixed", action="store_true",
                     help="chat workload: an iteration's extend chunks and decode rows share one attention launch")
     ap.add_argument("--page-size", type=int, default=1,
@@ -92,8 +100,9 @@ class FewShotBench:
     SLOTS = 262144
     SEED = 1
 
-    def __init__(self, n_batches, torch, B_mod, gen_t, kv_dtype="bf16", page_size=1):
+    def __init__(self, n_batches, torch, B_mod, gen_t, kv_dtype="bf16", page_size=1, shared_decode=False):
         self.fp8 = kv_dtype == "fp8"
+        self.shared_decode = shared_decode
         self.page_size = int(page_size)
         self.torch = torch
         self.Bm = B_mod
@@ -139,6 +148,14 @@ class FewShotBench:
         self.dec_pos = np.full(self.B, self.PREFIX + self.SUFFIX, dtype=np.int32)
         self.ws = torch.empty(B_mod.radix_decode_workspace_bytes(self.B, self.HQ, self.HKV, self.D, self.stride),
                               dtype=torch.uint8, device=self.dev)
+        # Shared decode: the batch is one group; every request holds the
+        # cached prefix's slots at positions 0 .. PREFIX-1 (each step checks
+        # that the prefix is still matched), and its own slots after them.
+        self.sl_dev = torch.full((self.B,), self.PREFIX, dtype=torch.int32, device=self.dev)
+        self.gs_dev = torch.tensor([0, self.B], dtype=torch.int32, device=self.dev)
+        self.ws_shared = torch.empty(B_mod.radix_decode_shared_workspace_bytes(
+            self.B, self.HQ, self.HKV, self.D, 1, self.B, self.PREFIX, self.SUFFIX + 1), dtype=torch.uint8,
+            device=self.dev)
         self.o_ext = torch.empty((self.B * self.SUFFIX, self.HQ, self.D), dtype=bf16, device=self.dev)
         self.o_dec = torch.empty((self.B, self.HQ, self.D), dtype=bf16, device=self.dev)
         self.sm_scale = 1.0 / np.sqrt(self.D)
@@ -151,6 +168,7 @@ class FewShotBench:
         self.dec_bytes = []
         self.host_s = []
         self.step_lens = []
+        self.dec_distinct = []
 
     def gen_inputs(self, n_batches):
         """Q/K/V of every suffix position and of the generated token, in HBM."""
@@ -293,9 +311,14 @@ class FewShotBench:
         else:  # slot-table entry and K/V row of the new token in one launch
             Bm.decode_append(self.r2t_dev, d_rows, d_pos, d_dslots, self.k_pool, self.v_pool, kd, vd,
                              stream=self.stream)
-        dec = Bm.radix_decode_attention_fp8kv if self.fp8 else Bm.radix_decode_attention
-        dec(qd, self.o_dec, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pos, P0 + S + 1, self.sm_scale,
-            self.ws, stream=self.stream)
+        if self.shared_decode:
+            dec = Bm.radix_decode_attention_shared_fp8kv if self.fp8 else Bm.radix_decode_attention_shared
+            dec(qd, self.o_dec, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pos, self.sl_dev, self.gs_dev, B,
+                P0, S + 1, self.sm_scale, self.ws_shared, stream=self.stream)
+        else:
+            dec = Bm.radix_decode_attention_fp8kv if self.fp8 else Bm.radix_decode_attention
+            dec(qd, self.o_dec, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pos, P0 + S + 1, self.sm_scale,
+                self.ws, stream=self.stream)
         if ev is not None:
             ev[2].record(self.stream)
         # finish: prompt + generated token into the tree
@@ -318,13 +341,17 @@ class FewShotBench:
             self.flops.append(4.0 * self.D * self.HQ * rows_keys)
             self.ext_tokens.append(int(el.sum()) + B)
             self.dec_bytes.append(B * (P0 + S + 1) * (self.HKV * self.D * eb * 2 + 4) + 2 * B * self.HQ * self.D * 2)
+            # the prefix once, every request's own tail
+            self.dec_distinct.append(P0 * self.HKV * self.D * eb * 2 + B * (S + 1) * (self.HKV * self.D * eb * 2 + 4)
+                                     + 2 * B * self.HQ * self.D * 2)
 
 
 def run_few_shot(args, torch):
     from prefix_shared_kv_rt_amd import binding as Bm
     from synth import torch_gen
     n = args.warmup + args.steps
-    fb = FewShotBench(n, torch, Bm, torch_gen, kv_dtype=args.kv_dtype, page_size=args.page_size)
+    fb = FewShotBench(n, torch, Bm, torch_gen, kv_dtype=args.kv_dtype, page_size=args.page_size,
+                      shared_decode=(args.decode or "shared") == "shared")
     fb.gen_inputs(n)
     fb.warm_prefix()
     fb.settle_clocks()
@@ -369,11 +396,12 @@ def run_few_shot(args, torch):
             "batch": fb.B, "prefix_len": fb.PREFIX, "suffix_len": fb.SUFFIX, "num_q_heads": fb.HQ,
             "num_kv_heads": fb.HKV, "head_dim": fb.D, "pool_slots": fb.SLOTS,
             "kv_dtype": "fp8_e4m3" if fb.fp8 else "bf16", "page_size": fb.page_size,
+            "decode": "radix_decode_attention_shared" if fb.shared_decode else "radix_decode_attention",
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "radix_extend_attention_fp8kv (extend_bf16<128, 1, true>)" if fb.fp8 else
-                      "radix_extend_attention (extend_bf16<128, 1, false>)",
+            "kernel": "radix_extend_attention_fp8kv (extend_bf16<128, 1, true, false>)" if fb.fp8 else
+                      "radix_extend_attention (extend_bf16<128, 1, false, false>)",
             "achieved": achieved_tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -387,6 +415,7 @@ def run_few_shot(args, torch):
             "extend_tokens_per_s": (fb.B * fb.SUFFIX) / ext_avg_s,
             "decode_us": dec_avg_s * 1e6,   # decode_append + split-K decode attention
             "decode_hbm_gbs": float(np.mean(fb.dec_bytes)) / dec_avg_s / 1e9,
+            "decode_distinct_gbs": float(np.mean(fb.dec_distinct)) / dec_avg_s / 1e9,
             # host time to run one step's tree work and enqueue its GPU work
             # (the step is host-bound when this is near ms_per_step)
             "host_us_per_step": float(np.mean(fb.host_s)) * 1e6,
@@ -405,9 +434,10 @@ class DecodeBench:
     step allocates one slot per request, scatters its slot and K/V, and runs
     decode attention over the whole context."""
 
-    def __init__(self, name, torch, Bm, gen_t, n_steps, kv_dtype="bf16"):
+    def __init__(self, name, torch, Bm, gen_t, n_steps, kv_dtype="bf16", shared_decode=False):
         self.torch, self.Bm, self.T = torch, Bm, gen_t
         self.fp8 = kv_dtype == "fp8"
+        self.shared_decode = shared_decode
         self.dev = torch.device("cuda:0")
         self.stream = torch.cuda.Stream(self.dev)
         self.name = name
@@ -486,6 +516,14 @@ class DecodeBench:
         self.o = torch.empty((self.B, self.HQ, self.D), dtype=torch.bfloat16, device=self.dev)
         self.ws = torch.empty(Bm.radix_decode_workspace_bytes(self.B, self.HQ, self.HKV, self.D, self.stride),
                               dtype=torch.uint8, device=self.dev)
+        if self.shared_decode:
+            # group g = requests g*per .. (g+1)*per - 1, which share the first `shared` slots of their rows
+            self.sl_dev = torch.full((self.B,), self.shared, dtype=torch.int32, device=self.dev)
+            self.gs_dev = torch.arange(0, self.B + 1, per, dtype=torch.int32, device=self.dev)
+            need = max(Bm.radix_decode_shared_workspace_bytes(self.B, self.HQ, self.HKV, self.D, self.groups, per,
+                                                              self.shared, self.private + s + 1)
+                       for s in range(self.n_steps))
+            self.ws_shared = torch.empty(need, dtype=torch.uint8, device=self.dev)
         self.events = []
         torch.cuda.synchronize()
 
@@ -518,9 +556,15 @@ class DecodeBench:
             if timed:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(self.stream)
-            decode = Bm.radix_decode_attention_fp8kv if self.fp8 else Bm.radix_decode_attention
-            decode(self.q[s], self.o, self.k_pool, self.v_pool, self.r2t_dev, self.rows_dev, d_pos,
-                   self.prompt_len + s + 1, self.sm_scale, self.ws, stream=self.stream)
+            if self.shared_decode:
+                decode = Bm.radix_decode_attention_shared_fp8kv if self.fp8 else Bm.radix_decode_attention_shared
+                decode(self.q[s], self.o, self.k_pool, self.v_pool, self.r2t_dev, self.rows_dev, d_pos, self.sl_dev,
+                       self.gs_dev, self.B // self.groups, self.shared, self.private + s + 1, self.sm_scale,
+                       self.ws_shared, stream=self.stream)
+            else:
+                decode = Bm.radix_decode_attention_fp8kv if self.fp8 else Bm.radix_decode_attention
+                decode(self.q[s], self.o, self.k_pool, self.v_pool, self.r2t_dev, self.rows_dev, d_pos,
+                       self.prompt_len + s + 1, self.sm_scale, self.ws, stream=self.stream)
             if timed:
                 e1.record(self.stream)
                 self.events.append((e0, e1, int(pos[0]) + 1))
@@ -531,7 +575,8 @@ def run_decode_bench(args, torch):
     from prefix_shared_kv_rt_amd import binding as Bm
     from synth import torch_gen
     n = args.warmup + args.steps
-    db = DecodeBench(args.workload, torch, Bm, torch_gen, n, kv_dtype=args.kv_dtype)
+    db = DecodeBench(args.workload, torch, Bm, torch_gen, n, kv_dtype=args.kv_dtype,
+                     shared_decode=(args.decode or "plain") == "shared")
     db.setup()
     db.settle_clocks()
     for s in range(args.warmup):
@@ -554,7 +599,9 @@ def run_decode_bench(args, torch):
     row = db.HKV * db.D * (1 if db.fp8 else 2)   # one K (or V) pool row
     alg_bytes = db.B * kv * (2 * row + 4) + 2 * db.B * db.HQ * db.D * 2
     distinct = db.groups * db.shared * 2 * row + db.B * (kv - db.shared) * (2 * row + 4)
-    achieved = alg_bytes / avg_s / 1e9
+    # The plain decode reads every request's whole context; the shared
+    # decode must read only the distinct bytes (each group's shared part once).
+    achieved = (distinct if db.shared_decode else alg_bytes) / avg_s / 1e9
     label = ("long-context decode: 32 requests x (16384 shared + 16384 private) context, Hq 64 / Hkv 8 / D 128"
              if db.name == "long_context" else
              "fork decode: 16 prompts x 2048 tokens, 8 branches each (batch 128), Hq 32 / Hkv 8 / D 128")
@@ -563,13 +610,16 @@ def run_decode_bench(args, torch):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": label, "batch": db.B, "num_q_heads": db.HQ, "num_kv_heads": db.HKV,
-                   "head_dim": db.D, "pool_slots": db.SLOTS, "kv_dtype": "fp8_e4m3" if db.fp8 else "bf16"},
+                   "head_dim": db.D, "pool_slots": db.SLOTS, "kv_dtype": "fp8_e4m3" if db.fp8 else "bf16",
+                   "shared_decode": bool(db.shared_decode)},
         "roofline": {"bound": "hbm",
-                     "kernel": ("radix_decode_attention_fp8kv" if db.fp8 else "radix_decode_attention")
-                               + " (split + combine)",
+                     "kernel": ("radix_decode_attention_shared" if db.shared_decode else "radix_decode_attention")
+                               + ("_fp8kv" if db.fp8 else "")
+                               + (" (shared pass + private split + combine), bytes = distinct bytes"
+                                  if db.shared_decode else " (split + combine)"),
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": profiled_traffic("decode_split_fp8" if db.fp8 else "decode_split_bf16")
-                                if db.name == "long_context" else None,
+                                if db.name == "long_context" and not db.shared_decode else None,
                      "bytes_per_launch": alg_bytes, "distinct_bytes_per_launch": distinct,
                      "avg_launch_us": avg_s * 1e6},
     }

@@ -348,6 +348,44 @@ int radix_decode_attention(const void* q, void* o, const void* k_pool, const voi
                            float sm_scale, int dtype, void* workspace, int64_t workspace_bytes,
                            void* stream);
 
+/* Decode for batches whose requests share cached prefixes.  The radix tree
+ * hands requests that matched the same path the same slots for that path
+ * [P2 section 04: requests that match a common prefix reference one copy of
+ * its K/V]; this call reads such a shared part once per group instead of
+ * once per request.  The result is radix_decode_attention's (same q, o,
+ * pools, req_to_token, req_pool_indices, prefix_lens = positions), computed
+ * in two passes whose split-K partials one combine merges exactly:
+ *  - shared pass: for each group, the queries of all its members (x all
+ *    heads of a KV head) against the group's shared keys, as MFMA tiles
+ *    (the extend kernel, without a causal mask);
+ *  - private pass: each request's keys shared_lens[b] .. prefix_lens[b]
+ *    (the split-K decode).
+ * Groups: requests group_start[g] .. group_start[g+1] - 1 (device, int32
+ * [n_groups + 1]; group_start[0] = 0, increasing, group_start[n_groups] =
+ * batch), so the groups are consecutive runs of the batch.  shared_lens
+ * (device, int32 [batch]): every member of a group has the same value S_g,
+ * and the members' req_to_token rows hold the same slots at 0 .. S_g - 1;
+ * 0 <= S_g <= prefix_lens[b] + 1 (a group of one with S_g = 0 is a plain
+ * decode row).  None of this is checked on the device.  Host bounds:
+ * max_group_size >= every group's size, max_shared_len >= every S_g,
+ * max_private_len >= every prefix_lens[b] + 1 - shared_lens[b] (>= 1);
+ * req_to_token_stride >= max_shared_len + max_private_len.  bf16 q / o and
+ * pools; at most 16 query heads per KV head.  workspace (device) of at least
+ * radix_decode_shared_workspace_bytes(...) bytes.  Rounding differs from
+ * radix_decode_attention's (other chunking and operand order); both are
+ * fp32-accumulated. */
+int64_t radix_decode_shared_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t n_groups, int32_t max_group_size,
+                                            int32_t max_shared_len, int32_t max_private_len);
+int radix_decode_attention_shared(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                  const int32_t* req_to_token, int32_t req_to_token_stride,
+                                  const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                  const int32_t* shared_lens, const int32_t* group_start, int32_t batch,
+                                  int32_t n_groups, int32_t max_group_size, int32_t max_shared_len,
+                                  int32_t max_private_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, float sm_scale, void* workspace, int64_t workspace_bytes,
+                                  void* stream);
+
 /* FP8 K/V pool [P4 the v0.2 release was measured in FP8 as well as bf16;
  * the pool format is OCP 8-bit floating point E4M3: sign, 4 exponent bits
  * with bias 7, 3 mantissa bits, no infinity, S.1111.111 NaN, largest finite
@@ -392,6 +430,17 @@ int radix_extend_attention_fp8kv(const void* q, void* o, const void* k_pool, con
                                  const int32_t* extend_lens, const int32_t* qo_indptr, int32_t batch,
                                  int32_t max_extend_len, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, float sm_scale, float k_scale, float v_scale, void* stream);
+
+/* radix_decode_attention_shared over FP8 pools (q, o bf16; pools and scales
+ * as in radix_decode_attention_fp8kv). */
+int radix_decode_attention_shared_fp8kv(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                        const int32_t* req_to_token, int32_t req_to_token_stride,
+                                        const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                        const int32_t* shared_lens, const int32_t* group_start, int32_t batch,
+                                        int32_t n_groups, int32_t max_group_size, int32_t max_shared_len,
+                                        int32_t max_private_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, float sm_scale, float k_scale, float v_scale,
+                                        void* workspace, int64_t workspace_bytes, void* stream);
 
 /* radix_mixed_attention over FP8 pools (q, o bf16; pools and scales as in
  * radix_extend_attention_fp8kv). */

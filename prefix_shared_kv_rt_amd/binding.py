@@ -26,6 +26,7 @@ EXPORTS = [
     "kv_store", "req_to_token_scatter", "decode_append", "kv_store_fp8", "radix_decode_attention_fp8kv",
     "radix_extend_attention_fp8kv", "decode_append_fp8", "kv_store_extend", "kv_store_extend_fp8",
     "radix_mixed_attention", "radix_mixed_attention_fp8kv",
+    "radix_decode_shared_workspace_bytes", "radix_decode_attention_shared", "radix_decode_attention_shared_fp8kv",
     "radix_extend_attention", "radix_decode_workspace_bytes", "radix_decode_attention",
 ]
 
@@ -125,6 +126,13 @@ def lib():
                                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                            ctypes.c_int32, ctypes.c_float, ctypes.c_float,
                                                            ctypes.c_float, _vp]),
+            "radix_decode_shared_workspace_bytes": (ctypes.c_int64, [ctypes.c_int32] * 8),
+            "radix_decode_attention_shared": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
+                                                             _vp] + [ctypes.c_int32] * 8 + [ctypes.c_float, _vp,
+                                                                                             ctypes.c_int64, _vp]),
+            "radix_decode_attention_shared_fp8kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp,
+                                                                   _vp, _vp] + [ctypes.c_int32] * 8 +
+                                                    [ctypes.c_float] * 3 + [_vp, ctypes.c_int64, _vp]),
             "radix_extend_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
@@ -488,3 +496,37 @@ def radix_decode_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices,
                                         _dptr(extend_lens), batch, int(max_kv_len), hq, hkv, d, float(sm_scale),
                                         _dtype_code(q), _dptr(workspace), workspace.numel() * workspace.element_size(),
                                         _stream(stream)))
+
+
+def radix_decode_shared_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, n_groups, max_group_size,
+                                        max_shared_len, max_private_len):
+    return int(lib().radix_decode_shared_workspace_bytes(int(batch), int(num_q_heads), int(num_kv_heads),
+                                                         int(head_dim), int(n_groups), int(max_group_size),
+                                                         int(max_shared_len), int(max_private_len)))
+
+
+def radix_decode_attention_shared(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens, shared_lens,
+                                  group_start, max_group_size, max_shared_len, max_private_len, sm_scale, workspace,
+                                  stream=None):
+    """Decode with shared prefixes read once per group; group_start is a
+    device int32 tensor of n_groups + 1 entries."""
+    batch, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    _check(lib().radix_decode_attention_shared(
+        _dptr(q), _dptr(o), _dptr(k_pool), _dptr(v_pool), _dptr(req_to_token), req_to_token.shape[1],
+        _dptr(req_pool_indices), _dptr(prefix_lens), _dptr(shared_lens), _dptr(group_start), batch,
+        group_start.shape[0] - 1, int(max_group_size), int(max_shared_len), int(max_private_len), hq, hkv, d,
+        float(sm_scale), _dptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def radix_decode_attention_shared_fp8kv(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens,
+                                        shared_lens, group_start, max_group_size, max_shared_len, max_private_len,
+                                        sm_scale, workspace, k_scale=1.0, v_scale=1.0, stream=None):
+    batch, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    _check(lib().radix_decode_attention_shared_fp8kv(
+        _dptr(q), _dptr(o), _dptr(k_pool), _dptr(v_pool), _dptr(req_to_token), req_to_token.shape[1],
+        _dptr(req_pool_indices), _dptr(prefix_lens), _dptr(shared_lens), _dptr(group_start), batch,
+        group_start.shape[0] - 1, int(max_group_size), int(max_shared_len), int(max_private_len), hq, hkv, d,
+        float(sm_scale), float(k_scale), float(v_scale), _dptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -71,6 +71,43 @@ DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len, 
   return {splits, chunk};
 }
 
+// The shared-prefix decode: pass A (the extend kernel's partial mode) cuts
+// the longest shared part into n_a chunks of chunk_a keys (a multiple of the
+// extend tile, 128..2048 keys, about 256 items of (query tile, group, KV
+// head, chunk)); pass B is the split plan over the longest private tail.
+// Partial slots 0 .. n_a - 1 of each (request, head) hold pass A's chunks,
+// n_a .. n_a + b.splits - 1 pass B's.
+struct SharedPlan {
+  int n_a, chunk_a;
+  DecodePlan b;
+  int total() const { return n_a + b.splits; }
+};
+constexpr int kSharedRows = 128;  // query rows per item of the extend kernel
+#ifndef RT_SHARED_ITEMS
+#define RT_SHARED_ITEMS 256
+#endif
+#ifndef RT_SHARED_MIN_CHUNK
+#define RT_SHARED_MIN_CHUNK 128
+#endif
+constexpr int kSharedItems = RT_SHARED_ITEMS;        // target work items of the shared pass
+constexpr int kSharedMinChunk = RT_SHARED_MIN_CHUNK;  // shortest shared chunk (keys)
+SharedPlan plan_shared(int32_t batch, int32_t Hq, int32_t Hkv, int32_t n_groups, int32_t max_group_size,
+                       int32_t max_shared_len, int32_t max_private_len, int max_chunk) {
+  SharedPlan sp{0, 64, plan_decode(batch, Hkv, std::max(max_private_len, 1), max_chunk)};
+  if (max_shared_len > 0) {
+    const int64_t n_qt = (int64_t(max_group_size) * (Hq / Hkv) + kSharedRows - 1) / kSharedRows;
+    const int64_t units = std::max<int64_t>(1, n_qt * n_groups * Hkv);
+    int64_t c = (kSharedItems + units - 1) / units;
+    c = std::max<int64_t>(c, (max_shared_len + 2047) / 2048);
+    c = std::min<int64_t>(c, std::max<int64_t>(1, (max_shared_len + kSharedMinChunk - 1) / kSharedMinChunk));
+    int chunk = int((max_shared_len + c - 1) / c);
+    chunk = (chunk + 63) / 64 * 64;
+    sp.chunk_a = chunk;
+    sp.n_a = (max_shared_len + chunk - 1) / chunk;
+  }
+  return sp;
+}
+
 // ----------------------------------------------------------------- bf16 --
 // Persistent waves: the grid holds as many waves as fit on the chip; work
 // items (chunk s, KV head h, request b) are ordered with b innermost and cut
@@ -95,7 +132,12 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
     const char* __restrict__ q, const char* __restrict__ k_pool, const char* __restrict__ v_pool,
     const int32_t* __restrict__ req_to_token, int64_t stride, const int32_t* __restrict__ rpi,
     const int32_t* __restrict__ prefix_lens, int B, int Hq, int Hkv, int G, int S, int chunk, float scale_log2,
-    float v_scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
+    float v_scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    const int32_t* __restrict__ key_start = nullptr, int s_off = 0, int S_total = 0) {
+  // key_start (optional): request b's chunks cover keys key_start[b] ..
+  // prefix_lens[b] (the shared-prefix decode's private tails); its partials
+  // go to split slots s_off .. s_off + S - 1 of S_total (default: S).
+  if (S_total == 0) S_total = S;
   constexpr int KS = D / 32;      // 32-dim steps of the score contraction
   constexpr int VH = D / 64;      // 64-dim halves of the PV update
   constexpr int EB = KV8 ? 1 : 2; // bytes per pool element
@@ -118,7 +160,7 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
     const int kvh = (item / B) % Hkv;
     const int s = item / (B * Hkv);
     const int kv_len = prefix_lens[b] + 1;
-    const int start = s * chunk;
+    const int start = (key_start ? key_start[b] : 0) + s * chunk;
     const int end = min(kv_len, start + chunk);
     const int32_t* idx_row = req_to_token + int64_t(rpi ? rpi[b] : b) * stride;
     const char* kbase = k_pool + (int64_t(kvh) * D + 8 * grp) * EB;
@@ -236,7 +278,7 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
     if (col < G) {
-      const int64_t part = (int64_t(b) * Hq + kvh * G + col) * S + s;
+      const int64_t part = (int64_t(b) * Hq + kvh * G + col) * S_total + s_off + s;
       if (grp == 0) {
         ws_ml[part * 2 + 0] = m;
         ws_ml[part * 2 + 1] = l;
@@ -368,23 +410,24 @@ template <int D>
 void launch_decode(const void* q, void* o, const void* k_pool, const void* v_pool, const int32_t* r2t,
                    int64_t stride, const int32_t* rpi, const int32_t* plens, int B, int Hq, int Hkv,
                    DecodePlan pl, float scale_log2, float v_scale, int mode, float* ws_acc, float* ws_ml,
-                   hipStream_t st) {
+                   hipStream_t st, const int32_t* key_start = nullptr, int s_off = 0, int S_total = 0) {
   const int G = Hq / Hkv;
+  if (S_total == 0) S_total = pl.splits;
   if (mode == RT_BF16 || mode == kModeFp8Kv) {
     const int64_t items = int64_t(B) * Hkv * pl.splits;
     if (mode == RT_BF16) {
       const int64_t grid = std::min<int64_t>(resident_waves<D, false>(), (items + 7) / 8 * 8);
       hipLaunchKernelGGL((decode_split_bf16<D, false>), dim3(uint32_t(grid)), dim3(64), 0, st, (const char*)q,
                          (const char*)k_pool, (const char*)v_pool, r2t, stride, rpi, plens, B, Hq, Hkv, G, pl.splits,
-                         pl.chunk, scale_log2, 1.0f, ws_acc, ws_ml);
+                         pl.chunk, scale_log2, 1.0f, ws_acc, ws_ml, key_start, s_off, S_total);
     } else {
       const int64_t grid = std::min<int64_t>(resident_waves<D, true>(), (items + 7) / 8 * 8);
       hipLaunchKernelGGL((decode_split_bf16<D, true>), dim3(uint32_t(grid)), dim3(64), 0, st, (const char*)q,
                          (const char*)k_pool, (const char*)v_pool, r2t, stride, rpi, plens, B, Hq, Hkv, G, pl.splits,
-                         pl.chunk, scale_log2, v_scale, ws_acc, ws_ml);
+                         pl.chunk, scale_log2, v_scale, ws_acc, ws_ml, key_start, s_off, S_total);
     }
     hipLaunchKernelGGL((decode_combine<D, true>), dim3(uint32_t(int64_t(B) * Hq)), dim3(64), 0, st, ws_acc,
-                       ws_ml, pl.splits, o);
+                       ws_ml, S_total, o);
   } else {
     const uint32_t grid = uint32_t(int64_t(B) * Hq * pl.splits);
     hipLaunchKernelGGL(decode_split_f32<D>, dim3(grid), dim3(64), 0, st, (const float*)q,
@@ -468,4 +511,101 @@ extern "C" int radix_decode_attention_fp8kv(const void* q, void* o, const void* 
   return decode_entry("radix_decode_attention_fp8kv", q, o, k_pool, v_pool, req_to_token, req_to_token_stride,
                       req_pool_indices, prefix_lens, batch, max_kv_len, num_q_heads, num_kv_heads, head_dim,
                       sm_scale, k_scale, v_scale, kModeFp8Kv, workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+int shared_entry(const char* name, const void* q, void* o, const void* k_pool, const void* v_pool,
+                 const int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* req_pool_indices,
+                 const int32_t* prefix_lens, const int32_t* shared_lens, const int32_t* group_start, int32_t batch,
+                 int32_t n_groups, int32_t max_group_size, int32_t max_shared_len, int32_t max_private_len,
+                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float sm_scale, float k_scale,
+                 float v_scale, bool kv8, void* workspace, int64_t workspace_bytes, void* stream) {
+  const std::string fn(name);
+  if (batch < 0 || n_groups < 0 || (batch > 0 && (n_groups < 1 || n_groups > batch)) || max_group_size < 1 ||
+      max_shared_len < 0 || max_private_len < 1 || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 16 || (head_dim != 64 && head_dim != 128) ||
+      int64_t(req_to_token_stride) < int64_t(max_shared_len) + max_private_len || !(sm_scale > 0.f) ||
+      !(k_scale > 0.f) || !(v_scale > 0.f))
+    return rt::fail(RT_ERR_INVALID, fn + ": bad shape, count, stride or scale");
+  if (int64_t(max_shared_len) + max_private_len > int64_t(kMaxChunk) * 1024)
+    return rt::fail(RT_ERR_INVALID, fn + ": context above 2097152");
+  if (batch == 0) return RT_OK;
+  if (!q || !o || !k_pool || !v_pool || !req_to_token || !prefix_lens || !shared_lens || !group_start ||
+      !workspace)
+    return rt::fail(RT_ERR_INVALID, fn + ": null pointer");
+  const int64_t need = radix_decode_shared_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, n_groups,
+                                                           max_group_size, max_shared_len, max_private_len);
+  if (need < 0 || workspace_bytes < need)
+    return rt::fail(RT_ERR_INVALID, fn + ": workspace too small (need " + std::to_string(need) + ")");
+  const SharedPlan sp = plan_shared(batch, num_q_heads, num_kv_heads, n_groups, max_group_size, max_shared_len,
+                                    max_private_len, kv8 ? kMaxChunkFp8 : kMaxChunk);
+  float* ws_acc = static_cast<float*>(workspace);
+  float* ws_ml = ws_acc + int64_t(batch) * num_q_heads * sp.total() * head_dim;
+  const float scale_log2 = sm_scale * k_scale * kLog2e;
+  hipStream_t st = (hipStream_t)stream;
+  if (sp.n_a > 0) {
+    const int rc = rt::launch_extend_shared_part(q, k_pool, v_pool, req_to_token, req_to_token_stride,
+                                                 req_pool_indices, shared_lens, group_start, n_groups, max_group_size,
+                                                 sp.n_a, sp.chunk_a, sp.total(), num_q_heads, num_kv_heads, head_dim,
+                                                 scale_log2, v_scale, kv8, ws_acc, ws_ml, stream);
+    if (rc != RT_OK) return rc;
+  }
+  const int mode = kv8 ? kModeFp8Kv : RT_BF16;
+  if (head_dim == 128)
+    launch_decode<128>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
+                       batch, num_q_heads, num_kv_heads, sp.b, scale_log2, v_scale, mode, ws_acc, ws_ml, st,
+                       shared_lens, sp.n_a, sp.total());
+  else
+    launch_decode<64>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
+                      batch, num_q_heads, num_kv_heads, sp.b, scale_log2, v_scale, mode, ws_acc, ws_ml, st,
+                      shared_lens, sp.n_a, sp.total());
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return rt::fail(RT_ERR_HIP, fn + " launch: " + hipGetErrorString(e));
+  return RT_OK;
+}
+
+}  // namespace
+
+extern "C" int64_t radix_decode_shared_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                                       int32_t head_dim, int32_t n_groups, int32_t max_group_size,
+                                                       int32_t max_shared_len, int32_t max_private_len) {
+  if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || n_groups < 0 || max_group_size < 1 ||
+      max_shared_len < 0 || max_private_len < 1)
+    return -1;
+  const int splits = std::max(
+      plan_shared(batch, num_q_heads, num_kv_heads, n_groups, max_group_size, max_shared_len, max_private_len,
+                  kMaxChunk).total(),
+      plan_shared(batch, num_q_heads, num_kv_heads, n_groups, max_group_size, max_shared_len, max_private_len,
+                  kMaxChunkFp8).total());
+  return int64_t(batch) * num_q_heads * splits * (head_dim + 2) * int64_t(sizeof(float));
+}
+
+extern "C" int radix_decode_attention_shared(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                             const int32_t* req_to_token, int32_t req_to_token_stride,
+                                             const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                             const int32_t* shared_lens, const int32_t* group_start, int32_t batch,
+                                             int32_t n_groups, int32_t max_group_size, int32_t max_shared_len,
+                                             int32_t max_private_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, float sm_scale, void* workspace,
+                                             int64_t workspace_bytes, void* stream) {
+  return shared_entry("radix_decode_attention_shared", q, o, k_pool, v_pool, req_to_token, req_to_token_stride,
+                      req_pool_indices, prefix_lens, shared_lens, group_start, batch, n_groups, max_group_size,
+                      max_shared_len, max_private_len, num_q_heads, num_kv_heads, head_dim, sm_scale, 1.f, 1.f,
+                      false, workspace, workspace_bytes, stream);
+}
+
+extern "C" int radix_decode_attention_shared_fp8kv(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                                   const int32_t* req_to_token, int32_t req_to_token_stride,
+                                                   const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                                   const int32_t* shared_lens, const int32_t* group_start,
+                                                   int32_t batch, int32_t n_groups, int32_t max_group_size,
+                                                   int32_t max_shared_len, int32_t max_private_len,
+                                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                                   float sm_scale, float k_scale, float v_scale, void* workspace,
+                                                   int64_t workspace_bytes, void* stream) {
+  return shared_entry("radix_decode_attention_shared_fp8kv", q, o, k_pool, v_pool, req_to_token,
+                      req_to_token_stride, req_pool_indices, prefix_lens, shared_lens, group_start, batch, n_groups,
+                      max_group_size, max_shared_len, max_private_len, num_q_heads, num_kv_heads, head_dim, sm_scale,
+                      k_scale, v_scale, true, workspace, workspace_bytes, stream);
 }

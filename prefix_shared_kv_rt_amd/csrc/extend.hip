@@ -97,13 +97,22 @@ __device__ __forceinline__ int swz(int key, int chunk) {
   return key * ExtendCfg<D>::kRowBytes + ((chunk ^ (swz_f(key) & (ExtendCfg<D>::kCPR - 1))) << 4);
 }
 
-template <int D, int RB, bool KV8>
+// PART: the shared-prefix pass of radix_decode_attention_shared.  A
+// "request" b is then a group of consecutive decode rows (qo_indptr =
+// group_start: rows qo_indptr[b] .. qo_indptr[b+1] - 1, one query row each)
+// whose slot rows agree on their first shared_lens[qo_indptr[b]] entries;
+// item (query tile, group, KV head, chunk c) attends its rows to shared keys
+// [c * chunk_keys, (c + 1) * chunk_keys) without a causal mask and writes the
+// split-K partial (max, sum, unnormalised accumulator) of each (row, head) to
+// split slot c of the decode workspace instead of an output row.
+template <int D, int RB, bool KV8, bool PART = false>
 __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_bf16(
     const char* __restrict__ q, char* __restrict__ o, const char* __restrict__ k_pool,
     const char* __restrict__ v_pool, const int32_t* __restrict__ req_to_token, int64_t stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
     const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ qo_indptr, int B1, int B2, int Hq,
-    int Hkv, int G, int n_qt, int n_qt2, int seg2, float scale_log2, float v_scale) {
+    int Hkv, int G, int n_qt, int n_qt2, int seg2, float scale_log2, float v_scale, int n_chunks = 1,
+    int chunk_keys = 0, int S_total = 0, float* __restrict__ ws_acc = nullptr, float* __restrict__ ws_ml = nullptr) {
   using C = ExtendCfg<D>;
   constexpr int kWaveRows = 32 * RB;          // query rows per wave (RB blocks of 32)
   constexpr int kItemRows = kWaves * kWaveRows;  // query rows per work item
@@ -130,8 +139,14 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
   // mixed batch).  Each segment is spread over the XCDs on its own; the first
   // ends at block seg2 (a multiple of 8 when a second segment follows, so the
   // second starts on XCD 0), and its padding blocks have no work.
-  int qt, b, kvh;
-  if (int(blockIdx.x) < seg2) {
+  int qt, b, kvh, chunk = 0;
+  if (PART) {
+    const int work = xcd_slice(blockIdx.x, gridDim.x);
+    qt = work % n_qt;
+    b = (work / n_qt) % B1;
+    kvh = (work / (n_qt * B1)) % Hkv;
+    chunk = work / (n_qt * B1 * Hkv);
+  } else if (int(blockIdx.x) < seg2) {
     const int work = xcd_slice(blockIdx.x, seg2);
     if (work >= n_qt * B1 * Hkv) return;
     qt = work % n_qt;
@@ -144,12 +159,15 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
     kvh = work / (n_qt2 * B2);
   }
 
-  const int E = extend_lens[b];
+  // PART: E = the group's rows, keys [key0, P) of the shared part, no mask
+  // but the chunk's end.
+  const int E = PART ? qo_indptr[b + 1] - qo_indptr[b] : extend_lens[b];
   const int row0 = qt * kItemRows;            // first query row of this item
   if (row0 / G >= E) return;
-  const int P = prefix_lens[b];
+  const int P = PART ? min(prefix_lens[qo_indptr[b]], (chunk + 1) * chunk_keys) : prefix_lens[b];
+  const int key0 = PART ? chunk * chunk_keys : 0;   // a multiple of kBN
   const int j_last = min(E - 1, (row0 + kItemRows - 1) / G);
-  const int kv_end = P + j_last + 1;
+  const int kv_end = PART ? P : P + j_last + 1;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
 
   const int tid = threadIdx.x;
@@ -167,16 +185,18 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
     jrow[rb] = qrow / G;
     grow[rb] = qrow - jrow[rb] * G;
     row_ok[rb] = jrow[rb] < E;
-    limit[rb] = P + min(jrow[rb], E - 1);    // last visible key (invalid rows mimic the last row)
+    // last visible key (invalid rows mimic the last row)
+    limit[rb] = PART ? P - 1 : P + min(jrow[rb], E - 1);
   }
   const int wj_first = min((row0 + wave * kWaveRows) / G, E - 1);
   const int wj_last = min((row0 + wave * kWaveRows + kWaveRows - 1) / G, E - 1);
-  const int w_min_limit = P + wj_first;       // keys <= this are visible to every row of the wave
+  const int w_min_limit = PART ? P - 1 : P + wj_first;  // keys <= this are visible to every row of the wave
   // Keys >= w_end are invisible to every row of the wave; a wave whose rows
   // all lie past the request's extend rows computes nothing.
-  const int w_end = (row0 + wave * kWaveRows) / G < E ? P + wj_last + 1 : 0;
+  const int w_end = (row0 + wave * kWaveRows) / G < E ? (PART ? P : P + wj_last + 1) : 0;
 
-  const int32_t* idx_row = req_to_token + int64_t(rpi ? rpi[b] : b) * stride;
+  const int32_t* idx_row = req_to_token + int64_t(PART ? (rpi ? rpi[qo_indptr[b]] : qo_indptr[b])
+                                                        : (rpi ? rpi[b] : b)) * stride;
   const uint32_t pool_row = uint32_t(Hkv) * kSRow;
   const char* kbase = k_pool + int64_t(kvh) * kSRow;
   const char* vbase = v_pool + int64_t(kvh) * kSRow;
@@ -389,7 +409,7 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
   // Segments of kSeg keys: stage their slot indices in LDS, start tile 0 of
   // the segment, then stream its tiles through the two stages.
   const int tiles_per_seg = kSeg / kBN;
-  for (int seg_tile = 0; seg_tile < n_tiles; seg_tile += tiles_per_seg) {
+  for (int seg_tile = key0 / kBN; seg_tile < n_tiles; seg_tile += tiles_per_seg) {
     seg0 = seg_tile * kBN;
     seg_end = min(n_tiles, seg_tile + tiles_per_seg);
     __syncthreads();  // previous segment fully consumed
@@ -404,6 +424,31 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
 
   // ---- normalise and store: O^T tile dt row i = dim 32*dt + i; this lane holds
   // rows i = 8*(v/4) + 4*hi + (v%4) of its query rows.
+  if constexpr (PART) {
+    // Split-K partial of each (row, head): max m (log2 units), sum l and
+    // the unnormalised accumulator; an empty chunk writes (-inf, 0, 0).
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float lsum = l[rb] + __shfl_xor(l[rb], 32, 64);
+      if (!row_ok[rb]) continue;
+      const int64_t part = ((int64_t(qo_indptr[b]) + jrow[rb]) * Hq + int64_t(kvh) * G + grow[rb]) * S_total + chunk;
+      if (hi == 0) {
+        ws_ml[part * 2 + 0] = first ? -INFINITY : m[rb];
+        ws_ml[part * 2 + 1] = first ? 0.f : lsum;
+      }
+      float* acc = ws_acc + part * D;
+      const float sc = KV8 ? v_scale : 1.f;
+#pragma unroll
+      for (int dt = 0; dt < C::kR; ++dt)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const floatx4 w = {oacc[rb][dt][4 * v4 + 0] * sc, oacc[rb][dt][4 * v4 + 1] * sc,
+                             oacc[rb][dt][4 * v4 + 2] * sc, oacc[rb][dt][4 * v4 + 3] * sc};
+          *reinterpret_cast<floatx4*>(acc + 32 * dt + 8 * v4 + 4 * hi) = w;
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float lsum = l[rb] + __shfl_xor(l[rb], 32, 64);
@@ -502,6 +547,41 @@ int launch_extend_bf16(const void* q, void* o, const void* k_pool, const void* v
                        scale_log2, v_scale);
   return RT_OK;
 }
+
+}  // namespace
+
+namespace rt {
+
+int launch_extend_shared_part(const void* q, const void* k_pool, const void* v_pool, const int32_t* req_to_token,
+                              int64_t stride, const int32_t* rpi, const int32_t* shared_lens,
+                              const int32_t* group_start, int n_groups, int max_group_size, int n_chunks,
+                              int chunk_keys, int S_total, int Hq, int Hkv, int D, float scale_log2, float v_scale,
+                              bool kv8, float* ws_acc, float* ws_ml, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const int G = Hq / Hkv;
+  const int64_t item_rows = kWaves * 32 * kRB;
+  const int64_t n_qt = (int64_t(max_group_size) * G + item_rows - 1) / item_rows;
+  const int64_t grid = n_qt * n_groups * Hkv * n_chunks;
+  if (grid > INT32_MAX) return rt::fail(RT_ERR_INVALID, "radix_decode_attention_shared: grid too large");
+  if (grid == 0) return RT_OK;
+  if (chunk_keys % kBN != 0) return rt::fail(RT_ERR_INVALID, "shared pass: chunk not a multiple of the tile");
+#define RT_SHARED_LAUNCH(DD, K8)                                                                                    \
+  hipLaunchKernelGGL((extend_bf16<DD, kRB, K8, true>), dim3(uint32_t(grid)), dim3(64 * kWaves), 0, st,            \
+                     (const char*)q, (char*)nullptr, (const char*)k_pool, (const char*)v_pool, req_to_token, stride, \
+                     rpi, shared_lens, (const int32_t*)nullptr, group_start, n_groups, 0, Hq, Hkv, G, int(n_qt), 0,  \
+                     0, scale_log2, v_scale, n_chunks, chunk_keys, S_total, ws_acc, ws_ml)
+  if (D == 128) {
+    if (kv8) RT_SHARED_LAUNCH(128, true); else RT_SHARED_LAUNCH(128, false);
+  } else {
+    if (kv8) RT_SHARED_LAUNCH(64, true); else RT_SHARED_LAUNCH(64, false);
+  }
+#undef RT_SHARED_LAUNCH
+  return RT_OK;
+}
+
+}  // namespace rt
+
+namespace {
 
 // Shared checks and dispatch of the four entry points.  kv8: FP8 pools.
 int extend_entry(const char* name, bool kv8, const void* q, void* o, const void* k_pool, const void* v_pool,

@@ -1,9 +1,22 @@
 // Internal helpers shared by the library's translation units.
 #pragma once
 
+#include <stdint.h>
+
 #include <string>
 
 namespace rt {
 // Records `msg` as the calling thread's last error and returns `code`.
 int fail(int code, const std::string& msg);
+
+// The shared-prefix pass of radix_decode_attention_shared (extend.hip):
+// for each group of consecutive decode rows (group_start), KV head, query
+// tile and chunk of chunk_keys shared keys, write the split-K partial of
+// every (row, head) into split slot `chunk` of S_total.  bf16 queries; bf16
+// or FP8 (kv8) pools.
+int launch_extend_shared_part(const void* q, const void* k_pool, const void* v_pool, const int32_t* req_to_token,
+                              int64_t stride, const int32_t* rpi, const int32_t* shared_lens,
+                              const int32_t* group_start, int n_groups, int max_group_size, int n_chunks,
+                              int chunk_keys, int S_total, int Hq, int Hkv, int D, float scale_log2, float v_scale,
+                              bool kv8, float* ws_acc, float* ws_ml, void* stream);
 }  // namespace rt

@@ -34,15 +34,16 @@ def check_few_shot(fb, i):
     return {"max_abs_err": worst, "tol": TOL, "ok": worst <= TOL}
 
 
-@pytest.mark.parametrize("kv_dtype,page", [("bf16", 1), ("fp8", 1), ("bf16", 16)])
-def test_few_shot_full_size_bench_path(kv_dtype, page):
+@pytest.mark.parametrize("kv_dtype,page,shared", [("bf16", 1, False), ("fp8", 1, False), ("bf16", 16, False),
+                                                  ("bf16", 1, True), ("fp8", 1, True)])
+def test_few_shot_full_size_bench_path(kv_dtype, page, shared):
     """64 requests x (1024 shared + 128 distinct) per step, three steps: the
     extend rows actually computed (position >= matched prefix) and the
     decode row of sampled requests (bf16 pool, or FP8 E4M3 pool at unit
     scales against attention over the values the FP8 pool holds; token
     slots or pages of 16)."""
-    print(f"few-shot full size, {kv_dtype} pool, pages of {page}", flush=True)
-    fb = bench.FewShotBench(3, torch, B, torch_gen, kv_dtype=kv_dtype, page_size=page)
+    print(f"few-shot full size, {kv_dtype} pool, pages of {page}, shared decode {shared}", flush=True)
+    fb = bench.FewShotBench(3, torch, B, torch_gen, kv_dtype=kv_dtype, page_size=page, shared_decode=shared)
     fb.gen_inputs(3)
     fb.warm_prefix()
     worst = 0.0
@@ -56,14 +57,16 @@ def test_few_shot_full_size_bench_path(kv_dtype, page):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,steps,sample_steps,kv_dtype", [
-    ("fork", 256, (0, 127, 255), "bf16"),
-    ("long_context", 128, (0, 64, 127), "bf16"),
-    ("long_context", 128, (0, 127), "fp8"),
+@pytest.mark.parametrize("name,steps,sample_steps,kv_dtype,shared", [
+    ("fork", 256, (0, 127, 255), "bf16", False),
+    ("long_context", 128, (0, 64, 127), "bf16", False),
+    ("long_context", 128, (0, 127), "fp8", False),
+    ("fork", 256, (0, 255), "bf16", True),
+    ("long_context", 128, (0, 127), "bf16", True),
 ])
-def test_decode_full_size_bench_path(name, steps, sample_steps, kv_dtype):
-    print(f"{name} full size, {steps} decode steps, {kv_dtype} pool", flush=True)
-    db = bench.DecodeBench(name, torch, B, torch_gen, steps, kv_dtype=kv_dtype)
+def test_decode_full_size_bench_path(name, steps, sample_steps, kv_dtype, shared):
+    print(f"{name} full size, {steps} decode steps, {kv_dtype} pool, shared decode {shared}", flush=True)
+    db = bench.DecodeBench(name, torch, B, torch_gen, steps, kv_dtype=kv_dtype, shared_decode=shared)
     db.setup()
     saved = {}
     for s in range(steps):
