@@ -641,7 +641,7 @@ def run_chat(args, torch):
     src = QKVSource(wl.seed, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, torch.bfloat16)
     rt.events = []
     sch = Scheduler(rt, wl.requests, src, max_running=256, max_extend_tokens=16384, policy=args.policy,
-                    chunk_size=args.chunk_size, mixed=args.mixed)
+                    chunk_size=args.chunk_size, mixed=args.mixed, shared_decode=args.decode == "shared")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     marks = [0]
@@ -662,10 +662,11 @@ def run_chat(args, torch):
             it_ms.append(sum(x.elapsed_time(y) for _, x, y, _ in evs))
     per = {}
     for kind, a, b, info in rt.events:
-        d = per.setdefault(kind, {"launches": 0, "ms": 0.0, "tokens": 0, "flops": 0.0, "bytes": 0.0, "rows": 0})
+        d = per.setdefault(kind, {"launches": 0, "ms": 0.0, "tokens": 0, "flops": 0.0, "bytes": 0.0, "rows": 0,
+                                  "distinct_bytes": 0.0})
         d["launches"] += 1
         d["ms"] += a.elapsed_time(b)
-        for k in ("tokens", "flops", "bytes", "rows"):
+        for k in ("tokens", "flops", "bytes", "rows", "distinct_bytes"):
             d[k] += info.get(k, 0)
     rt.close()
     ext, dec, mix = per.get("extend", {}), per.get("decode", {}), per.get("mixed", {})
@@ -689,14 +690,16 @@ def run_chat(args, torch):
                                "U{128..384} user + 128 generated tokens per turn, pool 60% of the working set; "
                                "one pass of the whole workload, a step = one scheduler iteration",
                    "policy": args.policy, "chunk_size": args.chunk_size, "page_size": wl.page_size,
-                   "mixed_launch": bool(args.mixed),
+                   "mixed_launch": bool(args.mixed), "decode": args.decode or "plain",
                    "kv_dtype": "fp8_e4m3" if args.kv_dtype == "fp8" else "bf16",
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "pool_slots": wl.num_slots},
         "wall_tokens_per_s": tokens / wall,
         "kernels": {k: {"launches": d["launches"], "ms": d["ms"]} for k, d in per.items()},
         "extend": {"tokens": ext.get("tokens", 0), "tflops": ext_tf, "mfma_frac": ext_tf / PEAK_BF16_TFLOPS},
-        "decode": {"tokens": dec.get("tokens", 0), "gbs": dec_gbs, "hbm_frac": dec_gbs / PEAK_HBM_GBS},
+        "decode": {"tokens": dec.get("tokens", 0), "gbs": dec_gbs, "hbm_frac": dec_gbs / PEAK_HBM_GBS,
+                   "distinct_gbs": dec.get("distinct_bytes", 0.0) / max(dec.get("ms", 0.0), 1e-9) / 1e6,
+                   "shared_launches": sch.shared_decodes},
         "mixed": {"launches": mix.get("launches", 0), "tokens": mix.get("tokens", 0),
                   "tflops": mix.get("flops", 0.0) / max(mix.get("ms", 0.0), 1e-9) / 1e9},
         "hit_rate": {"cached": sch.cached_tokens, "prefill": sch.prefill_tokens,

@@ -158,8 +158,11 @@ class RadixRuntime:
                 self.events.append(("extend", e0, self._event(), {"tokens": int(el.sum()), "flops": flops}))
             return o
 
-    def run_decode(self, rows, positions, slots, q, k_new, v_new):
-        """Write the new slots into the table, store the new rows, decode."""
+    def run_decode(self, rows, positions, slots, q, k_new, v_new, shared_len=0):
+        """Write the new slots into the table, store the new rows, decode.
+        shared_len > 0: every row's first shared_len slots are the same (the
+        caller checked), so the batch decodes as one group through
+        radix_decode_attention_shared, reading those K/V once."""
         if self.device is None:
             return None
         n = len(rows)
@@ -167,23 +170,44 @@ class RadixRuntime:
             rows_d, pos_d, slots_d = self._to_dev(rows), self._to_dev(positions), self._to_dev(slots)
             o = torch.empty_like(q)
             max_kv = int(max(positions)) + 1
-            ws = self.workspace(n, max_kv)
             e0 = self._event() if self.events is not None else None
             if self.kv_fp8_scales:
                 B.decode_append_fp8(self.r2t_dev, rows_d, pos_d, slots_d, self.k_pool, self.v_pool, k_new, v_new,
                                     *self.kv_fp8_scales, stream=self.stream)
-                B.radix_decode_attention_fp8kv(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, max_kv,
-                                               self.sm_scale, ws, *self.kv_fp8_scales, stream=self.stream)
             else:
                 B.decode_append(self.r2t_dev, rows_d, pos_d, slots_d, self.k_pool, self.v_pool, k_new, v_new,
                                 stream=self.stream)
-                B.radix_decode_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, max_kv,
-                                         self.sm_scale, ws, stream=self.stream)
+            if shared_len > 0:
+                sl = self._to_dev(np.full(n, shared_len, dtype=np.int32))
+                gs = self._to_dev(np.array([0, n], dtype=np.int32))
+                priv = max_kv - shared_len
+                need = B.radix_decode_shared_workspace_bytes(n, self.hq, self.hkv, self.d, 1, n, shared_len, priv)
+                if self._ws.numel() < need:
+                    self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+                if self.kv_fp8_scales:
+                    B.radix_decode_attention_shared_fp8kv(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d,
+                                                          sl, gs, n, shared_len, priv, self.sm_scale, self._ws,
+                                                          *self.kv_fp8_scales, stream=self.stream)
+                else:
+                    B.radix_decode_attention_shared(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, sl,
+                                                    gs, n, shared_len, priv, self.sm_scale, self._ws,
+                                                    stream=self.stream)
+            else:
+                ws = self.workspace(n, max_kv)
+                if self.kv_fp8_scales:
+                    B.radix_decode_attention_fp8kv(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d,
+                                                   max_kv, self.sm_scale, ws, *self.kv_fp8_scales, stream=self.stream)
+                else:
+                    B.radix_decode_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, max_kv,
+                                             self.sm_scale, ws, stream=self.stream)
             if e0 is not None:
                 kv = np.asarray(positions, dtype=np.float64) + 1
                 eb, ekv = q.element_size(), self.k_pool.element_size()
-                nbytes = float(np.sum(kv * (2 * self.hkv * self.d * ekv + 4))) + 2.0 * n * self.hq * self.d * eb
-                self.events.append(("decode", e0, self._event(), {"tokens": n, "bytes": nbytes}))
+                row = 2 * self.hkv * self.d * ekv + 4
+                nbytes = float(np.sum(kv * row)) + 2.0 * n * self.hq * self.d * eb
+                distinct = nbytes - float(max(n - 1, 0) * shared_len * row)
+                self.events.append(("decode", e0, self._event(), {"tokens": n, "bytes": nbytes,
+                                                                   "distinct_bytes": distinct}))
             return o
 
     def run_mixed(self, ext_rows, prefix_lens, extend_lens, q, k_new, v_new, out_cache_loc, dec_rows, positions,
@@ -256,7 +280,7 @@ class Scheduler:
 
     def __init__(self, rt, requests, qkv_source, max_running=256, max_extend_tokens=16384,
                  skip_extend_attention=False, record=None, keep_dumps=False, policy="fcfs", graphs=None,
-                 chunk_size=None, mixed=False):
+                 chunk_size=None, mixed=False, shared_decode=False, shared_min=256):
         if rt.max_reqs < max_running:
             raise ValueError("the slot table needs a row per running request")
         if policy not in ("fcfs", "lspf"):
@@ -273,6 +297,12 @@ class Scheduler:
         # iteration's decode rows and overwritten before the launch reads them.
         self.mixed = bool(mixed)
         self.mixed_launches = 0
+        # shared_decode: a decode batch whose slot rows all begin with the same
+        # shared_min or more slots (requests that matched a common cached
+        # prefix) reads that common part once (radix_decode_attention_shared).
+        self.shared_decode = bool(shared_decode)
+        self.shared_min = int(shared_min)
+        self.shared_decodes = 0
         self.rt = rt
         self.pending = list(requests)
         self.qkv = qkv_source
@@ -446,9 +476,14 @@ class Scheduler:
                     self.mixed_launches += 1
                     ext = None
                 else:
-                    o = self.graphs.run(rows, positions, slots, q, k, v) if self.graphs is not None else None
-                    if o is None:
-                        o = rt.run_decode(rows, positions, slots, q, k, v)
+                    shared = self._common_slots(rows, positions) if self.shared_decode else 0
+                    if shared >= self.shared_min:
+                        o = rt.run_decode(rows, positions, slots, q, k, v, shared_len=shared)
+                        self.shared_decodes += 1
+                    else:
+                        o = self.graphs.run(rows, positions, slots, q, k, v) if self.graphs is not None else None
+                        if o is None:
+                            o = rt.run_decode(rows, positions, slots, q, k, v)
             if o is not None and self.record is not None:
                 for i, r in enumerate(dec):
                     self.record("dec", r.req.rid, r.generated, o[i:i + 1])
@@ -466,6 +501,19 @@ class Scheduler:
         self.iterations.append(rec)
         if self.keep_dumps:
             self.dumps.append(B.rt_tree_dump(rt.tree))
+
+    def _common_slots(self, rows, positions):
+        """Length of the common leading run of the decode rows' slots (the
+        K/V every request of the batch reads), at most the shortest context
+        before the new tokens."""
+        if len(rows) < 2:
+            return 0
+        L = int(np.min(positions))
+        if L <= 0:
+            return 0
+        m = self.rt.r2t_host[np.asarray(rows), :L]
+        eq = (m == m[0]).all(axis=0)
+        return L if bool(eq.all()) else int(np.argmin(eq))
 
     def _launch_extend(self, ext):
         rows, starts, ns, q, k, v, loc, tags = ext

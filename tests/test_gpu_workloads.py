@@ -19,7 +19,7 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
 def run_both(wl, want=None, max_running=256, max_extend_tokens=16384, max_reqs=None, policy="fcfs", graphs=False,
-             chunk_size=None, kv_fp8_scales=None, mixed=False):
+             chunk_size=None, kv_fp8_scales=None, mixed=False, shared_decode=False, shared_min=256):
     ora = run_workload(wl, want=want, max_running=max_running, max_extend_tokens=max_extend_tokens, policy=policy,
                        chunk_size=chunk_size, kv_fp8_scales=kv_fp8_scales)
     outs = {}
@@ -35,7 +35,8 @@ def run_both(wl, want=None, max_running=256, max_extend_tokens=16384, max_reqs=N
     dg = DecodeGraphs(rt, max_batch=max_running) if graphs else None
     sch = Scheduler(rt, wl.requests, src, max_running=max_running, max_extend_tokens=max_extend_tokens,
                     skip_extend_attention=wl.skip_extend_attention, record=record, policy=policy, graphs=dg,
-                    chunk_size=chunk_size, mixed=mixed).run()
+                    chunk_size=chunk_size, mixed=mixed, shared_decode=shared_decode,
+                    shared_min=shared_min).run()
     if graphs:
         assert dg.replays > 0
     from prefix_shared_kv_rt_amd import binding as B
@@ -197,3 +198,29 @@ def test_small_fork_mixed_falls_back_when_a_prompt_finishes():
     ora, sch, outs, dump, free = run_both(wl, max_running=8, max_extend_tokens=400, mixed=True)
     check_host_identical(ora, sch, dump, free)
     check_outputs(ora, outs, TOL["bf16"])
+
+
+@pytest.mark.parametrize("page,fp8", [(1, False), (16, False), (1, True)])
+def test_small_chat_shared_decode(page, fp8):
+    """Decode batches whose slot rows begin with a common run (the system
+    prompt every session matched) go through radix_decode_attention_shared:
+    host decisions as always, every output against the oracle's."""
+    print(f"chat shared decode (pages of {page}, fp8 {fp8})", flush=True)
+    wl = workloads.paged(workloads.chat(sessions=6, turns=3, system_len=64, user_lo=16, user_hi=48, gen_len=6), page)
+    sel = lambda kind, rid, step: kind == "dec" or step == 0
+    ora, sch, outs, dump, free = run_both(wl, want=sel, max_running=4, max_extend_tokens=128,
+                                          kv_fp8_scales=(0.5, 2.0) if fp8 else None, shared_decode=True,
+                                          shared_min=16)
+    check_host_identical(ora, sch, dump, free)
+    check_outputs(ora, outs, TOL["bf16"])
+    print(f"  {sch.shared_decodes} shared decodes", flush=True)
+    assert sch.shared_decodes > 0
+
+
+def test_small_few_shot_shared_decode():
+    print("few-shot (8 x [256 + 64], 2 decode steps), shared decode", flush=True)
+    wl = workloads.few_shot(batch=8, prefix_len=256, suffix_len=64, decode_steps=2, num_slots=4096)
+    ora, sch, outs, dump, free = run_both(wl, shared_decode=True, shared_min=64)
+    check_host_identical(ora, sch, dump, free)
+    check_outputs(ora, outs, TOL["bf16"])
+    assert sch.shared_decodes > 0
