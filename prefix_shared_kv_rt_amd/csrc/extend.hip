@@ -11,11 +11,11 @@
 // query rows).  The query rows of a tile are (extend row, group head) pairs
 // with the G = Hq / Hkv heads of one KV head innermost, so every K/V tile
 // staged in LDS serves all G heads at once.  Four wavefronts own 32 rows
-// each.  Per 64-key tile:
-//   * the slot indices of the item's keys are staged in LDS once per 2048
+// each.  Per 32-key tile:
+//   * the slot indices of the item's keys are staged in LDS once per 1024
 //     keys; each wave then issues direct HBM-to-LDS loads
 //     (global_load_lds_dwordx4, 1 KiB per instruction) for its share of the
-//     next tile's 64 K rows and 64 V rows while the current tile is used
+//     next tile's 32 K rows and 32 V rows while the current tile is used
 //     (two LDS stages);
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B =
 //     the wave's Q rows held in registers for the whole kernel).  With keys
@@ -24,7 +24,7 @@
 //   * Online softmax in the log2 domain with a lazy rescale: the running max
 //     moves only when a tile's max exceeds it by more than 2^8.  Q is
 //     multiplied by scale * log2(e) once (and rounded back to bf16), and the
-//     score accumulators start at -m instead of 0, so the MFMA hands back
+//     score accumulators start each tile at -m instead of 0, so the MFMA hands back
 //     scores already shifted by the running max and each probability costs
 //     one v_exp_f32.  Row sums add the bf16-rounded probabilities that the
 //     P V product uses, two per v_dot2_f32_bf16.
@@ -35,6 +35,10 @@
 //     one dim -- no register shuffles.
 //   * Causal masking is applied only on tiles that cross the wave's
 //     diagonal; tiles beyond a wave's last row are skipped.
+// Registers are held to 168 per lane so that three waves share each SIMD
+// (three work items per CU, 36 KiB of LDS each): with 64-key tiles and two
+// waves per SIMD the kernel measured slower, on few-shot, FP8-pool and
+// ragged chat batches alike.
 // Work items are laid out so that each XCD (blockIdx % 8 on MI355X) runs a
 // contiguous slice of (KV head, request) items: requests that share a
 // prefix read the same K/V rows and find them in that XCD's L2.
@@ -54,15 +58,16 @@ namespace {
 
 using namespace rtk;
 
-constexpr int kBN = 64;        // keys per LDS tile
+constexpr int kBN = 32;        // keys per LDS tile
 // 32-row query blocks per wave.  2 halves the LDS reads per MFMA but needs
 // more than 256 registers (one wave per SIMD); on gfx950 1 measures faster.
 constexpr int kRB = 1;
+constexpr int kWavesPerSimd = 3;  // occupancy the register budget is cut to
 // Waves per workgroup.  A work item's K/V tiles are gathered once for all of
 // its kWaves * 32 query rows.  8 waves halve that gather traffic but measure
 // slower than 4 on MI355X: the gather is not what bounds the kernel.
 constexpr int kWaves = 4;
-constexpr int kSeg = 2048;     // keys whose slot indices are staged in LDS at a time
+constexpr int kSeg = 1024;     // keys whose slot indices are staged in LDS at a time
 constexpr float kSlack = 8.f;  // log2 headroom of the lazy softmax rescale
 
 template <int D>
@@ -70,7 +75,6 @@ struct ExtendCfg {
   static constexpr int kRowBytes = D * 2;                 // one K or V row of one head
   static constexpr int kCPR = kRowBytes / 16;             // 16-byte chunks per row
   static constexpr int kKPI = 64 / kCPR;                  // rows per 64-lane LDS load (1 KiB)
-  static constexpr int kLoadsPerWave = kBN / kKPI / kWaves;  // per wave per tile, K and V each
   static constexpr int kKB = kBN / 32;                    // 32-key blocks per tile
   static constexpr int kTile = kBN * kRowBytes;           // bytes of one K (or V) tile
   static constexpr int kKS = D / 16;                      // 16-dim steps of Q K^T
@@ -106,7 +110,7 @@ __device__ __forceinline__ int swz(int key, int chunk) {
 // split-K partial (max, sum, unnormalised accumulator) of each (row, head) to
 // split slot c of the decode workspace instead of an output row.
 template <int D, int RB, bool KV8, bool PART = false>
-__global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_bf16(
+__global__ void __launch_bounds__(64 * kWaves, RB == 1 ? kWavesPerSimd : 1) extend_bf16(
     const char* __restrict__ q, char* __restrict__ o, const char* __restrict__ k_pool,
     const char* __restrict__ v_pool, const int32_t* __restrict__ req_to_token, int64_t stride,
     const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
@@ -122,7 +126,11 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
   constexpr int kSRow = KV8 ? D : C::kRowBytes;  // staged bytes per row
   constexpr int kSCPR = kSRow / 16;              // 16-byte chunks per staged row
   constexpr int kSKPI = 64 / kSCPR;              // staged rows per 64-lane load
-  constexpr int kSLoads = kBN / kSKPI / kWaves;  // loads per wave per tile, K and V each
+  constexpr int kSTileLoads = kBN / kSKPI;       // 64-lane loads per tile, K and V each
+  // Loads per wave per tile.  With fewer loads than waves (FP8 rows of 64
+  // dims) waves 0 .. kSTileLoads - 1 issue one each and the others none.
+  constexpr int kSLoads = kSTileLoads >= kWaves ? kSTileLoads / kWaves : 1;
+  static_assert(kSTileLoads % kWaves == 0 || kSTileLoads < kWaves, "tile loads must split evenly over the waves");
   // Two stages of K and V tiles: the next tile streams into one stage while
   // the other is used.  Separate arrays let the compiler see that LDS reads of
   // one stage never wait on the loads still landing in the other.
@@ -224,18 +232,15 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
     for (int r = 0; r < C::kR; ++r)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[rb][r][i] = 0.f;
-  // Scores come out of the MFMA already shifted by the running max: the
-  // accumulator starts at cm = -m (all 16 entries of a lane belong to one
+  // Scores come out of the MFMA already shifted by the running max: each
+  // tile's accumulator starts at -m (all 16 entries of a lane belong to one
   // query row), so p = exp2(acc) needs no per-score arithmetic.  m starts at
   // 0 with the first computed tile forced through the rescale path.
   float m[RB], l[RB];
-  floatx16 cm[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m[rb] = 0.f;
     l[rb] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) cm[rb][i] = 0.f;
   }
   bool first = true;  // wave-uniform
 
@@ -255,6 +260,7 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
   const int lchunk = KV8 ? ld_pchunk : ld_pchunk ^ (swz_f(krow0) & (C::kCPR - 1));
   const uint64_t lane_off = uint64_t(lchunk << 4);
   auto issue = [&](int tile, char* sk, char* sv) {
+    if (kSTileLoads < kWaves && wave >= kSTileLoads) return;  // wave-uniform: no rows of this tile
     const uint32_t* srow = s_slot + (tile * kBN - seg0) + krow0;
 #pragma unroll
     for (int it = 0; it < kSLoads; ++it) {
@@ -322,9 +328,10 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
         ka[ks] = *reinterpret_cast<const u32x4*>(sk + kb * 32 * C::kRowBytes + kofs[ks]);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        sacc[rb][kb] = mfma_32x32x16(as_bf16x8(ka[0]), qop[rb][0], cm[rb]);
 #pragma unroll
-        for (int ks = 1; ks < C::kKS; ++ks)
+        for (int i = 0; i < 16; ++i) sacc[rb][kb][i] = -m[rb];
+#pragma unroll
+        for (int ks = 0; ks < C::kKS; ++ks)
           sacc[rb][kb] = mfma_32x32x16(as_bf16x8(ka[ks]), qop[rb][ks], sacc[rb][kb]);
       }
     }
@@ -364,8 +371,6 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? 8 / kWaves : 1) extend_
         for (int kb = 0; kb < C::kKB; ++kb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) sacc[rb][kb][v] -= shift;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) cm[rb][i] = -m_new;
         m[rb] = m_new;
       }
     }
