@@ -143,6 +143,9 @@ class FewShotBench:
         self.meta_views = [(md[0:B], md[B:2 * B], md[2 * B:3 * B + 1], md[3 * B + 1:4 * B + 1],
                             md[4 * B + 1:5 * B + 1]) for md in self.meta_dev]
         self.copy_done = [torch.cuda.Event(), torch.cuda.Event()]
+        # (device, pinned host) views of each row set, for the per-step copy
+        self.copy_views = [(self.r2t_dev[rs * self.set_rows:(rs + 1) * self.set_rows],
+                            self.r2t_host_t[rs * self.set_rows:(rs + 1) * self.set_rows]) for rs in range(2)]
         self.copy_used = [False, False]
         self.rows = [np.arange(rs * self.set_rows, rs * self.set_rows + self.B, dtype=np.int32) for rs in range(2)]
         self.dec_pos = np.full(self.B, self.PREFIX + self.SUFFIX, dtype=np.int32)
@@ -323,8 +326,8 @@ class FewShotBench:
         max_e = int(el.max())
         # every launch names self.stream; the row copy goes on the current
         # stream, which is self.stream (the stream current at construction)
-        lo, hi = rs * self.set_rows, (rs + 1) * self.set_rows
-        self.r2t_dev[lo:hi].copy_(self.r2t_host_t[lo:hi], non_blocking=True)  # rows and metadata
+        dev_rows, host_rows = self.copy_views[rs]
+        dev_rows.copy_(host_rows, non_blocking=True)  # rows and metadata
         self.copy_done[rs].record(self.stream)
         self.copy_used[rs] = True
         self._store_extend(k, v, d_rows, d_pl, d_el, d_qo, max_e)

@@ -161,8 +161,18 @@ def _check(rc):
     return rc
 
 
+_addressof, _c_char = ctypes.addressof, ctypes.c_char
+
+
 def _p32(a):
-    return a.ctypes.data if a is not None else None
+    """Address of a host array's data.  The buffer-protocol route costs about
+    a third of ``a.ctypes.data``; read-only and empty arrays take the latter."""
+    if a is None:
+        return None
+    try:
+        return _addressof(_c_char.from_buffer(a))
+    except (TypeError, ValueError, BufferError):
+        return a.ctypes.data
 
 
 _p64 = _p32
@@ -353,22 +363,36 @@ def rt_finish_batch(tree, tokens, token_offsets, req_to_token, rows, prefix_lens
 
 # ---------------------------------------------------------------- device --
 def _dptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    # a plain int: ctypes turns it into the void* argument directly
+    return t.data_ptr() if t is not None else None
+
+
+_torch = None
+_dtype_codes = None
+
+
+def _torch_mod():
+    global _torch, _dtype_codes
+    if _torch is None:
+        import torch
+        _torch = torch
+        _dtype_codes = {torch.bfloat16: RT_BF16, torch.float32: RT_F32}
+    return _torch
 
 
 def _stream(stream):
-    import torch
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is None:
+        stream = _torch_mod().cuda.current_stream()
+    return stream.cuda_stream
 
 
 def _dtype_code(t):
-    import torch
-    if t.dtype == torch.bfloat16:
-        return RT_BF16
-    if t.dtype == torch.float32:
-        return RT_F32
-    raise ValueError(f"unsupported dtype {t.dtype}")
+    if _dtype_codes is None:
+        _torch_mod()
+    code = _dtype_codes.get(t.dtype)
+    if code is None:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return code
 
 
 def kv_store(k_pool, v_pool, k_new, v_new, out_cache_loc, stream=None):
