@@ -146,7 +146,7 @@ class FewShotBench:
         # (device, pinned host) views of each row set, for the per-step copy
         self.copy_views = [(self.r2t_dev[rs * self.set_rows:(rs + 1) * self.set_rows],
                             self.r2t_host_t[rs * self.set_rows:(rs + 1) * self.set_rows]) for rs in range(2)]
-        self.copy_used = [False, False]
+        self.copy_mark = [None, None]   # event whose completion frees each row set's staging
         self.rows = [np.arange(rs * self.set_rows, rs * self.set_rows + self.B, dtype=np.int32) for rs in range(2)]
         self.dec_pos = np.full(self.B, self.PREFIX + self.SUFFIX, dtype=np.int32)
         self.ws = torch.empty(B_mod.radix_decode_workspace_bytes(self.B, self.HQ, self.HKV, self.D, self.stride),
@@ -306,8 +306,8 @@ class FewShotBench:
         B, S, P0 = self.B, self.SUFFIX, self.PREFIX
         q, k, v, qd, kd, vd = self.inputs[i]
         rs = i % 2
-        if self.copy_used[rs]:
-            self.copy_done[rs].synchronize()       # host staging of this row set is free again
+        if self.copy_mark[rs] is not None:
+            self.copy_mark[rs].synchronize()       # host staging of this row set is free again
         rows = self.rows[rs]
         toks, full = self.tokens[i]
         pl, el, nodes, loc = Bm.rt_admit_batch(self.tree, toks, self.tok_off, self.r2t_host, rows)
@@ -328,11 +328,16 @@ class FewShotBench:
         # stream, which is self.stream (the stream current at construction)
         dev_rows, host_rows = self.copy_views[rs]
         dev_rows.copy_(host_rows, non_blocking=True)  # rows and metadata
-        self.copy_done[rs].record(self.stream)
-        self.copy_used[rs] = True
         self._store_extend(k, v, d_rows, d_pl, d_el, d_qo, max_e)
+        # the marker that frees this row set's staging: a timed step's first
+        # timing event follows the copy on the stream, so it serves; other
+        # steps record one of their own
         if ev is not None:
             ev[0].record(self.stream)
+            self.copy_mark[rs] = ev[0]
+        else:
+            self.copy_done[rs].record(self.stream)
+            self.copy_mark[rs] = self.copy_done[rs]
         self._extend(q, self.o_ext, d_rows, d_pl, d_el, d_qo, max_e)
         if ev is not None:
             ev[1].record(self.stream)
