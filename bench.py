@@ -324,10 +324,11 @@ class FewShotBench:
         meta[4 * B + 1:5 * B + 1] = Bm.rt_decode_slots_batch(self.tree, rows, self.dec_pos, self.r2t_host)
         d_pl, d_el, d_qo, d_rows, d_dslots = self.meta_views[rs]
         max_e = int(el.max())
-        # every launch names self.stream; the row copy goes on the current
-        # stream, which is self.stream (the stream current at construction)
+        # every launch names self.stream
         dev_rows, host_rows = self.copy_views[rs]
-        dev_rows.copy_(host_rows, non_blocking=True)  # rows and metadata
+        # rows and metadata, by a kernel on the step's stream that reads the
+        # pinned staging (no hand-over to a DMA engine and back)
+        Bm.rt_copy_from_host(dev_rows, host_rows, stream=self.stream)
         self._store_extend(k, v, d_rows, d_pl, d_el, d_qo, max_e)
         # the marker that frees this row set's staging: a timed step's first
         # timing event follows the copy on the stream, so it serves; other

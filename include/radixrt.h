@@ -250,6 +250,19 @@ int kv_store(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
 int req_to_token_scatter(int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* rows,
                          const int32_t* positions, const int32_t* slots, int32_t n, void* stream);
 
+/* Staging of a step's slot-table rows and metadata [P4 "CUDA Graph": the
+ * runtime writes req_pool_indices, seq_lens and out_cache_loc into fixed
+ * device buffers before each step]: copies bytes from pinned host memory
+ * src to device memory dst with a kernel on `stream`, so that the copy
+ * stays on the compute queue beside the step's kernels.  src must lie
+ * inside one pinned (hipHostMalloc) allocation, checked on the host through
+ * its device mapping; pageable memory is refused with RT_ERR_INVALID before
+ * anything is launched.  bytes a multiple of 4, both pointers 4-byte
+ * aligned (16-byte alignment takes the faster path).  dst (device) must hold
+ * bytes; the host must not change src until the copy has run (as for an
+ * asynchronous copy). */
+int rt_copy_from_host(void* dst, const void* src, int64_t bytes, void* stream);
+
 /* One decode step's writes in a single launch: req_to_token_scatter of
  * (rows, positions, slots) and kv_store of (k_new, v_new) at slots, for i < n
  * [P4 the decode step writes its new token's slot into req_to_token and its

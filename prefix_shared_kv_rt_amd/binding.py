@@ -28,6 +28,7 @@ EXPORTS = [
     "radix_mixed_attention", "radix_mixed_attention_fp8kv",
     "radix_decode_shared_workspace_bytes", "radix_decode_attention_shared", "radix_decode_attention_shared_fp8kv",
     "radix_extend_attention", "radix_decode_workspace_bytes", "radix_decode_attention",
+    "rt_copy_from_host",
 ]
 
 
@@ -133,6 +134,7 @@ def lib():
             "radix_decode_attention_shared_fp8kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp,
                                                                    _vp, _vp] + [ctypes.c_int32] * 8 +
                                                     [ctypes.c_float] * 3 + [_vp, ctypes.c_int64, _vp]),
+            "rt_copy_from_host": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, _vp]),
             "radix_extend_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
@@ -418,6 +420,17 @@ def kv_store_extend_fp8(k_pool, v_pool, k_new, v_new, req_to_token, req_pool_ind
                                      req_to_token.shape[1], _dptr(req_pool_indices), _dptr(prefix_lens),
                                      _dptr(extend_lens), _dptr(qo_indptr), prefix_lens.shape[0],
                                      int(max_extend_len), hkv, d, float(k_scale), float(v_scale), _stream(stream)))
+
+
+def rt_copy_from_host(dst, src, stream=None):
+    """Copy the pinned host tensor src into the device tensor dst (at least as
+    many bytes) with a kernel on `stream`; pageable memory is refused."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("rt_copy_from_host: destination smaller than source")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("rt_copy_from_host: tensors must be contiguous")
+    _check(lib().rt_copy_from_host(_dptr(dst), _dptr(src), n, _stream(stream)))
 
 
 def req_to_token_scatter(req_to_token, rows, positions, slots, stream=None):

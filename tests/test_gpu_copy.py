@@ -1,0 +1,46 @@
+"""rt_copy_from_host on the GPU: pinned host memory reaches device memory bit
+for bit through the copy kernel (16-byte and 4-byte paths, a word tail,
+offsets inside an allocation), and pageable memory is refused before any
+launch."""
+
+import numpy as np
+import pytest
+import torch
+
+from prefix_shared_kv_rt_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("n,src_off,dst_off", [(1_000_003, 0, 0), (4096 * 65, 0, 0), (1001, 3, 1), (7, 4, 4),
+                                               (1, 0, 5)])
+def test_copy_from_pinned_host(n, src_off, dst_off):
+    print(f"rt_copy_from_host n={n} src_off={src_off} dst_off={dst_off}", flush=True)
+    rng = np.random.default_rng(n + src_off)
+    host = torch.from_numpy(rng.integers(-2**31, 2**31 - 1, n + src_off + 8, dtype=np.int64).astype(np.int32))
+    host = host.pin_memory()
+    dev = torch.full((n + dst_off + 8,), -7, dtype=torch.int32, device="cuda")
+    B.rt_copy_from_host(dev[dst_off:dst_off + n], host[src_off:src_off + n])
+    torch.cuda.synchronize()
+    got = dev.cpu()
+    assert torch.equal(got[dst_off:dst_off + n], host[src_off:src_off + n])
+    assert bool((got[:dst_off] == -7).all()) and bool((got[dst_off + n:] == -7).all())
+
+
+def test_copy_from_host_refuses_pageable_memory():
+    src = torch.arange(64, dtype=torch.int32)          # ordinary (pageable) host memory
+    assert not src.is_pinned()
+    dev = torch.full((64,), -7, dtype=torch.int32, device="cuda")
+    with pytest.raises(B.RadixRTError):
+        B.rt_copy_from_host(dev, src)
+    torch.cuda.synchronize()
+    assert bool((dev.cpu() == -7).all())
+
+
+def test_copy_from_host_rejects_bad_sizes():
+    host = torch.zeros(16, dtype=torch.int32).pin_memory()
+    dev = torch.zeros(16, dtype=torch.int32, device="cuda")
+    rc = B.lib().rt_copy_from_host(dev.data_ptr(), host.data_ptr(), 6, None)   # not a multiple of 4
+    assert rc == B.RT_ERR_INVALID
+    rc = B.lib().rt_copy_from_host(dev.data_ptr(), host.data_ptr() + 2, 8, None)  # misaligned
+    assert rc == B.RT_ERR_INVALID
