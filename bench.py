@@ -131,6 +131,8 @@ class FewShotBench:
         self.meta_n = 5 * self.B + 1
         self.MR = -(-self.meta_n // self.stride)
         self.set_rows = self.B + self.MR
+        while (self.set_rows * self.stride) % 4:   # each row set starts 16-byte aligned
+            self.set_rows += 1
         self.r2t_host_t = torch.zeros((2 * self.set_rows, self.stride), dtype=torch.int32, pin_memory=True)
         self.r2t_host = self.r2t_host_t.numpy()
         self.r2t_dev = torch.zeros((2 * self.set_rows, self.stride), dtype=torch.int32, device=self.dev)
