@@ -258,8 +258,10 @@ int req_to_token_scatter(int32_t* req_to_token, int32_t req_to_token_stride, con
  * inside one pinned (hipHostMalloc) allocation, checked on the host through
  * its device mapping; pageable memory is refused with RT_ERR_INVALID before
  * anything is launched.  bytes a multiple of 4, both pointers 4-byte
- * aligned (16-byte alignment takes the faster path).  dst (device) must hold
- * bytes; the host must not change src until the copy has run (as for an
+ * aligned (16-byte alignment takes the faster path).  dst must be device
+ * memory, with [dst, dst + bytes) inside its allocation (checked on the
+ * host; the allocation may be a larger pool block than the caller's
+ * buffer).  The host must not change src until the copy has run (as for an
  * asynchronous copy). */
 int rt_copy_from_host(void* dst, const void* src, int64_t bytes, void* stream);
 

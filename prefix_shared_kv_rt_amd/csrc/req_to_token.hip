@@ -63,6 +63,17 @@ extern "C" int rt_copy_from_host(void* dst, const void* src, int64_t bytes, void
     (void)hipGetLastError();
     return rt::fail(RT_ERR_INVALID, std::string(name) + ": source is not inside one pinned host allocation");
   }
+  // dst must be device memory whose allocation holds the whole range.
+  hipPointerAttribute_t attr{};
+  void* base = nullptr;
+  size_t size = 0;
+  const bool dev_ok = hipPointerGetAttributes(&attr, dst) == hipSuccess && attr.type == hipMemoryTypeDevice &&
+                      hipMemGetAddressRange(&base, &size, dst) == hipSuccess &&
+                      static_cast<char*>(dst) + bytes <= static_cast<char*>(base) + size;
+  if (!dev_ok) {
+    (void)hipGetLastError();
+    return rt::fail(RT_ERR_INVALID, std::string(name) + ": destination is not device memory holding bytes");
+  }
   const bool vec = ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(dsrc)) & 15) == 0;
   const int64_t pieces = vec ? bytes / 16 : bytes / 4;
   const uint32_t blocks = uint32_t(std::min<int64_t>(1024, std::max<int64_t>(1, (pieces + 255) / 256)));

@@ -37,6 +37,14 @@ def test_copy_from_host_refuses_pageable_memory():
     assert bool((dev.cpu() == -7).all())
 
 
+def test_copy_from_host_refuses_host_destination():
+    src = torch.arange(64, dtype=torch.int32).pin_memory()
+    for dst in (torch.zeros(64, dtype=torch.int32), torch.zeros(64, dtype=torch.int32).pin_memory()):
+        with pytest.raises(B.RadixRTError):
+            B.rt_copy_from_host(dst, src)
+        assert bool((dst == 0).all())
+
+
 def test_copy_from_host_rejects_bad_sizes():
     host = torch.zeros(16, dtype=torch.int32).pin_memory()
     dev = torch.zeros(16, dtype=torch.int32, device="cuda")
