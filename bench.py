@@ -126,28 +126,32 @@ class FewShotBench:
         self.k_pool = torch.zeros((self.SLOTS + 1, self.HKV, self.D), dtype=pool_dt, device=self.dev)
         self.v_pool = torch.zeros_like(self.k_pool)
         # two row sets of 64 so that host writes for step i+1 never touch rows still being copied for step i
-        # Per row set: B slot-table rows, then MR rows that carry the step's
-        # metadata, so that one host-to-device copy moves both.
-        self.meta_n = 5 * self.B + 1
-        self.MR = -(-self.meta_n // self.stride)
-        self.set_rows = self.B + self.MR
+        # Per row set: B slot-table rows, then 5 rows whose columns from
+        # PREFIX on carry the step's metadata (prefix_lens, extend_lens,
+        # qo_indptr, rows, decode slots), so that one copy of the columns
+        # from PREFIX on moves a step's changes (below).
+        P0, B = self.PREFIX, self.B
+        assert self.stride - P0 >= B + 1
+        self.set_rows = B + 5
         while (self.set_rows * self.stride) % 4:   # each row set starts 16-byte aligned
             self.set_rows += 1
         self.r2t_host_t = torch.zeros((2 * self.set_rows, self.stride), dtype=torch.int32, pin_memory=True)
         self.r2t_host = self.r2t_host_t.numpy()
         self.r2t_dev = torch.zeros((2 * self.set_rows, self.stride), dtype=torch.int32, device=self.dev)
-        # pinned metadata staging per row set: prefix, extend, qo_indptr(65), rows, dec_slots
-        meta_rows = lambda t, rs: t[rs * self.set_rows + self.B:(rs + 1) * self.set_rows].reshape(-1)[:self.meta_n]
-        self.meta_host = [meta_rows(self.r2t_host, rs) for rs in range(2)]
-        self.meta_dev = [meta_rows(self.r2t_dev, rs) for rs in range(2)]
-        B = self.B
-        # device views of each row set's metadata: prefix_lens, extend_lens, qo_indptr, rows, decode slots
-        self.meta_views = [(md[0:B], md[B:2 * B], md[2 * B:3 * B + 1], md[3 * B + 1:4 * B + 1],
-                            md[4 * B + 1:5 * B + 1]) for md in self.meta_dev]
+        lens = (B, B, B + 1, B, B)
+        meta = lambda t, rs: tuple(t[rs * self.set_rows + B + k, P0:P0 + n] for k, n in enumerate(lens))
+        # host and device views of each row set's metadata: prefix_lens,
+        # extend_lens, qo_indptr, rows, decode slots
+        self.meta_host = [meta(self.r2t_host, rs) for rs in range(2)]
+        self.meta_views = [meta(self.r2t_dev, rs) for rs in range(2)]
         self.copy_done = [torch.cuda.Event(), torch.cuda.Event()]
-        # (device, pinned host) views of each row set, for the per-step copy
-        self.copy_views = [(self.r2t_dev[rs * self.set_rows:(rs + 1) * self.set_rows],
-                            self.r2t_host_t[rs * self.set_rows:(rs + 1) * self.set_rows]) for rs in range(2)]
+        # (device, pinned host) views of each row set, whole and from column
+        # PREFIX on, for the per-step copy
+        sets = [slice(rs * self.set_rows, (rs + 1) * self.set_rows) for rs in range(2)]
+        self.copy_views = [(self.r2t_dev[sl], self.r2t_host_t[sl], self.r2t_dev[sl, P0:], self.r2t_host_t[sl, P0:])
+                           for sl in sets]
+        self.rows_whole = [False, False]   # row set uploaded whole since its prefix columns last changed
+        self.prefix_slots = None           # the shared prefix's slots as last uploaded
         self.copy_mark = [None, None]   # event whose completion frees each row set's staging
         self.rows = [np.arange(rs * self.set_rows, rs * self.set_rows + self.B, dtype=np.int32) for rs in range(2)]
         self.dec_pos = np.full(self.B, self.PREFIX + self.SUFFIX, dtype=np.int32)
@@ -315,22 +319,34 @@ class FewShotBench:
         pl, el, nodes, loc = Bm.rt_admit_batch(self.tree, toks, self.tok_off, self.r2t_host, rows)
         if int(pl.min()) < P0:
             raise RuntimeError("the shared prefix left the cache; the pool is too small for this run")
-        meta = self.meta_host[rs]
-        meta[0:B] = pl
-        meta[B:2 * B] = el
+        h_pl, h_el, h_qo, h_rows, h_dslots = self.meta_host[rs]
+        h_pl[:] = pl
+        h_el[:] = el
         # request b's new rows are the last el[b] of its S rows of q / k / v
-        meta[2 * B:3 * B] = self.row_base + (pl - P0)
-        meta[3 * B] = B * S
-        meta[3 * B + 1:4 * B + 1] = rows
+        h_qo[:B] = self.row_base + (pl - P0)
+        h_qo[B] = B * S
+        h_rows[:] = rows
         # one decode slot per request, at position P0 + S
-        meta[4 * B + 1:5 * B + 1] = Bm.rt_decode_slots_batch(self.tree, rows, self.dec_pos, self.r2t_host)
+        h_dslots[:] = Bm.rt_decode_slots_batch(self.tree, rows, self.dec_pos, self.r2t_host)
         d_pl, d_el, d_qo, d_rows, d_dslots = self.meta_views[rs]
         max_e = int(el.max())
         # every launch names self.stream
-        dev_rows, host_rows = self.copy_views[rs]
-        # rows and metadata, by a kernel on the step's stream that reads the
-        # pinned staging (no hand-over to a DMA engine and back)
-        Bm.rt_copy_from_host(dev_rows, host_rows, stream=self.stream)
+        # Rows and metadata, by a kernel on the step's stream that reads the
+        # pinned staging (no hand-over to a DMA engine and back).  Every
+        # request matched the whole prefix (checked above) through the same
+        # tree nodes, so columns 0 .. P0-1 of its row hold the prefix's
+        # slots, which stay fixed while the prefix is cached: once a row set
+        # has gone up whole with those slots, only the columns from P0 on
+        # change.
+        dev_all, host_all, dev_tail, host_tail = self.copy_views[rs]
+        if self.prefix_slots is None or not np.array_equal(self.r2t_host[rows[0], :P0], self.prefix_slots):
+            self.prefix_slots = self.r2t_host[rows[0], :P0].copy()
+            self.rows_whole = [False, False]
+        if self.rows_whole[rs]:
+            Bm.rt_copy_from_host_2d(dev_tail, host_tail, stream=self.stream)
+        else:
+            Bm.rt_copy_from_host(dev_all, host_all, stream=self.stream)
+            self.rows_whole[rs] = True
         self._store_extend(k, v, d_rows, d_pl, d_el, d_qo, max_e)
         # the marker that frees this row set's staging: a timed step's first
         # timing event follows the copy on the stream, so it serves; other

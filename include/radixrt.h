@@ -265,6 +265,15 @@ int req_to_token_scatter(int32_t* req_to_token, int32_t req_to_token_stride, con
  * asynchronous copy). */
 int rt_copy_from_host(void* dst, const void* src, int64_t bytes, void* stream);
 
+/* rt_copy_from_host over height rows of width bytes: row r goes from
+ * src + r * src_pitch (pinned host) to dst + r * dst_pitch (device), so a
+ * step can move only the columns of its slot-table rows that changed.
+ * width and the pitches multiples of 4, pitches >= width when height > 1;
+ * the whole source span must lie in one pinned allocation and the whole
+ * destination span in one device allocation (checked as above). */
+int rt_copy_from_host_2d(void* dst, int64_t dst_pitch, const void* src, int64_t src_pitch, int64_t width,
+                         int64_t height, void* stream);
+
 /* One decode step's writes in a single launch: req_to_token_scatter of
  * (rows, positions, slots) and kv_store of (k_new, v_new) at slots, for i < n
  * [P4 the decode step writes its new token's slot into req_to_token and its

@@ -28,7 +28,7 @@ EXPORTS = [
     "radix_mixed_attention", "radix_mixed_attention_fp8kv",
     "radix_decode_shared_workspace_bytes", "radix_decode_attention_shared", "radix_decode_attention_shared_fp8kv",
     "radix_extend_attention", "radix_decode_workspace_bytes", "radix_decode_attention",
-    "rt_copy_from_host",
+    "rt_copy_from_host", "rt_copy_from_host_2d",
 ]
 
 
@@ -135,6 +135,8 @@ def lib():
                                                                    _vp, _vp] + [ctypes.c_int32] * 8 +
                                                     [ctypes.c_float] * 3 + [_vp, ctypes.c_int64, _vp]),
             "rt_copy_from_host": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, _vp]),
+            "rt_copy_from_host_2d": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, ctypes.c_int64, ctypes.c_int64,
+                                                    ctypes.c_int64, _vp]),
             "radix_extend_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
@@ -431,6 +433,16 @@ def rt_copy_from_host(dst, src, stream=None):
     if not (src.is_contiguous() and dst.is_contiguous()):
         raise ValueError("rt_copy_from_host: tensors must be contiguous")
     _check(lib().rt_copy_from_host(_dptr(dst), _dptr(src), n, _stream(stream)))
+
+
+def rt_copy_from_host_2d(dst, src, stream=None):
+    """Copy the 2-D pinned host view src (contiguous rows, any row stride)
+    into the device view dst of the same shape and dtype."""
+    if src.dim() != 2 or dst.shape != src.shape or dst.dtype != src.dtype or src.stride(1) != 1 or dst.stride(1) != 1:
+        raise ValueError("rt_copy_from_host_2d: needs 2-D views of one shape and dtype with contiguous rows")
+    es = src.element_size()
+    _check(lib().rt_copy_from_host_2d(_dptr(dst), dst.stride(0) * es, _dptr(src), src.stride(0) * es,
+                                      src.shape[1] * es, src.shape[0], _stream(stream)))
 
 
 def req_to_token_scatter(req_to_token, rows, positions, slots, stream=None):

@@ -26,40 +26,49 @@ __global__ void __launch_bounds__(256) r2t_scatter_kernel(int32_t* __restrict__ 
   if (i < n) r2t[int64_t(rows[i]) * stride + pos[i]] = slots[i];
 }
 
-// 16-byte pieces when both ends are 16-byte aligned (vec), else 4-byte
-// words; the grid strides over the pieces.
-__global__ void __launch_bounds__(256) host_copy_kernel(char* __restrict__ dst, const char* __restrict__ src,
-                                                        int64_t bytes, bool vec) {
+// height rows of width bytes, at the given pitches; 16-byte pieces when
+// every row start is 16-byte aligned (vec), else 4-byte words.  The grid
+// strides over the pieces of all rows.
+__global__ void __launch_bounds__(256) host_copy_kernel(char* __restrict__ dst, int64_t dst_pitch,
+                                                        const char* __restrict__ src, int64_t src_pitch,
+                                                        int64_t width, int64_t height, bool vec) {
   const int64_t step = int64_t(gridDim.x) * blockDim.x;
   const int64_t t0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  int64_t done = 0;
-  if (vec) {
-    const int64_t n16 = bytes / 16;
-    for (int64_t i = t0; i < n16; i += step)
-      reinterpret_cast<rtk::u32x4*>(dst)[i] = reinterpret_cast<const rtk::u32x4*>(src)[i];
-    done = n16 * 16;
+  const int64_t per_row = vec ? width / 16 : width / 4;
+  const int64_t total = per_row * height;
+  for (int64_t i = t0; i < total; i += step) {
+    const int64_t r = i / per_row, c = i - r * per_row;
+    if (vec)
+      *reinterpret_cast<rtk::u32x4*>(dst + r * dst_pitch + c * 16) =
+          *reinterpret_cast<const rtk::u32x4*>(src + r * src_pitch + c * 16);
+    else
+      *reinterpret_cast<uint32_t*>(dst + r * dst_pitch + c * 4) =
+          *reinterpret_cast<const uint32_t*>(src + r * src_pitch + c * 4);
   }
-  const int64_t n4 = (bytes - done) / 4;
-  for (int64_t i = t0; i < n4; i += step)
-    reinterpret_cast<uint32_t*>(dst + done)[i] = reinterpret_cast<const uint32_t*>(src + done)[i];
 }
 }  // namespace
 
-extern "C" int rt_copy_from_host(void* dst, const void* src, int64_t bytes, void* stream) {
-  const char* name = "rt_copy_from_host";
-  if (bytes < 0 || bytes % 4 != 0) return rt::fail(RT_ERR_INVALID, std::string(name) + ": bytes not a multiple of 4");
-  if (bytes == 0) return RT_OK;
+namespace {
+int copy_from_host(const char* name, void* dst, int64_t dst_pitch, const void* src, int64_t src_pitch,
+                   int64_t width, int64_t height, void* stream) {
+  if (width < 0 || height < 0 || width % 4 != 0 || dst_pitch % 4 != 0 || src_pitch % 4 != 0 ||
+      (height > 1 && (dst_pitch < width || src_pitch < width)))
+    return rt::fail(RT_ERR_INVALID, std::string(name) + ": sizes or pitches not multiples of 4, or pitch < width");
+  if (width == 0 || height == 0) return RT_OK;
   if (!dst || !src) return rt::fail(RT_ERR_INVALID, std::string(name) + ": null pointer");
   if ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 3)
     return rt::fail(RT_ERR_INVALID, std::string(name) + ": pointers not 4-byte aligned");
+  const int64_t src_span = (height - 1) * src_pitch + width;  // bytes from the first to past the last read
+  const int64_t dst_span = (height - 1) * dst_pitch + width;
   // The kernel reads src through its device mapping.  Both ends of the range
   // must resolve to one pinned allocation; anything else is refused here.
   void* dsrc = nullptr;
   void* dlast = nullptr;
-  char* last = const_cast<char*>(static_cast<const char*>(src)) + (bytes - 1);
+  char* last = const_cast<char*>(static_cast<const char*>(src)) + (src_span - 1);
   const hipError_t e0 = hipHostGetDevicePointer(&dsrc, const_cast<void*>(src), 0);
   const hipError_t e1 = e0 == hipSuccess ? hipHostGetDevicePointer(&dlast, last, 0) : e0;
-  if (e0 != hipSuccess || e1 != hipSuccess || !dsrc || static_cast<char*>(dlast) != static_cast<char*>(dsrc) + (bytes - 1)) {
+  if (e0 != hipSuccess || e1 != hipSuccess || !dsrc ||
+      static_cast<char*>(dlast) != static_cast<char*>(dsrc) + (src_span - 1)) {
     (void)hipGetLastError();
     return rt::fail(RT_ERR_INVALID, std::string(name) + ": source is not inside one pinned host allocation");
   }
@@ -69,19 +78,31 @@ extern "C" int rt_copy_from_host(void* dst, const void* src, int64_t bytes, void
   size_t size = 0;
   const bool dev_ok = hipPointerGetAttributes(&attr, dst) == hipSuccess && attr.type == hipMemoryTypeDevice &&
                       hipMemGetAddressRange(&base, &size, dst) == hipSuccess &&
-                      static_cast<char*>(dst) + bytes <= static_cast<char*>(base) + size;
+                      static_cast<char*>(dst) + dst_span <= static_cast<char*>(base) + size;
   if (!dev_ok) {
     (void)hipGetLastError();
-    return rt::fail(RT_ERR_INVALID, std::string(name) + ": destination is not device memory holding bytes");
+    return rt::fail(RT_ERR_INVALID, std::string(name) + ": destination is not device memory holding the range");
   }
-  const bool vec = ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(dsrc)) & 15) == 0;
-  const int64_t pieces = vec ? bytes / 16 : bytes / 4;
+  const bool vec = ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(dsrc) | uintptr_t(width) |
+                     uintptr_t(height > 1 ? dst_pitch | src_pitch : 0)) & 15) == 0;
+  const int64_t pieces = (vec ? width / 16 : width / 4) * height;
   const uint32_t blocks = uint32_t(std::min<int64_t>(1024, std::max<int64_t>(1, (pieces + 255) / 256)));
   hipLaunchKernelGGL(host_copy_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, static_cast<char*>(dst),
-                     static_cast<const char*>(dsrc), bytes, vec);
+                     dst_pitch, static_cast<const char*>(dsrc), src_pitch, width, height, vec);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return rt::fail(RT_ERR_HIP, std::string(name) + " launch: " + hipGetErrorString(e));
   return RT_OK;
+}
+}  // namespace
+
+extern "C" int rt_copy_from_host(void* dst, const void* src, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 4 != 0) return rt::fail(RT_ERR_INVALID, "rt_copy_from_host: bytes not a multiple of 4");
+  return copy_from_host("rt_copy_from_host", dst, bytes, src, bytes, bytes, 1, stream);
+}
+
+extern "C" int rt_copy_from_host_2d(void* dst, int64_t dst_pitch, const void* src, int64_t src_pitch,
+                                    int64_t width, int64_t height, void* stream) {
+  return copy_from_host("rt_copy_from_host_2d", dst, dst_pitch, src, src_pitch, width, height, stream);
 }
 
 extern "C" int req_to_token_scatter(int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* rows,

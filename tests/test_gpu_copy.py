@@ -1,7 +1,7 @@
-"""rt_copy_from_host on the GPU: pinned host memory reaches device memory bit
-for bit through the copy kernel (16-byte and 4-byte paths, a word tail,
-offsets inside an allocation), and pageable memory is refused before any
-launch."""
+"""rt_copy_from_host(_2d) on the GPU: pinned host memory reaches device
+memory bit for bit through the copy kernel (16-byte and 4-byte paths, a word
+tail, offsets inside an allocation, column blocks of row-pitched tables), and
+pageable memory is refused before any launch."""
 
 import numpy as np
 import pytest
@@ -25,6 +25,21 @@ def test_copy_from_pinned_host(n, src_off, dst_off):
     got = dev.cpu()
     assert torch.equal(got[dst_off:dst_off + n], host[src_off:src_off + n])
     assert bool((got[:dst_off] == -7).all()) and bool((got[dst_off + n:] == -7).all())
+
+
+@pytest.mark.parametrize("rows,cols,c0,c1", [(69, 1153, 1024, 1153), (64, 1156, 1024, 1156), (3, 40, 4, 36),
+                                              (1, 9, 2, 3)])
+def test_copy_from_host_2d_column_block(rows, cols, c0, c1):
+    print(f"rt_copy_from_host_2d rows={rows} cols={cols} columns {c0}..{c1}", flush=True)
+    rng = np.random.default_rng(rows * cols + c0)
+    host = torch.from_numpy(rng.integers(-2**31, 2**31 - 1, (rows, cols), dtype=np.int64).astype(np.int32))
+    host = host.pin_memory()
+    dev = torch.full((rows, cols), -7, dtype=torch.int32, device="cuda")
+    B.rt_copy_from_host_2d(dev[:, c0:c1], host[:, c0:c1])
+    torch.cuda.synchronize()
+    got = dev.cpu()
+    assert torch.equal(got[:, c0:c1], host[:, c0:c1])
+    assert bool((got[:, :c0] == -7).all()) and bool((got[:, c1:] == -7).all())
 
 
 def test_copy_from_host_refuses_pageable_memory():
