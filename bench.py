@@ -554,6 +554,12 @@ class DecodeBench:
         # decode inputs for every step
         gh = self._dev_hashes(prefix_hashes_rows_np(self.gen_toks, start))         # [B, steps]
         self.q = [self._values(gh[:, s].contiguous(), 1, self.HQ) for s in range(self.n_steps)]
+        # per-step positions and new slots: one pinned staging row per step
+        # (never reused within a run, so no step waits for an earlier copy)
+        # and its device row, copied by a kernel on the step's stream
+        self.meta_host_t = torch.zeros((self.n_steps, 2 * self.B), dtype=torch.int32, pin_memory=True)
+        self.meta_host = self.meta_host_t.numpy()
+        self.meta_dev = torch.zeros((self.n_steps, 2 * self.B), dtype=torch.int32, device=self.dev)
         self.k = [self._values(gh[:, s].contiguous(), 2, self.HKV) for s in range(self.n_steps)]
         self.v = [self._values(gh[:, s].contiguous(), 3, self.HKV) for s in range(self.n_steps)]
         self.r2t_dev.copy_(torch.from_numpy(self.r2t_host))
@@ -593,7 +599,10 @@ class DecodeBench:
         rows = np.arange(self.B, dtype=np.int32)
         slots = Bm.rt_decode_slots_batch(self.tree, rows, pos, self.r2t_host)
         with torch.cuda.stream(self.stream):
-            meta = torch.from_numpy(np.concatenate([pos, slots])).pin_memory().to(self.dev, non_blocking=True)
+            self.meta_host[s, :self.B] = pos
+            self.meta_host[s, self.B:] = slots
+            meta = self.meta_dev[s]
+            Bm.rt_copy_from_host(meta, self.meta_host_t[s], stream=self.stream)
             d_pos, d_slots = meta[:self.B], meta[self.B:]
             Bm.req_to_token_scatter(self.r2t_dev, self.rows_dev, d_pos, d_slots, stream=self.stream)
             store = Bm.kv_store_fp8 if self.fp8 else Bm.kv_store
