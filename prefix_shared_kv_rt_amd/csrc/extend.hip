@@ -53,6 +53,7 @@
 #include "dev_common.h"
 #include "radixrt.h"
 #include "rt_internal.h"
+#include "tile_layout.h"
 
 namespace {
 
@@ -80,26 +81,6 @@ struct ExtendCfg {
   static constexpr int kKS = D / 16;                      // 16-dim steps of Q K^T
   static constexpr int kR = D / 32;                       // 32-dim tiles of O^T
 };
-
-__device__ __forceinline__ int xcd_slice(int bid, int nblk) {
-  const int xcd = bid & 7, local = bid >> 3;
-  const int q = nblk >> 3, r = nblk & 7;
-  return xcd * q + min(xcd, r) + local;
-}
-
-// LDS tile layout: rows (keys) of D*2 bytes, unpadded; the 16-byte chunks of
-// row k are permuted by chunk ^ f(k).  f is a bijection on the low 4 bits of
-// k chosen so that both access patterns are free of bank conflicts whether
-// the LDS serves 128 or 256 bytes per cycle: 8 or 16 consecutive keys read at
-// one chunk index (the K operand) land on distinct bank groups, and so do 4
-// consecutive keys read at 2 or 4 consecutive chunks (the transpose reads).
-__device__ __forceinline__ int swz_f(int k) {
-  return ((0xCA60 >> (4 * (k & 3))) & 0xF) ^ ((k >> 2) & 1) ^ (((k >> 3) & 1) << 1);
-}
-template <int D>
-__device__ __forceinline__ int swz(int key, int chunk) {
-  return key * ExtendCfg<D>::kRowBytes + ((chunk ^ (swz_f(key) & (ExtendCfg<D>::kCPR - 1))) << 4);
-}
 
 // PART: the shared-prefix pass of radix_decode_attention_shared.  A
 // "request" b is then a group of consecutive decode rows (qo_indptr =

@@ -95,6 +95,8 @@ EXTEND_CASES = [
     ([10, 200, 0], [90, 45, 130], 12, 4, 64),
     ([0], [300], 4, 4, 64),
     ([50, 3], [0, 70], 32, 8, 128),
+    # keys beyond two 1024-key index segments, a wave with no rows left
+    ([2500, 7, 1900], [70, 2, 300], 32, 8, 128),
 ]
 
 
