@@ -372,6 +372,26 @@ int radix_decode_attention(const void* q, void* o, const void* k_pool, const voi
                            float sm_scale, int dtype, void* workspace, int64_t workspace_bytes,
                            void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * radix_decode_attention with the same arguments minus the workspace.  Its
+ * split-K partials go to a device array the library owns, of
+ * RT_NOALLOC_MAX_WORKSPACE_BYTES (32 MiB) per GPU, held until the process
+ * ends; nothing is allocated or freed by the call.
+ * Sizes whose radix_decode_workspace_bytes() exceeds that maximum are
+ * refused with RT_ERR_INVALID before any launch.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (concurrent
+ * streams, or host threads) race and must be ordered by the caller.  The
+ * array's device address is looked up on a device's first call
+ * (RT_ERR_HIP if that fails). */
+#define RT_NOALLOC_MAX_WORKSPACE_BYTES ((int64_t)32 << 20)
+int radix_decode_attention_noalloc(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                   const int32_t* req_to_token, int32_t req_to_token_stride,
+                                   const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                   const int32_t* extend_lens, int32_t batch, int32_t max_kv_len,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                                   int dtype, void* stream);
+
 /* Decode for batches whose requests share cached prefixes.  The radix tree
  * hands requests that matched the same path the same slots for that path
  * [P2 section 04: requests that match a common prefix reference one copy of

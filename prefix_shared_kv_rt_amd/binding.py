@@ -29,6 +29,7 @@ EXPORTS = [
     "radix_decode_shared_workspace_bytes", "radix_decode_attention_shared", "radix_decode_attention_shared_fp8kv",
     "radix_extend_attention", "radix_decode_workspace_bytes", "radix_decode_attention",
     "rt_copy_from_host", "rt_copy_from_host_2d",
+    "radix_decode_attention_noalloc",
 ]
 
 
@@ -147,6 +148,10 @@ def lib():
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
                                                       _vp, ctypes.c_int64, _vp]),
+            "radix_decode_attention_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp,
+                                                              _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                                              ctypes.c_int, _vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -545,6 +550,22 @@ def radix_decode_attention(q, o, k_pool, v_pool, req_to_token, req_pool_indices,
                                         _dptr(extend_lens), batch, int(max_kv_len), hq, hkv, d, float(sm_scale),
                                         _dtype_code(q), _dptr(workspace), workspace.numel() * workspace.element_size(),
                                         _stream(stream)))
+
+
+# RT_NOALLOC_MAX_WORKSPACE_BYTES of include/radixrt.h
+NOALLOC_MAX_WORKSPACE_BYTES = 32 << 20
+
+
+def radix_decode_attention_noalloc(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens, max_kv_len,
+                                   sm_scale, extend_lens=None, stream=None):
+    """radix_decode_attention with the split-K workspace in the library's own
+    device array (no allocation)."""
+    batch, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    _check(lib().radix_decode_attention_noalloc(_dptr(q), _dptr(o), _dptr(k_pool), _dptr(v_pool),
+                                                _dptr(req_to_token), req_to_token.shape[1], _dptr(req_pool_indices),
+                                                _dptr(prefix_lens), _dptr(extend_lens), batch, int(max_kv_len), hq,
+                                                hkv, d, float(sm_scale), _dtype_code(q), _stream(stream)))
 
 
 def radix_decode_shared_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, n_groups, max_group_size,

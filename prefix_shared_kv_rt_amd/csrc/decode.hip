@@ -30,6 +30,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
+#include <string>
 
 #include "dev_common.h"
 #include "radixrt.h"
@@ -511,6 +513,69 @@ extern "C" int radix_decode_attention_fp8kv(const void* q, void* o, const void* 
   return decode_entry("radix_decode_attention_fp8kv", q, o, k_pool, v_pool, req_to_token, req_to_token_stride,
                       req_pool_indices, prefix_lens, batch, max_kv_len, num_q_heads, num_kv_heads, head_dim,
                       sm_scale, k_scale, v_scale, kModeFp8Kv, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------------- no allocation --
+// radix_decode_attention_noalloc: the split-K partials go to `scratch`, a
+// file-scope device array of kNoAllocScratchBytes that every GPU the
+// library runs on holds until the process ends.  In host code `scratch` is
+// only a stand-in symbol; its device address on the current GPU comes from
+// hipGetSymbolAddress, looked up once per device (the entry point's first
+// call there) and kept.  The split kernel writes every partial slot the
+// combine reads (empty chunks included), so nothing needs clearing between
+// calls.
+namespace {
+
+constexpr int64_t kNoAllocScratchBytes = RT_NOALLOC_MAX_WORKSPACE_BYTES;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, or nullptr (error recorded).
+void* scratch_on_device(const char* name) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    rt::fail(RT_ERR_HIP, std::string(name) + ": no usable current device");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      rt::fail(RT_ERR_HIP, std::string(name) + ": scratch address: " + hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int radix_decode_attention_noalloc(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                              const int32_t* req_to_token, int32_t req_to_token_stride,
+                                              const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                              const int32_t* extend_lens, int32_t batch, int32_t max_kv_len,
+                                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                              float sm_scale, int dtype, void* stream) {
+  (void)extend_lens;
+  static const char* kName = "radix_decode_attention_noalloc";
+  if (dtype != RT_F32 && dtype != RT_BF16) return rt::fail(RT_ERR_INVALID, std::string(kName) + ": bad dtype");
+  const int64_t need = radix_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_kv_len);
+  if (need < 0) return rt::fail(RT_ERR_INVALID, std::string(kName) + ": bad shape");
+  if (need > kNoAllocScratchBytes)
+    return rt::fail(RT_ERR_INVALID, std::string(kName) + ": these sizes need " + std::to_string(need) +
+                                        " bytes of split-K workspace, above the library's " +
+                                        std::to_string(kNoAllocScratchBytes) + "-byte scratch array");
+  if (batch == 0) return RT_OK;
+  void* ws = scratch_on_device(kName);
+  if (!ws) return RT_ERR_HIP;
+  return decode_entry(kName, q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
+                      batch, max_kv_len, num_q_heads, num_kv_heads, head_dim, sm_scale, 1.0f, 1.0f, dtype, ws,
+                      kNoAllocScratchBytes, stream);
 }
 
 namespace {
