@@ -23,15 +23,16 @@ whole path:
 Q/K/V of every step are generated into HBM before the timed region.  Before
 the warm-up steps, about 200 ms of extend attention over the cached prefix
 lets the GPU's clocks settle at their level under sustained load (the first
-few dozen steps otherwise run 10-15 % slower).  A
-suffix that starts like an earlier finished request's suffix matches more
-than 1024 tokens; its already-cached rows are skipped by the scatter and by
-extend (they are not counted as work).
+few dozen steps otherwise run 10-15 % slower).  Suffix token ids are drawn
+over the Llama-3 vocabulary with first tokens distinct over the whole run,
+so no suffix matches an earlier one: every step extends 64 x 128 rows.
 
 Output: one JSON line (metric, value = extend + decode tokens per second of
 whole steps, roofline of the extend kernel from HIP events on its stream,
-CPU oracle baseline on a bounded sample).  ``--workload long_context`` or
-``fork`` time decode steps instead (extra lines, not the headline).
+ceilings measured on the box, CPU oracle baseline on a bounded sample, also
+on one thread).  ``--workload long_context`` or ``fork`` time decode steps
+instead, ``chat`` the multi-turn workload through the scheduler (extra
+lines, not the headline); decode rooflines count distinct bytes.
 """
 
 import argparse
@@ -82,14 +83,13 @@ def parse():
     ap.add_argument("--decode", choices=["plain", "shared"], default=None,
                     help="decode path of few_shot, long_context and fork: plain = radix_decode_attention (split-K "
                          "over each request's whole context), shared = radix_decode_attention_shared (K/V that a "
-                         "group of requests shares read once per group); default shared for few_shot, plain for "
-                         "the decode workloads")
+                         "group of requests shares read once per group); default shared")
     ap.add_argument("--mixed", action="store_true",
                     help="chat workload: an iteration's extend chunks and decode rows share one attention launch")
     ap.add_argument("--page-size", type=int, default=1,
                     help="KV slots per pool page (few_shot and chat); 1 = token-granular")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=192, help="requests in the oracle's timed sample")
+    ap.add_argument("--cpu-sample", type=int, default=192, help="few_shot: requests in the oracle's timed sample")
     return ap.parse_args()
 
 
@@ -99,6 +99,7 @@ class FewShotBench:
     HQ, HKV, D = 32, 8, 128
     SLOTS = 262144
     SEED = 1
+    VOCAB = 128256   # Llama-3 tokenizer
 
     def __init__(self, n_batches, torch, B_mod, gen_t, kv_dtype="bf16", page_size=1, shared_decode=False):
         self.fp8 = kv_dtype == "fp8"
@@ -116,8 +117,16 @@ class FewShotBench:
         self.stream = torch.cuda.current_stream(self.dev)
         rng = np.random.Generator(np.random.PCG64(self.SEED))
         self.prefix = rng.integers(0, 1000, size=self.PREFIX).astype(np.int32)
-        # every batch: 64 suffixes of 128 tokens + 1 generated token each
-        self.suffix = [rng.integers(0, 1000, size=(self.B, self.SUFFIX + 1)).astype(np.int32) for _ in range(n_batches)]
+        # every batch: 64 suffixes of 128 tokens + 1 generated token each,
+        # ids over the Llama-3 vocabulary; the suffixes' first tokens are
+        # pairwise distinct over the whole run, so no suffix matches an
+        # earlier one and every request extends exactly SUFFIX rows
+        firsts = rng.choice(self.VOCAB, size=n_batches * self.B, replace=False).astype(np.int32)
+        self.suffix = []
+        for i in range(n_batches):
+            sfx = rng.integers(0, self.VOCAB, size=(self.B, self.SUFFIX + 1)).astype(np.int32)
+            sfx[:, 0] = firsts[i * self.B:(i + 1) * self.B]
+            self.suffix.append(sfx)
         self.stride = self.PREFIX + self.SUFFIX + 1
         bf16 = torch.bfloat16
         self.pool = B_mod.rt_pool_create(self.SLOTS, self.page_size)
@@ -177,6 +186,7 @@ class FewShotBench:
         self.host_s = []
         self.step_lens = []
         self.dec_distinct = []
+        self.ext_rows = []
 
     def gen_inputs(self, n_batches):
         """Q/K/V of every suffix position and of the generated token, in HBM."""
@@ -386,6 +396,7 @@ class FewShotBench:
             rows_keys = float(np.sum(pl.astype(np.float64) * el + el.astype(np.float64) * (el + 1) / 2))
             self.flops.append(4.0 * self.D * self.HQ * rows_keys)
             self.ext_tokens.append(int(el.sum()) + B)
+            self.ext_rows.append(int(el.sum()))
             self.dec_bytes.append(B * (P0 + S + 1) * (self.HKV * self.D * eb * 2 + 4) + 2 * B * self.HQ * self.D * 2)
             # the prefix once, every request's own tail
             self.dec_distinct.append(P0 * self.HKV * self.D * eb * 2 + B * (S + 1) * (self.HKV * self.D * eb * 2 + 4)
@@ -457,10 +468,15 @@ def run_few_shot(args, torch):
         },
         "kernels": {
             "extend_us": ext_avg_s * 1e6,
-            "extend_tokens_per_s": (fb.B * fb.SUFFIX) / ext_avg_s,
+            "extend_rows_per_step": float(np.mean(fb.ext_rows)),
+            "extend_tokens_per_s": float(np.mean(fb.ext_rows)) / ext_avg_s,
             "decode_us": dec_avg_s * 1e6,   # decode attention, replayed after the timed steps
-            "decode_hbm_gbs": float(np.mean(fb.dec_bytes)) / dec_avg_s / 1e9,
+            # bytes each request's whole context would move (the shared
+            # prefix counted once per request: an upper bound, not HBM traffic)
+            "decode_per_request_gbs": float(np.mean(fb.dec_bytes)) / dec_avg_s / 1e9,
+            # bytes the step must read at least once (prefix once, every tail)
             "decode_distinct_gbs": float(np.mean(fb.dec_distinct)) / dec_avg_s / 1e9,
+            "decode_distinct_frac": float(np.mean(fb.dec_distinct)) / dec_avg_s / 1e9 / PEAK_HBM_GBS,
             # host time to run one step's tree work and enqueue its GPU work
             # (the step is host-bound when this is near ms_per_step)
             "host_us_per_step": float(np.mean(fb.host_s)) * 1e6,
@@ -527,6 +543,44 @@ class DecodeBench:
             store(self.k_pool, self.v_pool, self._values(h, 2, self.HKV), self._values(h, 3, self.HKV), loc,
                   stream=self.torch.cuda.current_stream())
 
+    def cold_extend(self, sh_hash, rows, reps=5):
+        """Fork: the 16 cold prompts' extend pass (P = 0, E = 2048 each)
+        through kv_store and radix_extend_attention, as a serving step runs
+        it; the K/V it stores are the ones the branches decode against.
+        Repeated ``reps`` times after one untimed pass (the repeats rewrite
+        the same slots and outputs); returns the mean time per pass."""
+        torch, Bm = self.torch, self.Bm
+        n = self.groups * self.shared
+        h = self._dev_hashes(sh_hash.reshape(-1))
+        q = self._values(h, 1, self.HQ)
+        k = self._values(h, 2, self.HKV)
+        v = self._values(h, 3, self.HKV)
+        o = torch.empty_like(q)
+        g = self.groups
+        meta = torch.from_numpy(np.concatenate([rows, np.zeros(g), np.full(g, self.shared),
+                                                np.arange(g + 1) * self.shared]).astype(np.int32)).to(self.dev)
+        d_rows, d_pl, d_el, d_qo = meta[:g], meta[g:2 * g], meta[2 * g:3 * g], meta[3 * g:]
+        r2t_dev = self.r2t_dev
+        r2t_dev.copy_(torch.from_numpy(self.r2t_host))
+        store = Bm.kv_store_extend_fp8 if self.fp8 else Bm.kv_store_extend
+        ext = Bm.radix_extend_attention_fp8kv if self.fp8 else Bm.radix_extend_attention
+        evs = []
+        with torch.cuda.stream(self.stream):
+            for r in range(reps + 1):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                store(self.k_pool, self.v_pool, k, v, r2t_dev, d_rows, d_pl, d_el, d_qo, self.shared,
+                      stream=self.stream)
+                e0.record(self.stream)
+                ext(q, o, self.k_pool, self.v_pool, r2t_dev, d_rows, d_pl, d_el, d_qo, self.shared, self.sm_scale,
+                    stream=self.stream)
+                e1.record(self.stream)
+                if r > 0:
+                    evs.append((e0, e1))
+        self.stream.synchronize()
+        self.cold_o = o
+        assert n == q.shape[0]
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) / 1e3
+
     def setup(self):
         torch, Bm, T = self.torch, self.Bm, self.T
         per = self.B // self.groups
@@ -537,7 +591,12 @@ class DecodeBench:
         off = np.arange(0, self.groups * self.shared + 1, self.shared, dtype=np.int64)
         rows = np.arange(self.B, self.B + self.groups, dtype=np.int32)
         pl, el, nodes, loc = Bm.rt_admit_batch(self.tree, toks, off, self.r2t_host, rows)
-        self._store(sh_hash.reshape(-1), loc)
+        self.cold_extend_s = None
+        if self.name == "fork":
+            # cold prompts: the real extend pass (scatter + extend attention)
+            self.cold_extend_s = self.cold_extend(sh_hash, rows)
+        else:
+            self._store(sh_hash.reshape(-1), loc)
         Bm.rt_finish_batch(self.tree, toks, off, self.r2t_host, rows, pl, nodes)
         # the decoding requests: match the shared part, store their private part
         prompts = np.concatenate([np.repeat(self.shared_toks, per, axis=0), self.private_toks], axis=1)
@@ -630,7 +689,7 @@ def run_decode_bench(args, torch):
     from synth import torch_gen
     n = args.warmup + args.steps
     db = DecodeBench(args.workload, torch, Bm, torch_gen, n, kv_dtype=args.kv_dtype,
-                     shared_decode=(args.decode or "plain") == "shared")
+                     shared_decode=(args.decode or "shared") == "shared")
     db.setup()
     db.settle_clocks()
     for s in range(args.warmup):
@@ -651,11 +710,16 @@ def run_decode_bench(args, torch):
     avg_s = float(np.mean(ms)) / 1e3
     kv = np.mean([k for _, _, k in db.events])
     row = db.HKV * db.D * (1 if db.fp8 else 2)   # one K (or V) pool row
-    alg_bytes = db.B * kv * (2 * row + 4) + 2 * db.B * db.HQ * db.D * 2
-    distinct = db.groups * db.shared * 2 * row + db.B * (kv - db.shared) * (2 * row + 4)
-    # The plain decode reads every request's whole context; the shared
-    # decode must read only the distinct bytes (each group's shared part once).
-    achieved = (distinct if db.shared_decode else alg_bytes) / avg_s / 1e9
+    # every request's whole context (the shared part once per request: what
+    # the plain decode's waves request, much of it served by L2 / MALL)
+    per_request = db.B * kv * (2 * row + 4) + 2 * db.B * db.HQ * db.D * 2
+    # what a step must read at least once: each group's shared part once,
+    # every request's own tail, q and o
+    distinct = (db.groups * db.shared * 2 * row + db.B * (kv - db.shared) * (2 * row + 4)
+                + 2 * db.B * db.HQ * db.D * 2)
+    achieved = distinct / avg_s / 1e9
+    frac = achieved / PEAK_HBM_GBS
+    assert frac <= 1.0, f"decode roofline above HBM peak ({frac:.3f}): the byte count is wrong"
     label = ("long-context decode: 32 requests x (16384 shared + 16384 private) context, Hq 64 / Hkv 8 / D 128"
              if db.name == "long_context" else
              "fork decode: 16 prompts x 2048 tokens, 8 branches each (batch 128), Hq 32 / Hkv 8 / D 128")
@@ -669,14 +733,22 @@ def run_decode_bench(args, torch):
         "roofline": {"bound": "hbm",
                      "kernel": ("radix_decode_attention_shared" if db.shared_decode else "radix_decode_attention")
                                + ("_fp8kv" if db.fp8 else "")
-                               + (" (shared pass + private split + combine), bytes = distinct bytes"
-                                  if db.shared_decode else " (split + combine)"),
-                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": profiled_traffic("decode_split_fp8" if db.fp8 else "decode_split_bf16")
-                                if db.name == "long_context" and not db.shared_decode else None,
-                     "bytes_per_launch": alg_bytes, "distinct_bytes_per_launch": distinct,
+                               + (" (shared pass + private split + combine)" if db.shared_decode
+                                  else " (split + combine)") + "; bytes = distinct bytes",
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": frac,
+                     "traffic": profiled_traffic(("decode_shared" if db.shared_decode else "decode_split")
+                                                 + ("_fp8" if db.fp8 else "_bf16") + "_" + db.name),
+                     "bytes_per_launch": distinct, "per_request_bytes_per_launch": per_request,
                      "avg_launch_us": avg_s * 1e6},
     }
+    if db.cold_extend_s is not None:
+        g, e = db.groups, db.shared
+        flops = 4.0 * db.D * db.HQ * g * e * (e + 1) / 2
+        tf = flops / db.cold_extend_s / 1e12
+        result["cold_extend"] = {"what": f"{g} cold prompts x {e} tokens (P = 0): kv_store_extend + "
+                                         "radix_extend_attention, extend timed (HIP events, mean of 5 passes)",
+                                 "us": db.cold_extend_s * 1e6, "flops": flops, "tflops": tf,
+                                 "mfma_frac": tf / PEAK_BF16_TFLOPS}
     return result
 
 
@@ -736,6 +808,19 @@ def run_chat(args, torch):
                 re_extended += max(0, min(len(byrid[rid].prompt), len(prev.prompt) + len(prev.gen)) - p)
     ext_tf = ext.get("flops", 0.0) / max(ext.get("ms", 0.0), 1e-9) / 1e9
     dec_gbs = dec.get("bytes", 0.0) / max(dec.get("ms", 0.0), 1e-9) / 1e6
+    # roofline of the kernel kind with the most summed time
+    dom = max(per, key=lambda k: per[k]["ms"])
+    d = per[dom]
+    if dom == "decode":
+        ach = d["distinct_bytes"] / (d["ms"] / 1e3) / 1e9
+        roof = {"bound": "hbm", "kernel": "radix_decode_attention (all decode launches); bytes = distinct bytes",
+                "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
+    else:
+        ach = d["flops"] / (d["ms"] / 1e3) / 1e12
+        roof = {"bound": "mfma", "kernel": f"radix_{dom}_attention (all {dom} launches)", "achieved": ach,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS}
+    roof.update({"traffic": None, "launches": d["launches"], "avg_launch_us": d["ms"] * 1e3 / d["launches"]})
+    assert roof["frac"] <= 1.0, roof
     return {
         "metric": METRIC + " (chat, mixed)", "value": tokens / kernel_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": len(sch.iterations), "warmup": 0, "ms_per_step": wall / len(sch.iterations) * 1e3,
@@ -748,6 +833,7 @@ def run_chat(args, torch):
                    "kv_dtype": "fp8_e4m3" if args.kv_dtype == "fp8" else "bf16",
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "pool_slots": wl.num_slots},
+        "roofline": roof,
         "wall_tokens_per_s": tokens / wall,
         "kernels": {k: {"launches": d["launches"], "ms": d["ms"]} for k, d in per.items()},
         "extend": {"tokens": ext.get("tokens", 0), "tflops": ext_tf, "mfma_frac": ext_tf / PEAK_BF16_TFLOPS},
@@ -831,25 +917,123 @@ def run_decode_graph(args, torch):
     }
 
 
-def cpu_baseline(args):
-    """The oracle, unchanged, on a bounded sample of the same workload: a
-    batch of --cpu-sample requests (1024 shared + 128 distinct tokens, one
-    decode step) through the naive tree and float64 full recompute."""
-    from oracle.runner import run_workload
-    from synth import workloads
+def _oracle_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+        return max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
     except Exception:
-        cores = os.cpu_count() or 1
-    wl = workloads.few_shot(batch=args.cpu_sample, decode_steps=1)
-    t0 = time.perf_counter()
-    run_workload(wl, want=lambda kind, rid, step: rid != 0)
-    dt = time.perf_counter() - t0
-    tokens = args.cpu_sample * (128 + 1)
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{args.cpu_sample} few-shot requests (1024 shared + 128 distinct tokens + 1 decode step) "
-                      f"after the warm-up prefix, naive tree + float64 full recompute; {dt:.1f} s"}
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(args):
+    """The oracle, unchanged, on a bounded sample of the same workload
+    (about 10-30 s of CPU work), timed on this host's cores, plus the same
+    kind of sample on one thread.  Tokens/s = attention outputs recomputed
+    (one query row = one token) / oracle wall time (tree work included)."""
+    from synth import workloads
+    cores = _oracle_threads()
+    wl_name = args.workload
+    if wl_name == "few_shot":
+        wl = workloads.few_shot(batch=args.cpu_sample, decode_steps=1)
+        want = lambda kind, rid, step: rid != 0
+        per_output = lambda k: 128 if k[0] == "ext" else 1
+        sample = (f"{args.cpu_sample} few-shot requests (1024 shared + 128 distinct tokens + 1 decode step) after "
+                  f"the warm-up prefix")
+        wl1, want1 = workloads.few_shot(batch=16, decode_steps=1), want
+        sample1 = "16 few-shot requests"
+    elif wl_name == "fork":
+        wl = workloads.fork()
+        want = lambda kind, rid, step: kind == "dec" and step in (0, 127, 255) and (rid - 16) % 8 == 0
+        per_output = lambda k: 1
+        sample = ("fork: the tree over all 16 prompts x 8 branches x 256 steps; attention of one branch per prompt "
+                  "(16) at decode steps 0, 127, 255")
+        wl1 = workloads.fork()
+        want1 = lambda kind, rid, step: kind == "dec" and step == 0 and (rid - 16) % 8 == 0
+        sample1 = "fork tree + 16 branches at step 0"
+    elif wl_name == "long_context":
+        wl = workloads.long_context(decode_steps=1)
+        want = lambda kind, rid, step: kind == "dec" and step == 0 and rid in (1, 32)
+        per_output = lambda k: 1
+        sample = "long context: requests 1 and 32 (32769-key contexts) at decode step 0"
+        wl1 = wl
+        want1 = lambda kind, rid, step: kind == "dec" and step == 0 and rid == 1
+        sample1 = "long context: request 1 at decode step 0"
+    elif wl_name == "chat":
+        wl = workloads.chat()
+        want = lambda kind, rid, step: kind == "dec" and rid % 16 == 0 and step in (0, 64)
+        per_output = lambda k: 1
+        sample = ("chat: the tree and scheduler over all 256 sessions x 4 turns; attention of every 16th request's "
+                  "decode rows at steps 0 and 64")
+        wl1 = wl
+        want1 = lambda kind, rid, step: kind == "dec" and rid % 64 == 0 and step == 0
+        sample1 = "chat tree + every 64th request's decode row at step 0"
+    else:
+        return None
+
+    def run(w, f, threads):
+        from oracle.runner import run_workload
+        import contextlib
+        ctx = contextlib.nullcontext()
+        if threads is not None:
+            from threadpoolctl import threadpool_limits
+            ctx = threadpool_limits(limits=threads)
+        with ctx:
+            t0 = time.perf_counter()
+            tr = run_workload(w, want=f)
+            dt = time.perf_counter() - t0
+        return dt, sum(per_output(k) for k in tr.outputs)
+
+    dt, toks = run(wl, want, None)
+    dt1, toks1 = run(wl1, want1, 1)
+    return {"value": toks / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{sample}; naive tree + float64 full recompute; {toks} tokens in {dt:.1f} s",
+            "one_thread": {"value": toks1 / dt1, "unit": "tokens/s", "cores": 1,
+                           "sample": f"{sample1}; {toks1} tokens in {dt1:.1f} s"}}
+
+
+def ceilings(torch):
+    """Ceilings measured on this GPU in the same run, beside the published
+    peaks: a plain copy (kv_store over 262144 rows of 2 KiB: 1 GiB read and
+    1 GiB written), a read-only stream (torch sums over 2 GiB) and a large
+    bf16 GEMM (torch / hipBLASLt, 8192^3)."""
+    from prefix_shared_kv_rt_amd import binding as Bm
+    dev = torch.device("cuda:0")
+    n, hkv, d = 262144, 8, 128
+    pool_k = torch.empty((n + 1, hkv, d), dtype=torch.bfloat16, device=dev)
+    pool_v = torch.empty_like(pool_k)
+    src_k = torch.randn((n, hkv, d), device=dev).to(torch.bfloat16)
+    src_v = torch.randn((n, hkv, d), device=dev).to(torch.bfloat16)
+    loc = torch.arange(1, n + 1, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream(dev)
+
+    def timed(f, reps):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            f()
+        e1.record(st)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    t_copy = timed(lambda: Bm.kv_store(pool_k, pool_v, src_k, src_v, loc, stream=st), 20)
+    copy_bytes = 4.0 * n * hkv * d * 2
+    # read-only stream: a reduction over both 1 GiB pools
+    t_read = timed(lambda: (pool_k.view(torch.int32).sum(dtype=torch.int64),
+                            pool_v.view(torch.int32).sum(dtype=torch.int64)), 10)
+    read_bytes = 2.0 * pool_k.numel() * 2
+    a = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+    bm = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+    t_mm = timed(lambda: torch.matmul(a, bm), 20)
+    del pool_k, pool_v, src_k, src_v, a, bm
+    torch.cuda.empty_cache()
+    return {"copy_gbs": copy_bytes / t_copy / 1e9, "copy_frac_of_peak": copy_bytes / t_copy / 1e9 / PEAK_HBM_GBS,
+            "read_gbs": read_bytes / t_read / 1e9, "read_frac_of_peak": read_bytes / t_read / 1e9 / PEAK_HBM_GBS,
+            "bf16_gemm_tflops": 2.0 * 8192 ** 3 / t_mm / 1e12,
+            "bf16_gemm_frac_of_peak": 2.0 * 8192 ** 3 / t_mm / 1e12 / PEAK_BF16_TFLOPS,
+            "what": "measured after the timed steps: kv_store copy of 1 GiB (read) + 1 GiB (write); torch integer "
+                    "sums over 2 GiB (read); torch.matmul bf16 8192^3"}
 
 
 def main():
@@ -869,8 +1053,12 @@ def main():
         result = run_decode_graph(args, torch)
     else:
         result = run_decode_bench(args, torch)
-    if not args.no_cpu_baseline and args.workload == "few_shot":
-        result["cpu_baseline"] = cpu_baseline(args)
+    if args.workload != "decode_graph":
+        result["ceilings"] = ceilings(torch)
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(args)
+        if cb is not None:
+            result["cpu_baseline"] = cb
     print(json.dumps(result))
 
 
