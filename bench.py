@@ -73,6 +73,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--time-every", type=int, default=1,
+                    help="few_shot: HIP timing events around the extend launch of every K-th timed step")
     ap.add_argument("--workload", default="few_shot", choices=["few_shot", "long_context", "fork", "chat", "decode_graph"])
     ap.add_argument("--policy", default="fcfs", choices=["fcfs", "lspf"],
                     help="admission order of the chat workload's scheduler")
@@ -185,6 +187,8 @@ class FewShotBench:
         self.dec_bytes = []
         self.host_s = []
         self.step_lens = []
+        self.ext_lens = []     # (pl, el) of the steps whose extend launch carries timing events
+        self.wait_s = []       # host time blocked on a row set's staging (the GPU is behind)
         self.dec_distinct = []
         self.ext_rows = []
 
@@ -322,8 +326,12 @@ class FewShotBench:
         B, S, P0 = self.B, self.SUFFIX, self.PREFIX
         q, k, v, qd, kd, vd = self.inputs[i]
         rs = i % 2
+        waited = 0.0
         if self.copy_mark[rs] is not None:
             self.copy_mark[rs].synchronize()       # host staging of this row set is free again
+            waited = time.perf_counter() - t_host
+            if timed:
+                self.wait_s.append(waited)
         rows = self.rows[rs]
         toks, full = self.tokens[i]
         pl, el, nodes, loc = Bm.rt_admit_batch(self.tree, toks, self.tok_off, self.r2t_host, rows)
@@ -383,20 +391,24 @@ class FewShotBench:
         self.last_prefix_lens = pl
         if timed:
             # flops and bytes follow from (pl, el) after the timed region
-            self.ext_events.append((ev[0], ev[1]))
+            if ev is not None:
+                self.ext_events.append((ev[0], ev[1]))
+                self.ext_lens.append((pl, el))
             self.step_lens.append((pl, el))
-            self.host_s.append(time.perf_counter() - t_host)
+            self.host_s.append(time.perf_counter() - t_host - waited)
         return int(el.sum()) + B
 
     def accounting(self):
-        """Extend flops and decode bytes of every timed step."""
+        """Extend flops of every step whose extend launch was timed; decode
+        bytes of every timed step."""
         P0, S, B = self.PREFIX, self.SUFFIX, self.B
         eb = 1 if self.fp8 else 2
-        for pl, el in self.step_lens:
+        for pl, el in self.ext_lens:
             rows_keys = float(np.sum(pl.astype(np.float64) * el + el.astype(np.float64) * (el + 1) / 2))
             self.flops.append(4.0 * self.D * self.HQ * rows_keys)
-            self.ext_tokens.append(int(el.sum()) + B)
             self.ext_rows.append(int(el.sum()))
+        for pl, el in self.step_lens:
+            self.ext_tokens.append(int(el.sum()) + B)
             self.dec_bytes.append(B * (P0 + S + 1) * (self.HKV * self.D * eb * 2 + 4) + 2 * B * self.HQ * self.D * 2)
             # the prefix once, every request's own tail
             self.dec_distinct.append(P0 * self.HKV * self.D * eb * 2 + B * (S + 1) * (self.HKV * self.D * eb * 2 + 4)
@@ -411,14 +423,20 @@ def run_few_shot(args, torch):
                       shared_decode=(args.decode or "shared") == "shared")
     fb.gen_inputs(n)
     fb.warm_prefix()
+    # Collect before the clock settle: a collector pass between the warm-up
+    # and the timed steps idles the GPU long enough for its clocks to drop.
+    # Disabled until the timed steps end: a pass inside them would stall the
+    # host, not the path.
+    gc.collect()
+    gc.disable()
     fb.settle_clocks()
     for i in range(args.warmup):
         fb.step(i, timed=False)
     fb.stream.synchronize()
     torch.cuda.synchronize()
-    gc.collect()
-    gc.disable()  # a collector pass inside the timed steps would stall the host, not the path
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # timing events around the extend launch of every time_every-th step
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] if k % args.time_every == 0 else None
+           for k in range(args.steps)]
     t0 = time.perf_counter()
     tokens = 0
     for i in range(args.warmup, n):
@@ -477,9 +495,13 @@ def run_few_shot(args, torch):
             # bytes the step must read at least once (prefix once, every tail)
             "decode_distinct_gbs": float(np.mean(fb.dec_distinct)) / dec_avg_s / 1e9,
             "decode_distinct_frac": float(np.mean(fb.dec_distinct)) / dec_avg_s / 1e9 / PEAK_HBM_GBS,
-            # host time to run one step's tree work and enqueue its GPU work
-            # (the step is host-bound when this is near ms_per_step)
+            # host time to run one step's tree work and enqueue its GPU work,
+            # without the time blocked waiting for the GPU to release a row
+            # set's staging (the step is host-bound when this nears
+            # ms_per_step)
             "host_us_per_step": float(np.mean(fb.host_s)) * 1e6,
+            "host_wait_us_per_step": float(np.mean(fb.wait_s)) * 1e6 if fb.wait_s else 0.0,
+            "extend_timed_steps": len(fb.ext_events),
         },
     }
     return result, fb
@@ -691,13 +713,13 @@ def run_decode_bench(args, torch):
     db = DecodeBench(args.workload, torch, Bm, torch_gen, n, kv_dtype=args.kv_dtype,
                      shared_decode=(args.decode or "shared") == "shared")
     db.setup()
+    gc.collect()     # before the clock settle (see run_few_shot)
+    gc.disable()
     db.settle_clocks()
     for s in range(args.warmup):
         db.step(s, timed=False)
     db.stream.synchronize()
     torch.cuda.synchronize()
-    gc.collect()
-    gc.disable()
     t0 = time.perf_counter()
     tokens = 0
     for s in range(args.warmup, n):

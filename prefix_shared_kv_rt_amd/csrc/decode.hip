@@ -21,15 +21,18 @@
 //  * bf16: the G x 16-key score tile and the PV update are MFMA
 //    contractions (16x16x32 for Q K^T, 16x16x16 for P V) whose operands are
 //    loaded straight from HBM in the MFMA lane layout: K rows as 64-byte
-//    runs, V rows as 128-byte runs of 4 dims per lane (the PV contraction
-//    dimension is the key, so each lane takes 4 dims of 4 keys and the dims
-//    are regrouped in registers).
+//    runs, V rows whole (each lane takes D/16 consecutive dims, 16 bytes at
+//    D = 128, of 4 keys: the PV contraction dimension is the key, and the
+//    dims are regrouped in registers).
 //  * fp32 inputs take a plain VALU path (one lane per dim, wave-wide dot
 //    products); it exists for full-precision checks, not for speed.
 
 #include <math.h>
 
+#include <stdlib.h>
+
 #include <algorithm>
+#include <type_traits>
 #include <mutex>
 #include <string>
 
@@ -46,7 +49,13 @@ struct DecodePlan {
   int chunk;   // keys per chunk (multiple of 16, at most kMaxChunk)
 };
 
-constexpr int kMaxChunk = 2048;      // slot indices of one chunk staged in LDS (8 KiB)
+// Slot indices of one chunk are staged in LDS (16 KiB at 4096 keys).  On
+// MI355X, all-private decode of 32 x 16385 keys (Hkv 8, D 128, bf16) takes
+// 374 us with chunks of up to 4096 keys (6 per request and head) against
+// 399 us with up to 2048 (9): fewer, longer streams per wave read HBM closer
+// to a plain streaming read of the same bytes (6.3 TB/s).
+constexpr int kMaxChunk = 4096;
+constexpr int64_t kMaxKvLen = 2097152;  // longest context a decode call accepts
 // FP8 pools move half the bytes per key, so a wave streams a chunk's keys
 // with less in flight; shorter chunks (more items) keep HBM busier on long
 // contexts (32 x 32897 keys: 24 chunks in 327 us against 17 in 358 us).
@@ -118,15 +127,17 @@ SharedPlan plan_shared(int32_t batch, int32_t Hq, int32_t Hkv, int32_t n_groups,
 // same (s, h), so their concurrent waves on one XCD meet those rows in L2.
 // One 16-key block's operands as loaded: bf16 pools hold them as the MFMA
 // takes them; FP8 pools hold half the bytes, widened to bf16 when consumed.
+// A lane's V piece: D/16 consecutive elements of one row (16 bytes for bf16
+// at D = 128).
+template <int D, bool KV8> struct VPiece;
+template <> struct VPiece<128, false> { using T = u32x4; };
+template <> struct VPiece<64, false> { using T = u32x2; };
+template <> struct VPiece<128, true> { using T = u32x2; };
+template <> struct VPiece<64, true> { using T = uint32_t; };
 template <int D, bool KV8>
 struct DecBlock {
-  u32x4 k[D / 32];        // K operand rows: key kb + col, dims 32*ks + 8*grp .. +7
-  u32x2 v[D / 64][4];     // V rows kb + 4*grp + t, dims 64*h + 4*col .. +3
-};
-template <int D>
-struct DecBlock<D, true> {
-  u32x2 k[D / 32];
-  uint32_t v[D / 64][4];
+  typename std::conditional<KV8, u32x2, u32x4>::type k[D / 32];  // key kb + col, dims 32*ks + 8*grp .. +7
+  typename VPiece<D, KV8>::T v[4];  // V row kb + 4*grp + t, dims (D/16)*col .. +D/16-1
 };
 
 template <int D, bool KV8>
@@ -141,7 +152,7 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
   // go to split slots s_off .. s_off + S - 1 of S_total (default: S).
   if (S_total == 0) S_total = S;
   constexpr int KS = D / 32;      // 32-dim steps of the score contraction
-  constexpr int VH = D / 64;      // 64-dim halves of the PV update
+  constexpr int VW = D / 16;      // V elements per lane and key; also the PV update's 16-row tiles
   constexpr int EB = KV8 ? 1 : 2; // bytes per pool element
   __shared__ int32_t s_idx[kMaxChunk];
 
@@ -166,7 +177,7 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
     const int end = min(kv_len, start + chunk);
     const int32_t* idx_row = req_to_token + int64_t(rpi ? rpi[b] : b) * stride;
     const char* kbase = k_pool + (int64_t(kvh) * D + 8 * grp) * EB;
-    const char* vbase = v_pool + (int64_t(kvh) * D + 4 * col) * EB;
+    const char* vbase = v_pool + (int64_t(kvh) * D + VW * col) * EB;
 
     // Slot indices of the whole chunk into this wave's LDS, once.
     __syncthreads();  // the previous item's index reads are complete
@@ -184,9 +195,9 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
       for (int ks = 0; ks < KS; ++ks) qop[ks] = as_bf16x8(u32x4{0, 0, 0, 0});
     }
 
-    floatx4 o[VH * 4];
+    floatx4 o[VW];
 #pragma unroll
-    for (int i = 0; i < VH * 4; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < VW; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f;
 
     // Keys past `end` are clamped to the chunk's last key (masked below), so
@@ -204,14 +215,8 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int kv = min(kb + 4 * grp + t, end - 1) - start;
-        const char* vp = vbase + int64_t(uint32_t(s_idx[kv])) * row_bytes;
-#pragma unroll
-        for (int h = 0; h < VH; ++h) {
-          if constexpr (KV8)
-            blk.v[h][t] = ld4(vp + 64 * h);
-          else
-            blk.v[h][t] = ld8(vp + 128 * h);
-        }
+        blk.v[t] = *reinterpret_cast<const typename VPiece<D, KV8>::T*>(
+            vbase + int64_t(uint32_t(s_idx[kv])) * row_bytes);
       }
     };
 
@@ -238,7 +243,7 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
         const float alpha = __builtin_amdgcn_exp2f(m - m_new);
         l *= alpha;
 #pragma unroll
-        for (int i2 = 0; i2 < VH * 4; ++i2) o[i2] *= alpha;
+        for (int i2 = 0; i2 < VW; ++i2) o[i2] *= alpha;
         m = m_new;
       }
       float p[4];
@@ -246,20 +251,31 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
       for (int v = 0; v < 4; ++v) p[v] = __builtin_amdgcn_exp2f(sv[v] - m);
       l += (p[0] + p[1]) + (p[2] + p[3]);
       const bf16x4 pop = as_bf16x4(u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
+      // PV update: tile r (0 .. VW-1) has rows i = dims VW*i + r; its A operand
+      // takes element r of the four keys' pieces, as bf16 pairs.
+      constexpr int NW = VW / 2;
+      uint32_t w[4][NW];
 #pragma unroll
-      for (int h = 0; h < VH; ++h) {
-        u32x2 w[4];
+      for (int t = 0; t < 4; ++t) {
+        if constexpr (KV8 && D == 128) {
+          const u32x4 x = __builtin_bit_cast(u32x4, fp8x8_to_bf16x8(cur.v[t]));
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if constexpr (KV8)
-            w[t] = fp8x4_to_bf16x4(cur.v[h][t]);
-          else
-            w[t] = cur.v[h][t];
+          for (int j = 0; j < NW; ++j) w[t][j] = x[j];
+        } else if constexpr (KV8) {
+          const u32x2 x = fp8x4_to_bf16x4(cur.v[t]);
+#pragma unroll
+          for (int j = 0; j < NW; ++j) w[t][j] = x[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < NW; ++j) w[t][j] = cur.v[t][j];
         }
-        o[h * 4 + 0] = mfma_16x16x16(as_bf16x4(u32x2{pack_lo16(w[0].x, w[1].x), pack_lo16(w[2].x, w[3].x)}), pop, o[h * 4 + 0]);
-        o[h * 4 + 1] = mfma_16x16x16(as_bf16x4(u32x2{pack_hi16(w[0].x, w[1].x), pack_hi16(w[2].x, w[3].x)}), pop, o[h * 4 + 1]);
-        o[h * 4 + 2] = mfma_16x16x16(as_bf16x4(u32x2{pack_lo16(w[0].y, w[1].y), pack_lo16(w[2].y, w[3].y)}), pop, o[h * 4 + 2]);
-        o[h * 4 + 3] = mfma_16x16x16(as_bf16x4(u32x2{pack_hi16(w[0].y, w[1].y), pack_hi16(w[2].y, w[3].y)}), pop, o[h * 4 + 3]);
+      }
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        o[2 * j] = mfma_16x16x16(as_bf16x4(u32x2{pack_lo16(w[0][j], w[1][j]), pack_lo16(w[2][j], w[3][j])}), pop,
+                                 o[2 * j]);
+        o[2 * j + 1] = mfma_16x16x16(
+            as_bf16x4(u32x2{pack_hi16(w[0][j], w[1][j]), pack_hi16(w[2][j], w[3][j])}), pop, o[2 * j + 1]);
       }
     };
 
@@ -286,14 +302,14 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
         ws_ml[part * 2 + 1] = l;
       }
       float* acc = ws_acc + part * D;
-      // Tile (h, r) row i holds dim 64h + 4i + r; this lane holds rows i = 4*grp + v.
+      // This lane holds rows i = 4*grp + v of every tile r: dims VW*i + r.
 #pragma unroll
-      for (int h = 0; h < VH; ++h)
+      for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          floatx4 w = {o[h * 4 + 0][v], o[h * 4 + 1][v], o[h * 4 + 2][v], o[h * 4 + 3][v]};
+        for (int r4 = 0; r4 < VW / 4; ++r4) {
+          floatx4 w = {o[4 * r4 + 0][v], o[4 * r4 + 1][v], o[4 * r4 + 2][v], o[4 * r4 + 3][v]};
           if constexpr (KV8) w *= v_scale;
-          *reinterpret_cast<floatx4*>(acc + 64 * h + 16 * grp + 4 * v) = w;
+          *reinterpret_cast<floatx4*>(acc + VW * (4 * grp + v) + 4 * r4) = w;
         }
     }
   }
@@ -355,25 +371,56 @@ __global__ void __launch_bounds__(64) decode_split_f32(
 }
 
 // -------------------------------------------------------------- combine --
+// One wave per (request, query head): merges the S split partials exactly,
+// out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
+// Lane s (mod 64) reads partial s's (m, l), so the max and the weights take
+// wave reductions instead of a loop; the accumulators are then read eight
+// partials at a time with every load issued before the multiply-adds, so a
+// long split costs a few memory round trips, not one per partial.
 template <int D, bool BF16>
 __global__ void __launch_bounds__(64) decode_combine(const float* __restrict__ ws_acc,
                                                      const float* __restrict__ ws_ml, int S,
                                                      void* __restrict__ out) {
   constexpr int PER = D / 64;
+  constexpr int U = 8;  // partials per batch of loads
   const int lane = threadIdx.x;
   const int64_t bh = blockIdx.x;  // b * Hq + h
   const float* ml = ws_ml + bh * S * 2;
+  const float* acc_s = ws_acc + bh * S * D + lane;
   float mmax = -INFINITY;
-  for (int s = 0; s < S; ++s) mmax = fmaxf(mmax, ml[2 * s]);
+  for (int s = lane; s < S; s += 64) mmax = fmaxf(mmax, ml[2 * s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mmax = fmaxf(mmax, shfl_xor(mmax, off));
   float L = 0.f, acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float w = exp2f(ml[2 * s] - mmax);  // empty chunks have m = -inf -> 0
-    L = fmaf(w, ml[2 * s + 1], L);
-    const float* a = ws_acc + (bh * S + s) * D;
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    // weight of partial s0 + lane; empty chunks have m = -inf -> 0
+    const int n = min(64, S - s0);
+    const float w = lane < n ? exp2f(ml[2 * (s0 + lane)] - mmax) : 0.f;
+    float lw = lane < n ? w * ml[2 * (s0 + lane) + 1] : 0.f;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, a[lane + 64 * i], acc[i]);
+    for (int off = 32; off >= 1; off >>= 1) lw += shfl_xor(lw, off);
+    L += lw;
+    int j = 0;
+    for (; j + U <= n; j += U) {
+      float a[U][PER];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) a[u][i] = acc_s[int64_t(s0 + j + u) * D + 64 * i];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j + u));
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] = fmaf(wu, a[u][i], acc[i]);
+      }
+    }
+    for (; j < n; ++j) {
+      const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] = fmaf(wu, acc_s[int64_t(s0 + j) * D + 64 * i], acc[i]);
+    }
   }
   const float inv = 1.f / L;
 #pragma unroll
@@ -409,10 +456,13 @@ int resident_waves() {
 constexpr int kModeFp8Kv = 100;
 
 template <int D>
-void launch_decode(const void* q, void* o, const void* k_pool, const void* v_pool, const int32_t* r2t,
+hipError_t launch_decode(const void* q, void* o, const void* k_pool, const void* v_pool, const int32_t* r2t,
                    int64_t stride, const int32_t* rpi, const int32_t* plens, int B, int Hq, int Hkv,
                    DecodePlan pl, float scale_log2, float v_scale, int mode, float* ws_acc, float* ws_ml,
-                   hipStream_t st, const int32_t* key_start = nullptr, int s_off = 0, int S_total = 0) {
+                   hipStream_t st, const int32_t* key_start = nullptr, int s_off = 0, int S_total = 0,
+                   hipEvent_t combine_after = nullptr) {
+  // combine_after (optional): work on another stream that also writes
+  // partials; the combine waits for it.  Returns the wait's status.
   const int G = Hq / Hkv;
   if (S_total == 0) S_total = pl.splits;
   if (mode == RT_BF16 || mode == kModeFp8Kv) {
@@ -428,6 +478,10 @@ void launch_decode(const void* q, void* o, const void* k_pool, const void* v_poo
                          (const char*)k_pool, (const char*)v_pool, r2t, stride, rpi, plens, B, Hq, Hkv, G, pl.splits,
                          pl.chunk, scale_log2, v_scale, ws_acc, ws_ml, key_start, s_off, S_total);
     }
+    if (combine_after) {
+      const hipError_t we = hipStreamWaitEvent(st, combine_after, 0);
+      if (we != hipSuccess) return we;
+    }
     hipLaunchKernelGGL((decode_combine<D, true>), dim3(uint32_t(int64_t(B) * Hq)), dim3(64), 0, st, ws_acc,
                        ws_ml, S_total, o);
   } else {
@@ -438,6 +492,7 @@ void launch_decode(const void* q, void* o, const void* k_pool, const void* v_poo
     hipLaunchKernelGGL((decode_combine<D, false>), dim3(uint32_t(int64_t(B) * Hq)), dim3(64), 0, st, ws_acc,
                        ws_ml, pl.splits, o);
   }
+  return hipSuccess;
 }
 
 int decode_entry(const char* name, const void* q, void* o, const void* k_pool, const void* v_pool,
@@ -450,7 +505,7 @@ int decode_entry(const char* name, const void* q, void* o, const void* k_pool, c
       (head_dim != 64 && head_dim != 128) || max_kv_len < 1 || req_to_token_stride < max_kv_len ||
       !(sm_scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
     return rt::fail(RT_ERR_INVALID, fn + ": bad shape, stride or scale");
-  if (int64_t(max_kv_len) > int64_t(kMaxChunk) * 1024)
+  if (int64_t(max_kv_len) > kMaxKvLen)
     return rt::fail(RT_ERR_INVALID, fn + ": max_kv_len above 2097152");
   if (mode != RT_F32 && num_q_heads / num_kv_heads > 16)
     return rt::fail(RT_ERR_INVALID, fn + ": the bf16 path supports at most 16 query heads per KV head");
@@ -553,6 +608,62 @@ void* scratch_on_device(const char* name) {
   return g_scratch_ptr[dev];
 }
 
+// The shared-prefix decode runs its shared pass (MFMA-bound) on a second
+// stream of the library's, beside the private split (HBM-bound) on the
+// caller's stream, when the private tails are long enough to hide it: each
+// hop between the two hardware queues costs about 10 us on MI355X, which
+// only pays when the split itself is long (32 requests x 16384 private
+// keys: 421 us against 437 us on one stream; few-shot and fork batches,
+// whose splits take under 10 us, measured slower with the hops).  Each
+// device gets one such stream and a fork and a join event, made on first
+// use.  The mutex keeps one call's record/wait sequence whole when several
+// host threads call at once.
+// The threshold (K/V bytes of the private tails) can be set per call through
+// the environment variable RADIXRT_FORK_MIN_BYTES (0: always two streams).
+constexpr int64_t kForkMinPrivateBytes = int64_t(128) << 20;
+int64_t fork_min_private_bytes() {
+  const char* e = getenv("RADIXRT_FORK_MIN_BYTES");
+  if (!e || !*e) return kForkMinPrivateBytes;
+  char* end = nullptr;
+  const long long v = strtoll(e, &end, 10);
+  return (end && *end == 0 && v >= 0) ? int64_t(v) : kForkMinPrivateBytes;
+}
+struct ForkJoin {
+  hipStream_t aux = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_fj_mu;
+ForkJoin g_fj[kMaxDevices];
+
+// The current device's fork/join set, or nullptr (error recorded).  Called
+// with g_fj_mu held.
+ForkJoin* fork_join_on_device(const std::string& name) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    rt::fail(RT_ERR_HIP, name + ": no usable current device");
+    return nullptr;
+  }
+  ForkJoin& f = g_fj[dev];
+  if (!f.aux) {
+    hipStream_t aux = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&aux, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&b, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (b) (void)hipEventDestroy(b);
+      if (a) (void)hipEventDestroy(a);
+      if (aux) (void)hipStreamDestroy(aux);
+      rt::fail(RT_ERR_HIP, name + ": second stream: " + hipGetErrorString(e));
+      return nullptr;
+    }
+    f.fork = a;
+    f.join = b;
+    f.aux = aux;
+  }
+  return &f;
+}
+
 }  // namespace
 
 extern "C" int radix_decode_attention_noalloc(const void* q, void* o, const void* k_pool, const void* v_pool,
@@ -593,7 +704,7 @@ int shared_entry(const char* name, const void* q, void* o, const void* k_pool, c
       int64_t(req_to_token_stride) < int64_t(max_shared_len) + max_private_len || !(sm_scale > 0.f) ||
       !(k_scale > 0.f) || !(v_scale > 0.f))
     return rt::fail(RT_ERR_INVALID, fn + ": bad shape, count, stride or scale");
-  if (int64_t(max_shared_len) + max_private_len > int64_t(kMaxChunk) * 1024)
+  if (int64_t(max_shared_len) + max_private_len > kMaxKvLen)
     return rt::fail(RT_ERR_INVALID, fn + ": context above 2097152");
   if (batch == 0) return RT_OK;
   if (!q || !o || !k_pool || !v_pool || !req_to_token || !prefix_lens || !shared_lens || !group_start ||
@@ -609,22 +720,48 @@ int shared_entry(const char* name, const void* q, void* o, const void* k_pool, c
   float* ws_ml = ws_acc + int64_t(batch) * num_q_heads * sp.total() * head_dim;
   const float scale_log2 = sm_scale * k_scale * kLog2e;
   hipStream_t st = (hipStream_t)stream;
-  if (sp.n_a > 0) {
+  // Shared pass on the caller's stream, or, for long private tails, on the
+  // library's second stream, forked from and joined back into the caller's:
+  // the caller's later work still follows all of it.
+  std::unique_lock<std::mutex> lock(g_fj_mu, std::defer_lock);
+  hipEvent_t join = nullptr;
+  const int64_t private_bytes =
+      int64_t(batch) * max_private_len * num_kv_heads * head_dim * (kv8 ? 1 : 2) * 2;
+  if (sp.n_a > 0 && private_bytes < fork_min_private_bytes()) {
     const int rc = rt::launch_extend_shared_part(q, k_pool, v_pool, req_to_token, req_to_token_stride,
                                                  req_pool_indices, shared_lens, group_start, n_groups, max_group_size,
                                                  sp.n_a, sp.chunk_a, sp.total(), num_q_heads, num_kv_heads, head_dim,
                                                  scale_log2, v_scale, kv8, ws_acc, ws_ml, stream);
     if (rc != RT_OK) return rc;
+  } else if (sp.n_a > 0) {
+    lock.lock();
+    ForkJoin* fj = fork_join_on_device(fn);
+    if (!fj) return RT_ERR_HIP;
+    hipError_t e = hipEventRecord(fj->fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(fj->aux, fj->fork, 0);
+    if (e != hipSuccess) return rt::fail(RT_ERR_HIP, fn + " fork: " + hipGetErrorString(e));
+    const int rc = rt::launch_extend_shared_part(q, k_pool, v_pool, req_to_token, req_to_token_stride,
+                                                 req_pool_indices, shared_lens, group_start, n_groups, max_group_size,
+                                                 sp.n_a, sp.chunk_a, sp.total(), num_q_heads, num_kv_heads, head_dim,
+                                                 scale_log2, v_scale, kv8, ws_acc, ws_ml, fj->aux);
+    // the join is recorded even after a failed launch, so the caller's
+    // stream never waits on a fork that has no join
+    e = hipEventRecord(fj->join, fj->aux);
+    if (rc != RT_OK) return rc;
+    if (e != hipSuccess) return rt::fail(RT_ERR_HIP, fn + " join: " + hipGetErrorString(e));
+    join = fj->join;
   }
   const int mode = kv8 ? kModeFp8Kv : RT_BF16;
+  hipError_t we;
   if (head_dim == 128)
-    launch_decode<128>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
+    we = launch_decode<128>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
                        batch, num_q_heads, num_kv_heads, sp.b, scale_log2, v_scale, mode, ws_acc, ws_ml, st,
-                       shared_lens, sp.n_a, sp.total());
+                       shared_lens, sp.n_a, sp.total(), join);
   else
-    launch_decode<64>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
+    we = launch_decode<64>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
                       batch, num_q_heads, num_kv_heads, sp.b, scale_log2, v_scale, mode, ws_acc, ws_ml, st,
-                      shared_lens, sp.n_a, sp.total());
+                      shared_lens, sp.n_a, sp.total(), join);
+  if (we != hipSuccess) return rt::fail(RT_ERR_HIP, fn + " join wait: " + hipGetErrorString(we));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return rt::fail(RT_ERR_HIP, fn + " launch: " + hipGetErrorString(e));
   return RT_OK;

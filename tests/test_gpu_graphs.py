@@ -1,13 +1,16 @@
-"""Decode steps replayed from captured HIP graphs: every replay against an
-eager launch of the same step and against a float32 reference gathered from
-the pool, with eager work and synchronisation between replays; padding to
-the captured sizes; fallback beyond the largest size."""
+"""Decode steps replayed from captured HIP graphs: every replay against the
+same decode launched eagerly over the graph's own buffers (bit for bit),
+against the float64 oracle over the pool's contents, and against the
+runtime's own eager step, with eager work and synchronisation between
+replays; padding to the captured sizes; fallback beyond the largest size."""
 
 import numpy as np
 import pytest
 import torch
 
+from oracle.attention import causal_attention
 from oracle.fp8 import dequantize, store_codes
+from prefix_shared_kv_rt_amd import binding as B
 from prefix_shared_kv_rt_amd.graphs import DecodeGraphs, default_batch_sizes
 from prefix_shared_kv_rt_amd.runtime import RadixRuntime
 
@@ -42,23 +45,40 @@ def _runtime_fp8(seed, scales):
     return rt
 
 
-def _reference(rt, rows, positions, q):
-    """float32 decode attention gathered through the device slot table (for
-    FP8 pools: over the values the stored codes stand for)."""
+def _oracle(rt, rows, positions, q):
+    """The float64 oracle's decode attention over the K/V gathered through
+    the device slot table (for FP8 pools: the values the stored codes stand
+    for)."""
     r2t = rt.r2t_dev.cpu().numpy()
     if rt.kv_fp8_scales:
-        kp = torch.from_numpy(dequantize(rt.k_pool.cpu().numpy(), rt.kv_fp8_scales[0])).float()
-        vp = torch.from_numpy(dequantize(rt.v_pool.cpu().numpy(), rt.kv_fp8_scales[1])).float()
+        kp = dequantize(rt.k_pool.cpu().numpy(), rt.kv_fp8_scales[0])
+        vp = dequantize(rt.v_pool.cpu().numpy(), rt.kv_fp8_scales[1])
     else:
-        kp, vp = rt.k_pool.float().cpu(), rt.v_pool.float().cpu()
+        kp, vp = rt.k_pool.float().cpu().numpy(), rt.v_pool.float().cpu().numpy()
+    qh = q.float().cpu().numpy().astype(np.float64)
     out = []
     for i, (r, p) in enumerate(zip(rows, positions)):
-        sl = torch.from_numpy(r2t[r, :p + 1].astype(np.int64))
-        k = kp[sl].repeat_interleave(HQ // HKV, dim=1).permute(1, 0, 2)   # [Hq, L, D]
-        v = vp[sl].repeat_interleave(HQ // HKV, dim=1).permute(1, 0, 2)
-        s = torch.einsum("hd,hld->hl", q[i].float().cpu(), k) * rt.sm_scale
-        out.append(torch.einsum("hl,hld->hd", torch.softmax(s, -1), v))
-    return torch.stack(out)
+        sl = r2t[r, :p + 1].astype(np.int64)
+        out.append(causal_attention(qh[i:i + 1], kp[sl].astype(np.float64), vp[sl].astype(np.float64),
+                                    np.array([p]), rt.sm_scale)[0])
+    return np.stack(out)
+
+
+def _eager_over_graph_buffers(rt, graphs, n):
+    """The decode attention a replay of n requests ran (padded batch, the
+    graphs' full context length), launched eagerly into a fresh output."""
+    bs = graphs.padded_size(n)
+    o = torch.full_like(graphs.o[:bs], float("nan"))
+    ws = torch.empty_like(graphs.ws)
+    rows, pos = graphs.idx[0, :bs], graphs.idx[1, :bs]
+    if rt.kv_fp8_scales:
+        B.radix_decode_attention_fp8kv(graphs.q[:bs], o, rt.k_pool, rt.v_pool, rt.r2t_dev, rows, pos, graphs.max_kv,
+                                       rt.sm_scale, ws, *rt.kv_fp8_scales, stream=rt.stream)
+    else:
+        B.radix_decode_attention(graphs.q[:bs], o, rt.k_pool, rt.v_pool, rt.r2t_dev, rows, pos, graphs.max_kv,
+                                 rt.sm_scale, ws, stream=rt.stream)
+    rt.stream.synchronize()
+    return o[:n]
 
 
 def test_default_sizes_follow_the_handbook_list():
@@ -85,11 +105,16 @@ def test_graph_replays_match_eager_and_reference(pool):
         rt.stream.synchronize()
         # eager work between replays
         _ = (torch.randn(1024, device="cuda") * 2).sum().item()
-        out = graphs.run(rows, positions, slots, q, k, v).float()
+        out_bf16 = graphs.run(rows, positions, slots, q, k, v)
         rt.stream.synchronize()
+        out = out_bf16.float()
         assert graphs.replays == trial + 1
-        ref = _reference(rt, rows, positions, q)
-        assert (out.cpu() - ref).abs().max().item() <= 2e-2
+        # the same launches eagerly: bit for bit
+        again = _eager_over_graph_buffers(rt, graphs, n)
+        assert torch.equal(out_bf16.view(torch.int16), again.view(torch.int16))
+        want = _oracle(rt, rows, positions, q)
+        assert np.abs(out.cpu().numpy() - want).max() <= 2e-2
+        # the runtime's eager step (its own split plan): equal up to rounding
         assert (out - eager).abs().max().item() <= 2e-2
     # past the largest captured size: the caller falls back to eager
     n = 17

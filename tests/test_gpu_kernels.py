@@ -140,6 +140,10 @@ DECODE_CASES = [
     ([5000, 777, 3333], 64, 8, 128),
     ([40, 600, 1200], 16, 16, 64),
     ([513, 1024, 31], 8, 1, 128),
+    # 1536 (request, KV head) units: one chunk of up to 4096 keys each (the
+    # longest the plan makes), then two of 4000, ragged last blocks
+    ([4095, 4000, 2100] + [1 + (7 * i) % 40 for i in range(93)], 64, 16, 128),
+    ([7999, 4095, 17] + [3 + (5 * i) % 29 for i in range(189)], 32, 8, 64),
 ]
 
 

@@ -96,10 +96,22 @@ def _run_plain(case, q, hq, hkv, d, fp8=None):
     return o
 
 
+@pytest.fixture(params=["one stream", "two streams"])
+def streams(request, monkeypatch):
+    """The shared pass on the caller's stream (the default below 128 MiB of
+    private K/V, which every case here is), or forked onto the library's
+    second stream (forced through RADIXRT_FORK_MIN_BYTES=0)."""
+    if request.param == "two streams":
+        monkeypatch.setenv("RADIXRT_FORK_MIN_BYTES", "0")
+    else:
+        monkeypatch.delenv("RADIXRT_FORK_MIN_BYTES", raising=False)
+    return request.param
+
+
 @pytest.mark.parametrize("ci", range(len(CASES)))
-def test_shared_decode_matches_oracle_and_plain_decode(ci):
+def test_shared_decode_matches_oracle_and_plain_decode(ci, streams):
     groups, hq, hkv, d = CASES[ci]
-    print(f"shared decode case {ci}: {len(groups)} groups, hq={hq} hkv={hkv} d={d}", flush=True)
+    print(f"shared decode case {ci} ({streams}): {len(groups)} groups, hq={hq} hkv={hkv} d={d}", flush=True)
     rng = np.random.default_rng(900 + ci)
     case = make_shared_case(rng, groups, hq, hkv, d)
     case["kp"], case["vp"] = to_dev(case["kpool"], "bf16"), to_dev(case["vpool"], "bf16")
@@ -153,3 +165,53 @@ def test_shared_decode_rejects_bad_arguments():
             B.radix_decode_attention_shared(q, q, kp, kp, r2t, None, z, z, gs, mg, ms, mp, 0.125, ws)
     with pytest.raises(B.RadixRTError):  # workspace too small
         B.radix_decode_attention_shared(q, q, kp, kp, r2t, None, z, z, gs, 4, 4, 4, 0.125, ws[:16])
+
+
+@pytest.mark.parametrize("ci", [0, 2])
+def test_shared_decode_replays_from_a_captured_graph(ci, streams):
+    """Captured in a HIP graph, the shared decode (on one stream, or with its
+    shared pass forked onto the library's second stream and joined back)
+    replays bit for bit what the eager call computes, with eager work and
+    synchronisation between replays; the eager call matches the oracle."""
+    groups, hq, hkv, d = CASES[ci]
+    print(f"shared decode graph case {ci} ({streams})", flush=True)
+    rng = np.random.default_rng(990 + ci)
+    case = make_shared_case(rng, groups, hq, hkv, d)
+    kp, vp = to_dev(case["kpool"], "bf16"), to_dev(case["vpool"], "bf16")
+    n = len(case["prefix_lens"])
+    q_host = host_values(rng, (n, hq, d), "bf16")
+    q = to_dev(q_host, "bf16")
+    dev = [i32(case[k]) for k in ("r2t", "rows", "prefix_lens", "shared_lens", "group_start")]
+    ws = torch.empty(B.radix_decode_shared_workspace_bytes(n, hq, hkv, d, len(case["group_start"]) - 1,
+                                                           case["max_group"], case["max_shared"],
+                                                           case["max_private"]), dtype=torch.uint8, device="cuda")
+
+    def call(o):
+        B.radix_decode_attention_shared(q, o, kp, vp, *dev, case["max_group"], case["max_shared"],
+                                        case["max_private"], 1.0 / np.sqrt(d), ws)
+
+    eager = torch.full_like(q, float("nan"))
+    call(eager)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for b in range(n):
+        pos = int(case["prefix_lens"][b])
+        want = oracle_rows(q_host[b:b + 1], case["k"][b], case["v"][b], np.array([pos]), 1.0 / np.sqrt(d))
+        worst = max(worst, max_err(eager[b:b + 1], want))
+    assert worst <= TOL
+    out = torch.full_like(q, float("nan"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out)          # warm-up on the capturing stream
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        call(out)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        _ = (torch.randn(4096, device="cuda") * 2).sum().item()   # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
