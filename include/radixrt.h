@@ -166,10 +166,12 @@ int rt_alloc_with_evict(rt_tree* tree, int32_t n, int32_t* out_slots, int32_t* o
  * must hold that request's slot).  Every slot is written into its row and,
  * concatenated in run order, into host out_slots (out_cap entries).
  * *out_evicted (may be NULL) = tokens evicted.  With one-slot pages this is
- * rt_alloc_with_evict of all positions, in order. */
+ * rt_alloc_with_evict of all positions, in order.  The table has num_rows
+ * rows: a row outside [0, num_rows) or a run past the stride is
+ * RT_ERR_INVALID before anything is allocated. */
 int rt_alloc_positions(rt_tree* tree, int32_t n_runs, const int32_t* rows, const int32_t* first_positions,
-                       const int32_t* counts, int32_t* req_to_token, int64_t stride, int32_t* out_slots,
-                       int64_t out_cap, int32_t* out_evicted);
+                       const int32_t* counts, int32_t* req_to_token, int64_t stride, int32_t num_rows,
+                       int32_t* out_slots, int64_t out_cap, int32_t* out_evicted);
 
 /* Tokens held by unlocked nodes / by locked nodes (root excluded). */
 int64_t rt_evictable_size(const rt_tree* tree);
@@ -188,7 +190,9 @@ int rt_tree_dump(const rt_tree* tree, char* buf, int64_t cap, int64_t* out_len);
  * Compositions of the calls above for a whole batch, so that a batch costs
  * one crossing of the ABI.  Request i's tokens are
  * tokens[token_offsets[i] .. token_offsets[i+1]) (host).  Row r of the slot
- * table is req_to_token[r * stride .. r * stride + stride) (host). */
+ * table is req_to_token[r * stride .. r * stride + stride) (host), for r in
+ * [0, num_rows); every call checks each rows[i] against num_rows before it
+ * touches the table (RT_ERR_INVALID). */
 
 /* For i in order: rt_match_prefix, rt_lock; then one rt_alloc_positions of
  * positions prefix_len_i .. len_i - 1 of every request (with one-slot
@@ -200,7 +204,7 @@ int rt_tree_dump(const rt_tree* tree, char* buf, int64_t cap, int64_t* out_len);
  * matches' splits and stamps remain).  RT_ERR_INVALID if a request is
  * longer than stride. */
 int rt_admit_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_offsets,
-                   int32_t n, int32_t* req_to_token, int64_t stride, const int32_t* rows,
+                   int32_t n, int32_t* req_to_token, int64_t stride, int32_t num_rows, const int32_t* rows,
                    int32_t* prefix_lens, int32_t* extend_lens, rt_node* nodes,
                    int32_t* out_cache_loc, int64_t out_cache_cap, int64_t* out_num_new);
 
@@ -209,7 +213,7 @@ int rt_admit_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_of
  * req_to_token[rows[i] * stride + positions[i]] = slot i (host).
  * out_cache_loc (host, n) receives the slots. */
 int rt_decode_slots_batch(rt_tree* tree, int32_t n, const int32_t* rows, const int32_t* positions,
-                          int32_t* req_to_token, int64_t stride, int32_t* out_cache_loc);
+                          int32_t* req_to_token, int64_t stride, int32_t num_rows, int32_t* out_cache_loc);
 
 /* Finish requests: for i in order, rt_insert of the whole pages of tokens_i
  * (the first len_i - len_i % page_size) with row rows[i] of req_to_token,
@@ -219,7 +223,7 @@ int rt_decode_slots_batch(rt_tree* tree, int32_t n, const int32_t* rows, const i
  * rt_unlock(nodes[i]).  *out_freed (may be NULL) = total slots passed to
  * those frees. */
 int rt_finish_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_offsets,
-                    int32_t n, const int32_t* req_to_token, int64_t stride, const int32_t* rows,
+                    int32_t n, const int32_t* req_to_token, int64_t stride, int32_t num_rows, const int32_t* rows,
                     const int32_t* prefix_lens, const rt_node* nodes, int64_t* out_freed);
 
 /* -------------------------------------------------------------- device --

@@ -12,6 +12,12 @@ import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libradixrt.so")
+# Checking builds: RADIXRT_LIB names another build of the library to load;
+# with RADIXRT_HOST_ONLY=1 it may hold only the host half (tree, pool, batch
+# helpers), and the device entry points are left unbound (calling one fails).
+if os.environ.get("RADIXRT_LIB"):
+    LIB_PATH = os.environ["RADIXRT_LIB"]
+_HOST_ONLY = os.environ.get("RADIXRT_HOST_ONLY") == "1"
 
 RT_OK, RT_ERR_INVALID, RT_ERR_OOM, RT_ERR_LOCKED, RT_ERR_HIP = 0, -1, -2, -3, -4
 RT_F32, RT_BF16 = 0, 1
@@ -69,7 +75,7 @@ def lib():
             "rt_pool_create_paged": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_vp)]),
             "rt_pool_page_size": (ctypes.c_int32, [_vp]),
             "rt_alloc_positions": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p, _i32p, _i32p, _i32p, ctypes.c_int64,
-                                                  _i32p, ctypes.c_int64, _i32p]),
+                                                  ctypes.c_int32, _i32p, ctypes.c_int64, _i32p]),
             "rt_pool_destroy": (None, [_vp]),
             "rt_pool_alloc": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p]),
             "rt_pool_free": (ctypes.c_int, [_vp, _i32p, ctypes.c_int32]),
@@ -88,12 +94,13 @@ def lib():
             "rt_protected_size": (ctypes.c_int64, [_vp]),
             "rt_tree_num_nodes": (ctypes.c_int64, [_vp]),
             "rt_tree_dump": (ctypes.c_int, [_vp, ctypes.c_char_p, ctypes.c_int64, _i64p]),
-            "rt_admit_batch": (ctypes.c_int, [_vp, _i32p, _i64p, ctypes.c_int32, _i32p, ctypes.c_int64, _i32p,
-                                              _i32p, _i32p, _i64p, _i32p, ctypes.c_int64, _i64p]),
+            "rt_admit_batch": (ctypes.c_int, [_vp, _i32p, _i64p, ctypes.c_int32, _i32p, ctypes.c_int64,
+                                              ctypes.c_int32, _i32p, _i32p, _i32p, _i64p, _i32p, ctypes.c_int64,
+                                              _i64p]),
             "rt_decode_slots_batch": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p, _i32p, _i32p, ctypes.c_int64,
-                                                     _i32p]),
-            "rt_finish_batch": (ctypes.c_int, [_vp, _i32p, _i64p, ctypes.c_int32, _i32p, ctypes.c_int64, _i32p,
-                                               _i32p, _i64p, _i64p]),
+                                                     ctypes.c_int32, _i32p]),
+            "rt_finish_batch": (ctypes.c_int, [_vp, _i32p, _i64p, ctypes.c_int32, _i32p, ctypes.c_int64,
+                                               ctypes.c_int32, _i32p, _i32p, _i64p, _i64p]),
             "kv_store": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int, _vp]),
             "req_to_token_scatter": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int32, _vp]),
@@ -154,6 +161,8 @@ def lib():
                                                               ctypes.c_int, _vp]),
         }
         for name, (res, args) in sig.items():
+            if _HOST_ONLY and not hasattr(L, name):
+                continue
             f = getattr(L, name)
             f.restype = res
             f.argtypes = args
@@ -290,17 +299,26 @@ def rt_alloc_with_evict(tree, n):
     return out[:int(n)].copy(), int(ev.value)
 
 
+def _host_table(req_to_token):
+    """(stride, rows) of a host slot table: a C-contiguous 2-D int32 array,
+    which the library writes in place (so it must not be a converted copy)."""
+    if not (isinstance(req_to_token, np.ndarray) and req_to_token.dtype == np.int32 and req_to_token.ndim == 2
+            and req_to_token.flags.c_contiguous):
+        raise ValueError("req_to_token must be a C-contiguous 2-D int32 numpy array")
+    return req_to_token.shape[1], req_to_token.shape[0]
+
+
 def rt_alloc_positions(tree, rows, first_positions, counts, req_to_token):
     """Slots of runs of positions by the page rule, written into the host
     slot-table rows; returns (slots concatenated in run order, tokens
     evicted)."""
     rows, first, cnt = _i32(rows), _i32(first_positions), _i32(counts)
-    assert req_to_token.dtype == np.int32 and req_to_token.flags.c_contiguous
+    stride, num_rows = _host_table(req_to_token)
     total = int(cnt.sum()) if cnt.size else 0
     out = np.empty(max(total, 1), dtype=np.int32)
     ev = ctypes.c_int32()
     _check(lib().rt_alloc_positions(tree, rows.size, _p32(rows), _p32(first), _p32(cnt), _p32(req_to_token),
-                                    req_to_token.shape[1], _p32(out), out.size, ctypes.byref(ev)))
+                                    stride, num_rows, _p32(out), out.size, ctypes.byref(ev)))
     return out[:total].copy(), int(ev.value)
 
 
@@ -336,8 +354,7 @@ def rt_admit_batch(tree, tokens, token_offsets, req_to_token, rows):
     off = np.ascontiguousarray(token_offsets, dtype=np.int64)
     rows = _i32(rows)
     n = rows.size
-    assert req_to_token.dtype == np.int32 and req_to_token.flags.c_contiguous
-    stride = req_to_token.shape[1]
+    stride, num_rows = _host_table(req_to_token)
     pl = np.empty(n, dtype=np.int32)
     el = np.empty(n, dtype=np.int32)
     nodes = np.empty(n, dtype=np.int64)
@@ -346,16 +363,17 @@ def rt_admit_batch(tree, tokens, token_offsets, req_to_token, rows):
         _loc_scratch = np.empty(max(cap, 1), dtype=np.int32)
     loc = _loc_scratch
     nnew = ctypes.c_int64()
-    _check(lib().rt_admit_batch(tree, _p32(t), _p64(off), n, _p32(req_to_token), stride, _p32(rows), _p32(pl),
-                                _p32(el), _p64(nodes), _p32(loc), cap, ctypes.byref(nnew)))
+    _check(lib().rt_admit_batch(tree, _p32(t), _p64(off), n, _p32(req_to_token), stride, num_rows, _p32(rows),
+                                _p32(pl), _p32(el), _p64(nodes), _p32(loc), cap, ctypes.byref(nnew)))
     return pl, el, nodes, loc[:nnew.value].copy()
 
 
 def rt_decode_slots_batch(tree, rows, positions, req_to_token):
     rows, pos = _i32(rows), _i32(positions)
+    stride, num_rows = _host_table(req_to_token)
     out = np.empty(max(rows.size, 1), dtype=np.int32)
-    _check(lib().rt_decode_slots_batch(tree, rows.size, _p32(rows), _p32(pos), _p32(req_to_token),
-                                       req_to_token.shape[1], _p32(out)))
+    _check(lib().rt_decode_slots_batch(tree, rows.size, _p32(rows), _p32(pos), _p32(req_to_token), stride, num_rows,
+                                       _p32(out)))
     return out[:rows.size].copy()
 
 
@@ -364,8 +382,9 @@ def rt_finish_batch(tree, tokens, token_offsets, req_to_token, rows, prefix_lens
     off = np.ascontiguousarray(token_offsets, dtype=np.int64)
     rows, pl = _i32(rows), _i32(prefix_lens)
     nodes = np.ascontiguousarray(nodes, dtype=np.int64)
+    stride, num_rows = _host_table(req_to_token)
     freed = ctypes.c_int64()
-    _check(lib().rt_finish_batch(tree, _p32(t), _p64(off), rows.size, _p32(req_to_token), req_to_token.shape[1],
+    _check(lib().rt_finish_batch(tree, _p32(t), _p64(off), rows.size, _p32(req_to_token), stride, num_rows,
                                  _p32(rows), _p32(pl), _p64(nodes), ctypes.byref(freed)))
     return int(freed.value)
 

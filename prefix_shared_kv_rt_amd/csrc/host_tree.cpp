@@ -36,6 +36,14 @@
 #include "rt_internal.h"
 
 namespace rt {
+// memcpy of n int32 values; n == 0 copies nothing (and lets either pointer
+// be null, which memcpy itself does not allow).
+inline void copy_i32(int32_t* dst, const int32_t* src, int64_t n) {
+  if (n > 0) std::memcpy(dst, src, sizeof(int32_t) * size_t(n));
+}
+}  // namespace rt
+
+namespace rt {
 
 // ------------------------------------------------------------------ pool --
 // Slots 1..capacity in pages of `page` slots: page j holds slots
@@ -66,8 +74,8 @@ struct Pool {
                                                std::to_string(free_slots()));
     if (page == 1) {  // runs of slots move with at most two block copies
       const int64_t first = std::min<int64_t>(k, pages - head);
-      std::memcpy(out, ring.data() + head, sizeof(int32_t) * first);
-      std::memcpy(out + first, ring.data(), sizeof(int32_t) * (k - first));
+      copy_i32(out, ring.data() + head, first);
+      copy_i32(out + first, ring.data(), k - first);
     } else {
       for (int32_t i = 0; i < k; ++i) {
         const int32_t f = ring[(head + i) % pages];
@@ -89,8 +97,8 @@ struct Pool {
     if (page == 1) {
       if (int64_t(count) + n > pages) return fail(RT_ERR_INVALID, "pool: free list overflow (double free?)");
       const int64_t first = std::min<int64_t>(n, pages - tail);
-      std::memcpy(ring.data() + tail, slots, sizeof(int32_t) * first);
-      std::memcpy(ring.data(), slots + first, sizeof(int32_t) * (n - first));
+      copy_i32(ring.data() + tail, slots, first);
+      copy_i32(ring.data(), slots + first, n - first);
       count += int32_t(n);
       return RT_OK;
     }
@@ -366,12 +374,12 @@ struct Tree {
       k -= k % P;  // at least one page: the first page matched
       if (k < int64_t(child->key.size())) {
         Node* upper = split(child, k);
-        if (out) std::memcpy(out + len, upper->value.data(), sizeof(int32_t) * k);
+        if (out) copy_i32(out + len, upper->value.data(), k);
         len += k;
         node = upper;
         break;
       }
-      if (out) std::memcpy(out + len, child->value.data(), sizeof(int32_t) * k);
+      if (out) copy_i32(out + len, child->value.data(), k);
       len += k;
       pos += k;
       node = child;
@@ -492,11 +500,12 @@ struct Tree {
   // takes the slot after the previous position's, read from that request's
   // row.  Writes every slot into its row and into out (concatenated).
   int alloc_positions(int32_t n_runs, const int32_t* rows, const int32_t* first, const int32_t* counts,
-                      int32_t* req_to_token, int64_t stride, int32_t* out, int64_t out_cap,
+                      int32_t* req_to_token, int64_t stride, int32_t num_rows, int32_t* out, int64_t out_cap,
                       int32_t* out_evicted) {
     int64_t starts = 0, total = 0;
     for (int32_t i = 0; i < n_runs; ++i) {
-      if (rows[i] < 0 || first[i] < 0 || counts[i] < 0 || int64_t(first[i]) + counts[i] > stride)
+      if (rows[i] < 0 || rows[i] >= num_rows || first[i] < 0 || counts[i] < 0 ||
+          int64_t(first[i]) + counts[i] > stride)
         return fail(RT_ERR_INVALID, "alloc_positions: bad run " + std::to_string(i));
       // multiples of P in [first, first + count)
       starts += (int64_t(first[i]) + counts[i] + P - 1) / P - (int64_t(first[i]) + P - 1) / P;
@@ -513,8 +522,8 @@ struct Tree {
       int32_t* row = req_to_token + int64_t(rows[i]) * stride;
       const int64_t x0 = first[i], cnt = counts[i];
       if (P == 1) {  // every position starts a page: the fresh slots in order
-        std::memcpy(row + x0, fresh + next, sizeof(int32_t) * cnt);
-        std::memcpy(out + o, fresh + next, sizeof(int32_t) * cnt);
+        copy_i32(row + x0, fresh + next, cnt);
+        copy_i32(out + o, fresh + next, cnt);
         next += cnt;
         o += cnt;
         continue;
@@ -685,20 +694,21 @@ int rt_evict_lru_leaves(rt_tree* tree, int32_t num_tokens, int32_t* out_evicted,
   if (out_evicted) *out_evicted = int32_t(ev);
   if (out_freed_slots) {
     int64_t m = std::min<int64_t>(int64_t(freed.size()), std::max(freed_cap, 0));
-    std::memcpy(out_freed_slots, freed.data(), sizeof(int32_t) * m);
+    rt::copy_i32(out_freed_slots, freed.data(), m);
   }
   return RT_OK;
   RT_GUARD_END
 }
 
 int rt_alloc_positions(rt_tree* tree, int32_t n_runs, const int32_t* rows, const int32_t* first_positions,
-                       const int32_t* counts, int32_t* req_to_token, int64_t stride, int32_t* out_slots,
-                       int64_t out_cap, int32_t* out_evicted) {
-  if (!tree || n_runs < 0 || (n_runs > 0 && (!rows || !first_positions || !counts || !req_to_token)) || stride < 1)
+                       const int32_t* counts, int32_t* req_to_token, int64_t stride, int32_t num_rows,
+                       int32_t* out_slots, int64_t out_cap, int32_t* out_evicted) {
+  if (!tree || n_runs < 0 || (n_runs > 0 && (!rows || !first_positions || !counts || !req_to_token)) ||
+      stride < 1 || num_rows < 0)
     return fail(RT_ERR_INVALID, "rt_alloc_positions: bad argument");
   RT_GUARD_BEGIN
-  return tree->impl.alloc_positions(n_runs, rows, first_positions, counts, req_to_token, stride, out_slots, out_cap,
-                                    out_evicted);
+  return tree->impl.alloc_positions(n_runs, rows, first_positions, counts, req_to_token, stride, num_rows, out_slots,
+                                    out_cap, out_evicted);
   RT_GUARD_END
 }
 
@@ -727,12 +737,12 @@ int rt_tree_dump(const rt_tree* tree, char* buf, int64_t cap, int64_t* out_len) 
 }
 
 int rt_admit_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_offsets, int32_t n,
-                   int32_t* req_to_token, int64_t stride, const int32_t* rows, int32_t* prefix_lens,
-                   int32_t* extend_lens, rt_node* nodes, int32_t* out_cache_loc,
+                   int32_t* req_to_token, int64_t stride, int32_t num_rows, const int32_t* rows,
+                   int32_t* prefix_lens, int32_t* extend_lens, rt_node* nodes, int32_t* out_cache_loc,
                    int64_t out_cache_cap, int64_t* out_num_new) {
   if (!tree || n < 0 || !token_offsets || (n > 0 && (!tokens || !req_to_token || !rows || !prefix_lens ||
                                                       !extend_lens || !nodes)) ||
-      stride < 1 || !out_num_new)
+      stride < 1 || num_rows < 0 || !out_num_new)
     return fail(RT_ERR_INVALID, "rt_admit_batch: bad argument");
   RT_GUARD_BEGIN
   rt::Tree& t = tree->impl;
@@ -740,7 +750,7 @@ int rt_admit_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_of
   for (int32_t i = 0; i < n; ++i) {
     int64_t len = token_offsets[i + 1] - token_offsets[i];
     if (len < 0 || len > stride) return fail(RT_ERR_INVALID, "rt_admit_batch: request longer than stride");
-    if (rows[i] < 0) return fail(RT_ERR_INVALID, "rt_admit_batch: negative row");
+    if (rows[i] < 0 || rows[i] >= num_rows) return fail(RT_ERR_INVALID, "rt_admit_batch: row out of range");
     total += len;
   }
   int64_t new_total = 0;
@@ -770,7 +780,7 @@ int rt_admit_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_of
   }
   // slots of positions [prefix, prefix + extend) of every request, by the
   // page rule, written into the rows and into out_cache_loc
-  int rc = t.alloc_positions(n, rows, prefix_lens, extend_lens, req_to_token, stride, out_cache_loc,
+  int rc = t.alloc_positions(n, rows, prefix_lens, extend_lens, req_to_token, stride, num_rows, out_cache_loc,
                              out_cache_cap, nullptr);
   if (rc != RT_OK) {
     unlock_all();
@@ -782,30 +792,32 @@ int rt_admit_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_of
 }
 
 int rt_decode_slots_batch(rt_tree* tree, int32_t n, const int32_t* rows, const int32_t* positions,
-                          int32_t* req_to_token, int64_t stride, int32_t* out_cache_loc) {
-  if (!tree || n < 0 || (n > 0 && (!rows || !positions || !req_to_token || !out_cache_loc)) || stride < 1)
+                          int32_t* req_to_token, int64_t stride, int32_t num_rows, int32_t* out_cache_loc) {
+  if (!tree || n < 0 || (n > 0 && (!rows || !positions || !req_to_token || !out_cache_loc)) || stride < 1 ||
+      num_rows < 0)
     return fail(RT_ERR_INVALID, "rt_decode_slots_batch: bad argument");
   for (int32_t i = 0; i < n; ++i)
-    if (rows[i] < 0 || positions[i] < 0 || positions[i] >= stride)
+    if (rows[i] < 0 || rows[i] >= num_rows || positions[i] < 0 || positions[i] >= stride)
       return fail(RT_ERR_INVALID, "rt_decode_slots_batch: row or position out of range");
   RT_GUARD_BEGIN
   std::vector<int32_t> ones(size_t(n), 1);
-  return tree->impl.alloc_positions(n, rows, positions, ones.data(), req_to_token, stride, out_cache_loc, n,
-                                    nullptr);
+  return tree->impl.alloc_positions(n, rows, positions, ones.data(), req_to_token, stride, num_rows, out_cache_loc,
+                                    n, nullptr);
   RT_GUARD_END
 }
 
 int rt_finish_batch(rt_tree* tree, const int32_t* tokens, const int64_t* token_offsets, int32_t n,
-                    const int32_t* req_to_token, int64_t stride, const int32_t* rows,
+                    const int32_t* req_to_token, int64_t stride, int32_t num_rows, const int32_t* rows,
                     const int32_t* prefix_lens, const rt_node* nodes, int64_t* out_freed) {
   if (!tree || n < 0 || !token_offsets ||
-      (n > 0 && (!tokens || !req_to_token || !rows || !prefix_lens || !nodes)) || stride < 1)
+      (n > 0 && (!tokens || !req_to_token || !rows || !prefix_lens || !nodes)) || stride < 1 || num_rows < 0)
     return fail(RT_ERR_INVALID, "rt_finish_batch: bad argument");
   RT_GUARD_BEGIN
   rt::Tree& t = tree->impl;
   for (int32_t i = 0; i < n; ++i) {
     int64_t len = token_offsets[i + 1] - token_offsets[i];
-    if (len < 0 || len > stride || rows[i] < 0 || prefix_lens[i] < 0 || prefix_lens[i] > len)
+    if (len < 0 || len > stride || rows[i] < 0 || rows[i] >= num_rows || prefix_lens[i] < 0 ||
+        prefix_lens[i] > len)
       return fail(RT_ERR_INVALID, "rt_finish_batch: bad request " + std::to_string(i));
     if (!t.find(nodes[i])) return fail(RT_ERR_INVALID, "rt_finish_batch: unknown node");
   }

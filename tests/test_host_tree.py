@@ -198,6 +198,42 @@ def test_errors_match_and_leave_state_unchanged():
     pr.close()
 
 
+def test_batch_helpers_refuse_rows_outside_the_table():
+    """Every batch helper checks its rows against the table's row count
+    before it writes the table or allocates: the call fails and the tree,
+    the pool and the table are as they were."""
+    pr = Pair(64)
+    r2t = np.zeros((4, 16), dtype=np.int32)
+    toks = np.array([1, 2, 3, 4, 5], dtype=np.int32)
+    off = np.array([0, 5], dtype=np.int64)
+    pl, el, nodes, loc = B.rt_admit_batch(pr.ctree, toks, off, r2t, np.array([1], dtype=np.int32))
+    before = r2t.copy()
+    free_before = B.rt_pool_available(pr.cpool)
+    for bad in (4, 5, -1, 1 << 20):
+        rows = np.array([bad], dtype=np.int32)
+        with pytest.raises(B.RadixRTError):
+            B.rt_admit_batch(pr.ctree, toks, off, r2t, rows)
+        with pytest.raises(B.RadixRTError):
+            B.rt_decode_slots_batch(pr.ctree, rows, np.array([5], dtype=np.int32), r2t)
+        with pytest.raises(B.RadixRTError):
+            B.rt_alloc_positions(pr.ctree, rows, np.array([5], dtype=np.int32), np.array([2], dtype=np.int32), r2t)
+        with pytest.raises(B.RadixRTError):
+            B.rt_finish_batch(pr.ctree, toks, off, r2t, rows, pl, nodes)
+    # a bad row after good ones: nothing is written for the good ones either
+    with pytest.raises(B.RadixRTError):
+        B.rt_decode_slots_batch(pr.ctree, np.array([0, 4], dtype=np.int32), np.array([0, 0], dtype=np.int32), r2t)
+    assert np.array_equal(r2t, before)
+    assert B.rt_pool_available(pr.cpool) == free_before
+    # the host table must be one writable int32 block
+    with pytest.raises(ValueError):
+        B.rt_decode_slots_batch(pr.ctree, np.array([0], dtype=np.int32), np.array([5], dtype=np.int32),
+                                r2t.astype(np.int64))
+    with pytest.raises(ValueError):
+        B.rt_decode_slots_batch(pr.ctree, np.array([0], dtype=np.int32), np.array([5], dtype=np.int32), r2t[:, ::2])
+    B.rt_finish_batch(pr.ctree, toks, off, r2t, np.array([1], dtype=np.int32), pl, nodes)
+    pr.close()
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_batch_helpers_equal_the_primitive_sequence(seed):
     rng = random.Random(seed)
