@@ -260,7 +260,7 @@ int req_to_token_scatter(int32_t* req_to_token, int32_t req_to_token_stride, con
  * src to device memory dst with a kernel on `stream`, so that the copy
  * stays on the compute queue beside the step's kernels.  src must lie
  * inside one pinned (hipHostMalloc) allocation, checked on the host through
- * its device mapping; pageable memory is refused with RT_ERR_INVALID before
+ * the allocation's recorded range; pageable memory is refused with RT_ERR_INVALID before
  * anything is launched.  bytes a multiple of 4, both pointers 4-byte
  * aligned (16-byte alignment takes the faster path).  dst must be device
  * memory, with [dst, dst + bytes) inside its allocation (checked on the
@@ -277,6 +277,14 @@ int rt_copy_from_host(void* dst, const void* src, int64_t bytes, void* stream);
  * destination span in one device allocation (checked as above). */
 int rt_copy_from_host_2d(void* dst, int64_t dst_pitch, const void* src, int64_t src_pitch, int64_t width,
                          int64_t height, void* stream);
+
+/* The host-side checks of rt_copy_from_host_2d alone, launching nothing:
+ * RT_OK when the copy would be accepted, else RT_ERR_INVALID with the
+ * reason in rt_last_error().  The source range must lie inside one pinned
+ * host allocation as the HIP runtime records it (hipMemGetAddressRange),
+ * the destination range inside one device allocation. */
+int rt_copy_from_host_check(void* dst, int64_t dst_pitch, const void* src, int64_t src_pitch, int64_t width,
+                            int64_t height);
 
 /* One decode step's writes in a single launch: req_to_token_scatter of
  * (rows, positions, slots) and kv_store of (k_new, v_new) at slots, for i < n

@@ -34,7 +34,7 @@ EXPORTS = [
     "radix_mixed_attention", "radix_mixed_attention_fp8kv",
     "radix_decode_shared_workspace_bytes", "radix_decode_attention_shared", "radix_decode_attention_shared_fp8kv",
     "radix_extend_attention", "radix_decode_workspace_bytes", "radix_decode_attention",
-    "rt_copy_from_host", "rt_copy_from_host_2d",
+    "rt_copy_from_host", "rt_copy_from_host_2d", "rt_copy_from_host_check",
     "radix_decode_attention_noalloc",
 ]
 
@@ -155,6 +155,8 @@ def lib():
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
                                                       _vp, ctypes.c_int64, _vp]),
+            "rt_copy_from_host_check": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, ctypes.c_int64, ctypes.c_int64,
+                                                       ctypes.c_int64]),
             "radix_decode_attention_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp,
                                                               _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
@@ -467,6 +469,16 @@ def rt_copy_from_host_2d(dst, src, stream=None):
     es = src.element_size()
     _check(lib().rt_copy_from_host_2d(_dptr(dst), dst.stride(0) * es, _dptr(src), src.stride(0) * es,
                                       src.shape[1] * es, src.shape[0], _stream(stream)))
+
+
+def rt_copy_from_host_check(dst, src, dst_pitch=None, src_pitch=None, width=None, height=1):
+    """The host-side checks of a copy from host tensor src to device tensor
+    dst, launching nothing (raises RadixRTError when refused).  Defaults:
+    one row of src's bytes."""
+    nbytes = src.numel() * src.element_size()
+    width = nbytes if width is None else int(width)
+    _check(lib().rt_copy_from_host_check(_dptr(dst), int(width if dst_pitch is None else dst_pitch), _dptr(src),
+                                         int(width if src_pitch is None else src_pitch), width, int(height)))
 
 
 def req_to_token_scatter(req_to_token, rows, positions, slots, stream=None):

@@ -49,30 +49,36 @@ __global__ void __launch_bounds__(256) host_copy_kernel(char* __restrict__ dst, 
 }  // namespace
 
 namespace {
-int copy_from_host(const char* name, void* dst, int64_t dst_pitch, const void* src, int64_t src_pitch,
-                   int64_t width, int64_t height, void* stream) {
+// Host-side checks of a copy (nothing is launched); on success *dsrc is the
+// device mapping of src.
+int check_copy(const char* name, void* dst, int64_t dst_pitch, const void* src, int64_t src_pitch, int64_t width,
+               int64_t height, const void** dsrc) {
   if (width < 0 || height < 0 || width % 4 != 0 || dst_pitch % 4 != 0 || src_pitch % 4 != 0 ||
       (height > 1 && (dst_pitch < width || src_pitch < width)))
     return rt::fail(RT_ERR_INVALID, std::string(name) + ": sizes or pitches not multiples of 4, or pitch < width");
+  *dsrc = nullptr;
   if (width == 0 || height == 0) return RT_OK;
   if (!dst || !src) return rt::fail(RT_ERR_INVALID, std::string(name) + ": null pointer");
   if ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 3)
     return rt::fail(RT_ERR_INVALID, std::string(name) + ": pointers not 4-byte aligned");
   const int64_t src_span = (height - 1) * src_pitch + width;  // bytes from the first to past the last read
   const int64_t dst_span = (height - 1) * dst_pitch + width;
-  // The kernel reads src through its device mapping.  Both ends of the range
-  // must resolve to one pinned allocation; anything else is refused here.
-  void* dsrc = nullptr;
-  void* dlast = nullptr;
-  char* last = const_cast<char*>(static_cast<const char*>(src)) + (src_span - 1);
-  const hipError_t e0 = hipHostGetDevicePointer(&dsrc, const_cast<void*>(src), 0);
-  const hipError_t e1 = e0 == hipSuccess ? hipHostGetDevicePointer(&dlast, last, 0) : e0;
-  if (e0 != hipSuccess || e1 != hipSuccess || !dsrc ||
-      static_cast<char*>(dlast) != static_cast<char*>(dsrc) + (src_span - 1)) {
+  // src: pinned host memory whose allocation (as the runtime records it)
+  // holds the whole range; the kernel reads it through its device mapping.
+  hipPointerAttribute_t sattr{};
+  void* sbase = nullptr;
+  size_t ssize = 0;
+  void* mapped = nullptr;
+  const bool src_ok = hipPointerGetAttributes(&sattr, src) == hipSuccess && sattr.type == hipMemoryTypeHost &&
+                      hipMemGetAddressRange(&sbase, &ssize, const_cast<void*>(src)) == hipSuccess &&
+                      static_cast<const char*>(src) >= static_cast<char*>(sbase) &&
+                      static_cast<const char*>(src) + src_span <= static_cast<char*>(sbase) + ssize &&
+                      hipHostGetDevicePointer(&mapped, const_cast<void*>(src), 0) == hipSuccess && mapped;
+  if (!src_ok) {
     (void)hipGetLastError();
     return rt::fail(RT_ERR_INVALID, std::string(name) + ": source is not inside one pinned host allocation");
   }
-  // dst must be device memory whose allocation holds the whole range.
+  // dst: device memory whose allocation holds the whole range.
   hipPointerAttribute_t attr{};
   void* base = nullptr;
   size_t size = 0;
@@ -83,6 +89,15 @@ int copy_from_host(const char* name, void* dst, int64_t dst_pitch, const void* s
     (void)hipGetLastError();
     return rt::fail(RT_ERR_INVALID, std::string(name) + ": destination is not device memory holding the range");
   }
+  *dsrc = mapped;
+  return RT_OK;
+}
+
+int copy_from_host(const char* name, void* dst, int64_t dst_pitch, const void* src, int64_t src_pitch,
+                   int64_t width, int64_t height, void* stream) {
+  const void* dsrc = nullptr;
+  const int rc = check_copy(name, dst, dst_pitch, src, src_pitch, width, height, &dsrc);
+  if (rc != RT_OK || width == 0 || height == 0) return rc;
   const bool vec = ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(dsrc) | uintptr_t(width) |
                      uintptr_t(height > 1 ? dst_pitch | src_pitch : 0)) & 15) == 0;
   const int64_t pieces = (vec ? width / 16 : width / 4) * height;
@@ -94,6 +109,12 @@ int copy_from_host(const char* name, void* dst, int64_t dst_pitch, const void* s
   return RT_OK;
 }
 }  // namespace
+
+extern "C" int rt_copy_from_host_check(void* dst, int64_t dst_pitch, const void* src, int64_t src_pitch,
+                                       int64_t width, int64_t height) {
+  const void* dsrc = nullptr;
+  return check_copy("rt_copy_from_host_check", dst, dst_pitch, src, src_pitch, width, height, &dsrc);
+}
 
 extern "C" int rt_copy_from_host(void* dst, const void* src, int64_t bytes, void* stream) {
   if (bytes < 0 || bytes % 4 != 0) return rt::fail(RT_ERR_INVALID, "rt_copy_from_host: bytes not a multiple of 4");

@@ -67,3 +67,26 @@ def test_copy_from_host_rejects_bad_sizes():
     assert rc == B.RT_ERR_INVALID
     rc = B.lib().rt_copy_from_host(dev.data_ptr(), host.data_ptr() + 2, 8, None)  # misaligned
     assert rc == B.RT_ERR_INVALID
+
+
+def test_copy_check_launches_nothing_and_follows_the_allocations():
+    """rt_copy_from_host_check alone: accepts what the copy accepts, refuses
+    pageable sources, ranges past the pinned source allocation, host
+    destinations and ranges past the device allocation; no kernel runs."""
+    src = torch.arange(1024, dtype=torch.int32).pin_memory()
+    dst = torch.full((1024,), -7, dtype=torch.int32, device="cuda")
+    B.rt_copy_from_host_check(dst, src)
+    B.rt_copy_from_host_check(dst[:512], src[512:])
+    B.rt_copy_from_host_check(dst.view(32, 32)[:, 4:12], src.view(32, 32)[:, 4:12], dst_pitch=128, src_pitch=128,
+                              width=32, height=32)
+    with pytest.raises(B.RadixRTError, match="pinned"):
+        B.rt_copy_from_host_check(dst, torch.arange(1024, dtype=torch.int32))     # pageable
+    with pytest.raises(B.RadixRTError, match="pinned"):
+        B.rt_copy_from_host_check(dst, src, width=64 << 20)                        # past the pinned block
+    with pytest.raises(B.RadixRTError, match="destination"):
+        B.rt_copy_from_host_check(torch.zeros(1024, dtype=torch.int32).pin_memory(), src)
+    big = torch.full((64 << 20,), 0, dtype=torch.uint8)
+    with pytest.raises(B.RadixRTError, match="destination"):
+        B.rt_copy_from_host_check(dst, big.pin_memory())                           # past the device block
+    torch.cuda.synchronize()
+    assert bool((dst.cpu() == -7).all())

@@ -15,15 +15,19 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-2
 
 
-def check_few_shot(fb, i):
-    """Sampled outputs of batch i against the oracle's full recompute."""
-    o_ext = fb.o_ext.float().cpu().numpy()
-    o_dec = fb.o_dec.float().cpu().numpy()
+SAMPLED = (0, 9, 18, 27, 36, 45, 54, 63)   # requests checked in every step
+
+
+def check_few_shot(fb, i, o_ext, o_dec, prefix_lens):
+    """Sampled outputs of batch i (host copies o_ext, o_dec) against the
+    oracle's full recompute: for each sampled request the first extend row
+    actually computed (position = matched prefix), a middle one, the last,
+    and the decode row."""
     fp8 = (1.0, 1.0) if fb.fp8 else None
     worst = 0.0
-    for b in (0, 31, 63):
+    for b in SAMPLED:
         toks = list(fb.prefix) + list(fb.suffix[i][b])
-        p = int(fb.last_prefix_lens[b])  # rows below p were cached, not recomputed
+        p = int(prefix_lens[b])  # rows below p were cached, not recomputed
         rows = sorted({p, (p + fb.PREFIX + fb.SUFFIX) // 2, fb.PREFIX + fb.SUFFIX - 1})
         want = recompute_rows(toks, rows, fb.HQ, fb.HKV, fb.D, fb.SEED, fb.sm_scale, kv_fp8_scales=fp8)
         got = o_ext[[b * fb.SUFFIX + (r - fb.PREFIX) for r in rows]]
@@ -37,20 +41,31 @@ def check_few_shot(fb, i):
 @pytest.mark.parametrize("kv_dtype,page,shared", [("bf16", 1, False), ("fp8", 1, False), ("bf16", 16, False),
                                                   ("bf16", 1, True), ("fp8", 1, True)])
 def test_few_shot_full_size_bench_path(kv_dtype, page, shared):
-    """64 requests x (1024 shared + 128 distinct) per step, three steps: the
-    extend rows actually computed (position >= matched prefix) and the
-    decode row of sampled requests (bf16 pool, or FP8 E4M3 pool at unit
-    scales against attention over the values the FP8 pool holds; token
-    slots or pages of 16)."""
+    """64 requests x (1024 shared + 128 distinct) per step, run as bench.py
+    runs them: clocks settled, then five steps back to back with no
+    synchronisation between them (the row sets' staging alternates as in
+    the timed loop); each step's outputs are copied on the step's stream
+    right after its kernels.  Eight requests per step are checked: the extend
+    rows actually computed and the decode row (bf16 pool, or FP8 E4M3 pool at
+    unit scales against attention over the values the FP8 pool holds; token
+    slots or pages of 16).  Every suffix starts with its own token, so each
+    request matches exactly the 1024-token prefix."""
     print(f"few-shot full size, {kv_dtype} pool, pages of {page}, shared decode {shared}", flush=True)
-    fb = bench.FewShotBench(3, torch, B, torch_gen, kv_dtype=kv_dtype, page_size=page, shared_decode=shared)
-    fb.gen_inputs(3)
+    n = 5
+    fb = bench.FewShotBench(n, torch, B, torch_gen, kv_dtype=kv_dtype, page_size=page, shared_decode=shared)
+    fb.gen_inputs(n)
     fb.warm_prefix()
-    worst = 0.0
-    for i in range(3):
+    fb.settle_clocks(ms=50.0)
+    outs = []
+    for i in range(n):
         fb.step(i, timed=False)
-        fb.stream.synchronize()
-        res = check_few_shot(fb, i)
+        with torch.cuda.stream(fb.stream):
+            outs.append((fb.o_ext.clone(), fb.o_dec.clone(), fb.last_prefix_lens.copy()))
+    fb.stream.synchronize()
+    worst = 0.0
+    for i, (o_ext, o_dec, pl) in enumerate(outs):
+        assert (pl == fb.PREFIX).all()
+        res = check_few_shot(fb, i, o_ext.float().cpu().numpy(), o_dec.float().cpu().numpy(), pl)
         print(f"  step {i}: {res}", flush=True)
         worst = max(worst, res["max_abs_err"])
     assert worst <= TOL
