@@ -82,8 +82,9 @@ class RadixRuntime:
         self.r2t_dev = torch.zeros((self.max_reqs, self.max_ctx), dtype=torch.int32, device=self.device)
         self._ws = torch.empty(0, dtype=torch.uint8, device=self.device)
         # When a list, every device step appends (kind, start event, end event,
-        # info) for the kernels it launches; kind is 'kv_store', 'extend' or
-        # 'decode' (the decode entry covers its slot-table and K/V writes too).
+        # info) for the kernels it launches; kind is 'kv_store', 'extend',
+        # 'decode' (the attention launch alone; the step's slot-table and K/V
+        # append runs just before it) or 'mixed'.
         self.events = None
 
     def _event(self):
@@ -170,7 +171,6 @@ class RadixRuntime:
             rows_d, pos_d, slots_d = self._to_dev(rows), self._to_dev(positions), self._to_dev(slots)
             o = torch.empty_like(q)
             max_kv = int(max(positions)) + 1
-            e0 = self._event() if self.events is not None else None
             if self.kv_fp8_scales:
                 B.decode_append_fp8(self.r2t_dev, rows_d, pos_d, slots_d, self.k_pool, self.v_pool, k_new, v_new,
                                     *self.kv_fp8_scales, stream=self.stream)
@@ -184,6 +184,9 @@ class RadixRuntime:
                 need = B.radix_decode_shared_workspace_bytes(n, self.hq, self.hkv, self.d, 1, n, shared_len, priv)
                 if self._ws.numel() < need:
                     self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+                # the timing events bracket the attention launch alone (its
+                # inputs and workspace are ready before the first event)
+                e0 = self._event() if self.events is not None else None
                 if self.kv_fp8_scales:
                     B.radix_decode_attention_shared_fp8kv(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d,
                                                           sl, gs, n, shared_len, priv, self.sm_scale, self._ws,
@@ -194,6 +197,7 @@ class RadixRuntime:
                                                     stream=self.stream)
             else:
                 ws = self.workspace(n, max_kv)
+                e0 = self._event() if self.events is not None else None
                 if self.kv_fp8_scales:
                     B.radix_decode_attention_fp8kv(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d,
                                                    max_kv, self.sm_scale, ws, *self.kv_fp8_scales, stream=self.stream)
