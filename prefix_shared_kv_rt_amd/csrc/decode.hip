@@ -60,6 +60,10 @@ constexpr int64_t kMaxKvLen = 2097152;  // longest context a decode call accepts
 // with less in flight; shorter chunks (more items) keep HBM busier on long
 // contexts (32 x 32897 keys: 24 chunks in 327 us against 17 in 358 us).
 constexpr int kMaxChunkFp8 = 1408;
+constexpr int kMaxChunkFp8Lds = 2048;  // longest FP8 chunk: kMaxKvLen / 1024 splits
+static_assert(kMaxKvLen <= int64_t(1024) * kMaxChunkFp8Lds && kMaxChunkFp8 <= kMaxChunkFp8Lds &&
+                  kMaxChunkFp8Lds <= kMaxChunk,
+              "a plan's chunk must fit the kernel's staged index array");
 // About six work items per CU: fewer, longer chunks amortise each item's
 // index staging, Q load and partial write.  On MI355X, 1536 is faster than
 // 6144 for few-shot (35 against 45 us), fork (108 against 112 us) and long
@@ -154,7 +158,9 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
   constexpr int KS = D / 32;      // 32-dim steps of the score contraction
   constexpr int VW = D / 16;      // V elements per lane and key; also the PV update's 16-row tiles
   constexpr int EB = KV8 ? 1 : 2; // bytes per pool element
-  __shared__ int32_t s_idx[kMaxChunk];
+  // FP8 chunks hold at most 1408 keys, or 2048 when a context needs more
+  // than 1024 of them: the smaller array keeps LDS from limiting occupancy.
+  __shared__ int32_t s_idx[KV8 ? kMaxChunkFp8Lds : kMaxChunk];
 
   const int lane = threadIdx.x;
   const int col = lane & 15;      // MFMA column: query head within the group / key within block
@@ -465,6 +471,8 @@ hipError_t launch_decode(const void* q, void* o, const void* k_pool, const void*
   // partials; the combine waits for it.  Returns the wait's status.
   const int G = Hq / Hkv;
   if (S_total == 0) S_total = pl.splits;
+  // the chunk's slot indices must fit the kernel's LDS array
+  if (pl.chunk > (mode == kModeFp8Kv ? kMaxChunkFp8Lds : kMaxChunk)) return hipErrorInvalidValue;
   if (mode == RT_BF16 || mode == kModeFp8Kv) {
     const int64_t items = int64_t(B) * Hkv * pl.splits;
     if (mode == RT_BF16) {
@@ -520,12 +528,15 @@ int decode_entry(const char* name, const void* q, void* o, const void* k_pool, c
   float* ws_ml = ws_acc + int64_t(batch) * num_q_heads * pl.splits * head_dim;
   const float scale_log2 = sm_scale * k_scale * kLog2e;
   hipStream_t st = (hipStream_t)stream;
-  if (head_dim == 128)
-    launch_decode<128>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
-                       batch, num_q_heads, num_kv_heads, pl, scale_log2, v_scale, mode, ws_acc, ws_ml, st);
-  else
-    launch_decode<64>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
-                      batch, num_q_heads, num_kv_heads, pl, scale_log2, v_scale, mode, ws_acc, ws_ml, st);
+  const hipError_t le =
+      head_dim == 128
+          ? launch_decode<128>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices,
+                               prefix_lens, batch, num_q_heads, num_kv_heads, pl, scale_log2, v_scale, mode, ws_acc,
+                               ws_ml, st)
+          : launch_decode<64>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices,
+                              prefix_lens, batch, num_q_heads, num_kv_heads, pl, scale_log2, v_scale, mode, ws_acc,
+                              ws_ml, st);
+  if (le != hipSuccess) return rt::fail(RT_ERR_HIP, fn + ": " + hipGetErrorString(le));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return rt::fail(RT_ERR_HIP, fn + " launch: " + hipGetErrorString(e));
   return RT_OK;
