@@ -269,7 +269,12 @@ class NaiveRadixTree:
 
     def alloc_with_evict(self, n):
         """Allocate n slots (whole pages), evicting the deficit first if the
-        pool is short.  Raises OracleOOM (allocating nothing) if still short."""
+        pool is short.  An allocation that cannot succeed even after every
+        unlocked node is evicted (free + evictable < n, the quantity the
+        scheduler's admission test uses) raises OracleOOM before anything is
+        evicted or allocated."""
+        if n > self.pool.available() + self.evictable_size():
+            raise OracleOOM(f"need {n}, have {self.pool.available()} free + {self.evictable_size()} evictable")
         short = n - self.pool.available()
         freed = []
         if short > 0:

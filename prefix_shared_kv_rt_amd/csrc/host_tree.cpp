@@ -485,6 +485,13 @@ struct Tree {
   // n slots (whole pages); the deficit is evicted first.
   int alloc_with_evict(int32_t n, int32_t* out, int32_t* out_evicted) {
     if (n < 0 || n % P) return fail(RT_ERR_INVALID, "allocation must be a whole number of pages");
+    if (out_evicted) *out_evicted = 0;
+    // An allocation that would fail even after evicting every unlocked node
+    // fails before evicting anything (free + evictable is what the
+    // scheduler's admission test counts as available).
+    if (int64_t(n) > pool->free_slots() + evictable)
+      return fail(RT_ERR_OOM, "need " + std::to_string(n) + " slots, " + std::to_string(pool->free_slots()) +
+                                  " free + " + std::to_string(evictable) + " evictable");
     int64_t ev = 0;
     if (n > pool->free_slots()) ev = evict(int64_t(n) - pool->free_slots(), nullptr);
     if (out_evicted) *out_evicted = int32_t(ev);

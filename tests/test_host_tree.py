@@ -198,6 +198,23 @@ def test_errors_match_and_leave_state_unchanged():
     pr.close()
 
 
+def test_allocation_beyond_free_plus_evictable_evicts_nothing_on_library():
+    """The library and the oracle agree: free + evictable < n fails before
+    any eviction; a fitting allocation evicts the deficit."""
+    pr = Pair(10)
+    for toks in ([1, 2, 3], [4, 5, 6]):
+        s = pr.alloc(3)
+        pr.insert(toks, s)
+    _, node = pr.match([4, 5, 6])
+    pr.lock(node)
+    assert pr.alloc(8) is None
+    pr.same()
+    assert B.rt_evictable_size(pr.ctree) == 3 and B.rt_pool_available(pr.cpool) == 4
+    assert pr.alloc(7) is not None
+    pr.same()
+    pr.close()
+
+
 def test_batch_helpers_refuse_rows_outside_the_table():
     """Every batch helper checks its rows against the table's row count
     before it writes the table or allocates: the call fails and the tree,

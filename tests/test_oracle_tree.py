@@ -248,6 +248,25 @@ def test_unlock_underflow_and_oom_are_errors():
     assert pool.available() == before
 
 
+def test_allocation_beyond_free_plus_evictable_evicts_nothing():
+    """free + evictable < n: OOM before any eviction, so the cache keeps
+    every unlocked prefix (and an allocation that fits after evicting still
+    evicts only the deficit)."""
+    pool = NaivePool(10)
+    tree = NaiveRadixTree(pool)
+    tree.insert([1, 2, 3], pool.alloc(3))
+    tree.insert([4, 5, 6], pool.alloc(3))
+    _, node = tree.match_prefix([4, 5, 6])
+    tree.lock(node)                      # 4 free, [1, 2, 3] evictable, [4, 5, 6] locked
+    assert pool.available() == 4 and tree.evictable_size() == 3
+    with pytest.raises(OracleOOM):
+        tree.alloc_with_evict(8)         # 4 + 3 < 8
+    assert pool.available() == 4 and tree.evictable_size() == 3
+    assert tree.match_prefix([1, 2, 3])[0] != []
+    slots, freed = tree.alloc_with_evict(7)   # 4 + 3 = 7: evicts [1, 2, 3]
+    assert len(slots) == 7 and len(freed) == 3 and tree.evictable_size() == 0
+
+
 def test_eviction_takes_least_recent_leaf_and_spares_locked_paths():
     pool = NaivePool(100)
     tree = NaiveRadixTree(pool)
