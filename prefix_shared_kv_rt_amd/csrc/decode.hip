@@ -74,9 +74,10 @@ constexpr float kSlack = 8.f;        // log2 headroom of the lazy softmax rescal
 // Chunk the context into about kTargetItems (chunk, KV head, request) work
 // items; chunks hold at least 64 keys and at most max_chunk (at most
 // kMaxChunk in any case).  Depends only on the call's sizes and pool format.
-DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len, int max_chunk = kMaxChunk) {
+DecodePlan plan_decode(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len, int max_chunk = kMaxChunk,
+                       int target_items = kTargetItems) {
   const int64_t units = int64_t(batch) * num_kv_heads;
-  int64_t s = (kTargetItems + units - 1) / units;
+  int64_t s = (target_items + units - 1) / units;
   s = std::max<int64_t>(s, (max_kv_len + max_chunk - 1) / max_chunk);
   s = std::min<int64_t>(s, std::max(1, (max_kv_len + 63) / 64));
   s = std::max<int64_t>(std::min<int64_t>(s, 1024), 1);
@@ -105,10 +106,15 @@ constexpr int kSharedRows = 128;  // query rows per item of the extend kernel
 #define RT_SHARED_MIN_CHUNK 128
 #endif
 constexpr int kSharedItems = RT_SHARED_ITEMS;        // target work items of the shared pass
+// Target work items of the private pass.  Long-context private tails (32 x
+// 16385 keys beside the overlapped shared pass): 1024 or 512 -> 416 us per
+// call, 1536 -> 421, 3072 -> 446; few-shot tails (130 keys) are the same
+// 30-31 us for all four.
+constexpr int kPrivateItems = 1024;
 constexpr int kSharedMinChunk = RT_SHARED_MIN_CHUNK;  // shortest shared chunk (keys)
 SharedPlan plan_shared(int32_t batch, int32_t Hq, int32_t Hkv, int32_t n_groups, int32_t max_group_size,
                        int32_t max_shared_len, int32_t max_private_len, int max_chunk) {
-  SharedPlan sp{0, 64, plan_decode(batch, Hkv, std::max(max_private_len, 1), max_chunk)};
+  SharedPlan sp{0, 64, plan_decode(batch, Hkv, std::max(max_private_len, 1), max_chunk, kPrivateItems)};
   if (max_shared_len > 0) {
     const int64_t n_qt = (int64_t(max_group_size) * (Hq / Hkv) + kSharedRows - 1) / kSharedRows;
     const int64_t units = std::max<int64_t>(1, n_qt * n_groups * Hkv);
