@@ -387,8 +387,9 @@ __global__ void __launch_bounds__(64) decode_split_f32(
 // out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
 // Lane s (mod 64) reads partial s's (m, l), so the max and the weights take
 // wave reductions instead of a loop; the accumulators are then read eight
-// partials at a time with every load issued before the multiply-adds, so a
-// long split costs a few memory round trips, not one per partial.
+// partials at a time (a short last batch padded with weight-0 repeats) with
+// every load issued before the multiply-adds, so a long split costs a few
+// memory round trips, not one per partial.
 template <int D, bool BF16>
 __global__ void __launch_bounds__(64) decode_combine(const float* __restrict__ ws_acc,
                                                      const float* __restrict__ ws_ml, int S,
@@ -414,24 +415,24 @@ __global__ void __launch_bounds__(64) decode_combine(const float* __restrict__ w
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) lw += shfl_xor(lw, off);
     L += lw;
-    int j = 0;
-    for (; j + U <= n; j += U) {
+    // batches of U partials; a short last batch repeats partial n - 1 with
+    // weight 0, so every batch issues all its loads at once
+    for (int j = 0; j < n; j += U) {
       float a[U][PER];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
+        const int64_t sp = s0 + min(j + u, n - 1);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) a[u][i] = acc_s[int64_t(s0 + j + u) * D + 64 * i];
+        for (int i = 0; i < PER; ++i) a[u][i] = acc_s[sp * D + 64 * i];
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j + u));
+        const int src = min(j + u, 63);
+        float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), src));
+        if (j + u >= n) wu = 0.f;
 #pragma unroll
         for (int i = 0; i < PER; ++i) acc[i] = fmaf(wu, a[u][i], acc[i]);
       }
-    }
-    for (; j < n; ++j) {
-      const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-#pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = fmaf(wu, acc_s[int64_t(s0 + j) * D + 64 * i], acc[i]);
     }
   }
   const float inv = 1.f / L;
