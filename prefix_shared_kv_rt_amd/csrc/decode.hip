@@ -191,12 +191,9 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
     const char* kbase = k_pool + (int64_t(kvh) * D + 8 * grp) * EB;
     const char* vbase = v_pool + (int64_t(kvh) * D + VW * col) * EB;
 
-    // Slot indices of the whole chunk into this wave's LDS, once.
-    __syncthreads();  // the previous item's index reads are complete
-    for (int i = lane; i < end - start; i += 64) s_idx[i] = idx_row[start + i];
-    __syncthreads();
-
     // Q^T operand: column = query head kvh*G + col, k = dims 32*ks + 8*grp + t.
+    // Its loads go out before the slot indices' below, so the two round
+    // trips overlap.
     bf16x8 qop[KS];
     if (col < G) {
       const char* qp = q + (int64_t(b) * Hq + kvh * G + col) * D * 2;
@@ -206,6 +203,33 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qop[ks] = as_bf16x8(u32x4{0, 0, 0, 0});
     }
+
+    // Slot indices of the whole chunk into this wave's LDS, once.  The
+    // workgroup is this one wave, whose LDS accesses complete in program
+    // order, so no barrier (and no wait for the Q loads) is needed between
+    // the previous item's index reads, these writes and the reads below.
+    // Sixteen loads per lane go out before the first store, so a chunk of up
+    // to 1024 keys costs one memory round trip (one per 1024 keys after).
+    __builtin_amdgcn_wave_barrier();
+    {
+      const int n = end - start;
+      const int32_t* src = idx_row + start;
+      constexpr int U = 16;
+      for (int base = 0; base < n; base += 64 * U) {
+        int32_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = base + 64 * u + lane;
+          v[u] = i < n ? src[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = base + 64 * u + lane;
+          if (i < n) s_idx[i] = v[u];
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
 
     floatx4 o[VW];
 #pragma unroll
@@ -779,7 +803,7 @@ int shared_entry(const char* name, const void* q, void* o, const void* k_pool, c
     we = launch_decode<64>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
                       batch, num_q_heads, num_kv_heads, sp.b, scale_log2, v_scale, mode, ws_acc, ws_ml, st,
                       shared_lens, sp.n_a, sp.total(), join);
-  if (we != hipSuccess) return rt::fail(RT_ERR_HIP, fn + " join wait: " + hipGetErrorString(we));
+  if (we != hipSuccess) return rt::fail(RT_ERR_HIP, fn + ": " + hipGetErrorString(we));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return rt::fail(RT_ERR_HIP, fn + " launch: " + hipGetErrorString(e));
   return RT_OK;
