@@ -36,6 +36,7 @@
 #include <mutex>
 #include <string>
 
+#include "decode_split.h"
 #include "dev_common.h"
 #include "radixrt.h"
 #include "rt_internal.h"
@@ -69,7 +70,6 @@ static_assert(kMaxKvLen <= int64_t(1024) * kMaxChunkFp8Lds && kMaxChunkFp8 <= kM
 // 6144 for few-shot (35 against 45 us), fork (108 against 112 us) and long
 // context (574 against 582 us) decode; 512 or fewer starve few-shot.
 constexpr int kTargetItems = 1536;
-constexpr float kSlack = 8.f;        // log2 headroom of the lazy softmax rescale
 
 // Chunk the context into about kTargetItems (chunk, KV head, request) work
 // items; chunks hold at least 64 keys and at most max_chunk (at most
@@ -130,26 +130,8 @@ SharedPlan plan_shared(int32_t batch, int32_t Hq, int32_t Hkv, int32_t n_groups,
 }
 
 // ----------------------------------------------------------------- bf16 --
-// Persistent waves: the grid holds as many waves as fit on the chip; work
-// items (chunk s, KV head h, request b) are ordered with b innermost and cut
-// into 8 contiguous slices, one per XCD (the hardware places block i on XCD
-// i % 8).  Requests that share a cached prefix read the same slots for the
-// same (s, h), so their concurrent waves on one XCD meet those rows in L2.
-// One 16-key block's operands as loaded: bf16 pools hold them as the MFMA
-// takes them; FP8 pools hold half the bytes, widened to bf16 when consumed.
-// A lane's V piece: D/16 consecutive elements of one row (16 bytes for bf16
-// at D = 128).
-template <int D, bool KV8> struct VPiece;
-template <> struct VPiece<128, false> { using T = u32x4; };
-template <> struct VPiece<64, false> { using T = u32x2; };
-template <> struct VPiece<128, true> { using T = u32x2; };
-template <> struct VPiece<64, true> { using T = uint32_t; };
-template <int D, bool KV8>
-struct DecBlock {
-  typename std::conditional<KV8, u32x2, u32x4>::type k[D / 32];  // key kb + col, dims 32*ks + 8*grp .. +7
-  typename VPiece<D, KV8>::T v[4];  // V row kb + 4*grp + t, dims (D/16)*col .. +D/16-1
-};
-
+// Persistent waves, one per 64-thread workgroup: the grid holds as many
+// waves as fit on the chip (rtk::dec::split_items has the item order).
 template <int D, bool KV8>
 __global__ void __launch_bounds__(64) decode_split_bf16(
     const char* __restrict__ q, const char* __restrict__ k_pool, const char* __restrict__ v_pool,
@@ -157,198 +139,12 @@ __global__ void __launch_bounds__(64) decode_split_bf16(
     const int32_t* __restrict__ prefix_lens, int B, int Hq, int Hkv, int G, int S, int chunk, float scale_log2,
     float v_scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     const int32_t* __restrict__ key_start = nullptr, int s_off = 0, int S_total = 0) {
-  // key_start (optional): request b's chunks cover keys key_start[b] ..
-  // prefix_lens[b] (the shared-prefix decode's private tails); its partials
-  // go to split slots s_off .. s_off + S - 1 of S_total (default: S).
-  if (S_total == 0) S_total = S;
-  constexpr int KS = D / 32;      // 32-dim steps of the score contraction
-  constexpr int VW = D / 16;      // V elements per lane and key; also the PV update's 16-row tiles
-  constexpr int EB = KV8 ? 1 : 2; // bytes per pool element
   // FP8 chunks hold at most 1408 keys, or 2048 when a context needs more
   // than 1024 of them: the smaller array keeps LDS from limiting occupancy.
   __shared__ int32_t s_idx[KV8 ? kMaxChunkFp8Lds : kMaxChunk];
-
-  const int lane = threadIdx.x;
-  const int col = lane & 15;      // MFMA column: query head within the group / key within block
-  const int grp = lane >> 4;      // MFMA k-group
-  const int64_t row_bytes = int64_t(Hkv) * D * EB;
-
-  // This wave's share of its XCD's slice of the item list.
-  const int n_items = B * Hkv * S;
-  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
-  const int q8 = n_items >> 3, r8 = n_items & 7;
-  const int lo = xcd * q8 + min(xcd, r8);
-  const int hi_item = lo + q8 + (xcd < r8 ? 1 : 0);
-
-  for (int item = lo + local; item < hi_item; item += per_xcd) {
-    const int b = item % B;
-    const int kvh = (item / B) % Hkv;
-    const int s = item / (B * Hkv);
-    const int kv_len = prefix_lens[b] + 1;
-    const int start = (key_start ? key_start[b] : 0) + s * chunk;
-    const int end = min(kv_len, start + chunk);
-    const int32_t* idx_row = req_to_token + int64_t(rpi ? rpi[b] : b) * stride;
-    const char* kbase = k_pool + (int64_t(kvh) * D + 8 * grp) * EB;
-    const char* vbase = v_pool + (int64_t(kvh) * D + VW * col) * EB;
-
-    // Q^T operand: column = query head kvh*G + col, k = dims 32*ks + 8*grp + t.
-    // Its loads go out before the slot indices' below, so the two round
-    // trips overlap.
-    bf16x8 qop[KS];
-    if (col < G) {
-      const char* qp = q + (int64_t(b) * Hq + kvh * G + col) * D * 2;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qop[ks] = as_bf16x8(ld16(qp + (32 * ks + 8 * grp) * 2));
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qop[ks] = as_bf16x8(u32x4{0, 0, 0, 0});
-    }
-
-    // Slot indices of the whole chunk into this wave's LDS, once.  The
-    // workgroup is this one wave, whose LDS accesses complete in program
-    // order, so no barrier (and no wait for the Q loads) is needed between
-    // the previous item's index reads, these writes and the reads below.
-    // Sixteen loads per lane go out before the first store, so a chunk of up
-    // to 1024 keys costs one memory round trip (one per 1024 keys after).
-    __builtin_amdgcn_wave_barrier();
-    {
-      const int n = end - start;
-      const int32_t* src = idx_row + start;
-      constexpr int U = 16;
-      for (int base = 0; base < n; base += 64 * U) {
-        int32_t v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int i = base + 64 * u + lane;
-          v[u] = i < n ? src[i] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int i = base + 64 * u + lane;
-          if (i < n) s_idx[i] = v[u];
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    floatx4 o[VW];
-#pragma unroll
-    for (int i = 0; i < VW; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, l = 0.f;
-
-    // Keys past `end` are clamped to the chunk's last key (masked below), so
-    // every load is valid and the loop needs no tail branches.
-    auto load = [&](DecBlock<D, KV8>& blk, int kb) {
-      const int kk = min(kb + col, end - 1) - start;
-      const char* kp = kbase + int64_t(uint32_t(s_idx[kk])) * row_bytes;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (KV8)
-          blk.k[ks] = ld8(kp + 32 * ks);
-        else
-          blk.k[ks] = ld16(kp + 64 * ks);
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int kv = min(kb + 4 * grp + t, end - 1) - start;
-        blk.v[t] = *reinterpret_cast<const typename VPiece<D, KV8>::T*>(
-            vbase + int64_t(uint32_t(s_idx[kv])) * row_bytes);
-      }
-    };
-
-    auto consume = [&](const DecBlock<D, KV8>& cur, int kb) {
-      floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (KV8)
-          sacc = mfma_16x16x32(fp8x8_to_bf16x8(cur.k[ks]), qop[ks], sacc);
-        else
-          sacc = mfma_16x16x32(as_bf16x8(cur.k[ks]), qop[ks], sacc);
-      }
-      // Scores of keys kb + 4*grp + v for head `col` (log2 domain); keys at or
-      // past `end` (a block wholly past it included) contribute nothing.
-      float sv[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sv[v] = (kb + 4 * grp + v < end) ? sacc[v] * scale_log2 : -INFINITY;
-      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      // Lazy rescale: m only moves when a score exceeds it by 2^kSlack.
-      if (__any(mx > m + kSlack)) {
-        const float m_new = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int i2 = 0; i2 < VW; ++i2) o[i2] *= alpha;
-        m = m_new;
-      }
-      float p[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) p[v] = __builtin_amdgcn_exp2f(sv[v] - m);
-      l += (p[0] + p[1]) + (p[2] + p[3]);
-      const bf16x4 pop = as_bf16x4(u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
-      // PV update: tile r (0 .. VW-1) has rows i = dims VW*i + r; its A operand
-      // takes element r of the four keys' pieces, as bf16 pairs.
-      constexpr int NW = VW / 2;
-      uint32_t w[4][NW];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if constexpr (KV8 && D == 128) {
-          const u32x4 x = __builtin_bit_cast(u32x4, fp8x8_to_bf16x8(cur.v[t]));
-#pragma unroll
-          for (int j = 0; j < NW; ++j) w[t][j] = x[j];
-        } else if constexpr (KV8) {
-          const u32x2 x = fp8x4_to_bf16x4(cur.v[t]);
-#pragma unroll
-          for (int j = 0; j < NW; ++j) w[t][j] = x[j];
-        } else {
-#pragma unroll
-          for (int j = 0; j < NW; ++j) w[t][j] = cur.v[t][j];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NW; ++j) {
-        o[2 * j] = mfma_16x16x16(as_bf16x4(u32x2{pack_lo16(w[0][j], w[1][j]), pack_lo16(w[2][j], w[3][j])}), pop,
-                                 o[2 * j]);
-        o[2 * j + 1] = mfma_16x16x16(
-            as_bf16x4(u32x2{pack_hi16(w[0][j], w[1][j]), pack_hi16(w[2][j], w[3][j])}), pop, o[2 * j + 1]);
-      }
-    };
-
-    // Two register buffers: the next 16-key block is always in flight while
-    // one is consumed (past `end` the loads repeat the clamped last row).
-    const int nb = end > start ? (end - start + 15) >> 4 : 0;
-    if (nb > 0) {
-      DecBlock<D, KV8> cur, nxt;
-      load(cur, start);
-      for (int i = 0; i < nb; ++i) {
-        const int kb = start + 16 * i;
-        load(nxt, kb + 16);
-        consume(cur, kb);
-        cur = nxt;
-      }
-    }
-
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
-    if (col < G) {
-      const int64_t part = (int64_t(b) * Hq + kvh * G + col) * S_total + s_off + s;
-      if (grp == 0) {
-        ws_ml[part * 2 + 0] = m;
-        ws_ml[part * 2 + 1] = l;
-      }
-      float* acc = ws_acc + part * D;
-      // This lane holds rows i = 4*grp + v of every tile r: dims VW*i + r.
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int r4 = 0; r4 < VW / 4; ++r4) {
-          floatx4 w = {o[4 * r4 + 0][v], o[4 * r4 + 1][v], o[4 * r4 + 2][v], o[4 * r4 + 3][v]};
-          if constexpr (KV8) w *= v_scale;
-          *reinterpret_cast<floatx4*>(acc + VW * (4 * grp + v) + 4 * r4) = w;
-        }
-    }
-  }
+  rtk::dec::split_items<D, KV8>(blockIdx.x & 7, blockIdx.x >> 3, gridDim.x >> 3, threadIdx.x, s_idx, q, k_pool,
+                                v_pool, req_to_token, stride, rpi, prefix_lens, B, Hq, Hkv, G, S, chunk, scale_log2,
+                                v_scale, ws_acc, ws_ml, key_start, s_off, S_total);
 }
 
 // ----------------------------------------------------------------- fp32 --
@@ -663,6 +459,14 @@ void* scratch_on_device(const char* name) {
 // The threshold (K/V bytes of the private tails) can be set per call through
 // the environment variable RADIXRT_FORK_MIN_BYTES (0: always two streams).
 constexpr int64_t kForkMinPrivateBytes = int64_t(128) << 20;
+// The single-launch path (shared pass and private split in one launch) is
+// on by default for private chunks up to rt::fused_max_private_chunk();
+// RADIXRT_SHARED_FUSED=0 turns it off (the two then run as two launches).
+bool shared_fused_enabled() {
+  const char* e = getenv("RADIXRT_SHARED_FUSED");
+  return !(e && e[0] == '0' && e[1] == 0);
+}
+
 int64_t fork_min_private_bytes() {
   const char* e = getenv("RADIXRT_FORK_MIN_BYTES");
   if (!e || !*e) return kForkMinPrivateBytes;
@@ -769,6 +573,23 @@ int shared_entry(const char* name, const void* q, void* o, const void* k_pool, c
   hipEvent_t join = nullptr;
   const int64_t private_bytes =
       int64_t(batch) * max_private_len * num_kv_heads * head_dim * (kv8 ? 1 : 2) * 2;
+  if (sp.n_a > 0 && private_bytes < fork_min_private_bytes() && sp.b.chunk <= rt::fused_max_private_chunk() &&
+      shared_fused_enabled()) {
+    const int rc = rt::launch_shared_fused(q, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices,
+                                           prefix_lens, shared_lens, group_start, n_groups, max_group_size, sp.n_a,
+                                           sp.chunk_a, batch, sp.b.splits, sp.b.chunk, sp.total(), num_q_heads,
+                                           num_kv_heads, head_dim, scale_log2, v_scale, kv8, ws_acc, ws_ml, stream);
+    if (rc != RT_OK) return rc;
+    if (head_dim == 128)
+      hipLaunchKernelGGL((decode_combine<128, true>), dim3(uint32_t(int64_t(batch) * num_q_heads)), dim3(64), 0, st,
+                         ws_acc, ws_ml, sp.total(), o);
+    else
+      hipLaunchKernelGGL((decode_combine<64, true>), dim3(uint32_t(int64_t(batch) * num_q_heads)), dim3(64), 0, st,
+                         ws_acc, ws_ml, sp.total(), o);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return rt::fail(RT_ERR_HIP, fn + " launch: " + hipGetErrorString(e));
+    return RT_OK;
+  }
   if (sp.n_a > 0 && private_bytes < fork_min_private_bytes()) {
     const int rc = rt::launch_extend_shared_part(q, k_pool, v_pool, req_to_token, req_to_token_stride,
                                                  req_pool_indices, shared_lens, group_start, n_groups, max_group_size,

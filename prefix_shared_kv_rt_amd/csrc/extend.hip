@@ -53,6 +53,7 @@
 #include "dev_common.h"
 #include "radixrt.h"
 #include "rt_internal.h"
+#include "decode_split.h"
 #include "tile_layout.h"
 
 namespace {
@@ -90,14 +91,17 @@ struct ExtendCfg {
 // [c * chunk_keys, (c + 1) * chunk_keys) without a causal mask and writes the
 // split-K partial (max, sum, unnormalised accumulator) of each (row, head) to
 // split slot c of the decode workspace instead of an output row.
-template <int D, int RB, bool KV8, bool PART = false>
-__global__ void __launch_bounds__(64 * kWaves, RB == 1 ? kWavesPerSimd : 1) extend_bf16(
-    const char* __restrict__ q, char* __restrict__ o, const char* __restrict__ k_pool,
-    const char* __restrict__ v_pool, const int32_t* __restrict__ req_to_token, int64_t stride,
-    const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
+// The workgroup body; vblock / vgrid stand for blockIdx.x / gridDim.x (the
+// single-launch shared decode runs it in the first vgrid workgroups of a
+// larger grid).
+template <int D, int RB, bool KV8, bool PART>
+__device__ __forceinline__ void extend_body(
+    const int vblock, const int vgrid, const char* __restrict__ q, char* __restrict__ o,
+    const char* __restrict__ k_pool, const char* __restrict__ v_pool, const int32_t* __restrict__ req_to_token,
+    int64_t stride, const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
     const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ qo_indptr, int B1, int B2, int Hq,
-    int Hkv, int G, int n_qt, int n_qt2, int seg2, float scale_log2, float v_scale, int n_chunks = 1,
-    int chunk_keys = 0, int S_total = 0, float* __restrict__ ws_acc = nullptr, float* __restrict__ ws_ml = nullptr) {
+    int Hkv, int G, int n_qt, int n_qt2, int seg2, float scale_log2, float v_scale, int n_chunks, int chunk_keys,
+    int S_total, float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
   using C = ExtendCfg<D>;
   constexpr int kWaveRows = 32 * RB;          // query rows per wave (RB blocks of 32)
   constexpr int kItemRows = kWaves * kWaveRows;  // query rows per work item
@@ -130,19 +134,19 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? kWavesPerSimd : 1) exte
   // second starts on XCD 0), and its padding blocks have no work.
   int qt, b, kvh, chunk = 0;
   if (PART) {
-    const int work = xcd_slice(blockIdx.x, gridDim.x);
+    const int work = xcd_slice(vblock, vgrid);
     qt = work % n_qt;
     b = (work / n_qt) % B1;
     kvh = (work / (n_qt * B1)) % Hkv;
     chunk = work / (n_qt * B1 * Hkv);
-  } else if (int(blockIdx.x) < seg2) {
-    const int work = xcd_slice(blockIdx.x, seg2);
+  } else if (vblock < seg2) {
+    const int work = xcd_slice(vblock, seg2);
     if (work >= n_qt * B1 * Hkv) return;
     qt = work % n_qt;
     b = (work / n_qt) % B1;
     kvh = work / (n_qt * B1);
   } else {
-    const int work = xcd_slice(int(blockIdx.x) - seg2, int(gridDim.x) - seg2);
+    const int work = xcd_slice(vblock - seg2, vgrid - seg2);
     qt = work % n_qt2;
     b = B1 + (work / n_qt2) % B2;
     kvh = work / (n_qt2 * B2);
@@ -453,6 +457,53 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? kWavesPerSimd : 1) exte
   }
 }
 
+template <int D, int RB, bool KV8, bool PART = false>
+__global__ void __launch_bounds__(64 * kWaves, RB == 1 ? kWavesPerSimd : 1) extend_bf16(
+    const char* __restrict__ q, char* __restrict__ o, const char* __restrict__ k_pool,
+    const char* __restrict__ v_pool, const int32_t* __restrict__ req_to_token, int64_t stride,
+    const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens,
+    const int32_t* __restrict__ extend_lens, const int32_t* __restrict__ qo_indptr, int B1, int B2, int Hq,
+    int Hkv, int G, int n_qt, int n_qt2, int seg2, float scale_log2, float v_scale, int n_chunks = 1,
+    int chunk_keys = 0, int S_total = 0, float* __restrict__ ws_acc = nullptr, float* __restrict__ ws_ml = nullptr) {
+  extend_body<D, RB, KV8, PART>(int(blockIdx.x), int(gridDim.x), q, o, k_pool, v_pool, req_to_token, stride, rpi,
+                                prefix_lens, extend_lens, qo_indptr, B1, B2, Hq, Hkv, G, n_qt, n_qt2, seg2,
+                                scale_log2, v_scale, n_chunks, chunk_keys, S_total, ws_acc, ws_ml);
+}
+
+// Single-launch shared-prefix decode (short private tails): workgroups
+// 0 .. nA - 1 run the shared pass (extend_body in partial mode); workgroups
+// from nA_pad (nA rounded up to a multiple of 8, so that the rest start on
+// XCD 0) on hold four split-K waves each, which take the private tails'
+// items as the split kernel's waves do; every partial lands in the decode
+// workspace for the combine.  The two parts share no data, so they run side
+// by side on the chip instead of one launch after the other.
+constexpr int kFusedMaxChunk = 512;  // longest private chunk (keys) of the single-launch path
+template <int D, bool KV8>
+__global__ void __launch_bounds__(64 * kWaves, kWavesPerSimd) shared_decode_fused(
+    const char* __restrict__ q, const char* __restrict__ k_pool, const char* __restrict__ v_pool,
+    const int32_t* __restrict__ req_to_token, int64_t stride, const int32_t* __restrict__ rpi,
+    const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ shared_lens,
+    const int32_t* __restrict__ group_start, int n_groups, int B, int Hq, int Hkv, int G, int n_qt, int n_chunks,
+    int chunk_keys, int S_b, int chunk_b, int S_total, float scale_log2, float v_scale, float* __restrict__ ws_acc,
+    float* __restrict__ ws_ml, int nA, int nA_pad, int nB) {
+  __shared__ int32_t s_idx[kWaves][kFusedMaxChunk];
+  const int bid = int(blockIdx.x);
+  if (bid < nA) {
+    extend_body<D, kRB, KV8, true>(bid, nA, q, nullptr, k_pool, v_pool, req_to_token, stride, rpi, shared_lens,
+                                   nullptr, group_start, n_groups, 0, Hq, Hkv, G, n_qt, 0, 0, scale_log2, v_scale,
+                                   n_chunks, chunk_keys, S_total, ws_acc, ws_ml);
+    return;
+  }
+  if (bid < nA_pad) return;
+  const int j = bid - nA_pad;                                          // j % 8 is this workgroup's XCD
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  rtk::dec::split_items<D, KV8>(j & 7, (j >> 3) * kWaves + wave, (nB >> 3) * kWaves, int(threadIdx.x) & 63,
+                                s_idx[wave], q, k_pool, v_pool, req_to_token, stride, rpi, prefix_lens, B, Hq, Hkv,
+                                G, S_b, chunk_b, scale_log2, v_scale, ws_acc, ws_ml, shared_lens, n_chunks,
+                                S_total);
+}
+
+
 // ----------------------------------------------------------------- fp32 --
 template <int D>
 __global__ void __launch_bounds__(64) extend_f32(const float* __restrict__ q, float* __restrict__ o,
@@ -564,6 +615,40 @@ int launch_extend_shared_part(const void* q, const void* k_pool, const void* v_p
 #undef RT_SHARED_LAUNCH
   return RT_OK;
 }
+
+int launch_shared_fused(const void* q, const void* k_pool, const void* v_pool, const int32_t* req_to_token,
+                        int64_t stride, const int32_t* rpi, const int32_t* prefix_lens, const int32_t* shared_lens,
+                        const int32_t* group_start, int n_groups, int max_group_size, int n_chunks, int chunk_keys,
+                        int batch, int S_b, int chunk_b, int S_total, int Hq, int Hkv, int D, float scale_log2,
+                        float v_scale, bool kv8, float* ws_acc, float* ws_ml, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const int G = Hq / Hkv;
+  const int64_t item_rows = kWaves * 32 * kRB;
+  const int64_t n_qt = (int64_t(max_group_size) * G + item_rows - 1) / item_rows;
+  const int64_t nA = n_qt * n_groups * Hkv * n_chunks;
+  const int64_t nA_pad = (nA + 7) / 8 * 8;
+  const int64_t items = int64_t(batch) * Hkv * S_b;           // one split wave per private item
+  const int64_t nB = ((items + kWaves - 1) / kWaves + 7) / 8 * 8;
+  if (nA_pad + nB > INT32_MAX) return rt::fail(RT_ERR_INVALID, "radix_decode_attention_shared: grid too large");
+  if (chunk_keys % kBN != 0) return rt::fail(RT_ERR_INVALID, "shared pass: chunk not a multiple of the tile");
+  if (chunk_b > kFusedMaxChunk || chunk_b < 1) return rt::fail(RT_ERR_INVALID, "single-launch shared decode: private chunk too long");
+  if (nA_pad + nB == 0) return RT_OK;
+#define RT_FUSED_LAUNCH(DD, K8)                                                                                    \
+  hipLaunchKernelGGL((shared_decode_fused<DD, K8>), dim3(uint32_t(nA_pad + nB)), dim3(64 * kWaves), 0, st,        \
+                     (const char*)q, (const char*)k_pool, (const char*)v_pool, req_to_token, stride, rpi,          \
+                     prefix_lens, shared_lens, group_start, n_groups, batch, Hq, Hkv, G, int(n_qt), n_chunks,       \
+                     chunk_keys, S_b, chunk_b, S_total, scale_log2, v_scale, ws_acc, ws_ml, int(nA), int(nA_pad),   \
+                     int(nB))
+  if (D == 128) {
+    if (kv8) RT_FUSED_LAUNCH(128, true); else RT_FUSED_LAUNCH(128, false);
+  } else {
+    if (kv8) RT_FUSED_LAUNCH(64, true); else RT_FUSED_LAUNCH(64, false);
+  }
+#undef RT_FUSED_LAUNCH
+  return RT_OK;
+}
+
+int fused_max_private_chunk() { return kFusedMaxChunk; }
 
 }  // namespace rt
 

@@ -19,4 +19,16 @@ int launch_extend_shared_part(const void* q, const void* k_pool, const void* v_p
                               const int32_t* group_start, int n_groups, int max_group_size, int n_chunks,
                               int chunk_keys, int S_total, int Hq, int Hkv, int D, float scale_log2, float v_scale,
                               bool kv8, float* ws_acc, float* ws_ml, void* stream);
+
+// The single-launch form of radix_decode_attention_shared for short private
+// tails (extend.hip): the shared pass above and the split-K pass over the
+// private tails (S_b chunks of chunk_b keys per request and KV head, chunk_b
+// at most fused_max_private_chunk(), partial slots n_chunks ..) in one
+// launch; the caller then runs the combine.
+int launch_shared_fused(const void* q, const void* k_pool, const void* v_pool, const int32_t* req_to_token,
+                        int64_t stride, const int32_t* rpi, const int32_t* prefix_lens, const int32_t* shared_lens,
+                        const int32_t* group_start, int n_groups, int max_group_size, int n_chunks, int chunk_keys,
+                        int batch, int S_b, int chunk_b, int S_total, int Hq, int Hkv, int D, float scale_log2,
+                        float v_scale, bool kv8, float* ws_acc, float* ws_ml, void* stream);
+int fused_max_private_chunk();
 }  // namespace rt

@@ -96,15 +96,19 @@ def _run_plain(case, q, hq, hkv, d, fp8=None):
     return o
 
 
-@pytest.fixture(params=["one stream", "two streams"])
+@pytest.fixture(params=["one launch", "two launches", "two streams"])
 def streams(request, monkeypatch):
-    """The shared pass on the caller's stream (the default below 128 MiB of
-    private K/V, which every case here is), or forked onto the library's
-    second stream (forced through RADIXRT_FORK_MIN_BYTES=0)."""
-    if request.param == "two streams":
+    """How the shared pass runs beside the private split: in one launch with
+    it (the default for private chunks of up to 512 keys below 128 MiB of
+    private K/V, which every case here is), as a launch of its own before it
+    on the caller's stream (RADIXRT_SHARED_FUSED=0), or forked onto the
+    library's second stream (RADIXRT_FORK_MIN_BYTES=0)."""
+    monkeypatch.delenv("RADIXRT_FORK_MIN_BYTES", raising=False)
+    monkeypatch.delenv("RADIXRT_SHARED_FUSED", raising=False)
+    if request.param == "two launches":
+        monkeypatch.setenv("RADIXRT_SHARED_FUSED", "0")
+    elif request.param == "two streams":
         monkeypatch.setenv("RADIXRT_FORK_MIN_BYTES", "0")
-    else:
-        monkeypatch.delenv("RADIXRT_FORK_MIN_BYTES", raising=False)
     return request.param
 
 
