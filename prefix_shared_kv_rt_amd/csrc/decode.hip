@@ -461,10 +461,14 @@ void* scratch_on_device(const char* name) {
 constexpr int64_t kForkMinPrivateBytes = int64_t(128) << 20;
 // The single-launch path (shared pass and private split in one launch) is
 // on by default for private chunks up to rt::fused_max_private_chunk();
-// RADIXRT_SHARED_FUSED=0 turns it off (the two then run as two launches).
-bool shared_fused_enabled() {
+// RADIXRT_SHARED_FUSED=0 turns it off (the two then run as two launches),
+// =force uses it for any private chunk length.
+int shared_fused_mode() {  // 0 off, 1 default, 2 forced
   const char* e = getenv("RADIXRT_SHARED_FUSED");
-  return !(e && e[0] == '0' && e[1] == 0);
+  if (!e) return 1;
+  if (std::string(e) == "0") return 0;
+  if (std::string(e) == "force") return 2;
+  return 1;
 }
 
 int64_t fork_min_private_bytes() {
@@ -573,8 +577,9 @@ int shared_entry(const char* name, const void* q, void* o, const void* k_pool, c
   hipEvent_t join = nullptr;
   const int64_t private_bytes =
       int64_t(batch) * max_private_len * num_kv_heads * head_dim * (kv8 ? 1 : 2) * 2;
-  if (sp.n_a > 0 && private_bytes < fork_min_private_bytes() && sp.b.chunk <= rt::fused_max_private_chunk() &&
-      shared_fused_enabled()) {
+  const int fused = shared_fused_mode();
+  if (sp.n_a > 0 && private_bytes < fork_min_private_bytes() &&
+      (fused == 2 || (fused == 1 && sp.b.chunk <= rt::fused_max_private_chunk()))) {
     const int rc = rt::launch_shared_fused(q, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices,
                                            prefix_lens, shared_lens, group_start, n_groups, max_group_size, sp.n_a,
                                            sp.chunk_a, batch, sp.b.splits, sp.b.chunk, sp.total(), num_q_heads,

@@ -38,9 +38,12 @@ struct DecBlock {
 // Work items (chunk s, KV head h, request b) are numbered with b innermost
 // and cut into 8 contiguous slices, one per XCD; the calling wave takes items
 // local, local + per_xcd, ... of slice `xcd` (the XCD it runs on).  s_idx:
-// this wave's LDS array of at least `chunk` slot indices.  Needs only its own
-// wave: it uses no workgroup barrier.
-template <int D, bool KV8>
+// this wave's LDS array of slot indices: with WIN = 0 it holds a whole chunk;
+// with WIN (a power of two) it is a ring of WIN entries, two windows of
+// WIN / 2 keys, and the wave fetches each next window's indices while it
+// streams the current one (so a chunk may be any length).  Needs only its
+// own wave: it uses no workgroup barrier.
+template <int D, bool KV8, int WIN = 0>
 __device__ __forceinline__ void split_items(
     int xcd, int local, int per_xcd, int lane, int32_t* s_idx, const char* __restrict__ q,
     const char* __restrict__ k_pool, const char* __restrict__ v_pool, const int32_t* __restrict__ req_to_token,
@@ -94,10 +97,13 @@ __device__ __forceinline__ void split_items(
     // the previous item's index reads, these writes and the reads below.
     // Sixteen loads per lane go out before the first store, so a chunk of up
     // to 1024 keys costs one memory round trip (one per 1024 keys after).
+    static_assert(WIN == 0 || (WIN >= 128 && (WIN & (WIN - 1)) == 0), "the index ring is a power of two");
+    constexpr int H = WIN / 2;           // keys per window of the ring
+    const int n_keys = end - start;
+    const int32_t* src = idx_row + start;
     __builtin_amdgcn_wave_barrier();
     {
-      const int n = end - start;
-      const int32_t* src = idx_row + start;
+      const int n = WIN ? min(n_keys, WIN) : n_keys;   // the ring's first two windows
       constexpr int U = 16;
       for (int base = 0; base < n; base += 64 * U) {
         int32_t v[U];
@@ -121,10 +127,13 @@ __device__ __forceinline__ void split_items(
     float m = -INFINITY, l = 0.f;
 
     // Keys past `end` are clamped to the chunk's last key (masked below), so
-    // every load is valid and the loop needs no tail branches.
+    // every load is valid and the loop needs no tail branches.  A 16-key
+    // block never straddles two windows (both are multiples of 16 keys from
+    // `start`).
+    auto slot = [&](int rel) { return uint32_t(s_idx[WIN ? (rel & (WIN - 1)) : rel]); };
     auto load = [&](DecBlock<D, KV8>& blk, int kb) {
       const int kk = min(kb + col, end - 1) - start;
-      const char* kp = kbase + int64_t(uint32_t(s_idx[kk])) * row_bytes;
+      const char* kp = kbase + int64_t(slot(kk)) * row_bytes;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if constexpr (KV8)
@@ -135,8 +144,7 @@ __device__ __forceinline__ void split_items(
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int kv = min(kb + 4 * grp + t, end - 1) - start;
-        blk.v[t] = *reinterpret_cast<const typename VPiece<D, KV8>::T*>(
-            vbase + int64_t(uint32_t(s_idx[kv])) * row_bytes);
+        blk.v[t] = *reinterpret_cast<const typename VPiece<D, KV8>::T*>(vbase + int64_t(slot(kv)) * row_bytes);
       }
     };
 
@@ -204,11 +212,38 @@ __device__ __forceinline__ void split_items(
     const int nb = end > start ? (end - start + 15) >> 4 : 0;
     if (nb > 0) {
       DecBlock<D, KV8> cur, nxt;
+      constexpr int PU = WIN ? H / 64 : 1;   // index loads per lane per window
+      int32_t pre[PU];
+      int pend = -1;                         // first key (from start) of fetched, unstored indices
       load(cur, start);
       for (int i = 0; i < nb; ++i) {
         const int kb = start + 16 * i;
+        if constexpr (WIN != 0) {
+          // The next block opens window w = rel / H >= 1: every block of
+          // window w - 1 has been loaded, so its half of the ring takes
+          // window w + 1, fetched now and stored after this block.
+          const int rel = kb + 16 - start;
+          if (rel % H == 0 && rel >= H && rel + H < n_keys) {
+            pend = rel + H;
+#pragma unroll
+            for (int u = 0; u < PU; ++u) {
+              const int k = pend + 64 * u + lane;
+              pre[u] = k < n_keys ? src[k] : 0;
+            }
+          }
+        }
         load(nxt, kb + 16);
         consume(cur, kb);
+        if constexpr (WIN != 0) {
+          if (pend >= 0) {
+#pragma unroll
+            for (int u = 0; u < PU; ++u) {
+              const int k = pend + 64 * u + lane;
+              if (k < n_keys) s_idx[k & (WIN - 1)] = pre[u];
+            }
+            pend = -1;
+          }
+        }
         cur = nxt;
       }
     }

@@ -470,14 +470,16 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? kWavesPerSimd : 1) exte
                                 scale_log2, v_scale, n_chunks, chunk_keys, S_total, ws_acc, ws_ml);
 }
 
-// Single-launch shared-prefix decode (short private tails): workgroups
-// 0 .. nA - 1 run the shared pass (extend_body in partial mode); workgroups
-// from nA_pad (nA rounded up to a multiple of 8, so that the rest start on
-// XCD 0) on hold four split-K waves each, which take the private tails'
-// items as the split kernel's waves do; every partial lands in the decode
-// workspace for the combine.  The two parts share no data, so they run side
-// by side on the chip instead of one launch after the other.
-constexpr int kFusedMaxChunk = 512;  // longest private chunk (keys) of the single-launch path
+// Single-launch shared-prefix decode: workgroups 0 .. nA - 1 run the shared
+// pass (extend_body in partial mode); workgroups from nA_pad (nA rounded up
+// to a multiple of 8, so that the rest start on XCD 0) on hold four split-K
+// waves each, which take the private tails' items as the split kernel's
+// waves do, with their slot indices in a ring of kFusedRing entries per wave
+// (16 KiB per workgroup beside the shared pass's 36 KiB: three workgroups
+// per CU); every partial lands in the decode workspace for the combine.
+// The two parts share no data, so they run side by side on the chip instead
+// of one launch after the other.
+constexpr int kFusedRing = 1024;
 template <int D, bool KV8>
 __global__ void __launch_bounds__(64 * kWaves, kWavesPerSimd) shared_decode_fused(
     const char* __restrict__ q, const char* __restrict__ k_pool, const char* __restrict__ v_pool,
@@ -486,7 +488,7 @@ __global__ void __launch_bounds__(64 * kWaves, kWavesPerSimd) shared_decode_fuse
     const int32_t* __restrict__ group_start, int n_groups, int B, int Hq, int Hkv, int G, int n_qt, int n_chunks,
     int chunk_keys, int S_b, int chunk_b, int S_total, float scale_log2, float v_scale, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, int nA, int nA_pad, int nB) {
-  __shared__ int32_t s_idx[kWaves][kFusedMaxChunk];
+  __shared__ int32_t s_idx[kWaves][kFusedRing];
   const int bid = int(blockIdx.x);
   if (bid < nA) {
     extend_body<D, kRB, KV8, true>(bid, nA, q, nullptr, k_pool, v_pool, req_to_token, stride, rpi, shared_lens,
@@ -497,7 +499,8 @@ __global__ void __launch_bounds__(64 * kWaves, kWavesPerSimd) shared_decode_fuse
   if (bid < nA_pad) return;
   const int j = bid - nA_pad;                                          // j % 8 is this workgroup's XCD
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
-  rtk::dec::split_items<D, KV8>(j & 7, (j >> 3) * kWaves + wave, (nB >> 3) * kWaves, int(threadIdx.x) & 63,
+  rtk::dec::split_items<D, KV8, kFusedRing>(j & 7, (j >> 3) * kWaves + wave, (nB >> 3) * kWaves,
+                                            int(threadIdx.x) & 63,
                                 s_idx[wave], q, k_pool, v_pool, req_to_token, stride, rpi, prefix_lens, B, Hq, Hkv,
                                 G, S_b, chunk_b, scale_log2, v_scale, ws_acc, ws_ml, shared_lens, n_chunks,
                                 S_total);
@@ -631,7 +634,7 @@ int launch_shared_fused(const void* q, const void* k_pool, const void* v_pool, c
   const int64_t nB = ((items + kWaves - 1) / kWaves + 7) / 8 * 8;
   if (nA_pad + nB > INT32_MAX) return rt::fail(RT_ERR_INVALID, "radix_decode_attention_shared: grid too large");
   if (chunk_keys % kBN != 0) return rt::fail(RT_ERR_INVALID, "shared pass: chunk not a multiple of the tile");
-  if (chunk_b > kFusedMaxChunk || chunk_b < 1) return rt::fail(RT_ERR_INVALID, "single-launch shared decode: private chunk too long");
+  if (chunk_b < 1) return rt::fail(RT_ERR_INVALID, "single-launch shared decode: empty private chunk");
   if (nA_pad + nB == 0) return RT_OK;
 #define RT_FUSED_LAUNCH(DD, K8)                                                                                    \
   hipLaunchKernelGGL((shared_decode_fused<DD, K8>), dim3(uint32_t(nA_pad + nB)), dim3(64 * kWaves), 0, st,        \
@@ -648,7 +651,10 @@ int launch_shared_fused(const void* q, const void* k_pool, const void* v_pool, c
   return RT_OK;
 }
 
-int fused_max_private_chunk() { return kFusedMaxChunk; }
+// Longer private chunks take the two-launch path: on long-context tails
+// (32 x 16385 keys) the single launch measured 517-519 us against 401-402 us
+// for the shared pass on a second stream beside the split kernel.
+int fused_max_private_chunk() { return kFusedRing; }
 
 }  // namespace rt
 

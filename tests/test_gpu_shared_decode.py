@@ -99,9 +99,9 @@ def _run_plain(case, q, hq, hkv, d, fp8=None):
 @pytest.fixture(params=["one launch", "two launches", "two streams"])
 def streams(request, monkeypatch):
     """How the shared pass runs beside the private split: in one launch with
-    it (the default for private chunks of up to 512 keys below 128 MiB of
-    private K/V, which every case here is), as a launch of its own before it
-    on the caller's stream (RADIXRT_SHARED_FUSED=0), or forked onto the
+    it (the default for private chunks of up to 1024 keys below 128 MiB of
+    private K/V), as a launch of its own before it on the caller's stream
+    (RADIXRT_SHARED_FUSED=0), or forked onto the
     library's second stream (RADIXRT_FORK_MIN_BYTES=0)."""
     monkeypatch.delenv("RADIXRT_FORK_MIN_BYTES", raising=False)
     monkeypatch.delenv("RADIXRT_SHARED_FUSED", raising=False)
@@ -219,3 +219,32 @@ def test_shared_decode_replays_from_a_captured_graph(ci, streams):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+
+
+def test_shared_decode_long_private_tails(streams, monkeypatch):
+    """Private tails long enough that each (request, KV head) splits them
+    into two chunks of more than 1024 keys (64 requests x Hkv 8 = 512 units,
+    tails of 2100..2399 keys, D 64).  The library sends such chunks to the
+    two-launch path; the single launch, forced here through
+    RADIXRT_SHARED_FUSED=force, streams each chunk through its ring of 1024
+    slot indices, refilled window by window."""
+    if streams == "one launch":
+        monkeypatch.setenv("RADIXRT_SHARED_FUSED", "force")
+    groups = [(96, [2100 + (37 * i) % 300 for i in range(64)])]
+    hq, hkv, d = 8, 8, 64
+    print(f"shared decode, long private tails ({streams})", flush=True)
+    rng = np.random.default_rng(1234)
+    case = make_shared_case(rng, groups, hq, hkv, d)
+    case["kp"], case["vp"] = to_dev(case["kpool"], "bf16"), to_dev(case["vpool"], "bf16")
+    n = len(case["prefix_lens"])
+    q_host = host_values(rng, (n, hq, d), "bf16")
+    q = to_dev(q_host, "bf16")
+    o = _run(case, q, hq, hkv, d)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for b in range(0, n, 7):
+        pos = int(case["prefix_lens"][b])
+        want = oracle_rows(q_host[b:b + 1], case["k"][b], case["v"][b], np.array([pos]), 1.0 / np.sqrt(d))
+        worst = max(worst, max_err(o[b:b + 1], want))
+    print(f"  max abs err {worst:.3e}", flush=True)
+    assert worst <= TOL
