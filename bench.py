@@ -20,10 +20,11 @@ whole path:
                             (--decode plain: split-K over whole contexts)
   host   rt_finish_batch    insert prompt + token, free duplicates, unlock
 
-Q/K/V of every step are generated into HBM before the timed region.  Before
-the warm-up steps, about 200 ms of extend attention over the cached prefix
-lets the GPU's clocks settle at their level under sustained load (the first
-few dozen steps otherwise run 10-15 % slower).  Suffix token ids are drawn
+Q/K/V of every step are generated into HBM before the timed region.  After
+the warm-up steps, about 200 ms of replays of the last warm-up step's
+launches (same rows, same values) let the GPU's clocks settle at their
+level under the step's own load before the timed steps (the first few dozen
+steps otherwise run 10-20 % slower).  Suffix token ids are drawn
 over the Llama-3 vocabulary with first tokens distinct over the whole run,
 so no suffix matches an earlier one: every step extends 64 x 128 rows.
 
@@ -247,7 +248,8 @@ class FewShotBench:
         Bm.rt_finish_batch(self.tree, toks, off, self.r2t_host, rows, pl, nodes)
 
     def settle_clocks(self, ms=200.0):
-        """Untimed: repeat an extend launch of the batch's own shape (64
+        """Untimed, when no warm-up step runs (else settle_on_step): repeat
+        an extend launch of the batch's own shape (64
         requests x 128 rows over 1152 keys, the first batch's queries) for
         about ``ms`` milliseconds, so that the GPU's clocks reach the level
         they hold under this load before any step runs; without it the first
@@ -299,6 +301,31 @@ class FewShotBench:
             dec = Bm.radix_decode_attention_fp8kv if self.fp8 else Bm.radix_decode_attention
             dec(qd, self.o_dec, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pos, P0 + S + 1, self.sm_scale,
                 self.ws, stream=self.stream)
+
+    def settle_on_step(self, i, ms=200.0):
+        """Untimed, after the warm-up steps: step i's launches (the K/V
+        scatter, extend, decode append and decode attention of the last
+        warm-up step, whose rows, metadata and K/V are still in place; every
+        launch rewrites the same values) again and again for about ``ms``
+        milliseconds, so that the timed steps start at the clock the chip
+        holds under the step's own mix of work.  An extend-only settle
+        (settle_clocks) leaves it in a state the steps then drift away from
+        for some 20 ms: over 80 timed steps after it the extend went from
+        175 to 204 us (step 15) and back down to 168 us."""
+        Bm = self.Bm
+        q, k, v, qd, kd, vd = self.inputs[i]
+        d_pl, d_el, d_qo, d_rows, d_dslots = self.meta_views[i % 2]
+        d_pos = self.pos_dev
+        max_e = self.last_max_e
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(4):
+                self._store_extend(k, v, d_rows, d_pl, d_el, d_qo, max_e)
+                self._extend(q, self.o_ext, d_rows, d_pl, d_el, d_qo, max_e)
+                append = Bm.decode_append_fp8 if self.fp8 else Bm.decode_append
+                append(self.r2t_dev, d_rows, d_pos, d_dslots, self.k_pool, self.v_pool, kd, vd, stream=self.stream)
+                self._decode(qd, d_rows, d_pos)
+            self.stream.synchronize()
 
     def replay_decode(self, i, reps=10):
         """Untimed, after the timed steps: the decode attention of step i
@@ -390,6 +417,7 @@ class FewShotBench:
         # finish: prompt + generated token into the tree
         Bm.rt_finish_batch(self.tree, full, self.full_off, self.r2t_host, rows, pl, nodes)
         self.last_prefix_lens = pl
+        self.last_max_e = max_e
         if timed:
             # flops and bytes follow from (pl, el) after the timed region
             if ev is not None:
@@ -430,9 +458,12 @@ def run_few_shot(args, torch):
     # host, not the path.
     gc.collect()
     gc.disable()
-    fb.settle_clocks()
-    for i in range(args.warmup):
-        fb.step(i, timed=False)
+    if args.warmup > 0:
+        for i in range(args.warmup):
+            fb.step(i, timed=False)
+        fb.settle_on_step(args.warmup - 1)
+    else:
+        fb.settle_clocks()
     fb.stream.synchronize()
     torch.cuda.synchronize()
     # timing events around the extend launch of every time_every-th step
@@ -661,8 +692,8 @@ class DecodeBench:
         torch.cuda.synchronize()
 
     def settle_clocks(self, ms=200.0):
-        """Untimed: decode attention over the prompts alone (pool reads, a
-        scratch output) for about ``ms`` milliseconds, so that the clocks
+        """Untimed, when no warm-up step runs (else settle_on_step): decode
+        attention over the prompts alone (pool reads, a scratch output) for about ``ms`` milliseconds, so that the clocks
         reach their level under sustained load before any step runs."""
         torch, Bm = self.torch, self.Bm
         d_pos = torch.full((self.B,), self.prompt_len - 1, dtype=torch.int32, device=self.dev)
@@ -674,6 +705,41 @@ class DecodeBench:
                 decode(self.q[0], o, self.k_pool, self.v_pool, self.r2t_dev, self.rows_dev, d_pos, self.prompt_len,
                        self.sm_scale, self.ws, stream=self.stream)
             self.stream.synchronize()
+
+    def settle_on_step(self, s, ms=200.0):
+        """Untimed, after the warm-up steps: step s's launches (slot-table
+        scatter, K/V store and decode attention of the last warm-up step,
+        whose metadata and K/V stay in place; each launch rewrites the same
+        values) again and again for about ``ms`` milliseconds, so that the
+        timed steps start at the clock the chip holds under their own work."""
+        torch, Bm = self.torch, self.Bm
+        meta = self.meta_dev[s]
+        d_pos, d_slots = meta[:self.B], meta[self.B:]
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(8):
+                self.launch_step(s, d_pos, d_slots)
+            self.stream.synchronize()
+
+    def launch_step(self, s, d_pos, d_slots):
+        """Step s's GPU work after its metadata copy, on the bench's stream."""
+        Bm = self.Bm
+        Bm.req_to_token_scatter(self.r2t_dev, self.rows_dev, d_pos, d_slots, stream=self.stream)
+        store = Bm.kv_store_fp8 if self.fp8 else Bm.kv_store
+        store(self.k_pool, self.v_pool, self.k[s], self.v[s], d_slots, stream=self.stream)
+        self.launch_decode(s, d_pos)
+
+    def launch_decode(self, s, d_pos):
+        Bm = self.Bm
+        if self.shared_decode:
+            decode = Bm.radix_decode_attention_shared_fp8kv if self.fp8 else Bm.radix_decode_attention_shared
+            decode(self.q[s], self.o, self.k_pool, self.v_pool, self.r2t_dev, self.rows_dev, d_pos, self.sl_dev,
+                   self.gs_dev, self.B // self.groups, self.shared, self.private + s + 1, self.sm_scale,
+                   self.ws_shared, stream=self.stream)
+        else:
+            decode = Bm.radix_decode_attention_fp8kv if self.fp8 else Bm.radix_decode_attention
+            decode(self.q[s], self.o, self.k_pool, self.v_pool, self.r2t_dev, self.rows_dev, d_pos,
+                   self.prompt_len + s + 1, self.sm_scale, self.ws, stream=self.stream)
 
     def step(self, s, timed):
         torch, Bm = self.torch, self.Bm
@@ -692,15 +758,7 @@ class DecodeBench:
             if timed:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(self.stream)
-            if self.shared_decode:
-                decode = Bm.radix_decode_attention_shared_fp8kv if self.fp8 else Bm.radix_decode_attention_shared
-                decode(self.q[s], self.o, self.k_pool, self.v_pool, self.r2t_dev, self.rows_dev, d_pos, self.sl_dev,
-                       self.gs_dev, self.B // self.groups, self.shared, self.private + s + 1, self.sm_scale,
-                       self.ws_shared, stream=self.stream)
-            else:
-                decode = Bm.radix_decode_attention_fp8kv if self.fp8 else Bm.radix_decode_attention
-                decode(self.q[s], self.o, self.k_pool, self.v_pool, self.r2t_dev, self.rows_dev, d_pos,
-                       self.prompt_len + s + 1, self.sm_scale, self.ws, stream=self.stream)
+            self.launch_decode(s, d_pos)
             if timed:
                 e1.record(self.stream)
                 self.events.append((e0, e1, int(pos[0]) + 1))
@@ -716,9 +774,12 @@ def run_decode_bench(args, torch):
     db.setup()
     gc.collect()     # before the clock settle (see run_few_shot)
     gc.disable()
-    db.settle_clocks()
-    for s in range(args.warmup):
-        db.step(s, timed=False)
+    if args.warmup > 0:
+        for s in range(args.warmup):
+            db.step(s, timed=False)
+        db.settle_on_step(args.warmup - 1)
+    else:
+        db.settle_clocks()
     db.stream.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
