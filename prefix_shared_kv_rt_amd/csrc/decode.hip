@@ -209,7 +209,9 @@ __global__ void __launch_bounds__(64) decode_split_f32(
 // wave reductions instead of a loop; the accumulators are then read eight
 // partials at a time (a short last batch padded with weight-0 repeats) with
 // every load issued before the multiply-adds, so a long split costs a few
-// memory round trips, not one per partial.
+// memory round trips, not one per partial; up to kCombineFast partials are
+// read in one batch beside their (m, l).
+constexpr int kCombineFast = 16;  // splits up to this many take the one-round-trip path
 template <int D, bool BF16>
 __global__ void __launch_bounds__(64) decode_combine(const float* __restrict__ ws_acc,
                                                      const float* __restrict__ ws_ml, int S,
@@ -220,6 +222,46 @@ __global__ void __launch_bounds__(64) decode_combine(const float* __restrict__ w
   const int64_t bh = blockIdx.x;  // b * Hq + h
   const float* ml = ws_ml + bh * S * 2;
   const float* acc_s = ws_acc + bh * S * D + lane;
+  if (S <= kCombineFast) {
+    // Short splits: every partial's accumulator loads go out with the
+    // (m, l) loads, so the whole merge waits for one memory round trip.
+    float a[kCombineFast][PER];
+#pragma unroll
+    for (int u = 0; u < kCombineFast; ++u) {
+      const int64_t sp = min(u, S - 1);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) a[u][i] = acc_s[sp * D + 64 * i];
+    }
+    const float m_s = lane < S ? ml[2 * lane] : -INFINITY;
+    const float l_s = lane < S ? ml[2 * lane + 1] : 0.f;
+    float mx = m_s;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+    const float w = lane < S ? exp2f(m_s - mx) : 0.f;
+    float L = w * l_s;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += shfl_xor(L, off);
+    float acc[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int u = 0; u < kCombineFast; ++u) {
+      // lanes past S hold weight 0, so the repeated loads of partial S - 1 add nothing
+      const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] = fmaf(wu, a[u][i], acc[i]);
+    }
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const float v = acc[i] * inv;
+      if (BF16)
+        reinterpret_cast<uint16_t*>(out)[bh * D + lane + 64 * i] = uint16_t(f32_to_bf16_bits(v));
+      else
+        reinterpret_cast<float*>(out)[bh * D + lane + 64 * i] = v;
+    }
+    return;
+  }
   float mmax = -INFINITY;
   for (int s = lane; s < S; s += 64) mmax = fmaxf(mmax, ml[2 * s]);
 #pragma unroll
