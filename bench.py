@@ -546,8 +546,9 @@ class DecodeBench:
     Hq 64 / Hkv 8 / D 128.  fork: 16 prompts of 2048 tokens, each matched
     whole by 8 branches (batch 128), Hq 32 / Hkv 8 / D 128.  Prompt K/V are
     scattered into the pool with kv_store (no extend attention); each timed
-    step allocates one slot per request, scatters its slot and K/V, and runs
-    decode attention over the whole context."""
+    step allocates one slot per request, writes its slot-table entry and K/V
+    row (decode_append, one launch), and runs decode attention over the whole
+    context."""
 
     def __init__(self, name, torch, Bm, gen_t, n_steps, kv_dtype="bf16", shared_decode=False):
         self.torch, self.Bm, self.T = torch, Bm, gen_t
@@ -723,11 +724,14 @@ class DecodeBench:
 
     def launch_step(self, s, d_pos, d_slots):
         """Step s's GPU work after its metadata copy, on the bench's stream."""
-        Bm = self.Bm
-        Bm.req_to_token_scatter(self.r2t_dev, self.rows_dev, d_pos, d_slots, stream=self.stream)
-        store = Bm.kv_store_fp8 if self.fp8 else Bm.kv_store
-        store(self.k_pool, self.v_pool, self.k[s], self.v[s], d_slots, stream=self.stream)
+        self.launch_append(s, d_pos, d_slots)
         self.launch_decode(s, d_pos)
+
+    def launch_append(self, s, d_pos, d_slots):
+        """Slot-table entry and K/V row of each request's new token, one launch."""
+        append = self.Bm.decode_append_fp8 if self.fp8 else self.Bm.decode_append
+        append(self.r2t_dev, self.rows_dev, d_pos, d_slots, self.k_pool, self.v_pool, self.k[s], self.v[s],
+               stream=self.stream)
 
     def launch_decode(self, s, d_pos):
         Bm = self.Bm
@@ -752,9 +756,7 @@ class DecodeBench:
             meta = self.meta_dev[s]
             Bm.rt_copy_from_host(meta, self.meta_host_t[s], stream=self.stream)
             d_pos, d_slots = meta[:self.B], meta[self.B:]
-            Bm.req_to_token_scatter(self.r2t_dev, self.rows_dev, d_pos, d_slots, stream=self.stream)
-            store = Bm.kv_store_fp8 if self.fp8 else Bm.kv_store
-            store(self.k_pool, self.v_pool, self.k[s], self.v[s], d_slots, stream=self.stream)
+            self.launch_append(s, d_pos, d_slots)
             if timed:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(self.stream)
