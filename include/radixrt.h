@@ -518,6 +518,55 @@ int radix_decode_attention_fp8kv(const void* q, void* o, const void* k_pool, con
                                  float sm_scale, float k_scale, float v_scale, void* workspace,
                                  int64_t workspace_bytes, void* stream);
 
+/* Decode with the step's append folded in [P4 "CUDA Graph": a decode
+ * forward receives out_cache_loc, the slot of each request's new token, and
+ * writes that token's K/V there before attending over the context]: the
+ * result of decode_append (bf16 pools) or decode_append_fp8 (FP8 pools, same
+ * encoding and scales) of (rows = req_pool_indices or 0 .. batch - 1,
+ * positions = prefix_lens, slots = new_slots, k_new, v_new) followed by the
+ * named decode call on the same arguments, in the launches of the decode
+ * call alone: the work item whose chunk holds key prefix_lens[b] writes the
+ * new token's K/V row of its KV head at new_slots[b] and, once per request,
+ * req_to_token[row_b][prefix_lens[b]] = new_slots[b], then reads that key
+ * back; the key's slot comes from new_slots, so the table entry need not be
+ * written beforehand.  Pools and req_to_token are written, hence not const.
+ * k_new, v_new: (device) bf16 [batch, num_kv_heads, head_dim]; new_slots:
+ * (device) int32 [batch], not read by any other request of the call; a slot
+ * repeated by padded entries (slot 0) races as in decode_append and only
+ * those entries' outputs are affected.  The _shared forms need the new token outside every shared run
+ * (shared_lens[b] <= prefix_lens[b]; not checked on the device).  bf16 q / o;
+ * other arguments, workspace and checks as in the decode call named. */
+int radix_decode_attention_append(const void* q, void* o, void* k_pool, void* v_pool, int32_t* req_to_token,
+                                  int32_t req_to_token_stride, const int32_t* req_pool_indices,
+                                  const int32_t* prefix_lens, int32_t batch, int32_t max_kv_len, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, float sm_scale, const void* k_new,
+                                  const void* v_new, const int32_t* new_slots, void* workspace,
+                                  int64_t workspace_bytes, void* stream);
+int radix_decode_attention_append_fp8kv(const void* q, void* o, void* k_pool, void* v_pool, int32_t* req_to_token,
+                                        int32_t req_to_token_stride, const int32_t* req_pool_indices,
+                                        const int32_t* prefix_lens, int32_t batch, int32_t max_kv_len,
+                                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                                        float k_scale, float v_scale, const void* k_new, const void* v_new,
+                                        const int32_t* new_slots, void* workspace, int64_t workspace_bytes,
+                                        void* stream);
+int radix_decode_attention_shared_append(const void* q, void* o, void* k_pool, void* v_pool, int32_t* req_to_token,
+                                         int32_t req_to_token_stride, const int32_t* req_pool_indices,
+                                         const int32_t* prefix_lens, const int32_t* shared_lens,
+                                         const int32_t* group_start, int32_t batch, int32_t n_groups,
+                                         int32_t max_group_size, int32_t max_shared_len, int32_t max_private_len,
+                                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                                         const void* k_new, const void* v_new, const int32_t* new_slots,
+                                         void* workspace, int64_t workspace_bytes, void* stream);
+int radix_decode_attention_shared_append_fp8kv(const void* q, void* o, void* k_pool, void* v_pool,
+                                               int32_t* req_to_token, int32_t req_to_token_stride,
+                                               const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                               const int32_t* shared_lens, const int32_t* group_start, int32_t batch,
+                                               int32_t n_groups, int32_t max_group_size, int32_t max_shared_len,
+                                               int32_t max_private_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, float sm_scale, float k_scale, float v_scale,
+                                               const void* k_new, const void* v_new, const int32_t* new_slots,
+                                               void* workspace, int64_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,8 @@ EXPORTS = [
     "radix_extend_attention", "radix_decode_workspace_bytes", "radix_decode_attention",
     "rt_copy_from_host", "rt_copy_from_host_2d", "rt_copy_from_host_check",
     "radix_decode_attention_noalloc",
+    "radix_decode_attention_append", "radix_decode_attention_append_fp8kv",
+    "radix_decode_attention_shared_append", "radix_decode_attention_shared_append_fp8kv",
 ]
 
 
@@ -161,6 +163,20 @@ def lib():
                                                               _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                                               ctypes.c_int, _vp]),
+            "radix_decode_attention_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp] +
+                                              [ctypes.c_int32] * 5 + [ctypes.c_float, _vp, _vp, _vp, _vp,
+                                                                      ctypes.c_int64, _vp]),
+            "radix_decode_attention_append_fp8kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp,
+                                                                   _vp] + [ctypes.c_int32] * 5 +
+                                                    [ctypes.c_float] * 3 + [_vp, _vp, _vp, _vp, ctypes.c_int64,
+                                                                            _vp]),
+            "radix_decode_attention_shared_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp,
+                                                                    _vp, _vp, _vp] + [ctypes.c_int32] * 8 +
+                                                     [ctypes.c_float, _vp, _vp, _vp, _vp, ctypes.c_int64, _vp]),
+            "radix_decode_attention_shared_append_fp8kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                                                          _vp, _vp, _vp, _vp] +
+                                                           [ctypes.c_int32] * 8 + [ctypes.c_float] * 3 +
+                                                           [_vp, _vp, _vp, _vp, ctypes.c_int64, _vp]),
         }
         for name, (res, args) in sig.items():
             if _HOST_ONLY and not hasattr(L, name):
@@ -631,3 +647,56 @@ def radix_decode_attention_shared_fp8kv(q, o, k_pool, v_pool, req_to_token, req_
         group_start.shape[0] - 1, int(max_group_size), int(max_shared_len), int(max_private_len), hq, hkv, d,
         float(sm_scale), float(k_scale), float(v_scale), _dptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def radix_decode_attention_append(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens, max_kv_len,
+                                  sm_scale, k_new, v_new, new_slots, workspace, stream=None):
+    """decode_append of (req_pool_indices, prefix_lens, new_slots, k_new,
+    v_new) and radix_decode_attention in the decode's launches (bf16)."""
+    batch, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    _check(lib().radix_decode_attention_append(
+        _dptr(q), _dptr(o), _dptr(k_pool), _dptr(v_pool), _dptr(req_to_token), req_to_token.shape[1],
+        _dptr(req_pool_indices), _dptr(prefix_lens), batch, int(max_kv_len), hq, hkv, d, float(sm_scale),
+        _dptr(k_new), _dptr(v_new), _dptr(new_slots), _dptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def radix_decode_attention_append_fp8kv(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens,
+                                        max_kv_len, sm_scale, k_new, v_new, new_slots, workspace, k_scale=1.0,
+                                        v_scale=1.0, stream=None):
+    batch, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    _check(lib().radix_decode_attention_append_fp8kv(
+        _dptr(q), _dptr(o), _dptr(k_pool), _dptr(v_pool), _dptr(req_to_token), req_to_token.shape[1],
+        _dptr(req_pool_indices), _dptr(prefix_lens), batch, int(max_kv_len), hq, hkv, d, float(sm_scale),
+        float(k_scale), float(v_scale), _dptr(k_new), _dptr(v_new), _dptr(new_slots), _dptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def radix_decode_attention_shared_append(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens,
+                                         shared_lens, group_start, max_group_size, max_shared_len, max_private_len,
+                                         sm_scale, k_new, v_new, new_slots, workspace, stream=None):
+    """decode_append and radix_decode_attention_shared in the decode's launches (bf16)."""
+    batch, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    _check(lib().radix_decode_attention_shared_append(
+        _dptr(q), _dptr(o), _dptr(k_pool), _dptr(v_pool), _dptr(req_to_token), req_to_token.shape[1],
+        _dptr(req_pool_indices), _dptr(prefix_lens), _dptr(shared_lens), _dptr(group_start), batch,
+        group_start.shape[0] - 1, int(max_group_size), int(max_shared_len), int(max_private_len), hq, hkv, d,
+        float(sm_scale), _dptr(k_new), _dptr(v_new), _dptr(new_slots), _dptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def radix_decode_attention_shared_append_fp8kv(q, o, k_pool, v_pool, req_to_token, req_pool_indices, prefix_lens,
+                                               shared_lens, group_start, max_group_size, max_shared_len,
+                                               max_private_len, sm_scale, k_new, v_new, new_slots, workspace,
+                                               k_scale=1.0, v_scale=1.0, stream=None):
+    batch, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    _check(lib().radix_decode_attention_shared_append_fp8kv(
+        _dptr(q), _dptr(o), _dptr(k_pool), _dptr(v_pool), _dptr(req_to_token), req_to_token.shape[1],
+        _dptr(req_pool_indices), _dptr(prefix_lens), _dptr(shared_lens), _dptr(group_start), batch,
+        group_start.shape[0] - 1, int(max_group_size), int(max_shared_len), int(max_private_len), hq, hkv, d,
+        float(sm_scale), float(k_scale), float(v_scale), _dptr(k_new), _dptr(v_new), _dptr(new_slots),
+        _dptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -132,19 +132,19 @@ SharedPlan plan_shared(int32_t batch, int32_t Hq, int32_t Hkv, int32_t n_groups,
 // ----------------------------------------------------------------- bf16 --
 // Persistent waves, one per 64-thread workgroup: the grid holds as many
 // waves as fit on the chip (rtk::dec::split_items has the item order).
-template <int D, bool KV8>
+template <int D, bool KV8, bool APP = false>
 __global__ void __launch_bounds__(64) decode_split_bf16(
     const char* __restrict__ q, const char* __restrict__ k_pool, const char* __restrict__ v_pool,
     const int32_t* __restrict__ req_to_token, int64_t stride, const int32_t* __restrict__ rpi,
     const int32_t* __restrict__ prefix_lens, int B, int Hq, int Hkv, int G, int S, int chunk, float scale_log2,
     float v_scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
-    const int32_t* __restrict__ key_start = nullptr, int s_off = 0, int S_total = 0) {
+    const int32_t* __restrict__ key_start, int s_off, int S_total, rt::AppendArgs app) {
   // FP8 chunks hold at most 1408 keys, or 2048 when a context needs more
   // than 1024 of them: the smaller array keeps LDS from limiting occupancy.
   __shared__ int32_t s_idx[KV8 ? kMaxChunkFp8Lds : kMaxChunk];
-  rtk::dec::split_items<D, KV8>(blockIdx.x & 7, blockIdx.x >> 3, gridDim.x >> 3, threadIdx.x, s_idx, q, k_pool,
+  rtk::dec::split_items<D, KV8, 0, APP>(blockIdx.x & 7, blockIdx.x >> 3, gridDim.x >> 3, threadIdx.x, s_idx, q, k_pool,
                                 v_pool, req_to_token, stride, rpi, prefix_lens, B, Hq, Hkv, G, S, chunk, scale_log2,
-                                v_scale, ws_acc, ws_ml, key_start, s_off, S_total);
+                                v_scale, ws_acc, ws_ml, key_start, s_off, S_total, app);
 }
 
 // ----------------------------------------------------------------- fp32 --
@@ -310,14 +310,14 @@ __global__ void __launch_bounds__(64) decode_combine(const float* __restrict__ w
 
 // Resident 64-thread blocks of the bf16 split kernel on this device
 // (occupancy x compute units, a multiple of 8), queried once per device.
-template <int D, bool KV8>
+template <int D, bool KV8, bool APP = false>
 int resident_waves() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 2048;
   if (cached[dev] == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_bf16<D, KV8>, 64, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_bf16<D, KV8, APP>, 64, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 ||
         cus < 1)
       return 2048;
@@ -335,7 +335,7 @@ hipError_t launch_decode(const void* q, void* o, const void* k_pool, const void*
                    int64_t stride, const int32_t* rpi, const int32_t* plens, int B, int Hq, int Hkv,
                    DecodePlan pl, float scale_log2, float v_scale, int mode, float* ws_acc, float* ws_ml,
                    hipStream_t st, const int32_t* key_start = nullptr, int s_off = 0, int S_total = 0,
-                   hipEvent_t combine_after = nullptr) {
+                   hipEvent_t combine_after = nullptr, const rt::AppendArgs& app = rt::AppendArgs()) {
   // combine_after (optional): work on another stream that also writes
   // partials; the combine waits for it.  Returns the wait's status.
   const int G = Hq / Hkv;
@@ -344,17 +344,19 @@ hipError_t launch_decode(const void* q, void* o, const void* k_pool, const void*
   if (pl.chunk > (mode == kModeFp8Kv ? kMaxChunkFp8Lds : kMaxChunk)) return hipErrorInvalidValue;
   if (mode == RT_BF16 || mode == kModeFp8Kv) {
     const int64_t items = int64_t(B) * Hkv * pl.splits;
+#define RT_SPLIT_LAUNCH(K8, AP)                                                                                  \
+  do {                                                                                                           \
+    const int64_t grid = std::min<int64_t>(resident_waves<D, K8, AP>(), (items + 7) / 8 * 8);                   \
+    hipLaunchKernelGGL((decode_split_bf16<D, K8, AP>), dim3(uint32_t(grid)), dim3(64), 0, st, (const char*)q,   \
+                       (const char*)k_pool, (const char*)v_pool, r2t, stride, rpi, plens, B, Hq, Hkv, G, pl.splits, \
+                       pl.chunk, scale_log2, K8 ? v_scale : 1.0f, ws_acc, ws_ml, key_start, s_off, S_total, app);  \
+  } while (0)
     if (mode == RT_BF16) {
-      const int64_t grid = std::min<int64_t>(resident_waves<D, false>(), (items + 7) / 8 * 8);
-      hipLaunchKernelGGL((decode_split_bf16<D, false>), dim3(uint32_t(grid)), dim3(64), 0, st, (const char*)q,
-                         (const char*)k_pool, (const char*)v_pool, r2t, stride, rpi, plens, B, Hq, Hkv, G, pl.splits,
-                         pl.chunk, scale_log2, 1.0f, ws_acc, ws_ml, key_start, s_off, S_total);
+      if (app.slots) RT_SPLIT_LAUNCH(false, true); else RT_SPLIT_LAUNCH(false, false);
     } else {
-      const int64_t grid = std::min<int64_t>(resident_waves<D, true>(), (items + 7) / 8 * 8);
-      hipLaunchKernelGGL((decode_split_bf16<D, true>), dim3(uint32_t(grid)), dim3(64), 0, st, (const char*)q,
-                         (const char*)k_pool, (const char*)v_pool, r2t, stride, rpi, plens, B, Hq, Hkv, G, pl.splits,
-                         pl.chunk, scale_log2, v_scale, ws_acc, ws_ml, key_start, s_off, S_total);
+      if (app.slots) RT_SPLIT_LAUNCH(true, true); else RT_SPLIT_LAUNCH(true, false);
     }
+#undef RT_SPLIT_LAUNCH
     if (combine_after) {
       const hipError_t we = hipStreamWaitEvent(st, combine_after, 0);
       if (we != hipSuccess) return we;
@@ -376,7 +378,8 @@ int decode_entry(const char* name, const void* q, void* o, const void* k_pool, c
                  const int32_t* req_to_token, int32_t req_to_token_stride, const int32_t* req_pool_indices,
                  const int32_t* prefix_lens, int32_t batch, int32_t max_kv_len, int32_t num_q_heads,
                  int32_t num_kv_heads, int32_t head_dim, float sm_scale, float k_scale, float v_scale, int mode,
-                 void* workspace, int64_t workspace_bytes, void* stream) {
+                 void* workspace, int64_t workspace_bytes, void* stream,
+                 const rt::AppendArgs& app = rt::AppendArgs()) {
   const std::string fn(name);
   if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
       (head_dim != 64 && head_dim != 128) || max_kv_len < 1 || req_to_token_stride < max_kv_len ||
@@ -387,8 +390,10 @@ int decode_entry(const char* name, const void* q, void* o, const void* k_pool, c
   if (mode != RT_F32 && num_q_heads / num_kv_heads > 16)
     return rt::fail(RT_ERR_INVALID, fn + ": the bf16 path supports at most 16 query heads per KV head");
   if (batch == 0) return RT_OK;
-  if (!q || !o || !k_pool || !v_pool || !req_to_token || !prefix_lens || !workspace)
+  if (!q || !o || !k_pool || !v_pool || !req_to_token || !prefix_lens || !workspace ||
+      (app.slots && (!app.k_new || !app.v_new)))
     return rt::fail(RT_ERR_INVALID, fn + ": null pointer");
+  if (app.slots && mode == RT_F32) return rt::fail(RT_ERR_INVALID, fn + ": bf16 or FP8 pools only");
   const int64_t need = radix_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_kv_len);
   if (workspace_bytes < need)
     return rt::fail(RT_ERR_INVALID, fn + ": workspace too small (need " + std::to_string(need) + ")");
@@ -401,10 +406,10 @@ int decode_entry(const char* name, const void* q, void* o, const void* k_pool, c
       head_dim == 128
           ? launch_decode<128>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices,
                                prefix_lens, batch, num_q_heads, num_kv_heads, pl, scale_log2, v_scale, mode, ws_acc,
-                               ws_ml, st)
+                               ws_ml, st, nullptr, 0, 0, nullptr, app)
           : launch_decode<64>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices,
                               prefix_lens, batch, num_q_heads, num_kv_heads, pl, scale_log2, v_scale, mode, ws_acc,
-                              ws_ml, st);
+                              ws_ml, st, nullptr, 0, 0, nullptr, app);
   if (le != hipSuccess) return rt::fail(RT_ERR_HIP, fn + ": " + hipGetErrorString(le));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return rt::fail(RT_ERR_HIP, fn + " launch: " + hipGetErrorString(e));
@@ -588,7 +593,8 @@ int shared_entry(const char* name, const void* q, void* o, const void* k_pool, c
                  const int32_t* prefix_lens, const int32_t* shared_lens, const int32_t* group_start, int32_t batch,
                  int32_t n_groups, int32_t max_group_size, int32_t max_shared_len, int32_t max_private_len,
                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float sm_scale, float k_scale,
-                 float v_scale, bool kv8, void* workspace, int64_t workspace_bytes, void* stream) {
+                 float v_scale, bool kv8, void* workspace, int64_t workspace_bytes, void* stream,
+                 const rt::AppendArgs& app = rt::AppendArgs()) {
   const std::string fn(name);
   if (batch < 0 || n_groups < 0 || (batch > 0 && (n_groups < 1 || n_groups > batch)) || max_group_size < 1 ||
       max_shared_len < 0 || max_private_len < 1 || num_q_heads < 1 || num_kv_heads < 1 ||
@@ -600,7 +606,7 @@ int shared_entry(const char* name, const void* q, void* o, const void* k_pool, c
     return rt::fail(RT_ERR_INVALID, fn + ": context above 2097152");
   if (batch == 0) return RT_OK;
   if (!q || !o || !k_pool || !v_pool || !req_to_token || !prefix_lens || !shared_lens || !group_start ||
-      !workspace)
+      !workspace || (app.slots && (!app.k_new || !app.v_new)))
     return rt::fail(RT_ERR_INVALID, fn + ": null pointer");
   const int64_t need = radix_decode_shared_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, n_groups,
                                                            max_group_size, max_shared_len, max_private_len);
@@ -625,7 +631,8 @@ int shared_entry(const char* name, const void* q, void* o, const void* k_pool, c
     const int rc = rt::launch_shared_fused(q, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices,
                                            prefix_lens, shared_lens, group_start, n_groups, max_group_size, sp.n_a,
                                            sp.chunk_a, batch, sp.b.splits, sp.b.chunk, sp.total(), num_q_heads,
-                                           num_kv_heads, head_dim, scale_log2, v_scale, kv8, ws_acc, ws_ml, stream);
+                                           num_kv_heads, head_dim, scale_log2, v_scale, kv8, ws_acc, ws_ml, stream,
+                                           app);
     if (rc != RT_OK) return rc;
     if (head_dim == 128)
       hipLaunchKernelGGL((decode_combine<128, true>), dim3(uint32_t(int64_t(batch) * num_q_heads)), dim3(64), 0, st,
@@ -666,11 +673,11 @@ int shared_entry(const char* name, const void* q, void* o, const void* k_pool, c
   if (head_dim == 128)
     we = launch_decode<128>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
                        batch, num_q_heads, num_kv_heads, sp.b, scale_log2, v_scale, mode, ws_acc, ws_ml, st,
-                       shared_lens, sp.n_a, sp.total(), join);
+                       shared_lens, sp.n_a, sp.total(), join, app);
   else
     we = launch_decode<64>(q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
                       batch, num_q_heads, num_kv_heads, sp.b, scale_log2, v_scale, mode, ws_acc, ws_ml, st,
-                      shared_lens, sp.n_a, sp.total(), join);
+                      shared_lens, sp.n_a, sp.total(), join, app);
   if (we != hipSuccess) return rt::fail(RT_ERR_HIP, fn + ": " + hipGetErrorString(we));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return rt::fail(RT_ERR_HIP, fn + " launch: " + hipGetErrorString(e));
@@ -720,4 +727,83 @@ extern "C" int radix_decode_attention_shared_fp8kv(const void* q, void* o, const
                       req_to_token_stride, req_pool_indices, prefix_lens, shared_lens, group_start, batch, n_groups,
                       max_group_size, max_shared_len, max_private_len, num_q_heads, num_kv_heads, head_dim, sm_scale,
                       k_scale, v_scale, true, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------ decode with the append --
+namespace {
+rt::AppendArgs append_args(int32_t* req_to_token, void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                           const int32_t* new_slots, float k_scale, float v_scale) {
+  rt::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slots = new_slots;
+  a.r2t = req_to_token;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_inv = 1.f / k_scale;
+  a.v_inv = 1.f / v_scale;
+  return a;
+}
+}  // namespace
+
+extern "C" int radix_decode_attention_append(const void* q, void* o, void* k_pool, void* v_pool,
+                                             int32_t* req_to_token, int32_t req_to_token_stride,
+                                             const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                             int32_t batch, int32_t max_kv_len, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                                             const void* k_new, const void* v_new, const int32_t* new_slots,
+                                             void* workspace, int64_t workspace_bytes, void* stream) {
+  static const char* kName = "radix_decode_attention_append";
+  if (!new_slots) return rt::fail(RT_ERR_INVALID, std::string(kName) + ": null pointer");
+  return decode_entry(kName, q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
+                      batch, max_kv_len, num_q_heads, num_kv_heads, head_dim, sm_scale, 1.f, 1.f, RT_BF16, workspace,
+                      workspace_bytes, stream,
+                      append_args(req_to_token, k_pool, v_pool, k_new, v_new, new_slots, 1.f, 1.f));
+}
+
+extern "C" int radix_decode_attention_append_fp8kv(const void* q, void* o, void* k_pool, void* v_pool,
+                                                   int32_t* req_to_token, int32_t req_to_token_stride,
+                                                   const int32_t* req_pool_indices, const int32_t* prefix_lens,
+                                                   int32_t batch, int32_t max_kv_len, int32_t num_q_heads,
+                                                   int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                                                   float k_scale, float v_scale, const void* k_new,
+                                                   const void* v_new, const int32_t* new_slots, void* workspace,
+                                                   int64_t workspace_bytes, void* stream) {
+  static const char* kName = "radix_decode_attention_append_fp8kv";
+  if (!new_slots) return rt::fail(RT_ERR_INVALID, std::string(kName) + ": null pointer");
+  return decode_entry(kName, q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
+                      batch, max_kv_len, num_q_heads, num_kv_heads, head_dim, sm_scale, k_scale, v_scale, kModeFp8Kv,
+                      workspace, workspace_bytes, stream,
+                      append_args(req_to_token, k_pool, v_pool, k_new, v_new, new_slots, k_scale, v_scale));
+}
+
+extern "C" int radix_decode_attention_shared_append(
+    const void* q, void* o, void* k_pool, void* v_pool, int32_t* req_to_token, int32_t req_to_token_stride,
+    const int32_t* req_pool_indices, const int32_t* prefix_lens, const int32_t* shared_lens,
+    const int32_t* group_start, int32_t batch, int32_t n_groups, int32_t max_group_size, int32_t max_shared_len,
+    int32_t max_private_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+    const void* k_new, const void* v_new, const int32_t* new_slots, void* workspace, int64_t workspace_bytes,
+    void* stream) {
+  static const char* kName = "radix_decode_attention_shared_append";
+  if (!new_slots) return rt::fail(RT_ERR_INVALID, std::string(kName) + ": null pointer");
+  return shared_entry(kName, q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
+                      shared_lens, group_start, batch, n_groups, max_group_size, max_shared_len, max_private_len,
+                      num_q_heads, num_kv_heads, head_dim, sm_scale, 1.f, 1.f, false, workspace, workspace_bytes,
+                      stream, append_args(req_to_token, k_pool, v_pool, k_new, v_new, new_slots, 1.f, 1.f));
+}
+
+extern "C" int radix_decode_attention_shared_append_fp8kv(
+    const void* q, void* o, void* k_pool, void* v_pool, int32_t* req_to_token, int32_t req_to_token_stride,
+    const int32_t* req_pool_indices, const int32_t* prefix_lens, const int32_t* shared_lens,
+    const int32_t* group_start, int32_t batch, int32_t n_groups, int32_t max_group_size, int32_t max_shared_len,
+    int32_t max_private_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+    float k_scale, float v_scale, const void* k_new, const void* v_new, const int32_t* new_slots, void* workspace,
+    int64_t workspace_bytes, void* stream) {
+  static const char* kName = "radix_decode_attention_shared_append_fp8kv";
+  if (!new_slots) return rt::fail(RT_ERR_INVALID, std::string(kName) + ": null pointer");
+  return shared_entry(kName, q, o, k_pool, v_pool, req_to_token, req_to_token_stride, req_pool_indices, prefix_lens,
+                      shared_lens, group_start, batch, n_groups, max_group_size, max_shared_len, max_private_len,
+                      num_q_heads, num_kv_heads, head_dim, sm_scale, k_scale, v_scale, true, workspace,
+                      workspace_bytes, stream,
+                      append_args(req_to_token, k_pool, v_pool, k_new, v_new, new_slots, k_scale, v_scale));
 }

@@ -9,6 +9,7 @@
 #include <type_traits>
 
 #include "dev_common.h"
+#include "rt_internal.h"
 
 namespace rtk {
 namespace dec {
@@ -43,13 +44,21 @@ struct DecBlock {
 // WIN / 2 keys, and the wave fetches each next window's indices while it
 // streams the current one (so a chunk may be any length).  Needs only its
 // own wave: it uses no workgroup barrier.
-template <int D, bool KV8, int WIN = 0>
+//
+// APP (with app.slots != nullptr): the launch also appends each
+// request's new token, the key at position prefix_lens[b].  The item whose
+// chunk holds that key takes its slot from app.slots[b] (the table entry is
+// not written yet), first stores the token's K and V rows of its KV head at
+// that slot and, for KV head 0, the slot-table entry, and waits for those
+// stores before its loads; no other item reads that key.
+template <int D, bool KV8, int WIN = 0, bool APP = false>
 __device__ __forceinline__ void split_items(
     int xcd, int local, int per_xcd, int lane, int32_t* s_idx, const char* __restrict__ q,
     const char* __restrict__ k_pool, const char* __restrict__ v_pool, const int32_t* __restrict__ req_to_token,
     int64_t stride, const int32_t* __restrict__ rpi, const int32_t* __restrict__ prefix_lens, int B, int Hq,
     int Hkv, int G, int S, int chunk, float scale_log2, float v_scale, float* __restrict__ ws_acc,
-    float* __restrict__ ws_ml, const int32_t* __restrict__ key_start, int s_off, int S_total) {
+    float* __restrict__ ws_ml, const int32_t* __restrict__ key_start, int s_off, int S_total,
+    const rt::AppendArgs& app = rt::AppendArgs()) {
   // key_start (optional): request b's chunks cover keys key_start[b] ..
   // prefix_lens[b] (the shared-prefix decode's private tails); its partials
   // go to split slots s_off .. s_off + S - 1 of S_total (default: S).
@@ -74,7 +83,8 @@ __device__ __forceinline__ void split_items(
     const int kv_len = prefix_lens[b] + 1;
     const int start = (key_start ? key_start[b] : 0) + s * chunk;
     const int end = min(kv_len, start + chunk);
-    const int32_t* idx_row = req_to_token + int64_t(rpi ? rpi[b] : b) * stride;
+    const int64_t row = rpi ? rpi[b] : b;
+    const int32_t* idx_row = req_to_token + row * stride;
     const char* kbase = k_pool + (int64_t(kvh) * D + 8 * grp) * EB;
     const char* vbase = v_pool + (int64_t(kvh) * D + VW * col) * EB;
 
@@ -101,6 +111,11 @@ __device__ __forceinline__ void split_items(
     constexpr int H = WIN / 2;           // keys per window of the ring
     const int n_keys = end - start;
     const int32_t* src = idx_row + start;
+    // Appending: the chunk holding the new token (its last key) reads that
+    // key's slot from app.slots.
+    const bool owner = APP && start < kv_len && end == kv_len;
+    const int own = owner ? n_keys - 1 : -1;
+    const int32_t new_slot = owner ? app.slots[b] : 0;
     __builtin_amdgcn_wave_barrier();
     {
       const int n = WIN ? min(n_keys, WIN) : n_keys;   // the ring's first two windows
@@ -110,7 +125,7 @@ __device__ __forceinline__ void split_items(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int i = base + 64 * u + lane;
-          v[u] = i < n ? src[i] : 0;
+          v[u] = i < n ? ((APP && i == own) ? new_slot : src[i]) : 0;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -120,6 +135,37 @@ __device__ __forceinline__ void split_items(
       }
     }
     __builtin_amdgcn_wave_barrier();
+
+    if (APP && owner) {
+      // The new token's K and V rows of this KV head (D / 8 lanes, 8
+      // elements each), its slot-table entry (KV head 0), then a wait for
+      // the stores: this wave's loads below read that row back.
+      const int64_t src_off = (int64_t(b) * Hkv + kvh) * D * 2;
+      const int64_t dst_off = int64_t(new_slot) * row_bytes + int64_t(kvh) * D * EB;
+      if (lane < D / 8) {
+        const u32x4 kw = ld16(static_cast<const char*>(app.k_new) + src_off + 16 * lane);
+        const u32x4 vw = ld16(static_cast<const char*>(app.v_new) + src_off + 16 * lane);
+        char* kd = static_cast<char*>(app.k_pool) + dst_off;
+        char* vd = static_cast<char*>(app.v_pool) + dst_off;
+        if constexpr (KV8) {
+          u32x2 ko = {0u, 0u}, vo = {0u, 0u};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t kb16 = (kw[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+            const uint32_t vb16 = (vw[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+            ko[i >> 2] |= f32_to_e4m3(__uint_as_float(kb16 << 16) * app.k_inv) << (8 * (i & 3));
+            vo[i >> 2] |= f32_to_e4m3(__uint_as_float(vb16 << 16) * app.v_inv) << (8 * (i & 3));
+          }
+          *reinterpret_cast<u32x2*>(kd + 8 * lane) = ko;
+          *reinterpret_cast<u32x2*>(vd + 8 * lane) = vo;
+        } else {
+          *reinterpret_cast<u32x4*>(kd + 16 * lane) = kw;
+          *reinterpret_cast<u32x4*>(vd + 16 * lane) = vw;
+        }
+      }
+      if (kvh == 0 && lane == 0) app.r2t[row * stride + (kv_len - 1)] = new_slot;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
 
     floatx4 o[VW];
 #pragma unroll
@@ -228,7 +274,7 @@ __device__ __forceinline__ void split_items(
 #pragma unroll
             for (int u = 0; u < PU; ++u) {
               const int k = pend + 64 * u + lane;
-              pre[u] = k < n_keys ? src[k] : 0;
+              pre[u] = k < n_keys ? ((APP && k == own) ? new_slot : src[k]) : 0;
             }
           }
         }

@@ -480,14 +480,14 @@ __global__ void __launch_bounds__(64 * kWaves, RB == 1 ? kWavesPerSimd : 1) exte
 // The two parts share no data, so they run side by side on the chip instead
 // of one launch after the other.
 constexpr int kFusedRing = 1024;
-template <int D, bool KV8>
+template <int D, bool KV8, bool APP = false>
 __global__ void __launch_bounds__(64 * kWaves, kWavesPerSimd) shared_decode_fused(
     const char* __restrict__ q, const char* __restrict__ k_pool, const char* __restrict__ v_pool,
     const int32_t* __restrict__ req_to_token, int64_t stride, const int32_t* __restrict__ rpi,
     const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ shared_lens,
     const int32_t* __restrict__ group_start, int n_groups, int B, int Hq, int Hkv, int G, int n_qt, int n_chunks,
     int chunk_keys, int S_b, int chunk_b, int S_total, float scale_log2, float v_scale, float* __restrict__ ws_acc,
-    float* __restrict__ ws_ml, int nA, int nA_pad, int nB) {
+    float* __restrict__ ws_ml, int nA, int nA_pad, int nB, rt::AppendArgs app) {
   __shared__ int32_t s_idx[kWaves][kFusedRing];
   const int bid = int(blockIdx.x);
   if (bid < nA) {
@@ -499,11 +499,11 @@ __global__ void __launch_bounds__(64 * kWaves, kWavesPerSimd) shared_decode_fuse
   if (bid < nA_pad) return;
   const int j = bid - nA_pad;                                          // j % 8 is this workgroup's XCD
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
-  rtk::dec::split_items<D, KV8, kFusedRing>(j & 7, (j >> 3) * kWaves + wave, (nB >> 3) * kWaves,
+  rtk::dec::split_items<D, KV8, kFusedRing, APP>(j & 7, (j >> 3) * kWaves + wave, (nB >> 3) * kWaves,
                                             int(threadIdx.x) & 63,
                                 s_idx[wave], q, k_pool, v_pool, req_to_token, stride, rpi, prefix_lens, B, Hq, Hkv,
                                 G, S_b, chunk_b, scale_log2, v_scale, ws_acc, ws_ml, shared_lens, n_chunks,
-                                S_total);
+                                S_total, app);
 }
 
 
@@ -623,7 +623,8 @@ int launch_shared_fused(const void* q, const void* k_pool, const void* v_pool, c
                         int64_t stride, const int32_t* rpi, const int32_t* prefix_lens, const int32_t* shared_lens,
                         const int32_t* group_start, int n_groups, int max_group_size, int n_chunks, int chunk_keys,
                         int batch, int S_b, int chunk_b, int S_total, int Hq, int Hkv, int D, float scale_log2,
-                        float v_scale, bool kv8, float* ws_acc, float* ws_ml, void* stream) {
+                        float v_scale, bool kv8, float* ws_acc, float* ws_ml, void* stream,
+                        const AppendArgs& app) {
   hipStream_t st = (hipStream_t)stream;
   const int G = Hq / Hkv;
   const int64_t item_rows = kWaves * 32 * kRB;
@@ -636,18 +637,23 @@ int launch_shared_fused(const void* q, const void* k_pool, const void* v_pool, c
   if (chunk_keys % kBN != 0) return rt::fail(RT_ERR_INVALID, "shared pass: chunk not a multiple of the tile");
   if (chunk_b < 1) return rt::fail(RT_ERR_INVALID, "single-launch shared decode: empty private chunk");
   if (nA_pad + nB == 0) return RT_OK;
-#define RT_FUSED_LAUNCH(DD, K8)                                                                                    \
-  hipLaunchKernelGGL((shared_decode_fused<DD, K8>), dim3(uint32_t(nA_pad + nB)), dim3(64 * kWaves), 0, st,        \
+#define RT_FUSED_LAUNCH1(DD, K8, AP)                                                                               \
+  hipLaunchKernelGGL((shared_decode_fused<DD, K8, AP>), dim3(uint32_t(nA_pad + nB)), dim3(64 * kWaves), 0, st,    \
                      (const char*)q, (const char*)k_pool, (const char*)v_pool, req_to_token, stride, rpi,          \
                      prefix_lens, shared_lens, group_start, n_groups, batch, Hq, Hkv, G, int(n_qt), n_chunks,       \
                      chunk_keys, S_b, chunk_b, S_total, scale_log2, v_scale, ws_acc, ws_ml, int(nA), int(nA_pad),   \
-                     int(nB))
+                     int(nB), app)
+#define RT_FUSED_LAUNCH(DD, K8)                                                                                    \
+  do {                                                                                                             \
+    if (app.slots) RT_FUSED_LAUNCH1(DD, K8, true); else RT_FUSED_LAUNCH1(DD, K8, false);                           \
+  } while (0)
   if (D == 128) {
     if (kv8) RT_FUSED_LAUNCH(128, true); else RT_FUSED_LAUNCH(128, false);
   } else {
     if (kv8) RT_FUSED_LAUNCH(64, true); else RT_FUSED_LAUNCH(64, false);
   }
 #undef RT_FUSED_LAUNCH
+#undef RT_FUSED_LAUNCH1
   return RT_OK;
 }
 

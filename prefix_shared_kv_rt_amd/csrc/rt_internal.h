@@ -9,6 +9,21 @@ namespace rt {
 // Records `msg` as the calling thread's last error and returns `code`.
 int fail(int code, const std::string& msg);
 
+// Each request's new token, stored by the decode launch itself (decode_append
+// folded into the attention): k_new / v_new bf16 [batch, Hkv, D] go to the
+// pools at slots[b] (as E4M3 codes of x * k_inv, x * v_inv over FP8 pools)
+// and slots[b] into the slot table at (row of b, prefix_lens[b]).  slots ==
+// nullptr: nothing to append.
+struct AppendArgs {
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  const int32_t* slots = nullptr;
+  int32_t* r2t = nullptr;
+  void* k_pool = nullptr;
+  void* v_pool = nullptr;
+  float k_inv = 1.f, v_inv = 1.f;
+};
+
 // The shared-prefix pass of radix_decode_attention_shared (extend.hip):
 // for each group of consecutive decode rows (group_start), KV head, query
 // tile and chunk of chunk_keys shared keys, write the split-K partial of
@@ -29,6 +44,7 @@ int launch_shared_fused(const void* q, const void* k_pool, const void* v_pool, c
                         int64_t stride, const int32_t* rpi, const int32_t* prefix_lens, const int32_t* shared_lens,
                         const int32_t* group_start, int n_groups, int max_group_size, int n_chunks, int chunk_keys,
                         int batch, int S_b, int chunk_b, int S_total, int Hq, int Hkv, int D, float scale_log2,
-                        float v_scale, bool kv8, float* ws_acc, float* ws_ml, void* stream);
+                        float v_scale, bool kv8, float* ws_acc, float* ws_ml, void* stream,
+                        const AppendArgs& app = AppendArgs());
 int fused_max_private_chunk();
 }  // namespace rt

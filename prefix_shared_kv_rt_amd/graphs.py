@@ -82,11 +82,14 @@ class DecodeGraphs:
     def _launch(self, bs, stream):
         rt = self.rt
         rows, pos, slots = self.idx[0, :bs], self.idx[1, :bs], self.idx[2, :bs]
-        if rt.kv_fp8_scales:
-            B.decode_append_fp8(rt.r2t_dev, rows, pos, slots, rt.k_pool, rt.v_pool, self.k[:bs], self.v[:bs],
-                                *rt.kv_fp8_scales, stream=stream)
-            B.radix_decode_attention_fp8kv(self.q[:bs], self.o[:bs], rt.k_pool, rt.v_pool, rt.r2t_dev, rows, pos,
-                                           self.max_kv, rt.sm_scale, self.ws, *rt.kv_fp8_scales, stream=stream)
+        if rt.kv_fp8_scales:   # append and decode in the decode's launches
+            B.radix_decode_attention_append_fp8kv(self.q[:bs], self.o[:bs], rt.k_pool, rt.v_pool, rt.r2t_dev, rows,
+                                                  pos, self.max_kv, rt.sm_scale, self.k[:bs], self.v[:bs], slots,
+                                                  self.ws, *rt.kv_fp8_scales, stream=stream)
+        elif rt.dtype == torch.bfloat16:
+            B.radix_decode_attention_append(self.q[:bs], self.o[:bs], rt.k_pool, rt.v_pool, rt.r2t_dev, rows, pos,
+                                            self.max_kv, rt.sm_scale, self.k[:bs], self.v[:bs], slots, self.ws,
+                                            stream=stream)
         else:
             B.decode_append(rt.r2t_dev, rows, pos, slots, rt.k_pool, rt.v_pool, self.k[:bs], self.v[:bs],
                             stream=stream)

@@ -161,6 +161,8 @@ class RadixRuntime:
 
     def run_decode(self, rows, positions, slots, q, k_new, v_new, shared_len=0):
         """Write the new slots into the table, store the new rows, decode.
+        bf16 and FP8 pools do all three in the decode's own launches (the
+        _append decode calls); fp32 pools run decode_append first.
         shared_len > 0: every row's first shared_len slots are the same (the
         caller checked), so the batch decodes as one group through
         radix_decode_attention_shared, reading those K/V once."""
@@ -171,10 +173,9 @@ class RadixRuntime:
             rows_d, pos_d, slots_d = self._to_dev(rows), self._to_dev(positions), self._to_dev(slots)
             o = torch.empty_like(q)
             max_kv = int(max(positions)) + 1
-            if self.kv_fp8_scales:
-                B.decode_append_fp8(self.r2t_dev, rows_d, pos_d, slots_d, self.k_pool, self.v_pool, k_new, v_new,
-                                    *self.kv_fp8_scales, stream=self.stream)
-            else:
+            fused = self.kv_fp8_scales is not None or self.dtype == torch.bfloat16
+            sc = tuple(self.kv_fp8_scales or ())
+            if not fused:
                 B.decode_append(self.r2t_dev, rows_d, pos_d, slots_d, self.k_pool, self.v_pool, k_new, v_new,
                                 stream=self.stream)
             if shared_len > 0:
@@ -184,26 +185,29 @@ class RadixRuntime:
                 need = B.radix_decode_shared_workspace_bytes(n, self.hq, self.hkv, self.d, 1, n, shared_len, priv)
                 if self._ws.numel() < need:
                     self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
-                # the timing events bracket the attention launch alone (its
+                # the timing events bracket the decode launches alone (their
                 # inputs and workspace are ready before the first event)
                 e0 = self._event() if self.events is not None else None
+                args = (q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, sl, gs, n, shared_len, priv,
+                        self.sm_scale)
                 if self.kv_fp8_scales:
-                    B.radix_decode_attention_shared_fp8kv(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d,
-                                                          sl, gs, n, shared_len, priv, self.sm_scale, self._ws,
-                                                          *self.kv_fp8_scales, stream=self.stream)
+                    B.radix_decode_attention_shared_append_fp8kv(*args, k_new, v_new, slots_d, self._ws, *sc,
+                                                                 stream=self.stream)
+                elif fused:
+                    B.radix_decode_attention_shared_append(*args, k_new, v_new, slots_d, self._ws,
+                                                           stream=self.stream)
                 else:
-                    B.radix_decode_attention_shared(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, sl,
-                                                    gs, n, shared_len, priv, self.sm_scale, self._ws,
-                                                    stream=self.stream)
+                    B.radix_decode_attention_shared(*args, self._ws, stream=self.stream)
             else:
                 ws = self.workspace(n, max_kv)
                 e0 = self._event() if self.events is not None else None
+                args = (q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, max_kv, self.sm_scale)
                 if self.kv_fp8_scales:
-                    B.radix_decode_attention_fp8kv(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d,
-                                                   max_kv, self.sm_scale, ws, *self.kv_fp8_scales, stream=self.stream)
+                    B.radix_decode_attention_append_fp8kv(*args, k_new, v_new, slots_d, ws, *sc, stream=self.stream)
+                elif fused:
+                    B.radix_decode_attention_append(*args, k_new, v_new, slots_d, ws, stream=self.stream)
                 else:
-                    B.radix_decode_attention(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows_d, pos_d, max_kv,
-                                             self.sm_scale, ws, stream=self.stream)
+                    B.radix_decode_attention(*args, ws, stream=self.stream)
             if e0 is not None:
                 kv = np.asarray(positions, dtype=np.float64) + 1
                 eb, ekv = q.element_size(), self.k_pool.element_size()
