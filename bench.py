@@ -13,11 +13,13 @@ whole path:
                             the req_to_token rows hold
   device extend attention   suffix rows against prefix + suffix K/V
   host   rt_decode_slots    one slot per request for its first generated token
-  device decode_append      the new token's req_to_token entry and K/V row
-  device decode attention   radix_decode_attention_shared: the batch is one
-                            group sharing the prefix's slots, read once for
-                            all 64 queries; each request's own tail split-K
-                            (--decode plain: split-K over whole contexts)
+  device decode attention   radix_decode_attention_shared_append: the new
+                            token's req_to_token entry and K/V row are
+                            written by the decode's own launches; the batch
+                            is one group sharing the prefix's slots, read
+                            once for all 64 queries; each request's own tail
+                            split-K (--decode plain: split-K over whole
+                            contexts, radix_decode_attention_append)
   host   rt_finish_batch    insert prompt + token, free duplicates, unlock
 
 Q/K/V of every step are generated into HBM before the timed region.  After
@@ -290,21 +292,25 @@ class FewShotBench:
         f = self.Bm.radix_extend_attention_fp8kv if self.fp8 else self.Bm.radix_extend_attention
         f(q, o, self.k_pool, self.v_pool, self.r2t_dev, rows, pl, el, qo, max_e, self.sm_scale, stream=self.stream)
 
-    def _decode(self, qd, d_rows, d_pos):
+    def _decode(self, qd, kd, vd, d_rows, d_pos, d_dslots):
+        """The decode step: each request's new token (K/V row kd / vd, slot
+        d_dslots) is stored and attended to by the decode call's own
+        launches (the _append entry points)."""
         B, S, P0 = self.B, self.SUFFIX, self.PREFIX
         Bm = self.Bm
         if self.shared_decode:
-            dec = Bm.radix_decode_attention_shared_fp8kv if self.fp8 else Bm.radix_decode_attention_shared
+            dec = Bm.radix_decode_attention_shared_append_fp8kv if self.fp8 else Bm.radix_decode_attention_shared_append
             dec(qd, self.o_dec, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pos, self.sl_dev, self.gs_dev, B,
-                P0, S + 1, self.sm_scale, self.ws_shared, stream=self.stream)
+                P0, S + 1, self.sm_scale, kd, vd, d_dslots, self.ws_shared, stream=self.stream)
         else:
-            dec = Bm.radix_decode_attention_fp8kv if self.fp8 else Bm.radix_decode_attention
+            dec = Bm.radix_decode_attention_append_fp8kv if self.fp8 else Bm.radix_decode_attention_append
             dec(qd, self.o_dec, self.k_pool, self.v_pool, self.r2t_dev, d_rows, d_pos, P0 + S + 1, self.sm_scale,
+                kd, vd, d_dslots,
                 self.ws, stream=self.stream)
 
     def settle_on_step(self, i, ms=200.0):
         """Untimed, after the warm-up steps: step i's launches (the K/V
-        scatter, extend, decode append and decode attention of the last
+        scatter, extend and decode (with its append) of the last
         warm-up step, whose rows, metadata and K/V are still in place; every
         launch rewrites the same values) again and again for about ``ms``
         milliseconds, so that the timed steps start at the clock the chip
@@ -322,23 +328,22 @@ class FewShotBench:
             for _ in range(4):
                 self._store_extend(k, v, d_rows, d_pl, d_el, d_qo, max_e)
                 self._extend(q, self.o_ext, d_rows, d_pl, d_el, d_qo, max_e)
-                append = Bm.decode_append_fp8 if self.fp8 else Bm.decode_append
-                append(self.r2t_dev, d_rows, d_pos, d_dslots, self.k_pool, self.v_pool, kd, vd, stream=self.stream)
-                self._decode(qd, d_rows, d_pos)
+                self._decode(qd, kd, vd, d_rows, d_pos, d_dslots)
             self.stream.synchronize()
 
     def replay_decode(self, i, reps=10):
-        """Untimed, after the timed steps: the decode attention of step i
-        (the last one, whose rows and K/V are still in place) again, reps
-        times, each bracketed by HIP events; returns the mean in seconds."""
+        """Untimed, after the timed steps: the decode call of step i (the
+        last one, whose rows and K/V are still in place; its append rewrites
+        the same entry and row) again, reps times, each bracketed by HIP
+        events; returns the mean in seconds."""
         torch = self.torch
         d_pl, d_el, d_qo, d_rows, d_dslots = self.meta_views[i % 2]
-        qd = self.inputs[i][3]
+        qd, kd, vd = self.inputs[i][3:6]
         ms = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(self.stream)
-            self._decode(qd, d_rows, self.pos_dev)
+            self._decode(qd, kd, vd, d_rows, self.pos_dev, d_dslots)
             e1.record(self.stream)
             ms.append((e0, e1))
         self.stream.synchronize()
@@ -406,14 +411,9 @@ class FewShotBench:
         self._extend(q, self.o_ext, d_rows, d_pl, d_el, d_qo, max_e)
         if ev is not None:
             ev[1].record(self.stream)
-        d_pos = self.pos_dev
-        if self.fp8:
-            Bm.decode_append_fp8(self.r2t_dev, d_rows, d_pos, d_dslots, self.k_pool, self.v_pool, kd, vd,
-                                 stream=self.stream)
-        else:  # slot-table entry and K/V row of the new token in one launch
-            Bm.decode_append(self.r2t_dev, d_rows, d_pos, d_dslots, self.k_pool, self.v_pool, kd, vd,
-                             stream=self.stream)
-        self._decode(qd, d_rows, d_pos)
+        # decode step: the new token's slot-table entry and K/V row are
+        # written by the decode's own launches
+        self._decode(qd, kd, vd, d_rows, self.pos_dev, d_dslots)
         # finish: prompt + generated token into the tree
         Bm.rt_finish_batch(self.tree, full, self.full_off, self.r2t_host, rows, pl, nodes)
         self.last_prefix_lens = pl
@@ -546,9 +546,9 @@ class DecodeBench:
     Hq 64 / Hkv 8 / D 128.  fork: 16 prompts of 2048 tokens, each matched
     whole by 8 branches (batch 128), Hq 32 / Hkv 8 / D 128.  Prompt K/V are
     scattered into the pool with kv_store (no extend attention); each timed
-    step allocates one slot per request, writes its slot-table entry and K/V
-    row (decode_append, one launch), and runs decode attention over the whole
-    context."""
+    step allocates one slot per request and runs decode attention over the
+    whole context, whose launches also write each request's slot-table entry
+    and K/V row (the _append decode entry points)."""
 
     def __init__(self, name, torch, Bm, gen_t, n_steps, kv_dtype="bf16", shared_decode=False):
         self.torch, self.Bm, self.T = torch, Bm, gen_t
@@ -724,26 +724,23 @@ class DecodeBench:
 
     def launch_step(self, s, d_pos, d_slots):
         """Step s's GPU work after its metadata copy, on the bench's stream."""
-        self.launch_append(s, d_pos, d_slots)
-        self.launch_decode(s, d_pos)
+        self.launch_decode(s, d_pos, d_slots)
 
-    def launch_append(self, s, d_pos, d_slots):
-        """Slot-table entry and K/V row of each request's new token, one launch."""
-        append = self.Bm.decode_append_fp8 if self.fp8 else self.Bm.decode_append
-        append(self.r2t_dev, self.rows_dev, d_pos, d_slots, self.k_pool, self.v_pool, self.k[s], self.v[s],
-               stream=self.stream)
-
-    def launch_decode(self, s, d_pos):
-        Bm = self.Bm
+    def launch_decode(self, s, d_pos, d_slots):
+        """Decode with the new tokens' append (slot-table entry and K/V row
+        of each request) in the decode's own launches."""
+        Bm = self.Bm   # FP8 pools: scales 1 (the binding's defaults)
         if self.shared_decode:
-            decode = Bm.radix_decode_attention_shared_fp8kv if self.fp8 else Bm.radix_decode_attention_shared
+            decode = Bm.radix_decode_attention_shared_append_fp8kv if self.fp8 else \
+                Bm.radix_decode_attention_shared_append
             decode(self.q[s], self.o, self.k_pool, self.v_pool, self.r2t_dev, self.rows_dev, d_pos, self.sl_dev,
-                   self.gs_dev, self.B // self.groups, self.shared, self.private + s + 1, self.sm_scale,
-                   self.ws_shared, stream=self.stream)
+                   self.gs_dev, self.B // self.groups, self.shared, self.private + s + 1, self.sm_scale, self.k[s],
+                   self.v[s], d_slots, self.ws_shared, stream=self.stream)
         else:
-            decode = Bm.radix_decode_attention_fp8kv if self.fp8 else Bm.radix_decode_attention
+            decode = Bm.radix_decode_attention_append_fp8kv if self.fp8 else Bm.radix_decode_attention_append
             decode(self.q[s], self.o, self.k_pool, self.v_pool, self.r2t_dev, self.rows_dev, d_pos,
-                   self.prompt_len + s + 1, self.sm_scale, self.ws, stream=self.stream)
+                   self.prompt_len + s + 1, self.sm_scale, self.k[s], self.v[s], d_slots, self.ws,
+                   stream=self.stream)
 
     def step(self, s, timed):
         torch, Bm = self.torch, self.Bm
@@ -756,11 +753,10 @@ class DecodeBench:
             meta = self.meta_dev[s]
             Bm.rt_copy_from_host(meta, self.meta_host_t[s], stream=self.stream)
             d_pos, d_slots = meta[:self.B], meta[self.B:]
-            self.launch_append(s, d_pos, d_slots)
             if timed:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(self.stream)
-            self.launch_decode(s, d_pos)
+            self.launch_decode(s, d_pos, d_slots)
             if timed:
                 e1.record(self.stream)
                 self.events.append((e0, e1, int(pos[0]) + 1))

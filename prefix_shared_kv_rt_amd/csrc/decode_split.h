@@ -125,7 +125,7 @@ __device__ __forceinline__ void split_items(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int i = base + 64 * u + lane;
-          v[u] = i < n ? ((APP && i == own) ? new_slot : src[i]) : 0;
+          v[u] = i < n ? src[i] : 0;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -133,6 +133,8 @@ __device__ __forceinline__ void split_items(
           if (i < n) s_idx[i] = v[u];
         }
       }
+      // the new token's entry (LDS accesses of one wave complete in order)
+      if (APP && own >= 0 && own < n && lane == 0) s_idx[own] = new_slot;
     }
     __builtin_amdgcn_wave_barrier();
 
@@ -274,7 +276,7 @@ __device__ __forceinline__ void split_items(
 #pragma unroll
             for (int u = 0; u < PU; ++u) {
               const int k = pend + 64 * u + lane;
-              pre[u] = k < n_keys ? ((APP && k == own) ? new_slot : src[k]) : 0;
+              pre[u] = k < n_keys ? src[k] : 0;
             }
           }
         }
@@ -287,6 +289,7 @@ __device__ __forceinline__ void split_items(
               const int k = pend + 64 * u + lane;
               if (k < n_keys) s_idx[k & (WIN - 1)] = pre[u];
             }
+            if (APP && own >= pend && own < pend + H && lane == 0) s_idx[own & (WIN - 1)] = new_slot;
             pend = -1;
           }
         }
