@@ -436,12 +436,16 @@ class FewShotBench:
             rows_keys = float(np.sum(pl.astype(np.float64) * el + el.astype(np.float64) * (el + 1) / 2))
             self.flops.append(4.0 * self.D * self.HQ * rows_keys)
             self.ext_rows.append(int(el.sum()))
+        # the decode's own append: each new token's K and V rows read (bf16)
+        # and written into the pool
+        append = B * self.HKV * self.D * (2 + eb) * 2
         for pl, el in self.step_lens:
             self.ext_tokens.append(int(el.sum()) + B)
-            self.dec_bytes.append(B * (P0 + S + 1) * (self.HKV * self.D * eb * 2 + 4) + 2 * B * self.HQ * self.D * 2)
+            self.dec_bytes.append(B * (P0 + S + 1) * (self.HKV * self.D * eb * 2 + 4) + 2 * B * self.HQ * self.D * 2
+                                  + append)
             # the prefix once, every request's own tail
             self.dec_distinct.append(P0 * self.HKV * self.D * eb * 2 + B * (S + 1) * (self.HKV * self.D * eb * 2 + 4)
-                                     + 2 * B * self.HQ * self.D * 2)
+                                     + 2 * B * self.HQ * self.D * 2 + append)
 
 
 def run_few_shot(args, torch):
@@ -502,7 +506,7 @@ def run_few_shot(args, torch):
             "batch": fb.B, "prefix_len": fb.PREFIX, "suffix_len": fb.SUFFIX, "num_q_heads": fb.HQ,
             "num_kv_heads": fb.HKV, "head_dim": fb.D, "pool_slots": fb.SLOTS,
             "kv_dtype": "fp8_e4m3" if fb.fp8 else "bf16", "page_size": fb.page_size,
-            "decode": "radix_decode_attention_shared" if fb.shared_decode else "radix_decode_attention",
+            "decode": "radix_decode_attention_shared_append" if fb.shared_decode else "radix_decode_attention_append",
         },
         "roofline": {
             "bound": "mfma",
@@ -794,11 +798,14 @@ def run_decode_bench(args, torch):
     row = db.HKV * db.D * (1 if db.fp8 else 2)   # one K (or V) pool row
     # every request's whole context (the shared part once per request: what
     # the plain decode's waves request, much of it served by L2 / MALL)
-    per_request = db.B * kv * (2 * row + 4) + 2 * db.B * db.HQ * db.D * 2
+    # the decode's own append: each new token's K and V rows read (bf16) and
+    # written into the pool
+    append = db.B * 2 * (db.HKV * db.D * 2 + row)
+    per_request = db.B * kv * (2 * row + 4) + 2 * db.B * db.HQ * db.D * 2 + append
     # what a step must read at least once: each group's shared part once,
     # every request's own tail, q and o
     distinct = (db.groups * db.shared * 2 * row + db.B * (kv - db.shared) * (2 * row + 4)
-                + 2 * db.B * db.HQ * db.D * 2)
+                + 2 * db.B * db.HQ * db.D * 2 + append)
     achieved = distinct / avg_s / 1e9
     frac = achieved / PEAK_HBM_GBS
     assert frac <= 1.0, f"decode roofline above HBM peak ({frac:.3f}): the byte count is wrong"
@@ -813,7 +820,8 @@ def run_decode_bench(args, torch):
                    "head_dim": db.D, "pool_slots": db.SLOTS, "kv_dtype": "fp8_e4m3" if db.fp8 else "bf16",
                    "shared_decode": bool(db.shared_decode)},
         "roofline": {"bound": "hbm",
-                     "kernel": ("radix_decode_attention_shared" if db.shared_decode else "radix_decode_attention")
+                     "kernel": ("radix_decode_attention_shared_append" if db.shared_decode
+                                else "radix_decode_attention_append")
                                + ("_fp8kv" if db.fp8 else "")
                                + (" (shared pass + private split + combine)" if db.shared_decode
                                   else " (split + combine)") + "; bytes = distinct bytes",
