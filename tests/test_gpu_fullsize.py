@@ -42,10 +42,11 @@ def check_few_shot(fb, i, o_ext, o_dec, prefix_lens):
                                                   ("bf16", 1, True), ("fp8", 1, True)])
 def test_few_shot_full_size_bench_path(kv_dtype, page, shared):
     """64 requests x (1024 shared + 128 distinct) per step, run as bench.py
-    runs them: clocks settled, then five steps back to back with no
-    synchronisation between them (the row sets' staging alternates as in
-    the timed loop); each step's outputs are copied on the step's stream
-    right after its kernels.  Eight requests per step are checked: the extend
+    runs them: warm-up steps, the clock settle that replays the last one's
+    launches, then more steps, all back to back with no synchronisation
+    between them (the row sets' staging alternates as in the timed loop);
+    each step's outputs are copied on the step's stream right after its
+    kernels (the decode with its append folded in).  Eight requests per step are checked: the extend
     rows actually computed and the decode row (bf16 pool, or FP8 E4M3 pool at
     unit scales against attention over the values the FP8 pool holds; token
     slots or pages of 16).  Every suffix starts with its own token, so each
@@ -55,15 +56,19 @@ def test_few_shot_full_size_bench_path(kv_dtype, page, shared):
     fb = bench.FewShotBench(n, torch, B, torch_gen, kv_dtype=kv_dtype, page_size=page, shared_decode=shared)
     fb.gen_inputs(n)
     fb.warm_prefix()
-    fb.settle_clocks(ms=50.0)
     outs = []
     for i in range(n):
         fb.step(i, timed=False)
         with torch.cuda.stream(fb.stream):
             outs.append((fb.o_ext.clone(), fb.o_dec.clone(), fb.last_prefix_lens.copy()))
+        if i == 1:
+            fb.settle_on_step(1, ms=20.0)   # rewrites step 1's rows and outputs with the same values
+            with torch.cuda.stream(fb.stream):
+                outs.append((fb.o_ext.clone(), fb.o_dec.clone(), fb.last_prefix_lens.copy()))
     fb.stream.synchronize()
     worst = 0.0
-    for i, (o_ext, o_dec, pl) in enumerate(outs):
+    steps = [0, 1, 1, 2, 3, 4]   # the third copy: step 1's outputs after the settle's replays
+    for i, (o_ext, o_dec, pl) in zip(steps, outs):
         assert (pl == fb.PREFIX).all()
         res = check_few_shot(fb, i, o_ext.float().cpu().numpy(), o_dec.float().cpu().numpy(), pl)
         print(f"  step {i}: {res}", flush=True)
@@ -86,6 +91,8 @@ def test_decode_full_size_bench_path(name, steps, sample_steps, kv_dtype, shared
     saved = {}
     for s in range(steps):
         db.step(s, timed=False)
+        if s == 3:
+            db.settle_on_step(3, ms=20.0)   # the bench's clock settle: step 3's launches replayed
         if s in sample_steps:
             db.stream.synchronize()
             saved[s] = db.o.float().cpu().numpy()
