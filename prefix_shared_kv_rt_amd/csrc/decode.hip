@@ -1,7 +1,8 @@
 // radix_decode_attention: batched decode attention over the token pool.
 //
 // Each request has one query row (its newest token, whose K/V the scatter
-// kernel already wrote) and attends its whole context: keys 0..prefix_len,
+// kernel already wrote, or, in the _append entry points, the decode launch
+// writes itself) and attends its whole context: keys 0..prefix_len,
 // gathered through the request's req_to_token row (the per-request slot
 // table of the SGLang v0.2 handbook chapter, "CUDA Graph" section).  The
 // cached prefix found by the radix tree is read in place, never recomputed
