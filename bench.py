@@ -485,6 +485,8 @@ def run_few_shot(args, torch):
     ext_ms = [a.elapsed_time(b) for a, b in fb.ext_events]
     dec_avg_s = fb.replay_decode(n - 1)
     ext_avg_s = float(np.mean(ext_ms)) / 1e3
+    dec_traffic = (profiled_traffic("decode_shared_bf16_few_shot")
+                   if fb.shared_decode and not fb.fp8 and args.page_size == 1 else None)
     flops_avg = float(np.mean(fb.flops))
     achieved_tflops = flops_avg / ext_avg_s / 1e12
     result = {
@@ -531,6 +533,9 @@ def run_few_shot(args, torch):
             # bytes the step must read at least once (prefix once, every tail)
             "decode_distinct_gbs": float(np.mean(fb.dec_distinct)) / dec_avg_s / 1e9,
             "decode_distinct_frac": float(np.mean(fb.dec_distinct)) / dec_avg_s / 1e9 / PEAK_HBM_GBS,
+            # the decode call's HBM traffic from the committed counter runs
+            # (None once its sources changed), over the same event time
+            "decode_traffic_frac": (dec_traffic / dec_avg_s / 1e9 / PEAK_HBM_GBS) if dec_traffic else None,
             # host time to run one step's tree work and enqueue its GPU work,
             # without the time blocked waiting for the GPU to release a row
             # set's staging (the step is host-bound when this nears
